@@ -1,0 +1,210 @@
+"""Oracle for the fused multi-tensor Adam / AdamW step (CPU, fp32, scalar).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  It shares
+no code with the HIP library and never imports it.
+
+The element arithmetic lives in ``adam_oracle.c`` (plain C, one IEEE binary32
+operation per printed operation, no fused multiply-add).  This module loads
+it with ctypes and adds the step-level rules around one call:
+
+* the capturable call returns at once when the noop flag is 1, and then the
+  step counter does not move either (apex patch "Enhance Distributed Fused
+  Adam (#1794)": DistAdamCapturableFunctor::operator() returns on noop == 1,
+  and DistributedFusedAdam.step() adds ``noop != 1`` to the counter);
+* otherwise the counter is incremented before the update, so the first
+  update uses t = 1 (apex distributed_fused_adam.py, step());
+* a group with no elements still advances its counter (TransformerEngine PR
+  "Advance FusedAdam step counter for empty param groups", section "Fix").
+
+Arrays are numpy: fp32 as ``float32``, bf16 as raw ``uint16`` bits, the
+remainders as ``int16``.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` to values fixed by
+the pages or by mathematics (closed forms, exact rational arithmetic,
+exhaustive encodings, a float64 library optimizer, a float64 shadow with a
+forward error bound); ``tests/test_oracle_mutants.py`` plants plausible
+mistakes in copies of the C source and checks that the pins catch each one.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_HERE, "liboracle.so")
+
+
+@dataclass
+class HParams:
+    """Per-group hyperparameters; defaults are apex's constructor defaults
+    (apex distributed_fused_adam.py, DistributedFusedAdam.__init__)."""
+
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+    mode: int = 1  # 0 = L2, 1 = AdamW
+    bias_correction: int = 1
+
+
+@dataclass
+class OracleTensor:
+    """One tensor of a group.  For fp32 params ``p`` is float32 and ``rem`` is
+    None; for remainder params ``p`` is bf16 bits (uint16) and ``rem`` int16.
+    ``g`` is float32 or bf16 bits (uint16).  ``p_out`` is bf16 bits or None."""
+
+    p: np.ndarray
+    m: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    p_out: Optional[np.ndarray] = None
+    rem: Optional[np.ndarray] = None
+
+    @property
+    def numel(self) -> int:
+        return int(self.p.size)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be contiguous"
+    return a.ctypes.data
+
+
+class Oracle:
+    """The oracle loaded from one compiled copy of ``adam_oracle.c``."""
+
+    def __init__(self, path: str = LIBRARY_PATH):
+        lib = ctypes.CDLL(path)
+        f32, i32, i64, vp = ctypes.c_float, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        f32p = ctypes.POINTER(ctypes.c_float)
+        lib.oracle_pow_int.argtypes = [ctypes.c_double, i32]
+        lib.oracle_pow_int.restype = ctypes.c_double
+        lib.oracle_bias_corrections.argtypes = [f32, f32, i32, i32, f32p, f32p]
+        lib.oracle_bias_corrections.restype = None
+        lib.oracle_bf16_rne_array.argtypes = [vp, vp, i64]
+        lib.oracle_bf16_rne_array.restype = None
+        lib.oracle_rem_encode_array.argtypes = [vp, vp, vp, i64]
+        lib.oracle_rem_encode_array.restype = None
+        lib.oracle_rem_decode_array.argtypes = [vp, vp, vp, i64]
+        lib.oracle_rem_decode_array.restype = None
+        common = [f32, f32, f32, f32, f32, i32, f32, f32, f32]
+        lib.oracle_adam_f32.argtypes = [vp, vp, vp, vp, i32, vp, i64, *common]
+        lib.oracle_adam_f32.restype = None
+        lib.oracle_adam_remainder.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, *common]
+        lib.oracle_adam_remainder.restype = None
+        self.lib = lib
+        self.path = path
+
+    # -- scalar pieces ------------------------------------------------------
+
+    def pow_int(self, beta: float, t: int) -> float:
+        """beta**t in double by binary exponentiation (1 for t <= 0)."""
+        return self.lib.oracle_pow_int(float(beta), int(t))
+
+    def bias_corrections(self, beta1: float, beta2: float, t: int,
+                         bias_correction: int):
+        """(bc1, bc2) as float32: 1 - beta^t rounded once to float, or 1 when
+        bias correction is off."""
+        b1, b2 = ctypes.c_float(), ctypes.c_float()
+        self.lib.oracle_bias_corrections(beta1, beta2, int(t), int(bias_correction),
+                                         ctypes.byref(b1), ctypes.byref(b2))
+        return np.float32(b1.value), np.float32(b2.value)
+
+    def bf16_rne(self, x: np.ndarray) -> np.ndarray:
+        """float32 array -> bf16 bits (uint16), round to nearest even."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.oracle_bf16_rne_array(_ptr(x), _ptr(out), x.size)
+        return out
+
+    def rem_encode(self, x: np.ndarray):
+        """float32 array -> (bf16 bits uint16, remainder int16)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        hi = np.empty(x.shape, dtype=np.uint16)
+        lo = np.empty(x.shape, dtype=np.int16)
+        self.lib.oracle_rem_encode_array(_ptr(x), _ptr(hi), _ptr(lo), x.size)
+        return hi, lo
+
+    def rem_decode(self, bf16: np.ndarray, rem: np.ndarray) -> np.ndarray:
+        """(bf16 bits, int16 remainder) -> float32 master value."""
+        bf16 = np.ascontiguousarray(bf16, dtype=np.uint16)
+        rem = np.ascontiguousarray(rem, dtype=np.int16)
+        out = np.empty(bf16.shape, dtype=np.float32)
+        self.lib.oracle_rem_decode_array(_ptr(bf16), _ptr(rem), _ptr(out), bf16.size)
+        return out
+
+    # -- one tensor, one call ------------------------------------------------
+
+    def update_tensor(self, t: OracleTensor, hp: HParams, lr: float, bc1, bc2,
+                      grad_scale: float, lo: int = 0, hi: Optional[int] = None) -> None:
+        """Applies the element update to elements [lo, hi) of one tensor."""
+        n = t.numel if hi is None else hi
+        count = n - lo
+        if count <= 0:
+            return
+        assert t.g.dtype in (np.float32, np.uint16)
+        g_is_bf16 = 1 if t.g.dtype == np.uint16 else 0
+        m_ptr = _ptr(t.m) + 4 * lo
+        v_ptr = _ptr(t.v) + 4 * lo
+        g_ptr = _ptr(t.g) + t.g.dtype.itemsize * lo
+        out_ptr = None if t.p_out is None else _ptr(t.p_out) + 2 * lo
+        scal = (float(lr), float(hp.beta1), float(hp.beta2), float(hp.eps),
+                float(hp.weight_decay), int(hp.mode), float(bc1), float(bc2),
+                float(grad_scale))
+        if t.rem is None:
+            assert t.p.dtype == np.float32
+            self.lib.oracle_adam_f32(_ptr(t.p) + 4 * lo, m_ptr, v_ptr, g_ptr,
+                                     g_is_bf16, out_ptr, count, *scal)
+        else:
+            assert t.p.dtype == np.uint16 and t.rem.dtype == np.int16
+            self.lib.oracle_adam_remainder(_ptr(t.p) + 2 * lo, _ptr(t.rem) + 2 * lo,
+                                           m_ptr, v_ptr, g_ptr, g_is_bf16, out_ptr,
+                                           count, *scal)
+
+    # -- one group, one step: the counter and noop rules --------------------
+
+    def group_step(self, tensors: Sequence[OracleTensor], hp: HParams, lr: float,
+                   step: List[int], grad_scale: float = 1.0,
+                   noop: Optional[int] = None) -> bool:
+        """One optimizer step of one group.
+
+        ``step`` is a one-element list holding the group's int32 counter,
+        updated in place.  ``noop`` is None for the non-capturable call, else
+        the device flag's value for the capturable call.  Returns True when
+        the element update ran.
+        """
+        if hp.mode not in (0, 1):
+            raise ValueError("mode must be 0 (L2) or 1 (AdamW)")
+        if hp.bias_correction not in (0, 1):
+            raise ValueError("bias_correction must be 0 or 1")
+        if noop is not None and int(noop) == 1:
+            return False
+        step[0] = ((int(step[0]) + 1 + 2**31) % 2**32) - 2**31  # int32 wrap
+        if sum(t.numel for t in tensors) == 0:
+            return False
+        bc1, bc2 = self.bias_corrections(hp.beta1, hp.beta2, step[0], hp.bias_correction)
+        for t in tensors:
+            self.update_tensor(t, hp, lr, bc1, bc2, grad_scale)
+        return True
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle built from this directory's ``adam_oracle.c``."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY_PATH):
+            from . import build as _build
+
+            _build.build()
+        _default = Oracle(LIBRARY_PATH)
+    return _default

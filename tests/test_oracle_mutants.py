@@ -1,0 +1,71 @@
+"""Mutation test of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake (a dropped term, a wrong sign, a
+transposed operand, an off-by-one, a wrong rounding) in a copy of
+``oracle/adam_oracle.c``, builds the copy into a temporary directory, and
+requires at least one quick pin from tests/pins.py to fail on it.  The real
+oracle must pass all of them.  Nothing here touches the GPU path.
+"""
+import os
+
+import pytest
+
+import pins
+from oracle import Oracle
+from oracle import build as oracle_build
+
+SOURCE = oracle_build.SOURCE
+
+MUTANTS = {
+    "l2_decay_dropped": [("scaled_grad = grad_part + decay_part;", "scaled_grad = grad_part;")],
+    "l2_decay_sign": [("scaled_grad = grad_part + decay_part;", "scaled_grad = grad_part - decay_part;")],
+    "update_sign": [("return P - step;", "return P + step;")],
+    "adamw_decay_dropped": [("update = update + decay_part;", "update = update;")],
+    "adamw_decay_sign": [("update = update + decay_part;", "update = update - decay_part;")],
+    "eps_inside_root": [("sqrtf(v_unbiased) + s->eps", "sqrtf(v_unbiased + s->eps)")],
+    "root_missing": [("sqrtf(v_unbiased) + s->eps", "v_unbiased + s->eps")],
+    "moment_average_transposed": [("float keep = beta * m;", "float keep = beta * x;"),
+                                  ("float take = one_minus_beta * x;", "float take = one_minus_beta * m;")],
+    "second_moment_uses_beta1": [("moment_average(s->beta2, grad_sq, *V)",
+                                  "moment_average(s->beta1, grad_sq, *V)")],
+    "corrections_swapped": [("next_m / s->bc1", "next_m / s->bc2")],
+    "correction_off_by_one": [("oracle_pow_int((double)beta1, t)", "oracle_pow_int((double)beta1, t - 1)")],
+    "power_rounded_to_float": [("oracle_pow_int((double)beta2, t))", "(float)oracle_pow_int((double)beta2, t))")],
+    "correction_flag_ignored": [("if (bias_correction == 1) {", "if (1) {")],
+    "grad_scale_dropped_adamw": [("scaled_grad = G * s->grad_scale;", "scaled_grad = G;")],
+    "grad_scale_dropped_l2": [("float grad_part = G * s->grad_scale;", "float grad_part = G;")],
+    "square_of_raw_grad": [("float grad_sq = scaled_grad * scaled_grad;", "float grad_sq = scaled_grad * G;")],
+    "moments_stored_swapped": [("*M = next_m;\n    *V = next_v;", "*M = next_v;\n    *V = next_m;")],
+    "rne_ties_away": [("(dropped == 0x8000u && (kept & 1u))", "(dropped == 0x8000u)")],
+    "rne_truncates": [("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))", "if (0)")],
+    "nan_not_quieted": [("return (uint16_t)((b >> 16) | 0x0040u);", "return (uint16_t)(b >> 16);")],
+    "decode_sign_fix_dropped": [("(uint16_t)(bf16 - (rem < 0 ? 1u : 0u))", "(uint16_t)(bf16)")],
+    "encode_carry_dropped": [("(uint16_t)(high + (r < 0 ? 1u : 0u))", "(uint16_t)(high)")],
+    "decode_halves_swapped": [("((uint32_t)high << 16) | (uint32_t)low", "((uint32_t)low << 16) | (uint32_t)high")],
+    "param_out_truncated": [("p_out[i] = oracle_bf16_rne(P_new);", "p_out[i] = (uint16_t)(bits_from_f32(P_new) >> 16);")],
+    "remainder_param_out_rne": [("p_out[i] = p[i];", "p_out[i] = oracle_bf16_rne(P_new);")],
+    "bf16_grad_index_shift": [("((const uint16_t *)g)[i]", "((const uint16_t *)g)[i ? i - 1 : 0]")],
+    "one_minus_beta_wrong": [("float one_minus_beta = 1.0f - beta;", "float one_minus_beta = beta - 1.0f;")],
+}
+
+
+def _mutant_library(tmp_path, name):
+    src = open(SOURCE).read()
+    for old, new in MUTANTS[name]:
+        assert src.count(old) == 1, (name, old)
+        src = src.replace(old, new)
+    path = os.path.join(str(tmp_path), f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src)
+    return Oracle(oracle_build.build(source=path, output=os.path.join(str(tmp_path), f"lib{name}.so"),
+                                     werror=False))
+
+
+def test_real_oracle_passes_quick_pins(oracle_default):
+    assert pins.run_quick(oracle_default) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(tmp_path, name):
+    failures = pins.run_quick(_mutant_library(tmp_path, name), stop_at_first=True)
+    assert failures, f"no pin caught the planted mistake {name!r}"

@@ -1,0 +1,259 @@
+"""Seeded synthetic inputs for the fused Adam / AdamW step.
+
+This module only draws numbers and describes shapes; it holds none of the
+update's arithmetic, so the oracle and the HIP path can both be fed from it.
+Shapes and value distributions follow the pages' workloads:
+
+* the benchmark script in TransformerEngine issue "[Performance] FusedAdam
+  capturable kernel is ~1.9x slower than regular Adam on GB300" (201 fp32
+  tensors of 320*65536 elements, p ~ N(0,1), g ~ N(0,1)*1e-3, lr 1.6e-3,
+  betas (0.9, 0.95), eps 1e-8, weight decay 0.1, AdamW);
+* a ragged single-GPU shard of a 30B-class transformer (per-layer matrices,
+  RMSNorm vectors and an embedding), standing in for the Nemotron training
+  run that issue reports on, which is not available here;
+* a ZeRO-style local shard cut into buckets (apex distributed_fused_adam.py,
+  bucket sizes rounded to the 128-byte alignment of the grad-sync dtype);
+* bf16 params with int16 remainders.
+
+Host arrays are numpy (bf16 as raw uint16 bits).  Large inputs are drawn on
+the GPU with torch's generator (see ``device_*`` helpers) so no 100 GB host
+copy is needed; tests that compare such inputs against the oracle copy the
+sampled elements' initial values to the host before the step runs.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Workload descriptions
+# ---------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    sizes: Tuple[int, ...]                 # elements per tensor (group 0)
+    g_dtype: str                           # "f32" or "bf16"
+    p_kind: str                            # "f32" or "bf16_rem"
+    p_out: bool                            # bf16 param-out copy
+    lr: float
+    beta1: float
+    beta2: float
+    eps: float
+    weight_decay: float
+    mode: int                              # 0 = L2, 1 = AdamW
+    grad_scale: float = 1.0
+    grad_multiplier: float = 1.0           # loss scale folded into the grads
+    seed: int = 0
+    extra_groups: Tuple[Tuple[Tuple[int, ...], float], ...] = ()  # (sizes, wd)
+
+    @property
+    def numel(self) -> int:
+        return sum(self.sizes) + sum(sum(s) for s, _ in self.extra_groups)
+
+    @property
+    def bytes_per_elem(self) -> int:
+        """Algorithmic HBM bytes per element: every state word is read once and
+        written once; the gradient is read once."""
+        p = 4 if self.p_kind == "f32" else 4  # fp32 p, or bf16 p + int16 rem
+        g = 4 if self.g_dtype == "f32" else 2
+        read = p + 4 + 4 + g
+        write = p + 4 + 4 + (2 if self.p_out else 0)
+        return read + write
+
+
+TINY_SIZES = (4096, 1000, 7)
+
+TRANSFORMER_LAYERS = 48
+HIDDEN = 4096
+KV_DIM = 1024
+FFN = 14336
+VOCAB = 131072
+
+
+def transformer_shard_sizes() -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
+    """(decay group sizes, no-decay group sizes) of the 30B-class shard: per
+    layer q and o (4096x4096), k and v (4096x1024), two 4096x14336 MLP inputs
+    and one 14336x4096 MLP output, and one 4096 RMSNorm vector; plus a
+    131072x4096 embedding in the decay group."""
+    decay: List[int] = []
+    no_decay: List[int] = []
+    for _ in range(TRANSFORMER_LAYERS):
+        decay += [HIDDEN * HIDDEN, HIDDEN * KV_DIM, HIDDEN * KV_DIM, HIDDEN * HIDDEN,
+                  HIDDEN * FFN, HIDDEN * FFN, FFN * HIDDEN]
+        no_decay.append(HIDDEN)
+    decay.append(VOCAB * HIDDEN)
+    return tuple(decay), tuple(no_decay)
+
+
+def zero_bucket_sizes(total: int = 1_000_000_000, count: int = 2048,
+                      lo: int = 65536, hi: int = 2_097_152, align: int = 64,
+                      seed: int = 4) -> Tuple[int, ...]:
+    """Bucket sizes of a ZeRO local shard: ``count`` sizes drawn log-uniform in
+    [lo, hi], rescaled to sum to ``total``, clamped to the range, rounded to
+    multiples of ``align`` (64 bf16 elements = 128 bytes), with the last
+    bucket absorbing what is left."""
+    rng = np.random.default_rng(seed)
+    raw = np.exp(rng.uniform(math.log(lo), math.log(hi), size=count))
+    raw *= total / raw.sum()
+    sizes = np.clip(np.round(raw / align) * align, lo, hi).astype(np.int64)
+    sizes[-1] += total - int(sizes.sum())
+    assert int(sizes.sum()) == total and sizes[-1] > 0
+    return tuple(int(s) for s in sizes)
+
+
+def ragged_sizes(total: int, count: int, lo: int, hi: int, seed: int) -> Tuple[int, ...]:
+    """Ragged tensor sizes (any residue mod 4), log-uniform in [lo, hi],
+    rescaled to sum to ``total``; the last tensor absorbs the rounding."""
+    rng = np.random.default_rng(seed)
+    raw = np.exp(rng.uniform(math.log(lo), math.log(hi), size=count))
+    raw *= total / raw.sum()
+    sizes = np.maximum(np.floor(raw), 1).astype(np.int64)
+    sizes += rng.integers(0, 4, size=count)  # ragged tails
+    sizes[-1] += total - int(sizes.sum())
+    assert int(sizes.sum()) == total and sizes[-1] > 0
+    return tuple(int(s) for s in sizes)
+
+
+def workloads() -> dict:
+    decay, no_decay = transformer_shard_sizes()
+    return {
+        "tiny": Workload("tiny", TINY_SIZES, "f32", "f32", False,
+                         lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                         weight_decay=0.01, mode=1, seed=1),
+        "bench201": Workload("bench201", (320 * 65536,) * 201, "f32", "f32", False,
+                             lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                             weight_decay=0.1, mode=1, seed=2),
+        "shard30b": Workload("shard30b", decay, "bf16", "f32", False,
+                             lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                             weight_decay=0.1, mode=1, grad_scale=2.0 ** -16,
+                             grad_multiplier=65536.0, seed=3,
+                             extra_groups=((no_decay, 0.0),)),
+        "zero1e9": Workload("zero1e9", zero_bucket_sizes(), "bf16", "f32", True,
+                            lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                            weight_decay=0.1, mode=1, seed=4),
+        "rem5e8": Workload("rem5e8", ragged_sizes(500_000_000, 300, 1, 8_000_000, seed=5),
+                           "bf16", "bf16_rem", False,
+                           lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                           weight_decay=0.1, mode=1, seed=5),
+    }
+
+
+# ---------------------------------------------------------------------------
+# Host (numpy) inputs
+# ---------------------------------------------------------------------------
+
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits with torch's CPU cast (a library conversion: the
+    input generator does not use either side's rounding code)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+@dataclass
+class HostTensor:
+    p: np.ndarray                     # float32, or bf16 bits (uint16)
+    m: np.ndarray                     # float32
+    v: np.ndarray                     # float32
+    g: np.ndarray                     # float32, or bf16 bits (uint16)
+    p_out: Optional[np.ndarray] = None
+    rem: Optional[np.ndarray] = None  # int16
+
+    def copy(self) -> "HostTensor":
+        c = lambda a: None if a is None else a.copy()
+        return HostTensor(c(self.p), c(self.m), c(self.v), c(self.g), c(self.p_out),
+                          c(self.rem))
+
+
+def host_tensors(sizes: Sequence[int], *, g_dtype: str = "f32", p_kind: str = "f32",
+                 p_out: bool = False, seed: int = 0, g_std: float = 1e-3,
+                 g_multiplier: float = 1.0, m_v_init: str = "zero") -> List[HostTensor]:
+    """p ~ N(0,1), g ~ N(0,1)*g_std*g_multiplier.  m = v = 0 by default;
+    ``m_v_init="random"`` draws m ~ N(0,1)*1e-3 and v ~ |N(0,1)|*1e-6 (a
+    state part-way through training).  Remainder params: bf16 p drawn as the
+    cast of N(0,1) and the int16 remainder uniform over all 65536 values, so
+    every (bf16, remainder) pair is a valid master weight."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for n in sizes:
+        p32 = rng.standard_normal(n, dtype=np.float32)
+        g32 = (rng.standard_normal(n, dtype=np.float32) * np.float32(g_std)
+               * np.float32(g_multiplier)).astype(np.float32)
+        if m_v_init == "zero":
+            m = np.zeros(n, np.float32)
+            v = np.zeros(n, np.float32)
+        else:
+            m = (rng.standard_normal(n, dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
+            v = (np.abs(rng.standard_normal(n, dtype=np.float32)) * np.float32(1e-6)).astype(np.float32)
+        g = g32 if g_dtype == "f32" else _to_bf16_bits(g32)
+        rem = None
+        if p_kind == "f32":
+            p = p32
+        else:
+            p = _to_bf16_bits(p32)
+            rem = rng.integers(-32768, 32768, size=n, dtype=np.int64).astype(np.int16)
+        po = np.zeros(n, np.uint16) if p_out else None
+        out.append(HostTensor(p, m, v, g, po, rem))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Device (torch) inputs for full-size workloads
+# ---------------------------------------------------------------------------
+
+
+def device_flat(total: int, *, g_dtype: str, p_kind: str, p_out: bool, seed: int,
+                device="cuda", g_std: float = 1e-3, g_multiplier: float = 1.0,
+                chunk: int = 1 << 28):
+    """Flat device buffers for ``total`` elements, drawn with torch's CUDA
+    generator in chunks: p ~ N(0,1), g ~ N(0,1)*g_std*g_multiplier, m = v = 0.
+    Returns a dict of torch tensors (bf16 kept as torch.bfloat16; remainders
+    as torch.int16)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    bufs = {}
+    if p_kind == "f32":
+        bufs["p"] = torch.empty(total, dtype=torch.float32, device=device)
+    else:
+        bufs["p"] = torch.empty(total, dtype=torch.bfloat16, device=device)
+        bufs["rem"] = torch.empty(total, dtype=torch.int16, device=device)
+    bufs["m"] = torch.zeros(total, dtype=torch.float32, device=device)
+    bufs["v"] = torch.zeros(total, dtype=torch.float32, device=device)
+    bufs["g"] = torch.empty(total, dtype=torch.float32 if g_dtype == "f32" else torch.bfloat16,
+                            device=device)
+    if p_out:
+        bufs["p_out"] = torch.zeros(total, dtype=torch.bfloat16, device=device)
+    scale = float(g_std * g_multiplier)
+    for lo in range(0, total, chunk):
+        hi = min(total, lo + chunk)
+        n = hi - lo
+        tmp = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+        bufs["p"][lo:hi].copy_(tmp)
+        tmp = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+        tmp.mul_(scale)
+        bufs["g"][lo:hi].copy_(tmp)
+        if "rem" in bufs:
+            r = torch.randint(-32768, 32768, (n,), generator=gen, device=device,
+                              dtype=torch.int32)
+            bufs["rem"][lo:hi].copy_(r)
+        del tmp
+    return bufs
+
+
+def split_views(buf, sizes: Sequence[int]):
+    """Contiguous views of a flat buffer, one per tensor size."""
+    views = []
+    off = 0
+    for n in sizes:
+        views.append(buf[off:off + n])
+        off += n
+    return views
