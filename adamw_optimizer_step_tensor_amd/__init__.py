@@ -1,0 +1,290 @@
+"""Python binding of libadamw_mi355x.so: the fused multi-tensor Adam / AdamW
+step on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the update runs in the HIP library
+(``csrc/adam.hip``) behind the C ABI of ``include/adam.h``; the functions here
+carry the same names and turn torch tensors (or raw device addresses) into
+the C structs.  PyTorch provides device memory and streams, nothing else.
+There is no fallback: if the library is missing, importing the binding's
+functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(_PKG, "libadamw_mi355x.so")
+
+ADAM_OK, ADAM_EINVAL, ADAM_EDTYPE, ADAM_ENOMEM, ADAM_EHIP = 0, -1, -2, -3, -4
+DT_NONE, DT_F32, DT_BF16 = 0, 1, 2
+
+c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class AdamTensor(ctypes.Structure):
+    """adam_tensor"""
+    _fields_ = [("p", c_vp), ("rem", c_vp), ("m", c_vp), ("v", c_vp), ("g", c_vp),
+                ("p_out", c_vp), ("numel", c_i64)]
+
+
+class AdamTlDesc(ctypes.Structure):
+    """adam_tl_desc"""
+    _fields_ = [("p", c_i32), ("g", c_i32), ("p_out", c_i32), ("with_remainders", c_i32),
+                ("chunk_elems", c_i64), ("grid_blocks", c_i32), ("reserved", c_i32)]
+
+
+class AdamHParams(ctypes.Structure):
+    """adam_hparams (defaults: apex's constructor defaults)."""
+    _fields_ = [("beta1", c_f32), ("beta2", c_f32), ("eps", c_f32), ("weight_decay", c_f32),
+                ("mode", c_i32), ("bias_correction", c_i32)]
+
+    def __init__(self, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, mode=1,
+                 bias_correction=1):
+        super().__init__(beta1, beta2, eps, weight_decay, mode, bias_correction)
+
+
+class AdamTlStats(ctypes.Structure):
+    """adam_tl_stats"""
+    _fields_ = [("tensors", c_i64), ("nonempty", c_i64), ("chunks", c_i64), ("elements", c_i64),
+                ("chunk_elems", c_i64), ("vector_tensors", c_i64), ("bytes_per_elem", c_i32),
+                ("grid_blocks", c_i32), ("block_threads", c_i32), ("device", c_i32)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class AdamError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {lib().adam_status_string(status).decode()} ({status})")
+
+
+_lib = None
+
+EXPORTED = ("adam_abi_version", "adam_status_string", "adam_tl_plan", "adam_tl_build",
+            "adam_tl_destroy", "adam_tl_info", "adam_step", "adam_step_capturable",
+            "adam_step_remainders")
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY_PATH):
+        raise ImportError(
+            f"{LIBRARY_PATH} is missing: build it with "
+            "`python -m adamw_optimizer_step_tensor_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIBRARY_PATH)
+    L.adam_abi_version.argtypes = []
+    L.adam_abi_version.restype = c_i32
+    L.adam_status_string.argtypes = [c_i32]
+    L.adam_status_string.restype = ctypes.c_char_p
+    L.adam_tl_plan.argtypes = [ctypes.POINTER(AdamTensor), c_i64, ctypes.POINTER(AdamTlDesc),
+                               ctypes.POINTER(AdamTlStats)]
+    L.adam_tl_plan.restype = c_i32
+    L.adam_tl_build.argtypes = [ctypes.POINTER(AdamTensor), c_i64, ctypes.POINTER(AdamTlDesc), c_vp,
+                                ctypes.POINTER(c_vp)]
+    L.adam_tl_build.restype = c_i32
+    L.adam_tl_destroy.argtypes = [c_vp]
+    L.adam_tl_destroy.restype = None
+    L.adam_tl_info.argtypes = [c_vp, ctypes.POINTER(AdamTlStats)]
+    L.adam_tl_info.restype = c_i32
+    L.adam_step.argtypes = [c_vp, ctypes.POINTER(AdamHParams), c_f32, ctypes.POINTER(c_i32), c_f32,
+                            c_vp, c_vp]
+    L.adam_step.restype = c_i32
+    L.adam_step_remainders.argtypes = L.adam_step.argtypes
+    L.adam_step_remainders.restype = c_i32
+    L.adam_step_capturable.argtypes = [c_vp, ctypes.POINTER(AdamHParams), c_vp, c_vp, c_vp, c_vp, c_vp]
+    L.adam_step_capturable.restype = c_i32
+    if L.adam_abi_version() != 1:
+        raise ImportError("libadamw_mi355x.so has an unexpected ABI version")
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------------------
+# Marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _addr(x) -> Optional[int]:
+    """Device address of a torch tensor, or an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _get(t, key):
+    if isinstance(t, dict):
+        return t.get(key)
+    return getattr(t, key, None)
+
+
+def _numel(t) -> int:
+    n = _get(t, "numel")
+    if n is not None and not callable(n):
+        return int(n)
+    p = _get(t, "p")
+    return 0 if p is None else int(p.numel())
+
+
+def _check_tensor(x, name, dtypes, device_type="cuda"):
+    import torch
+
+    if not isinstance(x, torch.Tensor):
+        return
+    if x.device.type != device_type:
+        raise ValueError(f"{name} must be a {device_type} tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if x.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {x.dtype}, expected one of {dtypes}")
+
+
+def _tensor_array(tensors: Sequence, desc: AdamTlDesc):
+    arr = (AdamTensor * max(1, len(tensors)))()
+    torch_dtypes = None
+    try:
+        import torch
+
+        f32, bf16, i16 = torch.float32, torch.bfloat16, torch.int16
+        torch_dtypes = {DT_F32: (f32,), DT_BF16: (bf16, i16)}
+    except ImportError:  # raw addresses only
+        pass
+    for i, t in enumerate(tensors):
+        n = _numel(t)
+        if torch_dtypes is not None:
+            _check_tensor(_get(t, "p"), "p", torch_dtypes[desc.p])
+            _check_tensor(_get(t, "m"), "m", torch_dtypes[DT_F32])
+            _check_tensor(_get(t, "v"), "v", torch_dtypes[DT_F32])
+            _check_tensor(_get(t, "g"), "g", torch_dtypes[desc.g])
+            if _get(t, "p_out") is not None:
+                _check_tensor(_get(t, "p_out"), "p_out", torch_dtypes[DT_BF16])
+            if _get(t, "rem") is not None:
+                _check_tensor(_get(t, "rem"), "rem", torch_dtypes[DT_BF16])
+        arr[i] = AdamTensor(_addr(_get(t, "p")), _addr(_get(t, "rem")), _addr(_get(t, "m")),
+                            _addr(_get(t, "v")), _addr(_get(t, "g")), _addr(_get(t, "p_out")), n)
+    return arr
+
+
+def make_desc(*, g="f32", p="f32", p_out=None, chunk_elems=0, grid_blocks=0) -> AdamTlDesc:
+    """Descriptor from short names: g in {"f32","bf16"}, p in {"f32","bf16_rem"},
+    p_out in {None, "bf16"}."""
+    gd = {"f32": DT_F32, "bf16": DT_BF16}[g]
+    rem = 1 if p == "bf16_rem" else 0
+    pd = DT_BF16 if rem else {"f32": DT_F32}[p]
+    od = {None: DT_NONE, "bf16": DT_BF16}[p_out]
+    return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), int(grid_blocks), 0)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, what: str):
+    if status != ADAM_OK:
+        raise AdamError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# The C ABI, one function each
+# ---------------------------------------------------------------------------
+
+def adam_tl_plan(tensors: Sequence, desc: AdamTlDesc) -> dict:
+    """Host-only validation and planning; returns the statistics dict."""
+    arr = _tensor_array(tensors, desc)
+    st = AdamTlStats()
+    _check(lib().adam_tl_plan(arr, len(tensors), ctypes.byref(desc), ctypes.byref(st)),
+           "adam_tl_plan")
+    return st.as_dict()
+
+
+class TensorList:
+    """Owns an adam_tl handle (and keeps its tensors referenced)."""
+
+    def __init__(self, handle: int, tensors: Sequence, desc: AdamTlDesc):
+        self.handle = handle
+        self._tensors = list(tensors)  # keep the buffers alive
+        self.desc = desc
+
+    def info(self) -> dict:
+        st = AdamTlStats()
+        _check(lib().adam_tl_info(self.handle, ctypes.byref(st)), "adam_tl_info")
+        return st.as_dict()
+
+    def destroy(self):
+        if self.handle:
+            lib().adam_tl_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def adam_tl_build(tensors: Sequence, desc: AdamTlDesc, stream=None) -> TensorList:
+    """Builds a handle for one group (see include/adam.h).  ``tensors`` holds
+    dicts or objects with p, m, v, g and optional rem / p_out (torch tensors
+    or int device addresses plus ``numel``)."""
+    arr = _tensor_array(tensors, desc)
+    out = c_vp()
+    s = _stream(stream) if len(tensors) and any(_numel(t) for t in tensors) else (stream or 0)
+    _check(lib().adam_tl_build(arr, len(tensors), ctypes.byref(desc), s, ctypes.byref(out)),
+           "adam_tl_build")
+    return TensorList(out.value, tensors, desc)
+
+
+class HostStep:
+    """A host int32 step counter (the non-capturable counter)."""
+
+    def __init__(self, value: int = 0):
+        self._c = c_i32(value)
+
+    @property
+    def value(self) -> int:
+        return self._c.value
+
+    @value.setter
+    def value(self, v: int):
+        self._c.value = v
+
+
+def _step_args(tl, hp, lr, step: HostStep, grad_scale, d_grad_scale, stream):
+    s = _stream(stream) if tl.info()["chunks"] else (0 if stream is None else _stream(stream))
+    return (tl.handle, ctypes.byref(hp), float(lr), ctypes.byref(step._c), float(grad_scale),
+            _addr(d_grad_scale), s)
+
+
+def adam_step(tl: TensorList, hp: AdamHParams, lr: float, step: HostStep,
+              grad_scale: float = 1.0, d_grad_scale=None, stream=None) -> None:
+    """Non-capturable step of an fp32-param handle."""
+    _check(lib().adam_step(*_step_args(tl, hp, lr, step, grad_scale, d_grad_scale, stream)),
+           "adam_step")
+
+
+def adam_step_remainders(tl: TensorList, hp: AdamHParams, lr: float, step: HostStep,
+                         grad_scale: float = 1.0, d_grad_scale=None, stream=None) -> None:
+    """Non-capturable step of a bf16 + int16-remainder handle."""
+    _check(lib().adam_step_remainders(*_step_args(tl, hp, lr, step, grad_scale, d_grad_scale,
+                                                  stream)), "adam_step_remainders")
+
+
+def adam_step_capturable(tl: TensorList, hp: AdamHParams, d_lr, d_step, d_grad_scale=None,
+                         d_noop=None, stream=None) -> None:
+    """Capturable step: lr (float32), step (int32), grad scale (float32) and
+    noop flag (int32) are device tensors (or addresses)."""
+    _check(lib().adam_step_capturable(tl.handle, ctypes.byref(hp), _addr(d_lr), _addr(d_step),
+                                      _addr(d_grad_scale), _addr(d_noop), _stream(stream)),
+           "adam_step_capturable")

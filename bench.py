@@ -1,0 +1,303 @@
+"""Benchmark of the fused multi-tensor AdamW step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bench201]
+
+Default workload: 201 fp32 tensors of 320*65536 = 20,971,520 elements
+(4,215,275,520 elements; p, g, m, v fp32), AdamW, lr 1.6e-3, betas
+(0.9, 0.95), eps 1e-8, weight decay 0.1: the shape of the benchmark script in
+TransformerEngine issue "[Performance] FusedAdam capturable kernel is ~1.9x
+slower than regular Adam on GB300".  Inputs are synthetic (p ~ N(0,1),
+g ~ N(0,1)*1e-3, m = v = 0), drawn on the GPU and resident in HBM before the
+timed region.
+
+One step is one call of the library's non-capturable ``adam_step`` over the
+whole list (one launch of the update kernel).  The timed region is exactly K
+steps between two device synchronisations.  ``value`` is effective HBM GB/s
+counting algorithmic bytes (every state word read and written once, the
+gradient read once: 28 B/element here).  The same K steps are also timed for
+the capturable call (device lr/step/grad scale/noop) and for a HIP-graph
+replay of the capturable call; per-launch kernel durations come from HIP
+events recorded on the launch stream around each launch.
+
+The CPU baseline is the oracle (plain scalar C) on a bounded sample of the
+same workload, run on the host's cores (one thread per core, each on a
+contiguous slice).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused AdamW step effective HBM GB/s (% of MI355X peak) and elements/s"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "adamw_optimizer_step_tensor_amd", "csrc", "adam.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none for this workload or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, sample_tensors: int, sample_steps: int) -> dict:
+    """The oracle on `sample_tensors` whole tensors of the workload for
+    `sample_steps` steps, on all host cores (static contiguous slices)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    o = oracle.default()
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    sizes = list(w.sizes[:sample_tensors])
+    n = sum(sizes)
+    rng = np.random.default_rng(w.seed)
+    p = rng.standard_normal(n, dtype=np.float32)
+    g = (rng.standard_normal(n, dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
+    t = oracle.OracleTensor(p, np.zeros(n, np.float32), np.zeros(n, np.float32), g)
+    hp = oracle.HParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
+    bounds = [(i * n // cores, (i + 1) * n // cores) for i in range(cores)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        for step in range(1, sample_steps + 1):
+            bc1, bc2 = o.bias_corrections(w.beta1, w.beta2, step, 1)
+            list(ex.map(lambda b: o.update_tensor(t, hp, w.lr, bc1, bc2, 1.0, b[0], b[1]), bounds))
+    dt = time.perf_counter() - t0
+    gbps = n * sample_steps * w.bytes_per_elem / dt / 1e9
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample_tensors} of {len(w.sizes)} tensors ({n:,} elements) x "
+                      f"{sample_steps} steps, {dt:.2f} s wall",
+            "elements_per_s": round(n * sample_steps / dt, 1), "cpu_model": cpu_model}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="bench201")
+    ap.add_argument("--chunk-elems", type=int, default=0)
+    ap.add_argument("--max-blocks", type=int, default=0)
+    ap.add_argument("--cpu-tensors", type=int, default=8)
+    ap.add_argument("--cpu-steps", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-capturable", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import adamw_optimizer_step_tensor_amd as A
+    from workloads import device_flat, split_views, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    A.lib()
+    w = workloads()[args.workload]
+    groups = [(w.sizes, w.weight_decay)] + list(w.extra_groups)
+    total = w.numel
+    log(f"workload {w.name}: {total:,} elements in {sum(len(s) for s, _ in groups)} tensors, "
+        f"{w.bytes_per_elem} B/elem, {total * w.bytes_per_elem / 1e9:.2f} GB per step")
+
+    t0 = time.perf_counter()
+    bufs = device_flat(total, g_dtype=w.g_dtype, p_kind=w.p_kind, p_out=w.p_out, seed=w.seed,
+                       g_multiplier=w.grad_multiplier)
+    torch.cuda.synchronize()
+    log(f"inputs drawn on the GPU in {time.perf_counter() - t0:.1f} s")
+
+    # one handle per group, views into the flat buffers
+    handles = []
+    off = 0
+    for sizes, wd in groups:
+        n = sum(sizes)
+        views = {k: split_views(v[off:off + n], sizes) for k, v in bufs.items()}
+        tensors = [{k: views[k][i] for k in views} for i in range(len(sizes))]
+        desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out="bf16" if w.p_out else None,
+                           chunk_elems=args.chunk_elems, grid_blocks=args.grid_blocks)
+        tl = A.adam_tl_build(tensors, desc)
+        hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
+        # each group keeps its own counter, host and device
+        handles.append((tl, hp, n, A.HostStep(0), torch.zeros(1, dtype=torch.int32, device="cuda")))
+        off += n
+    info = handles[0][0].info()
+    log(f"work table: {info['chunks']} items of {info['chunk_elems']} elements, grid "
+        f"{info['grid_blocks']} x {info['block_threads']}")
+
+    step_fn = A.adam_step_remainders if w.p_kind == "bf16_rem" else A.adam_step
+    stream = torch.cuda.current_stream()
+    d_scale = torch.tensor([w.grad_scale], dtype=torch.float32, device="cuda")
+
+    def one_step_noncap():
+        for tl, hp, _, host_step, _ in handles:
+            step_fn(tl, hp, w.lr, host_step, 1.0, d_scale, stream)
+
+    def timed(step_once, k, events=True):
+        """Runs k steps between two synchronisations; returns (wall ms per
+        step, mean per-launch event ms of the first handle's launches)."""
+        ev = []
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(k):
+            if events:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                step_once()
+                e1.record(stream)
+                ev.append((e0, e1))
+            else:
+                step_once()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t_start) * 1e3 / k
+        per = [a.elapsed_time(b) for a, b in ev]
+        return wall, per
+
+    # --- non-capturable -----------------------------------------------------
+    for _ in range(args.warmup):
+        one_step_noncap()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+    wall_ms, per_ms = timed(one_step_noncap, args.steps)
+    log(f"non-capturable: {wall_ms:.3f} ms/step wall, event median {statistics.median(per_ms):.3f} ms")
+    bytes_step = total * w.bytes_per_elem
+    gbps = bytes_step / (wall_ms * 1e-3) / 1e9
+    launch_ms = statistics.mean(per_ms)
+    launch_bytes = handles[0][2] * w.bytes_per_elem
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (p~N(0,1), g~N(0,1)*1e-3, m=v=0; drawn on the GPU)",
+        "config": {
+            "workload": f"{w.name}: {len(w.sizes)} tensors, {total:,} elements, "
+                        f"p {w.p_kind}, g {w.g_dtype}, m/v f32, p_out {'bf16' if w.p_out else 'none'}, "
+                        f"{'AdamW' if w.mode else 'L2'}, lr {w.lr}, betas ({w.beta1}, {w.beta2}), "
+                        f"eps {w.eps}, wd {w.weight_decay}",
+            "path": f"{step_fn.__name__} (non-capturable), one launch per group per step",
+            "bytes_per_elem": w.bytes_per_elem,
+            "chunk_elems": info["chunk_elems"],
+            "grid_blocks": info["grid_blocks"],
+            "block_threads": info["block_threads"],
+        },
+        "elements_per_s": round(total / (wall_ms * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "adam_update (fp32 p/m/v, AdamW, non-capturable)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(w.name),
+            "launch_ms_mean": round(launch_ms, 4),
+            "algorithmic_bytes_per_launch": launch_bytes,
+        },
+    }
+
+    # --- capturable, eager and graph -----------------------------------------
+    if not args.no_capturable and w.p_kind == "f32":
+        d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
+        d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+        def one_step_cap(s=stream):
+            for tl, hp, _, _, d_step in handles:
+                A.adam_step_capturable(tl, hp, d_lr, d_step, d_scale, d_noop, s)
+
+        for _ in range(args.warmup):
+            one_step_cap()
+        cap_wall, cap_per = timed(one_step_cap, args.steps)
+        log(f"capturable: {cap_wall:.3f} ms/step wall")
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            one_step_cap(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            one_step_cap(side)
+        torch.cuda.synchronize()
+        g_wall, _ = timed(graph.replay, args.steps, events=False)
+        log(f"graph replay: {g_wall:.3f} ms/step wall")
+        result["capturable"] = {
+            "ms_per_step": round(cap_wall, 4),
+            "value": round(bytes_step / (cap_wall * 1e-3) / 1e9, 2),
+            "launch_ms_mean": round(statistics.mean(cap_per), 4),
+            "vs_noncapturable": round(cap_wall / wall_ms, 4),
+        }
+        result["graph_replay"] = {
+            "ms_per_step": round(g_wall, 4),
+            "value": round(bytes_step / (g_wall * 1e-3) / 1e9, 2),
+            "vs_noncapturable": round(g_wall / wall_ms, 4),
+        }
+
+    for h in handles:
+        h[0].destroy()
+    del bufs
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tensors, len(w.sizes)), args.cpu_steps)
+        log(f"cpu baseline: {result['cpu_baseline']['value']} GB/s on {result['cpu_baseline']['cores']} cores")
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,202 @@
+/*
+ * adam.h - C ABI of libadamw_mi355x.so, the fused multi-tensor Adam / AdamW
+ * parameter update for AMD Instinct MI355X (gfx950).
+ *
+ * The update is the one defined by the apex patch "Enhance Distributed Fused
+ * Adam (#1794)" (multi_tensor_distopt_adam_kernel.cu hunk,
+ * DistAdamCapturableFunctor::local_step and operator()), with the step and
+ * flag rules of apex distributed_fused_adam.py (step(), _local_step,
+ * _local_step_with_param_remainders, _bf16_rem_to_fp32) and the empty-group
+ * counter rule of TransformerEngine PR "Advance FusedAdam step counter for
+ * empty param groups" (section "Fix").  For every element, with t the step
+ * after its increment, s the grad scale, wd the weight decay:
+ *
+ *   x   = g*s            (AdamW, mode 1)   or  g*s + wd*p   (L2, mode 0)
+ *   m'  = beta1*m + (1-beta1)*x
+ *   v'  = beta2*v + (1-beta2)*x*x
+ *   u   = (m'/bc1) / (sqrt(v'/bc2) + eps)        [+ wd*p in mode 1]
+ *   p'  = p - lr*u
+ *
+ * with bc1 = 1-beta1^t, bc2 = 1-beta2^t when bias_correction is 1, else 1.
+ * All arithmetic is IEEE binary32, rounded to nearest-even, in the order
+ * written (no fused multiply-add), with correctly rounded division and
+ * square root and fp32 denormals kept.  beta^t is computed from the float
+ * beta in double by binary exponentiation and 1-beta^t is rounded once to
+ * float.  The library therefore reproduces a scalar C evaluation of these
+ * expressions bit for bit.
+ *
+ * Conventions for every call below:
+ *   - Pointers marked "device" point to GPU memory on the device that was
+ *     current when the handle was built; "host" pointers to CPU memory.
+ *   - Calls return 0 (ADAM_OK) or a negative adam_status; they never throw
+ *     and never abort.  Argument errors are found before anything is
+ *     enqueued and before any counter changes.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs
+ *     asynchronously; faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - bf16 buffers hold raw bfloat16 bit patterns (uint16_t).
+ */
+#ifndef ADAMW_MI355X_ADAM_H
+#define ADAMW_MI355X_ADAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADAM_ABI_VERSION 1
+
+typedef enum {
+    ADAM_OK = 0,
+    ADAM_EINVAL = -1, /* bad argument (null pointer, size, flag value, overlap) */
+    ADAM_EDTYPE = -2, /* dtype combination the library does not implement     */
+    ADAM_ENOMEM = -3, /* device or host allocation failed                     */
+    ADAM_EHIP = -4    /* a HIP runtime call or kernel launch failed           */
+} adam_status;
+
+typedef enum {
+    ADAM_DT_NONE = 0, /* buffer absent (p_out only) */
+    ADAM_DT_F32 = 1,
+    ADAM_DT_BF16 = 2
+} adam_dtype;
+
+/* One tensor of a group: five (six with remainders) flat, dense arrays of
+ * `numel` elements each.  p, m, v (and rem) are read and updated in place;
+ * g is only read; p_out is only written.  The layout is the apex tensor-list
+ * order [p, m, v, g, p_out] (remainder mode: [p, rem, m, v, g, p_out]). */
+typedef struct {
+    void *p;          /* device: float (ADAM_DT_F32) or bf16 bits (remainder mode) */
+    int16_t *rem;     /* device: int16 remainders (remainder mode), else NULL      */
+    float *m;         /* device: first moment, float                               */
+    float *v;         /* device: second moment, float                              */
+    const void *g;    /* device: gradient, float or bf16 bits                      */
+    void *p_out;      /* device: bf16 copy of the new param, or NULL               */
+    int64_t numel;    /* >= 0; a tensor with numel == 0 may have NULL pointers     */
+} adam_tensor;
+
+/* The dtypes shared by every tensor of one handle, and tiling choices. */
+typedef struct {
+    adam_dtype p;            /* ADAM_DT_F32, or ADAM_DT_BF16 with remainders     */
+    adam_dtype g;            /* ADAM_DT_F32 or ADAM_DT_BF16                      */
+    adam_dtype p_out;        /* ADAM_DT_NONE or ADAM_DT_BF16                     */
+    int32_t with_remainders; /* 1: p is bf16 and rem holds the low fp32 halves  */
+    int64_t chunk_elems;     /* elements per work item; 0 = default (16384);
+                                else a positive multiple of 4096, <= 2^30       */
+    int32_t grid_blocks;     /* workgroups per launch; 0 = default (as many as
+                                are resident at once on the device); never more
+                                than the number of work items                   */
+    int32_t reserved;        /* must be 0                                       */
+} adam_tl_desc;
+
+/* Per-group hyperparameters (apex defaults: betas (0.9, 0.999), eps 1e-8,
+ * weight decay 0, AdamW mode, bias correction on). */
+typedef struct {
+    float beta1;
+    float beta2;
+    float eps;
+    float weight_decay;
+    int32_t mode;            /* 0 = L2 (decay in the gradient), 1 = AdamW       */
+    int32_t bias_correction; /* 1 = divide by 1-beta^t, 0 = do not              */
+} adam_hparams;
+
+/* What a handle (or a plan) contains. */
+typedef struct {
+    int64_t tensors;         /* tensors passed in                                 */
+    int64_t nonempty;        /* tensors with numel > 0                            */
+    int64_t chunks;          /* work items                                        */
+    int64_t elements;        /* sum of numel                                      */
+    int64_t chunk_elems;     /* elements per work item                            */
+    int64_t vector_tensors;  /* tensors whose buffers all allow 4-element vectors */
+    int32_t bytes_per_elem;  /* algorithmic HBM bytes per element (read + write)  */
+    int32_t grid_blocks;     /* workgroups per launch (0 from adam_tl_plan)       */
+    int32_t block_threads;   /* threads per workgroup                             */
+    int32_t device;          /* HIP device of the handle (-1 from adam_tl_plan)   */
+} adam_tl_stats;
+
+typedef struct adam_tl adam_tl; /* opaque handle: device work table */
+
+/* ABI version of the loaded library (ADAM_ABI_VERSION). */
+int adam_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char *adam_status_string(int status);
+
+/* Validates a tensor list and computes its work table on the host only (no
+ * HIP call, no allocation); fills *stats (grid_blocks = 0, device = -1).
+ * Errors: ADAM_EINVAL for a NULL desc/stats, count < 0, NULL `tensors` with
+ * count > 0, numel < 0, a NULL required pointer in a non-empty tensor, a
+ * pointer given where the dtype says none, a bad chunk_elems, reserved != 0,
+ * or two buffers that overlap (gradients may overlap other gradients; no
+ * other pair may share a byte); ADAM_EDTYPE for an unsupported dtype set.
+ * Supported sets: p F32, g F32|BF16, p_out NONE|BF16, no remainders; or
+ * p BF16 with remainders, g F32|BF16, p_out NONE|BF16 (apex: bf16 params
+ * need fp32 optimizer state for the remainder scheme). */
+int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
+                 adam_tl_stats *stats);
+
+/* Builds a handle for one group: validates as adam_tl_plan, then copies the
+ * work table (one 64-byte record per chunk) to the current device, using
+ * `stream`, and waits for that copy.  `tensors` (host array of `count`) is
+ * not retained; the device buffers it names must stay allocated and in place
+ * for the handle's life.  On success *out owns device memory; release it with
+ * adam_tl_destroy.  A list whose elements sum to 0 gives a valid handle that
+ * holds no device memory.  Errors: as adam_tl_plan; ADAM_ENOMEM; ADAM_EHIP. */
+int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
+                  hipStream_t stream, adam_tl **out);
+
+/* Frees a handle (NULL is allowed).  Work enqueued with it must be finished. */
+void adam_tl_destroy(adam_tl *tl);
+
+/* Copies a handle's statistics to *stats (host). ADAM_EINVAL on NULL. */
+int adam_tl_info(const adam_tl *tl, adam_tl_stats *stats);
+
+/* Non-capturable step on an fp32-param handle.
+ *   lr          host value.
+ *   step_io     host int32 counter: incremented first (the first update uses
+ *               t = 1), also when the handle has no elements.  ADAM_EINVAL if
+ *               it is INT32_MAX or below 0 (the counter would not give t >= 1).
+ *   grad_scale  host multiplier of the gradient, used when d_grad_scale is
+ *               NULL; d_grad_scale (device float, nullable) is read on the
+ *               device instead (apex passes its grad scale as a device
+ *               tensor).
+ * On ADAM_EHIP from the launch the counter is restored.  Errors: ADAM_EINVAL
+ * (NULL tl/hp/step_io, mode not 0/1, bias_correction not 0/1, a remainder
+ * handle). */
+int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
+              float grad_scale, const float *d_grad_scale, hipStream_t stream);
+
+/* Capturable step on an fp32-param handle: every per-step scalar lives in
+ * device memory, nothing is allocated, nothing is read back, and the host
+ * never waits, so the call can be recorded into a HIP graph and replayed.
+ *   d_lr          device float.
+ *   d_step        device int32 counter; advanced by one on the device after
+ *                 the update, unless *d_noop == 1 (int32 wrap-around).
+ *   d_grad_scale  device float, nullable (NULL = 1.0).
+ *   d_noop        device int32 flag, nullable (NULL = never skip).  When
+ *                 *d_noop == 1 no buffer and not the counter is written; any
+ *                 other value runs the step.
+ * Errors: ADAM_EINVAL (NULL tl/hp/d_lr/d_step, bad mode/flag, remainder
+ * handle); ADAM_EHIP. */
+int adam_step_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
+                         int32_t *d_step, const float *d_grad_scale, const int32_t *d_noop,
+                         hipStream_t stream);
+
+/* Non-capturable step on a remainder handle (bf16 params + int16
+ * remainders, fp32 m and v).  Each element's fp32 master is rebuilt from its
+ * bf16 bits and remainder as apex's _bf16_rem_to_fp32 defines, updated as
+ * above, and stored back in the same encoding (remainder = low 16 bits of the
+ * fp32 word; bf16 = high 16 bits, plus one when that remainder is negative
+ * as an int16, mod 2^16: a round to nearest with ties away from zero).
+ * p_out, if present, receives the new bf16 param bits.  Arguments and errors
+ * as adam_step; ADAM_EINVAL for an fp32-param handle. */
+int adam_step_remainders(const adam_tl *tl, const adam_hparams *hp, float lr,
+                         int32_t *step_io, float grad_scale, const float *d_grad_scale,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADAMW_MI355X_ADAM_H */

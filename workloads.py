@@ -94,28 +94,47 @@ def zero_bucket_sizes(total: int = 1_000_000_000, count: int = 2048,
                       lo: int = 65536, hi: int = 2_097_152, align: int = 64,
                       seed: int = 4) -> Tuple[int, ...]:
     """Bucket sizes of a ZeRO local shard: ``count`` sizes drawn log-uniform in
-    [lo, hi], rescaled to sum to ``total``, clamped to the range, rounded to
-    multiples of ``align`` (64 bf16 elements = 128 bytes), with the last
-    bucket absorbing what is left."""
+    [lo, hi], scaled (and clamped to the range) until they sum to about
+    ``total``, rounded to multiples of ``align`` (64 bf16 elements = 128
+    bytes), then nudged one ``align`` at a time, within the range, until the
+    sum is exactly ``total``."""
+    assert total % align == 0 and lo % align == 0 and hi % align == 0
+    assert lo * count <= total <= hi * count
     rng = np.random.default_rng(seed)
     raw = np.exp(rng.uniform(math.log(lo), math.log(hi), size=count))
-    raw *= total / raw.sum()
-    sizes = np.clip(np.round(raw / align) * align, lo, hi).astype(np.int64)
-    sizes[-1] += total - int(sizes.sum())
-    assert int(sizes.sum()) == total and sizes[-1] > 0
+    f = total / raw.sum()
+    for _ in range(100):
+        cur = np.clip(raw * f, lo, hi)
+        f *= total / cur.sum()
+    units = np.clip(np.round(np.clip(raw * f, lo, hi) / align), lo // align, hi // align).astype(np.int64)
+    diff = total // align - int(units.sum())
+    order = rng.permutation(count)
+    i = 0
+    while diff != 0:
+        k = order[i % count]
+        if diff > 0 and units[k] < hi // align:
+            units[k] += 1
+            diff -= 1
+        elif diff < 0 and units[k] > lo // align:
+            units[k] -= 1
+            diff += 1
+        i += 1
+    sizes = units * align
+    assert int(sizes.sum()) == total and sizes.min() >= lo and sizes.max() <= hi
     return tuple(int(s) for s in sizes)
 
 
 def ragged_sizes(total: int, count: int, lo: int, hi: int, seed: int) -> Tuple[int, ...]:
     """Ragged tensor sizes (any residue mod 4), log-uniform in [lo, hi],
-    rescaled to sum to ``total``; the last tensor absorbs the rounding."""
+    scaled to sum to ``total``; the largest tensor absorbs the rounding."""
     rng = np.random.default_rng(seed)
     raw = np.exp(rng.uniform(math.log(lo), math.log(hi), size=count))
     raw *= total / raw.sum()
     sizes = np.maximum(np.floor(raw), 1).astype(np.int64)
     sizes += rng.integers(0, 4, size=count)  # ragged tails
-    sizes[-1] += total - int(sizes.sum())
-    assert int(sizes.sum()) == total and sizes[-1] > 0
+    big = int(np.argmax(sizes))
+    sizes[big] += total - int(sizes.sum())
+    assert int(sizes.sum()) == total and sizes.min() > 0
     return tuple(int(s) for s in sizes)
 
 
