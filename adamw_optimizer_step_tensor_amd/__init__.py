@@ -32,7 +32,7 @@ class AdamTensor(ctypes.Structure):
 class AdamTlDesc(ctypes.Structure):
     """adam_tl_desc"""
     _fields_ = [("p", c_i32), ("g", c_i32), ("p_out", c_i32), ("with_remainders", c_i32),
-                ("chunk_elems", c_i64), ("grid_blocks", c_i32), ("reserved", c_i32)]
+                ("chunk_elems", c_i64), ("reserved0", c_i32), ("reserved1", c_i32)]
 
 
 class AdamHParams(ctypes.Structure):
@@ -48,8 +48,9 @@ class AdamHParams(ctypes.Structure):
 class AdamTlStats(ctypes.Structure):
     """adam_tl_stats"""
     _fields_ = [("tensors", c_i64), ("nonempty", c_i64), ("chunks", c_i64), ("elements", c_i64),
-                ("chunk_elems", c_i64), ("vector_tensors", c_i64), ("bytes_per_elem", c_i32),
-                ("grid_blocks", c_i32), ("block_threads", c_i32), ("device", c_i32)]
+                ("chunk_elems", c_i64), ("vector_tensors", c_i64), ("grid_blocks", c_i64),
+                ("tile_elems", c_i32), ("block_threads", c_i32), ("bytes_per_elem", c_i32),
+                ("device", c_i32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -158,10 +159,10 @@ def _tensor_array(tensors: Sequence, desc: AdamTlDesc):
     for i, t in enumerate(tensors):
         n = _numel(t)
         if torch_dtypes is not None:
-            _check_tensor(_get(t, "p"), "p", torch_dtypes[desc.p])
+            _check_tensor(_get(t, "p"), "p", torch_dtypes.get(desc.p, ()))
             _check_tensor(_get(t, "m"), "m", torch_dtypes[DT_F32])
             _check_tensor(_get(t, "v"), "v", torch_dtypes[DT_F32])
-            _check_tensor(_get(t, "g"), "g", torch_dtypes[desc.g])
+            _check_tensor(_get(t, "g"), "g", torch_dtypes.get(desc.g, ()))
             if _get(t, "p_out") is not None:
                 _check_tensor(_get(t, "p_out"), "p_out", torch_dtypes[DT_BF16])
             if _get(t, "rem") is not None:
@@ -171,14 +172,14 @@ def _tensor_array(tensors: Sequence, desc: AdamTlDesc):
     return arr
 
 
-def make_desc(*, g="f32", p="f32", p_out=None, chunk_elems=0, grid_blocks=0) -> AdamTlDesc:
+def make_desc(*, g="f32", p="f32", p_out=None, chunk_elems=0) -> AdamTlDesc:
     """Descriptor from short names: g in {"f32","bf16"}, p in {"f32","bf16_rem"},
     p_out in {None, "bf16"}."""
     gd = {"f32": DT_F32, "bf16": DT_BF16}[g]
     rem = 1 if p == "bf16_rem" else 0
     pd = DT_BF16 if rem else {"f32": DT_F32}[p]
     od = {None: DT_NONE, "bf16": DT_BF16}[p_out]
-    return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), int(grid_blocks), 0)
+    return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), 0, 0)
 
 
 def _stream(stream) -> Optional[int]:

@@ -66,6 +66,119 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+PROFILE_COMMANDS = {
+    "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/trace_{w} "
+             "-o run -- python3 <repo>/bench.py --workload {w} --steps 10 --warmup 2 --no-cpu",
+    "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_fetch_{w} "
+             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+    "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc_write_{w} "
+             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+    "summary": "python bench.py --summarize-profiles --workload {w} --trace-dir gpurun_out/trace_{w} "
+               "--fetch-dir gpurun_out/pmc_fetch_{w} --write-dir gpurun_out/pmc_write_{w}",
+}
+
+
+def _short(name: str) -> str:
+    """A readable kernel name: the update kernel with its configuration, other
+    kernels without template arguments (plus the functor they apply)."""
+    import re
+
+    n = name.replace("(anonymous namespace)::", "")
+    if "adam_update" in n:
+        cfg = n[n.index("Config<") + 7:n.index(">")]
+        return f"adam_update<{cfg}>"
+    base = re.split(r"[<(]", n.replace("void ", ""), maxsplit=1)[0]
+    m = re.search(r"(\w+Functor)<", n)
+    return base + (f"[{m.group(1)}]" if m else "")
+
+
+def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> None:
+    """Writes profiles/<kernel>_<workload>_{kernel_trace,pmc}.txt and updates
+    profiles/traffic.json from rocprofv3 CSV output.
+
+    HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the update
+    kernel, each scaled by the factor that makes the same counter agree with
+    the known bytes of the plain elementwise kernel that scales the gradient
+    while the inputs are drawn (torch's in-place multiply: every gradient
+    element read once and written once, fp32)."""
+    import csv
+
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    cmds = {k: v.format(w=w.name) for k, v in PROFILE_COMMANDS.items()}
+
+    # kernel trace summary
+    rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
+    lines = [f"rocprofv3 kernel trace: workload {w.name} ({w.numel:,} elements, "
+             f"{w.bytes_per_elem} B/elem algorithmic = {w.numel * w.bytes_per_elem / 1e9:.3f} GB per step)",
+             f"command: {cmds['trace']}", f"summary: {cmds['summary']}", "",
+             f"{'kernel':62s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} {'max ms':>9s} {'GB/s(avg)':>10s}"]
+    for r in rows:
+        name = _short(r["Name"])
+        avg = float(r["AverageNs"]) / 1e6
+        gbps = ""
+        if name.startswith("adam_update"):
+            gbps = f"{w.numel * w.bytes_per_elem / (avg * 1e-3) / 1e9:10.1f}"
+        lines.append(f"{name:62s} {int(r['Calls']):5d} {avg:9.3f} {float(r['MinNs']) / 1e6:9.3f} "
+                     f"{float(r['MaxNs']) / 1e6:9.3f} {gbps}")
+    trace_path = os.path.join(ROOT, "profiles", f"adam_update_{w.name}_kernel_trace.txt")
+    with open(trace_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    # counters
+    def per_kernel(path):
+        agg = {}
+        for r in csv.DictReader(open(os.path.join(path, "run_counter_collection.csv"))):
+            agg.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return agg
+
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    cal = [k for k in fetch if "AUnaryFunctor" in k]
+    assert cal, "calibration kernel (elementwise multiply) not found"
+    known_kib = w.numel * (4 if w.g_dtype == "f32" else 4) / 1024  # fp32 temp, read once, written once
+    f_factor = known_kib / sum(fetch[cal[0]])
+    w_factor = known_kib / sum(write[cal[0]])
+    upd = [k for k in fetch if k.startswith("adam_update")]
+    assert len(upd) == 1, upd
+    k = upd[0]
+    fetch_kib = statistics.mean(fetch[k])
+    write_kib = statistics.mean(write[k])
+    traffic = (fetch_kib * f_factor + write_kib * w_factor) * 1024
+    n0 = sum(w.sizes)
+    algo = n0 * w.bytes_per_elem
+    lines = [f"rocprofv3 counters: workload {w.name}, kernel {k}",
+             f"command (read): {cmds['fetch']}", f"command (write): {cmds['write']}",
+             f"summary: {cmds['summary']}", "",
+             "per-kernel mean counter value per dispatch (KiB), raw:",
+             f"{'kernel':62s} {'n':>3s} {'FETCH_SIZE':>14s} {'WRITE_SIZE':>14s}"]
+    for name in fetch:
+        lines.append(f"{name:62s} {len(fetch[name]):3d} {statistics.mean(fetch[name]):14.1f} "
+                     f"{statistics.mean(write.get(name, [0])):14.1f}")
+    lines += ["",
+              f"calibration: {cal[0]} moves {known_kib:,.0f} KiB read and {known_kib:,.0f} KiB written in total",
+              f"  (the gradient scaling while inputs are drawn); counters summed over its dispatches give",
+              f"  FETCH factor {f_factor:.4f}, WRITE factor {w_factor:.4f}",
+              f"update kernel per launch: read {fetch_kib * f_factor * 1024 / 1e9:.3f} GB, "
+              f"write {write_kib * w_factor * 1024 / 1e9:.3f} GB, total {traffic / 1e9:.3f} GB",
+              f"algorithmic bytes per launch: {algo / 1e9:.3f} GB ({n0:,} elements x {w.bytes_per_elem} B); "
+              f"measured / algorithmic = {traffic / algo:.4f}",
+              f"kernel source sha256[:16] = {source_hash()}"]
+    pmc_path = os.path.join(ROOT, "profiles", f"adam_update_{w.name}_pmc.txt")
+    with open(pmc_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[w.name] = {"bytes_per_launch": round(traffic), "algorithmic_bytes_per_launch": algo,
+                      "ratio": round(traffic / algo, 5), "fetch_factor": round(f_factor, 5),
+                      "write_factor": round(w_factor, 5), "kernel": k,
+                      "source_sha256_16": source_hash()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+    print("\n".join(open(trace_path).read().splitlines() + [""] + open(pmc_path).read().splitlines()))
+
+
 def cpu_baseline(w, sample_tensors: int, sample_steps: int) -> dict:
     """The oracle on `sample_tensors` whole tensors of the workload for
     `sample_steps` steps, on all host cores (static contiguous slices)."""
@@ -114,12 +227,22 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="bench201")
     ap.add_argument("--chunk-elems", type=int, default=0)
-    ap.add_argument("--max-blocks", type=int, default=0)
     ap.add_argument("--cpu-tensors", type=int, default=8)
     ap.add_argument("--cpu-steps", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-capturable", action="store_true")
+    ap.add_argument("--summarize-profiles", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 CSV directories (no GPU)")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        from workloads import workloads
+
+        summarize_profiles(workloads()[args.workload], args.trace_dir, args.fetch_dir, args.write_dir)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -155,15 +278,16 @@ def main() -> int:
         views = {k: split_views(v[off:off + n], sizes) for k, v in bufs.items()}
         tensors = [{k: views[k][i] for k in views} for i in range(len(sizes))]
         desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out="bf16" if w.p_out else None,
-                           chunk_elems=args.chunk_elems, grid_blocks=args.grid_blocks)
+                           chunk_elems=args.chunk_elems)
         tl = A.adam_tl_build(tensors, desc)
         hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
         # each group keeps its own counter, host and device
         handles.append((tl, hp, n, A.HostStep(0), torch.zeros(1, dtype=torch.int32, device="cuda")))
         off += n
     info = handles[0][0].info()
-    log(f"work table: {info['chunks']} items of {info['chunk_elems']} elements, grid "
-        f"{info['grid_blocks']} x {info['block_threads']}")
+    log(f"work table: {info['chunks']} records of {info['chunk_elems']} elements; "
+        f"{info['grid_blocks']} workgroups of {info['block_threads']} threads, "
+        f"{info['tile_elems']} elements each")
 
     step_fn = A.adam_step_remainders if w.p_kind == "bf16_rem" else A.adam_step
     stream = torch.cuda.current_stream()
@@ -230,6 +354,7 @@ def main() -> int:
             "chunk_elems": info["chunk_elems"],
             "grid_blocks": info["grid_blocks"],
             "block_threads": info["block_threads"],
+            "tile_elems": info["tile_elems"],
         },
         "elements_per_s": round(total / (wall_ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),

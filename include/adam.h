@@ -76,18 +76,20 @@ typedef struct {
     int64_t numel;    /* >= 0; a tensor with numel == 0 may have NULL pointers     */
 } adam_tensor;
 
-/* The dtypes shared by every tensor of one handle, and tiling choices. */
+/* The dtypes shared by every tensor of one handle, and the work-table
+ * granularity. */
 typedef struct {
     adam_dtype p;            /* ADAM_DT_F32, or ADAM_DT_BF16 with remainders     */
     adam_dtype g;            /* ADAM_DT_F32 or ADAM_DT_BF16                      */
     adam_dtype p_out;        /* ADAM_DT_NONE or ADAM_DT_BF16                     */
     int32_t with_remainders; /* 1: p is bf16 and rem holds the low fp32 halves  */
-    int64_t chunk_elems;     /* elements per work item; 0 = default (16384);
-                                else a positive multiple of 4096, <= 2^30       */
-    int32_t grid_blocks;     /* workgroups per launch; 0 = default (as many as
-                                are resident at once on the device); never more
-                                than the number of work items                   */
-    int32_t reserved;        /* must be 0                                       */
+    int64_t chunk_elems;     /* elements per work-table record: 0 = automatic
+                                (the largest power of two <= 65536 that wastes
+                                under 1% of workgroups on ragged tensor ends);
+                                else a power of two from 1024 to 2^30.  Results
+                                do not depend on it.                           */
+    int32_t reserved0;       /* must be 0                                       */
+    int32_t reserved1;       /* must be 0                                       */
 } adam_tl_desc;
 
 /* Per-group hyperparameters (apex defaults: betas (0.9, 0.999), eps 1e-8,
@@ -105,13 +107,14 @@ typedef struct {
 typedef struct {
     int64_t tensors;         /* tensors passed in                                 */
     int64_t nonempty;        /* tensors with numel > 0                            */
-    int64_t chunks;          /* work items                                        */
+    int64_t chunks;          /* work-table records                                */
     int64_t elements;        /* sum of numel                                      */
-    int64_t chunk_elems;     /* elements per work item                            */
+    int64_t chunk_elems;     /* elements per record                               */
     int64_t vector_tensors;  /* tensors whose buffers all allow 4-element vectors */
-    int32_t bytes_per_elem;  /* algorithmic HBM bytes per element (read + write)  */
-    int32_t grid_blocks;     /* workgroups per launch (0 from adam_tl_plan)       */
+    int64_t grid_blocks;     /* workgroups per launch of the update kernel        */
+    int32_t tile_elems;      /* elements per workgroup (one tile)                 */
     int32_t block_threads;   /* threads per workgroup                             */
+    int32_t bytes_per_elem;  /* algorithmic HBM bytes per element (read + write)  */
     int32_t device;          /* HIP device of the handle (-1 from adam_tl_plan)   */
 } adam_tl_stats;
 
@@ -124,7 +127,7 @@ int adam_abi_version(void);
 const char *adam_status_string(int status);
 
 /* Validates a tensor list and computes its work table on the host only (no
- * HIP call, no allocation); fills *stats (grid_blocks = 0, device = -1).
+ * HIP call, no device allocation); fills *stats (device = -1).
  * Errors: ADAM_EINVAL for a NULL desc/stats, count < 0, NULL `tensors` with
  * count > 0, numel < 0, a NULL required pointer in a non-empty tensor, a
  * pointer given where the dtype says none, a bad chunk_elems, reserved != 0,
@@ -137,8 +140,9 @@ int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *
                  adam_tl_stats *stats);
 
 /* Builds a handle for one group: validates as adam_tl_plan, then copies the
- * work table (one 64-byte record per chunk) to the current device, using
- * `stream`, and waits for that copy.  `tensors` (host array of `count`) is
+ * work table (one 64-byte record per chunk, plus a 64-byte scalar block used
+ * by adam_step_capturable) to the current device, using `stream`, and waits
+ * for that copy.  `tensors` (host array of `count`) is
  * not retained; the device buffers it names must stay allocated and in place
  * for the handle's life.  On success *out owns device memory; release it with
  * adam_tl_destroy.  A list whose elements sum to 0 gives a valid handle that
@@ -177,6 +181,10 @@ int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
  *   d_noop        device int32 flag, nullable (NULL = never skip).  When
  *                 *d_noop == 1 no buffer and not the counter is written; any
  *                 other value runs the step.
+ * The call enqueues a one-lane prologue (resolves these scalars and advances
+ * the counter) and then the update, which reads the resolved scalars from
+ * the handle's scalar block; capturable steps of one handle must therefore
+ * be ordered (one stream, or synchronised streams).
  * Errors: ADAM_EINVAL (NULL tl/hp/d_lr/d_step, bad mode/flag, remainder
  * handle); ADAM_EHIP. */
 int adam_step_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,

@@ -74,13 +74,23 @@ def status_of(ts, **kw):
 
 def test_plan_counts_chunks_and_bytes():
     st = plan(fake_tensors([4096, 1000, 7]), chunk_elems=4096)
+    tile = st["tile_elems"]
+    assert tile == 4 * st["block_threads"] and 4096 % tile == 0
     assert st["chunks"] == 3 and st["elements"] == 5103 and st["nonempty"] == 3
     assert st["bytes_per_elem"] == 28 and st["vector_tensors"] == 3
-    assert st["grid_blocks"] == 0 and st["device"] == -1
+    assert st["grid_blocks"] == 3 * (4096 // tile) and st["device"] == -1
     st = plan(fake_tensors([320 * 65536] * 3), chunk_elems=65536)
-    assert st["chunks"] == 3 * 320
-    st = plan(fake_tensors([10, 0, 16385]), chunk_elems=0)
-    assert st["chunk_elems"] == 16384 and st["chunks"] == 1 + 2 and st["nonempty"] == 2
+    assert st["chunks"] == 3 * 320 and st["grid_blocks"] == 3 * 320 * (65536 // tile)
+    # automatic chunk: 64K records when tensors are whole multiples of it ...
+    st = plan(fake_tensors([320 * 65536] * 3))
+    assert st["chunk_elems"] == 65536 and st["grid_blocks"] == 3 * 320 * 65536 // tile
+    # ... and smaller records when ragged ends would leave idle workgroups
+    st = plan(fake_tensors([10, 0, 16385]))
+    need = 1 + -(-16385 // tile)
+    assert st["nonempty"] == 2 and st["grid_blocks"] - need <= max(need // 100, 0)
+    st = plan(fake_tensors([65536 * 100 + 1000] * 4))
+    need = 4 * -(-(65536 * 100 + 1000) // tile)
+    assert st["grid_blocks"] - need <= need // 100
     assert plan(fake_tensors([8]), g="bf16")["bytes_per_elem"] == 26
     assert plan(fake_tensors([8], out=True), g="bf16", p_out="bf16")["bytes_per_elem"] == 28
     assert plan(fake_tensors([8], rem=True), g="bf16", p="bf16_rem")["bytes_per_elem"] == 26
@@ -110,8 +120,10 @@ def test_plan_rejects_bad_arguments():
     assert status_of(fake_tensors([64]), p="bf16_rem") == A.ADAM_EINVAL  # remainder mode, no rem
     assert status_of(fake_tensors([64], out=True)) == A.ADAM_EINVAL   # p_out with p_out NONE
     assert status_of(fake_tensors([64]), p_out="bf16") == A.ADAM_EINVAL
-    for chunk in (-4096, 100, 4095, 4096 * 3 + 1, 1 << 31):
+    for chunk in (-4096, 100, 4095, 4096 * 3 + 1, 3 * 4096, 512, 1 << 31):
         assert status_of(good, chunk_elems=chunk) == A.ADAM_EINVAL, chunk
+    for chunk in (1024, 2048, 1 << 20, 1 << 30):
+        assert status_of(good, chunk_elems=chunk) == 0, chunk
     # an empty tensor may carry null pointers
     empty = [dict(p=None, m=None, v=None, g=None, numel=0)]
     assert plan(empty)["chunks"] == 0
@@ -131,9 +143,10 @@ def test_plan_rejects_unsupported_dtypes():
     st = A.AdamTlStats()
     assert A.lib().adam_tl_plan(A._tensor_array(ts, desc), 1, ctypes.byref(d),
                                 ctypes.byref(st)) == A.ADAM_EINVAL
-    d = A.AdamTlDesc(A.DT_F32, A.DT_F32, A.DT_NONE, 0, 0, 0, 5)  # reserved != 0
-    assert A.lib().adam_tl_plan(A._tensor_array(ts, desc), 1, ctypes.byref(d),
-                                ctypes.byref(st)) == A.ADAM_EINVAL
+    for r0, r1 in ((5, 0), (0, 1)):  # reserved fields must be 0
+        d = A.AdamTlDesc(A.DT_F32, A.DT_F32, A.DT_NONE, 0, 0, r0, r1)
+        assert A.lib().adam_tl_plan(A._tensor_array(ts, desc), 1, ctypes.byref(d),
+                                    ctypes.byref(st)) == A.ADAM_EINVAL
     assert A.lib().adam_tl_plan(None, 1, ctypes.byref(d), ctypes.byref(st)) == A.ADAM_EINVAL
     assert A.lib().adam_tl_plan(None, 0, None, ctypes.byref(st)) == A.ADAM_EINVAL
 

@@ -95,13 +95,13 @@ def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
     assert_bitwise(got, ref, ctx=f"{g_dtype}/{p_kind}/{p_out}/{mode}")
 
 
-def test_results_do_not_depend_on_chunk_or_grid(torch, orc):
-    sizes = [70001, 4096 * 5, 123, 9]
+def test_results_do_not_depend_on_chunk(torch, orc):
+    sizes = [70001, 4096 * 5, 123, 9, 65536 * 2]
     host = host_tensors(sizes, g_dtype="bf16", p_out=True, seed=21, m_v_init="random")
     hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
     results = []
-    for kw in (dict(chunk_elems=4096, grid_blocks=1), dict(chunk_elems=4096),
-               dict(chunk_elems=65536, grid_blocks=7), dict()):
+    for kw in (dict(chunk_elems=1024), dict(chunk_elems=4096), dict(chunk_elems=65536),
+               dict(chunk_elems=1 << 20), dict()):
         got, ref, _, _ = run_both(orc, host, hl, hr, 1.6e-3, 2, desc_kw=kw)
         assert_bitwise(got, ref, ctx=str(kw))
         results.append(got)
