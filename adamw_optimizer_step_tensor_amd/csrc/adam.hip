@@ -27,9 +27,16 @@
 //    201-tensor step).
 //  * Loads and stores carry the non-temporal hint: every byte is touched
 //    exactly once (measured: 10-15% faster than without).
-//  * Tensors whose buffers are not all aligned to 4 elements take a
-//    per-element path (still coalesced, narrower accesses); the ragged tail
-//    of an aligned tensor's last tile is finished element by element.
+//  * Records start on a 128-byte boundary in every stream when one element
+//    index gets there for all of them (true for views at equal offsets into
+//    flat buffers, the usual layout), else on a 4-element boundary: a
+//    tensor's first record carries `head`, the 0..63 leading elements before
+//    that point, which tile 0 of the record updates element by element at
+//    negative indices.  Line-aligned tiles keep two workgroups from writing
+//    parts of one cache line (measured on ragged lists: 4% extra HBM traffic
+//    without it).  Tensors whose streams sit at different phases modulo 4
+//    elements take a per-element path (still coalesced, narrower accesses);
+//    the ragged tail of a body is finished element by element.
 //  * Per-step scalars are kernel arguments (non-capturable).  The capturable
 //    step first runs a one-lane prologue that reads the device lr, step,
 //    grad scale and noop flag, advances the step (unless noop == 1), and
@@ -72,6 +79,8 @@ constexpr int64_t kMaxChunk = int64_t(1) << 30;
 constexpr int64_t kAutoChunkMax = 65536;
 constexpr int64_t kMaxNumel = int64_t(1) << 56;
 constexpr int64_t kMaxGrid = int64_t(1) << 31;
+constexpr int64_t kMaxHead = 63;  // a 2-byte stream reaches a 128-byte boundary within 63 elements
+static_assert(kBlock > kMaxHead, "tile 0 updates the head with one element per lane");
 
 enum : uint32_t { kItemVector = 1u };
 
@@ -86,6 +95,8 @@ struct alignas(64) WorkItem {
     void *p_out;
     int32_t n;       // elements in the run, 1 .. chunk
     uint32_t flags;  // kItemVector: every stream allows 4-element accesses
+    int32_t head;    // elements just before the run, updated by its tile 0 (0..63)
+    int32_t unused;
 };
 static_assert(sizeof(WorkItem) == 64, "work item must be one 64-byte record");
 
@@ -374,6 +385,7 @@ __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict
     const int n = min(kTile, w.n - start);
     const int tid = threadIdx.x;
     if (w.flags & kItemVector) {
+        if (start == 0 && tid < w.head) update_single<C>(w, tid - w.head, c);
         const int nvec = n / kLaneElems;
         if (tid < nvec) {
             update_vector<C>(w, start / kLaneElems + tid, c);
@@ -507,8 +519,8 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
     st.device = -1;
 
     std::vector<Span> spans;
-    std::vector<int64_t> sizes;
-    std::vector<bool> vec_ok;
+    std::vector<int64_t> sizes;   // elements covered by records (a vector body excludes its head)
+    std::vector<int32_t> heads;   // head elements of a vector tensor, -1 for the element path
     spans.reserve(size_t(count) * 6);
     for (int64_t k = 0; k < count; ++k) {
         const adam_tensor &t = tensors[k];
@@ -528,14 +540,27 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
             uintptr_t(t.g) % g_size || (rem && uintptr_t(t.rem) % 2) ||
             (out && uintptr_t(t.p_out) % 2))
             return ADAM_EINVAL;
-        const bool vec = uintptr_t(t.p) % (4 * p_size) == 0 && uintptr_t(t.m) % 16 == 0 &&
-                         uintptr_t(t.v) % 16 == 0 && uintptr_t(t.g) % (4 * g_size) == 0 &&
-                         (!rem || uintptr_t(t.rem) % 8 == 0) && (!out || uintptr_t(t.p_out) % 8 == 0);
+        // the head: fewest leading elements after which every stream is
+        // 128-byte aligned, else 4-element aligned, else none (element path)
+        auto all_aligned = [&](int64_t e, bool line) {
+            auto ok = [&](const void *ptr, size_t size) {
+                const uintptr_t a = uintptr_t(ptr) + uintptr_t(e) * size;
+                return a % (line ? 128u : 4u * size) == 0;
+            };
+            return ok(t.p, p_size) && ok(t.m, 4) && ok(t.v, 4) && ok(t.g, g_size) &&
+                   (!rem || ok(t.rem, 2)) && (!out || ok(t.p_out, 2));
+        };
+        int64_t head = -1;
+        for (int64_t e = 0; e < kMaxHead + 1 && e < t.numel && head < 0; ++e)
+            if (all_aligned(e, true)) head = e;
+        for (int64_t e = 0; e < 4 && e < t.numel && head < 0; ++e)
+            if (all_aligned(e, false)) head = e;
+        const bool vec = head >= 0;
         st.nonempty += 1;
         st.elements += t.numel;
         st.vector_tensors += vec ? 1 : 0;
-        sizes.push_back(t.numel);
-        vec_ok.push_back(vec);
+        sizes.push_back(vec ? t.numel - head : t.numel);
+        heads.push_back(vec ? int32_t(head) : -1);
     }
     if (spans_conflict(spans)) return ADAM_EINVAL;
 
@@ -555,17 +580,21 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
     for (int64_t k = 0; k < count; ++k) {
         const adam_tensor &t = tensors[k];
         if (t.numel == 0) continue;
-        const bool vec = vec_ok[j++];
-        for (int64_t off = 0; off < t.numel; off += chunk) {
+        const int32_t head = heads[j];
+        const int64_t body = sizes[j++];
+        const int64_t first = head > 0 ? head : 0;  // element index where records start
+        for (int64_t off = 0; off < body; off += chunk) {
+            const int64_t e = first + off;
             WorkItem w = {};
-            w.p = static_cast<char *>(t.p) + off * int64_t(p_size);
-            w.rem = rem ? t.rem + off : nullptr;
-            w.m = t.m + off;
-            w.v = t.v + off;
-            w.g = static_cast<const char *>(t.g) + off * int64_t(g_size);
-            w.p_out = out ? static_cast<char *>(t.p_out) + off * 2 : nullptr;
-            w.n = int32_t(std::min(chunk, t.numel - off));
-            w.flags = vec ? kItemVector : 0u;
+            w.p = static_cast<char *>(t.p) + e * int64_t(p_size);
+            w.rem = rem ? t.rem + e : nullptr;
+            w.m = t.m + e;
+            w.v = t.v + e;
+            w.g = static_cast<const char *>(t.g) + e * int64_t(g_size);
+            w.p_out = out ? static_cast<char *>(t.p_out) + e * 2 : nullptr;
+            w.n = int32_t(std::min(chunk, body - off));
+            w.flags = head >= 0 ? kItemVector : 0u;
+            w.head = off == 0 && head > 0 ? head : 0;
             plan.items.push_back(w);
         }
     }

@@ -93,33 +93,49 @@ def _short(name: str) -> str:
 
 
 def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> None:
-    """Writes profiles/<kernel>_<workload>_{kernel_trace,pmc}.txt and updates
-    profiles/traffic.json from rocprofv3 CSV output.
+    """Writes profiles/adam_update_<workload>_{kernel_trace,pmc}.txt and
+    updates profiles/traffic.json from rocprofv3 CSV output.
 
-    HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the update
-    kernel, each scaled by the factor that makes the same counter agree with
-    the known bytes of the plain elementwise kernel that scales the gradient
-    while the inputs are drawn (torch's in-place multiply: every gradient
-    element read once and written once, fp32)."""
+    Durations of the update kernel come from the per-dispatch trace, grouped
+    by kernel configuration and grid size (the largest grid is the workload's
+    main group).  HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of
+    the main group's update dispatches, each scaled by the factor that makes
+    the same counter agree with the known bytes of a plain elementwise kernel
+    in the same run: torch's in-place multiply that scales the gradient while
+    the inputs are drawn, which reads and writes every element of an fp32
+    buffer of the workload's size once."""
     import csv
 
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     cmds = {k: v.format(w=w.name) for k, v in PROFILE_COMMANDS.items()}
+    n0 = sum(w.sizes)
+    algo = n0 * w.bytes_per_elem
 
-    # kernel trace summary
+    # kernel trace: all kernels (stats), then the update kernel per dispatch
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
-    lines = [f"rocprofv3 kernel trace: workload {w.name} ({w.numel:,} elements, "
-             f"{w.bytes_per_elem} B/elem algorithmic = {w.numel * w.bytes_per_elem / 1e9:.3f} GB per step)",
+    lines = [f"rocprofv3 kernel trace: workload {w.name} ({w.numel:,} elements; main group "
+             f"{n0:,} elements x {w.bytes_per_elem} B/elem algorithmic = {algo / 1e9:.3f} GB per launch)",
              f"command: {cmds['trace']}", f"summary: {cmds['summary']}", "",
-             f"{'kernel':62s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} {'max ms':>9s} {'GB/s(avg)':>10s}"]
+             "all kernels (rocprofv3 --stats):",
+             f"{'kernel':62s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} {'max ms':>9s}"]
     for r in rows:
-        name = _short(r["Name"])
-        avg = float(r["AverageNs"]) / 1e6
-        gbps = ""
+        lines.append(f"{_short(r['Name']):62s} {int(r['Calls']):5d} {float(r['AverageNs']) / 1e6:9.3f} "
+                     f"{float(r['MinNs']) / 1e6:9.3f} {float(r['MaxNs']) / 1e6:9.3f}")
+    per = {}
+    for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
+        name = _short(r["Kernel_Name"])
         if name.startswith("adam_update"):
-            gbps = f"{w.numel * w.bytes_per_elem / (avg * 1e-3) / 1e9:10.1f}"
-        lines.append(f"{name:62s} {int(r['Calls']):5d} {avg:9.3f} {float(r['MinNs']) / 1e6:9.3f} "
-                     f"{float(r['MaxNs']) / 1e6:9.3f} {gbps}")
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+            per.setdefault((name, int(r["Grid_Size_X"])), []).append(dur)
+    big = max(g for _, g in per)
+    lines += ["", "update kernel per dispatch (main group = the largest grid):",
+              f"{'kernel':46s} {'grid threads':>13s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} "
+              f"{'max ms':>9s} {'GB/s(avg)':>10s}"]
+    for (name, grid), durs in sorted(per.items()):
+        avg = statistics.mean(durs)
+        gbps = f"{algo / (avg * 1e-3) / 1e9:10.1f}" if grid == big else ""
+        lines.append(f"{name:46s} {grid:13d} {len(durs):5d} {avg:9.3f} {min(durs):9.3f} "
+                     f"{max(durs):9.3f} {gbps}")
     trace_path = os.path.join(ROOT, "profiles", f"adam_update_{w.name}_kernel_trace.txt")
     with open(trace_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -128,24 +144,25 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
     def per_kernel(path):
         agg = {}
         for r in csv.DictReader(open(os.path.join(path, "run_counter_collection.csv"))):
-            agg.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+            name = _short(r["Kernel_Name"])
+            if name.startswith("adam_update") and int(r["Grid_Size"]) != big:
+                name += " (small group)"
+            agg.setdefault(name, []).append(float(r["Counter_Value"]))
         return agg
 
     fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
     cal = [k for k in fetch if "AUnaryFunctor" in k]
     assert cal, "calibration kernel (elementwise multiply) not found"
-    known_kib = w.numel * (4 if w.g_dtype == "f32" else 4) / 1024  # fp32 temp, read once, written once
+    known_kib = w.numel * 4 / 1024  # fp32 temporary of all elements, read once and written once
     f_factor = known_kib / sum(fetch[cal[0]])
     w_factor = known_kib / sum(write[cal[0]])
-    upd = [k for k in fetch if k.startswith("adam_update")]
+    upd = [k for k in fetch if k.startswith("adam_update") and not k.endswith("(small group)")]
     assert len(upd) == 1, upd
     k = upd[0]
     fetch_kib = statistics.mean(fetch[k])
     write_kib = statistics.mean(write[k])
     traffic = (fetch_kib * f_factor + write_kib * w_factor) * 1024
-    n0 = sum(w.sizes)
-    algo = n0 * w.bytes_per_elem
-    lines = [f"rocprofv3 counters: workload {w.name}, kernel {k}",
+    lines = [f"rocprofv3 counters: workload {w.name}, kernel {k} (main group, {n0:,} elements)",
              f"command (read): {cmds['fetch']}", f"command (write): {cmds['write']}",
              f"summary: {cmds['summary']}", "",
              "per-kernel mean counter value per dispatch (KiB), raw:",
@@ -154,7 +171,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
         lines.append(f"{name:62s} {len(fetch[name]):3d} {statistics.mean(fetch[name]):14.1f} "
                      f"{statistics.mean(write.get(name, [0])):14.1f}")
     lines += ["",
-              f"calibration: {cal[0]} moves {known_kib:,.0f} KiB read and {known_kib:,.0f} KiB written in total",
+              f"calibration: {cal[0]} reads and writes {known_kib:,.0f} KiB in total",
               f"  (the gradient scaling while inputs are drawn); counters summed over its dispatches give",
               f"  FETCH factor {f_factor:.4f}, WRITE factor {w_factor:.4f}",
               f"update kernel per launch: read {fetch_kib * f_factor * 1024 / 1e9:.3f} GB, "
@@ -227,8 +244,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="bench201")
     ap.add_argument("--chunk-elems", type=int, default=0)
-    ap.add_argument("--cpu-tensors", type=int, default=8)
-    ap.add_argument("--cpu-steps", type=int, default=4)
+    ap.add_argument("--cpu-tensors", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=12)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-capturable", action="store_true")
     ap.add_argument("--summarize-profiles", action="store_true",
@@ -293,29 +310,37 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     d_scale = torch.tensor([w.grad_scale], dtype=torch.float32, device="cuda")
 
-    def one_step_noncap():
-        for tl, hp, _, host_step, _ in handles:
-            step_fn(tl, hp, w.lr, host_step, 1.0, d_scale, stream)
+    def launch_timed(ev, launch):
+        """Runs launch(); when ev is a list, brackets it with HIP events on the
+        launch stream and appends the pair."""
+        if ev is None:
+            launch()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        ev.append((e0, e1))
+
+    def one_step_noncap(ev=None):
+        """One step: every group once; events bracket the first (largest)
+        group's launch."""
+        for i, (tl, hp, _, host_step, _) in enumerate(handles):
+            launch_timed(ev if i == 0 else None,
+                         lambda: step_fn(tl, hp, w.lr, host_step, 1.0, d_scale, stream))
 
     def timed(step_once, k, events=True):
         """Runs k steps between two synchronisations; returns (wall ms per
-        step, mean per-launch event ms of the first handle's launches)."""
-        ev = []
+        step, per-launch event ms of the first group's launches)."""
+        ev = [] if events else None
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         for _ in range(k):
-            if events:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                step_once()
-                e1.record(stream)
-                ev.append((e0, e1))
-            else:
-                step_once()
+            step_once(ev)
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t_start) * 1e3 / k
-        per = [a.elapsed_time(b) for a, b in ev]
+        per = [a.elapsed_time(b) for a, b in (ev or [])]
         return wall, per
 
     # --- non-capturable -----------------------------------------------------
@@ -360,7 +385,8 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "adam_update (fp32 p/m/v, AdamW, non-capturable)",
+            "kernel": f"adam_update (p {w.p_kind}, g {w.g_dtype}, m/v f32, p_out "
+                      f"{'bf16' if w.p_out else 'none'}, {'AdamW' if w.mode else 'L2'}, non-capturable)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -376,9 +402,10 @@ def main() -> int:
         d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
         d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-        def one_step_cap(s=stream):
-            for tl, hp, _, _, d_step in handles:
-                A.adam_step_capturable(tl, hp, d_lr, d_step, d_scale, d_noop, s)
+        def one_step_cap(ev=None, s=stream):
+            for i, (tl, hp, _, _, d_step) in enumerate(handles):
+                launch_timed(ev if i == 0 else None,
+                             lambda: A.adam_step_capturable(tl, hp, d_lr, d_step, d_scale, d_noop, s))
 
         for _ in range(args.warmup):
             one_step_cap()
@@ -388,13 +415,13 @@ def main() -> int:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            one_step_cap(side)
+            one_step_cap(None, side)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=side):
-            one_step_cap(side)
+            one_step_cap(None, side)
         torch.cuda.synchronize()
-        g_wall, _ = timed(graph.replay, args.steps, events=False)
+        g_wall, _ = timed(lambda ev: graph.replay(), args.steps, events=False)
         log(f"graph replay: {g_wall:.3f} ms/step wall")
         result["capturable"] = {
             "ms_per_step": round(cap_wall, 4),

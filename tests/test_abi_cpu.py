@@ -109,6 +109,29 @@ def test_plan_marks_unaligned_tensors_for_the_element_path():
     assert plan(ts, g="bf16")["vector_tensors"] == 0
 
 
+def test_plan_peels_a_common_phase():
+    """Streams at the same offset modulo 4 elements (views into flat buffers)
+    keep the vector path after a head of up to 3 elements; the records then
+    cover the body only."""
+    one = {"p": 4, "m": 4, "v": 4, "g": 4}
+    st = plan(fake_tensors([100], offsets={0: one}))
+    assert st["vector_tensors"] == 1 and st["elements"] == 100
+    st = plan(fake_tensors([100], offsets={0: {"p": 4, "m": 4, "v": 4, "g": 2}}), g="bf16")
+    assert st["vector_tensors"] == 1
+    st = plan(fake_tensors([100], rem=True, out=True,
+                           offsets={0: {"p": 6, "rem": 6, "m": 12, "v": 12, "g": 6, "p_out": 6}}),
+              g="bf16", p="bf16_rem", p_out="bf16")
+    assert st["vector_tensors"] == 1
+    # a tensor no longer than its head stays on the element path
+    assert plan(fake_tensors([3], offsets={0: one}))["vector_tensors"] == 0
+    assert plan(fake_tensors([4], offsets={0: one}))["vector_tensors"] == 1
+    # records cover the 8192 - 3 body elements of a phase-1 tensor
+    st = plan(fake_tensors([8192], offsets={0: one}), chunk_elems=4096)
+    assert st["chunks"] == 2
+    st = plan(fake_tensors([8195], offsets={0: one}), chunk_elems=4096)
+    assert st["chunks"] == 2
+
+
 def test_plan_rejects_bad_arguments():
     good = fake_tensors([64, 64])
     assert status_of(good) == 0

@@ -95,6 +95,29 @@ def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
     assert_bitwise(got, ref, ctx=f"{g_dtype}/{p_kind}/{p_out}/{mode}")
 
 
+@pytest.mark.parametrize("g_dtype,p_kind,p_out,mode", [
+    ("f32", "f32", False, 1), ("bf16", "f32", True, 0), ("bf16", "bf16_rem", False, 1),
+    ("f32", "bf16_rem", True, 1)])
+def test_shared_offsets_take_the_peeled_vector_path(torch, orc, g_dtype, p_kind, p_out, mode):
+    """Every stream of a tensor at the same element offset 0..7 (views at one
+    offset into flat buffers): the 0..3 leading elements are peeled and the
+    rest vectorised; results stay bit-identical to the oracle."""
+    sizes = list(range(0, 20)) + [1021, 4095, 4099, 8193, 70001]
+    host = host_tensors(sizes, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=31,
+                        m_v_init="random")
+    roles = ("p", "rem", "m", "v", "g", "p_out")
+    offsets = [{r: k % 8 for r in roles} for k in range(len(sizes))]
+    desc = desc_for(host, chunk_elems=4096)
+    dev = DeviceSet(host, offsets)
+    st = A.adam_tl_build(dev.tensors, desc).info()
+    assert st["vector_tensors"] == sum(1 for k, n in enumerate(sizes) if n > (4 - k % 4) % 4)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    got, ref, s, rs = run_both(orc, host, hl, hr, 1.6e-3, 3, grad_scale=0.5,
+                               desc_kw=dict(chunk_elems=4096), offsets=offsets)
+    assert s == rs == 3
+    assert_bitwise(got, ref, ctx=f"{g_dtype}/{p_kind}/{p_out}/{mode}")
+
+
 def test_results_do_not_depend_on_chunk(torch, orc):
     sizes = [70001, 4096 * 5, 123, 9, 65536 * 2]
     host = host_tensors(sizes, g_dtype="bf16", p_out=True, seed=21, m_v_init="random")
