@@ -196,30 +196,40 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
     print("\n".join(open(trace_path).read().splitlines() + [""] + open(pmc_path).read().splitlines()))
 
 
-def cpu_baseline(w, sample_tensors: int, sample_steps: int) -> dict:
-    """The oracle on `sample_tensors` whole tensors of the workload for
-    `sample_steps` steps, on all host cores (static contiguous slices)."""
+def cpu_baseline(w, sample_elems: int, sample_steps: int) -> dict:
+    """The oracle on whole tensors from the start of the workload's list (at
+    least `sample_elems` elements, with the workload's dtypes) for
+    `sample_steps` steps, on the host's cores: one thread per core, each on
+    a contiguous slice of the concatenated sample."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
 
     import oracle
+    from workloads import host_tensors
 
     o = oracle.default()
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
-    sizes = list(w.sizes[:sample_tensors])
-    n = sum(sizes)
-    rng = np.random.default_rng(w.seed)
-    p = rng.standard_normal(n, dtype=np.float32)
-    g = (rng.standard_normal(n, dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
-    t = oracle.OracleTensor(p, np.zeros(n, np.float32), np.zeros(n, np.float32), g)
+    sizes = []
+    for n in w.sizes:
+        sizes.append(n)
+        if sum(sizes) >= sample_elems:
+            break
+    host = host_tensors(sizes, g_dtype=w.g_dtype, p_kind=w.p_kind, p_out=w.p_out, seed=w.seed,
+                        g_multiplier=w.grad_multiplier)
+    cat = lambda role: (None if getattr(host[0], role) is None
+                        else np.concatenate([getattr(h, role) for h in host]))
+    t = oracle.OracleTensor(cat("p"), cat("m"), cat("v"), cat("g"), cat("p_out"), cat("rem"))
+    del host
+    n = t.numel
     hp = oracle.HParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
     bounds = [(i * n // cores, (i + 1) * n // cores) for i in range(cores)]
     t0 = time.perf_counter()
     with ThreadPoolExecutor(cores) as ex:
         for step in range(1, sample_steps + 1):
             bc1, bc2 = o.bias_corrections(w.beta1, w.beta2, step, 1)
-            list(ex.map(lambda b: o.update_tensor(t, hp, w.lr, bc1, bc2, 1.0, b[0], b[1]), bounds))
+            list(ex.map(lambda b: o.update_tensor(t, hp, w.lr, bc1, bc2, w.grad_scale, b[0], b[1]),
+                        bounds))
     dt = time.perf_counter() - t0
     gbps = n * sample_steps * w.bytes_per_elem / dt / 1e9
     cpu_model = ""
@@ -232,8 +242,8 @@ def cpu_baseline(w, sample_tensors: int, sample_steps: int) -> dict:
     except OSError:
         pass
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{sample_tensors} of {len(w.sizes)} tensors ({n:,} elements) x "
-                      f"{sample_steps} steps, {dt:.2f} s wall",
+            "sample": f"first {len(sizes)} of {len(w.sizes)} tensors ({n:,} elements, workload dtypes) x "
+                      f"{sample_steps} steps: {n * sample_steps:,} element updates in {dt:.2f} s wall",
             "elements_per_s": round(n * sample_steps / dt, 1), "cpu_model": cpu_model}
 
 
@@ -244,8 +254,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="bench201")
     ap.add_argument("--chunk-elems", type=int, default=0)
-    ap.add_argument("--cpu-tensors", type=int, default=16)
-    ap.add_argument("--cpu-steps", type=int, default=12)
+    ap.add_argument("--cpu-elements", type=int, default=200_000_000)
+    ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-capturable", action="store_true")
     ap.add_argument("--summarize-profiles", action="store_true",
@@ -442,7 +452,7 @@ def main() -> int:
 
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tensors, len(w.sizes)), args.cpu_steps)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_elements, args.cpu_steps)
         log(f"cpu baseline: {result['cpu_baseline']['value']} GB/s on {result['cpu_baseline']['cores']} cores")
     else:
         result["cpu_baseline"] = None
