@@ -66,7 +66,7 @@ _lib = None
 
 EXPORTED = ("adam_abi_version", "adam_status_string", "adam_tl_plan", "adam_tl_build",
             "adam_tl_destroy", "adam_tl_info", "adam_step", "adam_step_capturable",
-            "adam_step_remainders")
+            "adam_step_remainders", "adam_grad_sumsq", "adam_clip_grad_scale")
 
 
 def lib():
@@ -100,6 +100,10 @@ def lib():
     L.adam_step_remainders.restype = c_i32
     L.adam_step_capturable.argtypes = [c_vp, ctypes.POINTER(AdamHParams), c_vp, c_vp, c_vp, c_vp, c_vp]
     L.adam_step_capturable.restype = c_i32
+    L.adam_grad_sumsq.argtypes = [c_vp, c_vp, c_i32, c_vp]
+    L.adam_grad_sumsq.restype = c_i32
+    L.adam_clip_grad_scale.argtypes = [c_vp, c_vp, c_f32, c_vp, c_vp, c_vp]
+    L.adam_clip_grad_scale.restype = c_i32
     if L.adam_abi_version() != 1:
         raise ImportError("libadamw_mi355x.so has an unexpected ABI version")
     _lib = L
@@ -289,3 +293,20 @@ def adam_step_capturable(tl: TensorList, hp: AdamHParams, d_lr, d_step, d_grad_s
     _check(lib().adam_step_capturable(tl.handle, ctypes.byref(hp), _addr(d_lr), _addr(d_step),
                                       _addr(d_grad_scale), _addr(d_noop), _stream(stream)),
            "adam_step_capturable")
+
+
+def adam_grad_sumsq(tl: TensorList, d_sumsq, accumulate: bool = False, stream=None) -> None:
+    """*d_sumsq (device float64) = (accumulate ? *d_sumsq : 0) + the sum of
+    squares of the handle's gradients."""
+    _check(lib().adam_grad_sumsq(tl.handle, _addr(d_sumsq), 1 if accumulate else 0, _stream(stream)),
+           "adam_grad_sumsq")
+
+
+def adam_clip_grad_scale(d_sumsq, d_grad_scale=None, max_norm: float = 0.0, d_norm=None,
+                         d_noop=None, stream=None) -> None:
+    """Norm, found-inf flag and clipped grad scale from a sum of squares
+    (device scalars; see include/adam.h)."""
+    _check(lib().adam_clip_grad_scale(_addr(d_sumsq), _addr(d_grad_scale), float(max_norm),
+                                      _addr(d_norm), _addr(d_noop), _stream(stream)),
+           "adam_clip_grad_scale")
+

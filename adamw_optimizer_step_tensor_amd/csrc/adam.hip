@@ -69,11 +69,12 @@
 #define ADAM_XCD_RUN 64
 #endif
 
+
 namespace {
 
 constexpr int kBlock = ADAM_BLOCK;          // threads per workgroup
 constexpr int kLaneElems = 4;               // elements per lane per access
-constexpr int kTile = kBlock * kLaneElems;  // elements per workgroup
+constexpr int kTile = kBlock * kLaneElems;  // elements per workgroup: one vector per lane
 constexpr int64_t kMinChunk = kTile > 1024 ? kTile : 1024;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
 constexpr int64_t kAutoChunkMax = 65536;
@@ -251,53 +252,66 @@ struct Config {
     static constexpr bool capturable = CAPT;
 };
 
-// Four consecutive elements of one lane, updated in registers.
+// Four consecutive elements of one lane.
+struct Lane4 {
+    float p[4], m[4], v[4], g[4];
+};
+
 template <class C>
-__device__ __forceinline__ void update_vector(const WorkItem &w, int vi, const Coeffs &c)
+__device__ __forceinline__ void load_lane(Lane4 &q, const WorkItem &w, int vi)
 {
-    // all loads first, so the lane has every stream's request in flight
     const f32x4 m4 = load_stream<f32x4>(w.m, vi);
     const f32x4 v4 = load_stream<f32x4>(w.v, vi);
-    float g[4], p[4], m[4] = {m4.x, m4.y, m4.z, m4.w}, v[4] = {v4.x, v4.y, v4.z, v4.w};
+    q.m[0] = m4.x; q.m[1] = m4.y; q.m[2] = m4.z; q.m[3] = m4.w;
+    q.v[0] = v4.x; q.v[1] = v4.y; q.v[2] = v4.z; q.v[3] = v4.w;
     if constexpr (C::g_bf16) {
         const u32x2 gb = load_stream<u32x2>(w.g, vi);
-        g[0] = __uint_as_float(gb.x << 16);
-        g[1] = __uint_as_float(gb.x & 0xFFFF0000u);
-        g[2] = __uint_as_float(gb.y << 16);
-        g[3] = __uint_as_float(gb.y & 0xFFFF0000u);
+        q.g[0] = __uint_as_float(gb.x << 16);
+        q.g[1] = __uint_as_float(gb.x & 0xFFFF0000u);
+        q.g[2] = __uint_as_float(gb.y << 16);
+        q.g[3] = __uint_as_float(gb.y & 0xFFFF0000u);
     } else {
         const f32x4 g4 = load_stream<f32x4>(w.g, vi);
-        g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
+        q.g[0] = g4.x; q.g[1] = g4.y; q.g[2] = g4.z; q.g[3] = g4.w;
     }
     if constexpr (C::p_rem) {
         const u32x2 h = load_stream<u32x2>(w.p, vi);
         const u32x2 r = load_stream<u32x2>(w.rem, vi);
-        p[0] = master_from(h.x & 0xFFFFu, r.x & 0xFFFFu);
-        p[1] = master_from(h.x >> 16, r.x >> 16);
-        p[2] = master_from(h.y & 0xFFFFu, r.y & 0xFFFFu);
-        p[3] = master_from(h.y >> 16, r.y >> 16);
+        q.p[0] = master_from(h.x & 0xFFFFu, r.x & 0xFFFFu);
+        q.p[1] = master_from(h.x >> 16, r.x >> 16);
+        q.p[2] = master_from(h.y & 0xFFFFu, r.y & 0xFFFFu);
+        q.p[3] = master_from(h.y >> 16, r.y >> 16);
     } else {
         const f32x4 p4 = load_stream<f32x4>(w.p, vi);
-        p[0] = p4.x; p[1] = p4.y; p[2] = p4.z; p[3] = p4.w;
+        q.p[0] = p4.x; q.p[1] = p4.y; q.p[2] = p4.z; q.p[3] = p4.w;
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) p[k] = update_element<C::mode>(p[k], g[k], m[k], v[k], c);
+}
 
-    store_stream<f32x4>(w.m, vi, f32x4{m[0], m[1], m[2], m[3]});
-    store_stream<f32x4>(w.v, vi, f32x4{v[0], v[1], v[2], v[3]});
+template <class C>
+__device__ __forceinline__ void compute_lane(Lane4 &q, const Coeffs &c)
+{
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q.p[k] = update_element<C::mode>(q.p[k], q.g[k], q.m[k], q.v[k], c);
+}
+
+template <class C>
+__device__ __forceinline__ void store_lane(const Lane4 &q, const WorkItem &w, int vi)
+{
+    store_stream<f32x4>(w.m, vi, f32x4{q.m[0], q.m[1], q.m[2], q.m[3]});
+    store_stream<f32x4>(w.v, vi, f32x4{q.v[0], q.v[1], q.v[2], q.v[3]});
     if constexpr (C::p_rem) {
         uint32_t h[4], r[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) master_to(p[k], h[k], r[k]);
+        for (int k = 0; k < 4; ++k) master_to(q.p[k], h[k], r[k]);
         const u32x2 hv = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
         store_stream<u32x2>(w.p, vi, hv);
         store_stream<u32x2>(w.rem, vi, u32x2{r[0] | (r[1] << 16), r[2] | (r[3] << 16)});
         if constexpr (C::out) store_stream<u32x2>(w.p_out, vi, hv);
     } else {
-        store_stream<f32x4>(w.p, vi, f32x4{p[0], p[1], p[2], p[3]});
+        store_stream<f32x4>(w.p, vi, f32x4{q.p[0], q.p[1], q.p[2], q.p[3]});
         if constexpr (C::out) {
-            const u32x2 o = u32x2{bf16_bits_rne(p[0]) | (bf16_bits_rne(p[1]) << 16),
-                                  bf16_bits_rne(p[2]) | (bf16_bits_rne(p[3]) << 16)};
+            const u32x2 o = u32x2{bf16_bits_rne(q.p[0]) | (bf16_bits_rne(q.p[1]) << 16),
+                                  bf16_bits_rne(q.p[2]) | (bf16_bits_rne(q.p[3]) << 16)};
             store_stream<u32x2>(w.p_out, vi, o);
         }
     }
@@ -387,11 +401,15 @@ __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict
     if (w.flags & kItemVector) {
         if (start == 0 && tid < w.head) update_single<C>(w, tid - w.head, c);
         const int nvec = n / kLaneElems;
+        const int base = start / kLaneElems;
         if (tid < nvec) {
-            update_vector<C>(w, start / kLaneElems + tid, c);
-        } else if (tid < nvec + (n - nvec * kLaneElems)) {
-            update_single<C>(w, start + nvec * kLaneElems + (tid - nvec), c);
+            Lane4 q;
+            load_lane<C>(q, w, base + tid);
+            compute_lane<C>(q, c);
+            store_lane<C>(q, w, base + tid);
         }
+        // the 0..3 elements after the last whole vector of a ragged tile
+        if (tid < n - nvec * kLaneElems) update_single<C>(w, start + nvec * kLaneElems + tid, c);
     } else {
         for (int i = tid; i < n; i += kBlock) update_single<C>(w, start + i, c);
     }
@@ -416,6 +434,130 @@ __global__ void adam_capture_prologue(StepBlock *block, const float *d_lr, int32
     s.scale = d_grad_scale != nullptr ? *d_grad_scale : 1.0f;
     corrections(beta1, beta2, t, bias_correction, s.bc1, s.bc2);
     *block = s;
+}
+
+// ---------------------------------------------------------------------------
+// Gradient sum of squares and the clip / found-inf step (apex
+// distributed_fused_adam.py: grad_norm, clip_grad_norm, the found-inf check
+// of step()).  Squares of float or bf16 gradients are exact in double; every
+// workgroup adds its squares in a fixed order, partial sums are folded in a
+// fixed order, so the result does not depend on scheduling.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNormRun = kXcdRun;  // tiles per reduction workgroup (the XCD run)
+constexpr int kNormUnroll = 4;          // tiles whose loads are in flight together
+constexpr int kFoldBlock = 256;
+
+// The gradient values lane `tid` owns in tile t, as floats (zeros where the
+// lane owns nothing): up to four in g, plus one head element (tile 0 of a
+// record with a head) and one element of a ragged tail in `extra`.
+template <bool G_BF16>
+__device__ __forceinline__ void tile_grads(const WorkItem *__restrict__ items, uint32_t shift,
+                                           uint32_t t, uint32_t last, int tid, float g[4],
+                                           float extra[2])
+{
+    g[0] = g[1] = g[2] = g[3] = 0.0f;
+    extra[0] = extra[1] = 0.0f;
+    if (t >= last) return;
+    const WorkItem w = items[t >> shift];
+    const int start = int(t & ((1u << shift) - 1u)) * kTile;
+    if (start >= w.n) return;
+    const int n = min(kTile, w.n - start);
+    auto one = [&](int i) {
+        return G_BF16 ? __uint_as_float(uint32_t(load_one<uint16_t>(w.g, i)) << 16) : load_one<float>(w.g, i);
+    };
+    if (w.flags & kItemVector) {
+        if (start == 0 && tid < w.head) extra[0] = one(tid - w.head);
+        const int nvec = n / kLaneElems;
+        if (tid < nvec) {
+            const int vi = start / kLaneElems + tid;
+            if constexpr (G_BF16) {
+                const u32x2 gb = load_stream<u32x2>(w.g, vi);
+                g[0] = __uint_as_float(gb.x << 16);
+                g[1] = __uint_as_float(gb.x & 0xFFFF0000u);
+                g[2] = __uint_as_float(gb.y << 16);
+                g[3] = __uint_as_float(gb.y & 0xFFFF0000u);
+            } else {
+                const f32x4 g4 = load_stream<f32x4>(w.g, vi);
+                g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
+            }
+        }
+        if (tid < n - nvec * kLaneElems) extra[1] = one(start + nvec * kLaneElems + tid);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kLaneElems; ++k)
+            if (tid + k * kBlock < n) g[k] = one(start + tid + k * kBlock);
+    }
+}
+
+// Sum over a workgroup of one double per lane, in a fixed tree order.
+template <int BLOCK>
+__device__ __forceinline__ double block_sum(double x)
+{
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    __shared__ double wave_sums[BLOCK / 64];
+    if (threadIdx.x % 64 == 0) wave_sums[threadIdx.x / 64] = x;
+    __syncthreads();
+    double total = 0.0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < BLOCK / 64; ++i) total += wave_sums[i];
+    return total;  // meaningful in thread 0
+}
+
+// Workgroup b adds the squares of the gradients of tiles [b*kNormRun,
+// (b+1)*kNormRun) and writes one partial sum.
+template <bool G_BF16>
+__global__ __launch_bounds__(kBlock) void grad_sumsq_partial(const WorkItem *__restrict__ items,
+                                                              uint32_t shift, uint32_t tiles,
+                                                              double *__restrict__ partials)
+{
+    const uint32_t first = blockIdx.x * kNormRun;
+    const uint32_t last = min(first + kNormRun, tiles);
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    for (uint32_t t0 = first; t0 < last; t0 += kNormUnroll) {
+        float g[kNormUnroll][4], extra[kNormUnroll][2];
+#pragma unroll
+        for (int u = 0; u < kNormUnroll; ++u) tile_grads<G_BF16>(items, shift, t0 + u, last, tid, g[u], extra[u]);
+#pragma unroll
+        for (int u = 0; u < kNormUnroll; ++u) {
+            acc += double(extra[u][0]) * double(extra[u][0]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc += double(g[u][k]) * double(g[u][k]);
+            acc += double(extra[u][1]) * double(extra[u][1]);
+        }
+    }
+    const double total = block_sum<kBlock>(acc);
+    if (tid == 0) partials[blockIdx.x] = total;
+}
+
+// One workgroup: *d_sumsq = (accumulate ? *d_sumsq : 0) + the partial sums.
+__global__ __launch_bounds__(kFoldBlock) void grad_sumsq_fold(const double *__restrict__ partials,
+                                                              uint32_t count, double *d_sumsq,
+                                                              int32_t accumulate)
+{
+    double acc = 0.0;
+    for (uint32_t i = threadIdx.x; i < count; i += kFoldBlock) acc += partials[i];
+    const double total = block_sum<kFoldBlock>(acc);
+    if (threadIdx.x == 0) *d_sumsq = (accumulate ? *d_sumsq : 0.0) + total;
+}
+
+// One lane: the norm, the found-inf flag and the clipped grad scale, in
+// float as the pages' tensors are.
+__global__ void clip_grad_scale_kernel(const double *d_sumsq, float *d_grad_scale, float max_norm,
+                                       float *d_norm, int32_t *d_noop)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    const float raw = float(sqrt(*d_sumsq));
+    const float scale = d_grad_scale != nullptr ? *d_grad_scale : 1.0f;
+    const float norm = raw * scale;
+    const bool found_inf = !isfinite(norm);
+    if (d_norm != nullptr) *d_norm = norm;
+    if (d_noop != nullptr) *d_noop = found_inf ? 1 : 0;
+    if (!found_inf && max_norm > 0.0f && d_grad_scale != nullptr) {
+        float coef = max_norm / (norm + 1e-6f);
+        if (coef > 1.0f) coef = 1.0f;
+        *d_grad_scale = scale * coef;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -636,6 +778,8 @@ struct adam_tl {
     bool out;
     WorkItem *d_items;   // device table, null when there is no work
     StepBlock *d_block;  // device scalar block of the capturable step (after the table)
+    double *d_partials;  // reduction partial sums (after the block), one per kNormRun tiles
+    uint32_t n_partials;
 };
 
 namespace {
@@ -729,6 +873,8 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     tl->out = desc->p_out == ADAM_DT_BF16;
     tl->d_items = nullptr;
     tl->d_block = nullptr;
+    tl->d_partials = nullptr;
+    tl->n_partials = 0;
     if (plan.items.empty()) {  // nothing to launch: no device state at all
         *out = tl;
         return ADAM_OK;
@@ -741,14 +887,17 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     }
     tl->stats.device = device;
     const size_t table_bytes = plan.items.size() * sizeof(WorkItem);
+    tl->n_partials = uint32_t((tl->stats.grid_blocks + kNormRun - 1) / kNormRun);
     void *mem = nullptr;
-    if (hipMalloc(&mem, table_bytes + sizeof(StepBlock)) != hipSuccess) {
+    if (hipMalloc(&mem, table_bytes + sizeof(StepBlock) + tl->n_partials * sizeof(double)) !=
+        hipSuccess) {
         (void)hipGetLastError();
         delete tl;
         return ADAM_ENOMEM;
     }
     tl->d_items = static_cast<WorkItem *>(mem);
     tl->d_block = reinterpret_cast<StepBlock *>(static_cast<char *>(mem) + table_bytes);
+    tl->d_partials = reinterpret_cast<double *>(static_cast<char *>(mem) + table_bytes + sizeof(StepBlock));
     if (hipMemcpyAsync(tl->d_items, plan.items.data(), table_bytes, hipMemcpyHostToDevice, stream) !=
             hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess) {
@@ -809,6 +958,34 @@ int adam_step_capturable(const adam_tl *tl, const adam_hparams *hp, const float 
     a.weight_decay = hp->weight_decay;
     a.block = tl->d_block;
     return launch_update(tl, hp->mode, true, a, stream);
+}
+
+int adam_grad_sumsq(const adam_tl *tl, double *d_sumsq, int32_t accumulate, hipStream_t stream)
+{
+    if (tl == nullptr || d_sumsq == nullptr || (accumulate != 0 && accumulate != 1)) return ADAM_EINVAL;
+    int device = tl->stats.device;
+    if (device < 0 && hipGetDevice(&device) != hipSuccess) return ADAM_EHIP;
+    DeviceGuard guard(device);
+    if (guard.status != hipSuccess) return ADAM_EHIP;
+    if (tl->n_partials > 0) {
+        auto fn = tl->g_bf16 ? grad_sumsq_partial<true> : grad_sumsq_partial<false>;
+        hipLaunchKernelGGL(fn, dim3(tl->n_partials), dim3(kBlock), 0, stream, tl->d_items, tl->shift,
+                           uint32_t(tl->stats.grid_blocks), tl->d_partials);
+        if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
+    }
+    hipLaunchKernelGGL(grad_sumsq_fold, dim3(1), dim3(kFoldBlock), 0, stream, tl->d_partials,
+                       tl->n_partials, d_sumsq, accumulate);
+    return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
+}
+
+int adam_clip_grad_scale(const double *d_sumsq, float *d_grad_scale, float max_norm, float *d_norm,
+                         int32_t *d_noop, hipStream_t stream)
+{
+    if (d_sumsq == nullptr || max_norm != max_norm) return ADAM_EINVAL;
+    if (max_norm > 0.0f && d_grad_scale == nullptr) return ADAM_EINVAL;
+    hipLaunchKernelGGL(clip_grad_scale_kernel, dim3(1), dim3(64), 0, stream, d_sumsq, d_grad_scale,
+                       max_norm, d_norm, d_noop);
+    return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
 }
 
 }  // extern "C"

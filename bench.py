@@ -445,6 +445,50 @@ def main() -> int:
             "vs_noncapturable": round(g_wall / wall_ms, 4),
         }
 
+        # The whole capturable optimizer step: reset the grad scale, gradient
+        # sum of squares over every group, clip / found-inf, capturable update
+        # of every group; eager, then as one graph.
+        d_sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+        d_norm = torch.zeros(1, dtype=torch.float32, device="cuda")
+        d_full_scale = torch.ones(1, dtype=torch.float32, device="cuda")
+        max_norm = 1.0
+
+        def one_full_step(ev=None, s=stream):
+            d_full_scale.fill_(w.grad_scale)
+            for i, (tl, _, _, _, _) in enumerate(handles):
+                launch_timed(ev if i == 0 else None,
+                             lambda: A.adam_grad_sumsq(tl, d_sumsq, i > 0, s))
+            A.adam_clip_grad_scale(d_sumsq, d_full_scale, max_norm, d_norm, d_noop, s)
+            for tl, hp, _, _, d_step in handles:
+                A.adam_step_capturable(tl, hp, d_lr, d_step, d_full_scale, d_noop, s)
+
+        for _ in range(args.warmup):
+            one_full_step()
+        full_wall, sumsq_per = timed(one_full_step, args.steps)
+        log(f"full capturable step (sum of squares, clip, update): {full_wall:.3f} ms/step wall")
+        graph2 = torch.cuda.CUDAGraph()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            one_full_step(None, side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph2, stream=side):
+            one_full_step(None, side)
+        torch.cuda.synchronize()
+        full_g_wall, _ = timed(lambda ev: graph2.replay(), args.steps, events=False)
+        log(f"full capturable step as one graph: {full_g_wall:.3f} ms/step wall")
+        g_bytes = handles[0][2] * (4 if w.g_dtype == "f32" else 2)
+        sumsq_ms = statistics.mean(sumsq_per)
+        result["full_capturable_step"] = {
+            "what": "grad-scale reset + gradient sum of squares (all groups) + clip/found-inf "
+                    "+ capturable update (all groups)",
+            "ms_per_step": round(full_wall, 4),
+            "graph_ms_per_step": round(full_g_wall, 4),
+            "graph_vs_update_only": round(full_g_wall / wall_ms, 4),
+            "grad_sumsq_launch_ms": round(sumsq_ms, 4),
+            "grad_sumsq_gbps": round(g_bytes / (sumsq_ms * 1e-3) / 1e9, 1),
+        }
+
     for h in handles:
         h[0].destroy()
     del bufs

@@ -203,6 +203,40 @@ int adam_step_remainders(const adam_tl *tl, const adam_hparams *hp, float lr,
                          int32_t *step_io, float grad_scale, const float *d_grad_scale,
                          hipStream_t stream);
 
+/* Sum of squares of every gradient element of a handle: the local part of
+ * the global gradient norm that apex's distributed_fused_adam.py computes in
+ * grad_norm (per-bucket L2 norms of the gradient shards, squared and summed,
+ * then all-reduced across ranks).  Each square of a float or bf16 gradient is
+ * exact in double; the sum is accumulated in double with a fixed order of
+ * additions, so repeated calls give identical bits.
+ *   d_sumsq     device double: *d_sumsq = (accumulate ? *d_sumsq : 0) + sum.
+ *               Calls for several groups chain with accumulate = 1.
+ *   accumulate  0 or 1.
+ * Non-finite gradients make the sum inf or NaN.  No allocation, no host wait
+ * (capturable).  Uses the handle's partial-sum scratch: calls on one handle
+ * must be ordered, like capturable steps.  Errors: ADAM_EINVAL (NULL tl or
+ * d_sumsq, accumulate not 0/1); ADAM_EHIP. */
+int adam_grad_sumsq(const adam_tl *tl, double *d_sumsq, int32_t accumulate, hipStream_t stream);
+
+/* The clip / found-inf step from a gradient sum of squares (apex
+ * distributed_fused_adam.py: grad_norm scales the raw norm by the grad
+ * scale; clip_grad_norm multiplies the grad scale by
+ * min(1, max_norm / (norm + 1e-6)); step() takes found_inf = the norm is not
+ * finite and, when capturable, copies it into the noop flag).  One device
+ * lane computes, in float:
+ *   norm      = float(sqrt(*d_sumsq)) * grad_scale   (grad_scale = *d_grad_scale, or 1 if NULL)
+ *   found_inf = norm is inf or NaN
+ *   *d_norm   = norm                                  (d_norm nullable)
+ *   *d_noop   = found_inf ? 1 : 0                     (d_noop nullable; overwritten)
+ *   if !found_inf and max_norm > 0:
+ *     *d_grad_scale = grad_scale * min(1, max_norm / (norm + 1e-6))
+ * With found_inf the grad scale is left as it is (the step will be skipped).
+ * max_norm <= 0 disables clipping.  No allocation, no host wait (capturable).
+ * Errors: ADAM_EINVAL (NULL d_sumsq, NaN max_norm, max_norm > 0 with a NULL
+ * d_grad_scale); ADAM_EHIP. */
+int adam_clip_grad_scale(const double *d_sumsq, float *d_grad_scale, float max_norm, float *d_norm,
+                         int32_t *d_noop, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,7 @@ mistakes in copies of the C source and checks that the pins catch each one.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from dataclasses import dataclass
 from typing import List, Optional, Sequence
@@ -99,6 +100,16 @@ class Oracle:
         lib.oracle_adam_f32.restype = None
         lib.oracle_adam_remainder.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, *common]
         lib.oracle_adam_remainder.restype = None
+        lib.oracle_acc_size.argtypes = []
+        lib.oracle_acc_size.restype = ctypes.c_size_t
+        lib.oracle_acc_clear.argtypes = [vp]
+        lib.oracle_acc_clear.restype = None
+        lib.oracle_acc_add_squares.argtypes = [vp, vp, i32, i64]
+        lib.oracle_acc_add_squares.restype = None
+        lib.oracle_acc_merge.argtypes = [vp, vp]
+        lib.oracle_acc_merge.restype = None
+        lib.oracle_acc_value.argtypes = [vp]
+        lib.oracle_acc_value.restype = ctypes.c_double
         self.lib = lib
         self.path = path
 
@@ -167,6 +178,77 @@ class Oracle:
             self.lib.oracle_adam_remainder(_ptr(t.p) + 2 * lo, _ptr(t.rem) + 2 * lo,
                                            m_ptr, v_ptr, g_ptr, g_is_bf16, out_ptr,
                                            count, *scal)
+
+    # -- gradient norm and clipping -------------------------------------------
+
+    def new_accumulator(self):
+        """An exact sum-of-squares accumulator, cleared."""
+        acc = ctypes.create_string_buffer(self.lib.oracle_acc_size())
+        self.lib.oracle_acc_clear(acc)
+        return acc
+
+    def accumulate_squares(self, total, grads: Sequence[np.ndarray], threads: int = 1) -> None:
+        """Adds the squares of every element of the gradient arrays (float32,
+        or bf16 bits as uint16) to the accumulator ``total``, exactly.
+        ``threads`` > 1 splits the work; the result does not depend on it."""
+        jobs = []  # (array, lo, hi)
+        for g in grads:
+            g = np.ascontiguousarray(g)
+            assert g.dtype in (np.float32, np.uint16)
+            n = g.size
+            per = max(1, -(-n // max(1, threads)))
+            for lo in range(0, n, per):
+                jobs.append((g, lo, min(n, lo + per)))
+        accs = [self.new_accumulator() for _ in jobs]
+
+        def run(k):
+            g, lo, hi = jobs[k]
+            self.lib.oracle_acc_add_squares(accs[k], _ptr(g) + g.dtype.itemsize * lo,
+                                            1 if g.dtype == np.uint16 else 0, hi - lo)
+
+        if threads > 1 and len(jobs) > 1:
+            from concurrent.futures import ThreadPoolExecutor
+
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(run, range(len(jobs))))
+        else:
+            for k in range(len(jobs)):
+                run(k)
+        for a in accs:
+            self.lib.oracle_acc_merge(total, a)
+
+    def accumulator_value(self, total) -> float:
+        """The accumulated sum rounded once to the nearest double."""
+        return self.lib.oracle_acc_value(total)
+
+    def grad_sumsq(self, grads: Sequence[np.ndarray], threads: int = 1) -> float:
+        """Sum of the squares of every element of the gradient arrays,
+        computed exactly and rounded once to double."""
+        total = self.new_accumulator()
+        self.accumulate_squares(total, grads, threads)
+        return self.accumulator_value(total)
+
+    @staticmethod
+    def clip_grad_scale(sumsq: float, grad_scale: Optional[float], max_norm: float):
+        """The clip / found-inf step in float32 (apex distributed_fused_adam.py:
+        grad_norm multiplies the raw norm by the grad scale, clip_grad_norm
+        scales the grad scale by min(1, max_norm / (norm + 1e-6)), step() sets
+        found_inf when the norm is not finite).  Returns (norm, new grad
+        scale, found_inf as 0/1); the grad scale is left as it is when
+        found_inf or max_norm <= 0."""
+        f32 = np.float32
+        raw = f32(math.sqrt(sumsq)) if sumsq == sumsq else f32(np.nan)
+        scale = f32(1.0) if grad_scale is None else f32(grad_scale)
+        with np.errstate(over="ignore", invalid="ignore"):
+            norm = f32(raw * scale)
+        found_inf = not np.isfinite(norm)
+        new_scale = scale
+        if not found_inf and max_norm > 0:
+            coef = f32(f32(max_norm) / f32(norm + f32(1e-6)))
+            if coef > f32(1.0):
+                coef = f32(1.0)
+            new_scale = f32(scale * coef)
+        return norm, new_scale, 1 if found_inf else 0
 
     # -- one group, one step: the counter and noop rules --------------------
 

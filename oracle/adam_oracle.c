@@ -275,3 +275,126 @@ void oracle_adam_remainder(uint16_t *p, int16_t *rem, float *m, float *v,
             p_out[i] = p[i];
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Sum of squares of the gradients, exactly, rounded once to double        */
+/* (the local part of the gradient norm: [P2] grad_norm squares and sums   */
+/* the per-bucket L2 norms of the gradient shards).                        */
+/* ---------------------------------------------------------------------- */
+
+/* Every square of a float (or bf16) is a double of the form M * 2^E with M a
+ * 53-bit integer and E >= -350 (the smallest float denormal is 2^-149, its
+ * square 2^-298).  The accumulator is one big fixed-point integer whose
+ * lowest bit is worth 2^-400, in 64-bit words; adding M * 2^E is an exact
+ * integer addition.  Inf and NaN are tracked apart. */
+#define ACC_WORDS 14
+#define ACC_LSB_EXP (-400)
+
+struct oracle_acc {
+    uint64_t w[ACC_WORDS];
+    int32_t has_inf;
+    int32_t has_nan;
+};
+
+void oracle_acc_clear(struct oracle_acc *a)
+{
+    memset(a, 0, sizeof *a);
+}
+
+static void acc_add_bits(struct oracle_acc *a, int word, uint64_t lo, uint64_t hi)
+{
+    /* adds (hi:lo) << (64 * word) with carry */
+    uint64_t s = a->w[word] + lo;
+    uint64_t carry = s < lo;
+    a->w[word] = s;
+    int k = word + 1;
+    uint64_t add = hi;
+    while (k < ACC_WORDS && (add != 0 || carry != 0)) {
+        uint64_t t = a->w[k] + add;
+        uint64_t c1 = t < add;
+        uint64_t t2 = t + carry;
+        uint64_t c2 = t2 < carry;
+        a->w[k] = t2;
+        carry = c1 + c2;
+        add = 0;
+        ++k;
+    }
+}
+
+static void acc_add_double(struct oracle_acc *a, double x)
+{
+    if (isnan(x)) {
+        a->has_nan = 1;
+        return;
+    }
+    if (isinf(x)) {
+        a->has_inf = 1;
+        return;
+    }
+    if (x == 0.0)
+        return;
+    int e;
+    double frac = frexp(x, &e);            /* x = frac * 2^e, 0.5 <= frac < 1 */
+    uint64_t m = (uint64_t)ldexp(frac, 53); /* exact 53-bit integer */
+    int shift = (e - 53) - ACC_LSB_EXP;    /* bit position of m's lowest bit */
+    int word = shift / 64;
+    int bit = shift % 64;
+    uint64_t lo = m << bit;
+    uint64_t hi = bit == 0 ? 0 : m >> (64 - bit);
+    acc_add_bits(a, word, lo, hi);
+}
+
+void oracle_acc_add_squares(struct oracle_acc *a, const void *g, int32_t g_is_bf16, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double x = (double)load_grad(g, g_is_bf16, i);
+        acc_add_double(a, x * x);          /* exact: at most 48 significant bits */
+    }
+}
+
+void oracle_acc_merge(struct oracle_acc *into, const struct oracle_acc *from)
+{
+    for (int k = 0; k < ACC_WORDS; ++k)
+        acc_add_bits(into, k, from->w[k], 0);
+    into->has_inf |= from->has_inf;
+    into->has_nan |= from->has_nan;
+}
+
+/* The accumulated value rounded to the nearest double, ties to even. */
+double oracle_acc_value(const struct oracle_acc *a)
+{
+    if (a->has_nan)
+        return NAN;
+    if (a->has_inf)
+        return INFINITY;
+    int top = -1;
+    for (int k = ACC_WORDS - 1; k >= 0 && top < 0; --k)
+        if (a->w[k] != 0)
+            top = k * 64 + 63 - __builtin_clzll(a->w[k]);
+    if (top < 0)
+        return 0.0;
+    /* the 53 bits from `top` down, then round on the bits below */
+    uint64_t m = 0;
+    for (int b = top; b > top - 53; --b) {
+        m <<= 1;
+        if (b >= 0 && ((a->w[b / 64] >> (b % 64)) & 1u))
+            m |= 1u;
+    }
+    int below = top - 53;                  /* highest bit not kept */
+    int round_up = 0;
+    if (below >= 0 && ((a->w[below / 64] >> (below % 64)) & 1u)) {
+        int sticky = 0;
+        for (int b = below - 1; b >= 0 && !sticky; --b)
+            if ((a->w[b / 64] >> (b % 64)) & 1u)
+                sticky = 1;
+        round_up = sticky || (m & 1u);
+    }
+    if (round_up)
+        m += 1;                            /* may become 2^53: still exact */
+    return ldexp((double)m, top - 52 + ACC_LSB_EXP);
+}
+
+size_t oracle_acc_size(void)
+{
+    return sizeof(struct oracle_acc);
+}

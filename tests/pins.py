@@ -24,7 +24,10 @@ What pins what:
                               exact round trip, and the nearest-value property
                               of the stored bf16 half;
 * noop flag, empty group    - the pages' step rules and the printed output of
-                              the empty-group reproduction (tests/golden).
+                              the empty-group reproduction (tests/golden);
+* gradient sum of squares   - math.fsum (a correctly rounded sum) of the
+                              squares, closed forms, non-finite inputs;
+* clip / found-inf step     - float64 torch.nn.utils.clip_grad_norm_.
 """
 from __future__ import annotations
 
@@ -515,6 +518,79 @@ def check_empty_group_counter(o: Oracle, golden_steps):
         assert [s[0] for s in steps] == list(golden_steps)
 
 
+# ---------------------------------------------------------------------------
+# Gradient sum of squares and the clip step
+# ---------------------------------------------------------------------------
+
+def _fsum_squares(values) -> float:
+    return math.fsum(float(x) * float(x) for x in values)
+
+
+def check_grad_sumsq(o: Oracle, n: int = 20001, seed: int = 40):
+    """The oracle's sum of squares is the correctly rounded exact sum:
+    equal to math.fsum of the (exact, double) squares, for values spread over
+    the whole float range, split over arrays and threads, and for bf16."""
+    rng = np.random.default_rng(seed)
+    g = (rng.standard_normal(n) * 10.0 ** rng.uniform(-44, 37, n)).astype(np.float32)
+    g[:6] = np.array([0.0, -0.0, 1e-45, 3.4e38, -1.0, 2.0 ** -149], np.float32)
+    want = _fsum_squares(g)
+    assert o.grad_sumsq([g]) == want
+    assert o.grad_sumsq([g[:7], g[7:1000], g[1000:]], threads=3) == want
+    gb = torch_bf16_bits(g[:5000])
+    wide = (gb.astype(np.uint32) << 16).view(np.float32)
+    assert o.grad_sumsq([gb]) == _fsum_squares(wide)
+    # many equal values: a carry-heavy exact case with a closed form
+    c = np.full(70000, 0.75, np.float32)
+    assert o.grad_sumsq([c], threads=4) == 70000 * 0.5625
+    ones = np.ones(1 << 20, np.float32)
+    assert o.grad_sumsq([ones]) == float(1 << 20)
+    # exact ties between two doubles round to the even one:
+    # 2^52 + 2^52 + 1 = 2^53 + 1 -> 2^53;  2^53 + 3 -> 2^53 + 4
+    big = np.float32(2.0 ** 26)
+    assert o.grad_sumsq([np.array([big, big, 1.0], np.float32)]) == 2.0 ** 53
+    assert o.grad_sumsq([np.array([big, big, 1.0, 1.0, 1.0], np.float32)]) == 2.0 ** 53 + 4
+    assert _fsum_squares([big, big, 1.0, 1.0, 1.0]) == 2.0 ** 53 + 4
+    # non-finite values, alone and after a threaded split
+    assert o.grad_sumsq([]) == 0.0
+    h = ones.copy()
+    h[12345] = np.inf
+    assert o.grad_sumsq([h], threads=4) == np.inf
+    h[777] = np.nan
+    assert np.isnan(o.grad_sumsq([h], threads=4))
+
+
+def check_clip_grad_scale(o: Oracle, seed: int = 41):
+    """Norm and clip factor agree with float64 torch.nn.utils.clip_grad_norm_
+    on the scaled gradients; below the threshold the scale is untouched;
+    a non-finite norm raises found_inf and leaves the scale; max_norm <= 0
+    does not clip."""
+    import torch
+
+    rng = np.random.default_rng(seed)
+    for trial in range(12):
+        g = (rng.standard_normal(1000) * 10.0 ** rng.uniform(-4, 2)).astype(np.float32)
+        s = f32(rng.choice([1.0, 0.5, 2.0 ** -16, 3.0]))
+        max_norm = f32(10.0 ** rng.uniform(-3, 2))
+        norm, new_s, found = o.clip_grad_scale(o.grad_sumsq([g]), s, max_norm)
+        assert found == 0
+        t = torch.nn.Parameter(torch.zeros(1000, dtype=torch.float64))
+        t.grad = torch.from_numpy(g.astype(np.float64) * s)
+        before = t.grad.clone()
+        total = float(torch.nn.utils.clip_grad_norm_([t], float(max_norm)))
+        factor = float((t.grad / before)[np.argmax(np.abs(g))])
+        assert abs(float(norm) - total) <= 1e-6 * total, (trial, norm, total)
+        assert abs(float(new_s) / float(s) - factor) <= 2e-6 * factor, (trial, new_s, s, factor)
+        if total < float(max_norm) * (1 - 1e-5):
+            assert new_s == np.float32(s)
+    norm, new_s, found = o.clip_grad_scale(4.0, 1.0, 1.0)
+    assert norm == np.float32(2.0) and new_s == np.float32(1.0) / np.float32(np.float32(2.0) + np.float32(1e-6))
+    for bad in (np.inf, np.nan):
+        norm, new_s, found = o.clip_grad_scale(bad, 0.5, 1.0)
+        assert found == 1 and new_s == np.float32(0.5) and not np.isfinite(norm)
+    norm, new_s, found = o.clip_grad_scale(1e6, 0.25, 0.0)
+    assert found == 0 and new_s == np.float32(0.25) and norm == np.float32(1000.0 * 0.25)
+
+
 QUICK_CHECKS = (
     "check_bias_corrections_quick",
     "check_first_step_adamw",
@@ -528,6 +604,8 @@ QUICK_CHECKS = (
     "check_remainder_codec_quick",
     "check_param_out_and_remainder_update",
     "check_noop_and_counter",
+    "check_grad_sumsq",
+    "check_clip_grad_scale",
 )
 
 

@@ -1,0 +1,255 @@
+"""GPU parity of the gradient sum of squares and the clip / found-inf step,
+and of the whole capturable step they feed (sum -> clip -> update), through
+the C ABI against the oracle."""
+import gc
+import zlib
+
+import numpy as np
+import pytest
+
+import adamw_optimizer_step_tensor_amd as A
+import oracle
+from gpu_helpers import DeviceSet, assert_bitwise, copies, desc_for, hp_pair, oracle_tensors, torch_mod
+from workloads import device_flat, host_tensors, split_views, workloads
+
+pytestmark = pytest.mark.gpu
+
+# The library adds squares in double in a fixed order; against the exact sum
+# its relative error is bounded by (additions on the longest path) * 2^-53:
+# at most 256 + 16 + 8 + 20 additions here, far below this tolerance.
+SUMSQ_RTOL = 1e-12
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    A.lib()
+    return t
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+@pytest.fixture(autouse=True)
+def free_memory():
+    yield
+    t = torch_mod()
+    gc.collect()
+    if t.cuda.is_available():
+        t.cuda.empty_cache()
+
+
+SIZES = list(range(0, 68)) + [4095, 4096, 4097, 33000, 65537, 200003]
+
+
+def gpu_sumsq(torch, tl, accumulate=False, start=0.0):
+    d = torch.tensor([start], dtype=torch.float64, device="cuda")
+    A.adam_grad_sumsq(tl, d, accumulate)
+    torch.cuda.synchronize()
+    return float(d.item())
+
+
+@pytest.mark.parametrize("g_dtype,p_kind,layout", [
+    ("f32", "f32", "aligned"), ("bf16", "f32", "shared"), ("f32", "f32", "random"),
+    ("bf16", "bf16_rem", "shared"), ("bf16", "f32", "random")])
+def test_grad_sumsq_matches_the_exact_sum(torch, orc, g_dtype, p_kind, layout):
+    rng = np.random.default_rng(zlib.crc32(f"{g_dtype}{p_kind}{layout}".encode()))
+    host = host_tensors(SIZES, g_dtype=g_dtype, p_kind=p_kind, seed=51)
+    for h in host[::5]:  # magnitudes across many decades
+        if h.g.dtype == np.float32 and h.g.size:
+            h.g *= np.float32(10.0 ** rng.uniform(-20, 20))
+    roles = ("p", "rem", "m", "v", "g", "p_out")
+    if layout == "aligned":
+        offsets = None
+    elif layout == "shared":
+        offsets = [{r: k % 8 for r in roles} for k in range(len(SIZES))]
+    else:
+        offsets = [{r: int(rng.integers(0, 8)) for r in roles} for _ in SIZES]
+    dev = DeviceSet(host, offsets)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    got = gpu_sumsq(torch, tl)
+    want = orc.grad_sumsq([h.g for h in host])
+    assert abs(got - want) <= SUMSQ_RTOL * want, (got, want)
+    # deterministic, and accumulate adds to what is there
+    assert gpu_sumsq(torch, tl) == got
+    assert gpu_sumsq(torch, tl, True, 0.5) == 0.5 + got
+    tl.destroy()
+
+
+@pytest.mark.parametrize("g_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout,chunk", [("aligned", 0), ("aligned", 4096), ("shared", 0)])
+def test_grad_sumsq_every_tail_length(torch, orc, g_dtype, layout, chunk):
+    st = A.adam_tl_plan([dict(p=1 << 40, m=2 << 40, v=3 << 40, g=4 << 40, numel=8)], A.make_desc())
+    tile = st["tile_elems"]
+    sizes = [tile + r for r in range(tile)] + [3 * tile - 1, 3 * tile - 5]
+    host = host_tensors(sizes, g_dtype=g_dtype, seed=62)
+    roles = ("p", "rem", "m", "v", "g", "p_out")
+    offsets = None if layout == "aligned" else [{r: k % 67 for r in roles} for k in range(len(sizes))]
+    dev = DeviceSet(host, offsets)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host, chunk_elems=chunk))
+    got = gpu_sumsq(torch, tl)
+    want = orc.grad_sumsq([h.g for h in host])
+    assert abs(got - want) <= SUMSQ_RTOL * want, (got, want)
+
+
+def test_grad_sumsq_of_an_empty_group_and_of_chained_groups(torch, orc):
+    empty = A.adam_tl_build([], A.make_desc(), stream=0)
+    assert gpu_sumsq(torch, empty) == 0.0
+    assert gpu_sumsq(torch, empty, True, 3.25) == 3.25
+    h1 = host_tensors([1000, 77], seed=52)
+    h2 = host_tensors([4096 * 3 + 1], g_dtype="bf16", seed=53)
+    d1, d2 = DeviceSet(h1), DeviceSet(h2)
+    t1 = A.adam_tl_build(d1.tensors, desc_for(h1))
+    t2 = A.adam_tl_build(d2.tensors, desc_for(h2))
+    a, b = gpu_sumsq(torch, t1), gpu_sumsq(torch, t2)
+    d = torch.zeros(1, dtype=torch.float64, device="cuda")
+    A.adam_grad_sumsq(t1, d, False)
+    A.adam_grad_sumsq(empty, d, True)
+    A.adam_grad_sumsq(t2, d, True)
+    torch.cuda.synchronize()
+    assert float(d.item()) == a + b
+    want = orc.grad_sumsq([h.g for h in h1] + [h.g for h in h2])
+    assert abs(a + b - want) <= SUMSQ_RTOL * want
+
+
+def test_grad_sumsq_of_non_finite_gradients(torch):
+    host = host_tensors([5000, 300], seed=54)
+    host[0].g[1234] = np.inf
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    assert gpu_sumsq(torch, tl) == np.inf
+    dev.tensors[1]["g"][5] = float("nan")
+    assert np.isnan(gpu_sumsq(torch, tl))
+
+
+@pytest.mark.parametrize("case", ["clip", "no_clip", "max_norm_zero", "inf", "nan"])
+def test_clip_grad_scale_equals_the_oracle_bitwise(torch, orc, case):
+    host = host_tensors([30000, 513], g_dtype="bf16", seed=55)
+    if case == "inf":
+        host[1].g[7] = 0x7F80  # bf16 +inf
+    if case == "nan":
+        host[0].g[9] = 0x7FC0
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    d_sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    A.adam_grad_sumsq(tl, d_sumsq, False)
+    scale0 = 0.37
+    max_norm = {"clip": 1e-3, "no_clip": 1e6, "max_norm_zero": 0.0}.get(case, 1.0)
+    d_scale = torch.tensor([scale0], dtype=torch.float32, device="cuda")
+    d_norm = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d_noop = torch.tensor([1], dtype=torch.int32, device="cuda")  # overwritten either way
+    A.adam_clip_grad_scale(d_sumsq, d_scale, max_norm, d_norm, d_noop)
+    torch.cuda.synchronize()
+    norm, new_s, found = orc.clip_grad_scale(float(d_sumsq.item()), np.float32(scale0), max_norm)
+    got_norm = np.float32(d_norm.item())
+    assert (got_norm == norm) or (np.isnan(got_norm) and np.isnan(norm))
+    assert np.float32(d_scale.item()) == new_s
+    assert int(d_noop.item()) == found == (1 if case in ("inf", "nan") else 0)
+    if case == "clip":
+        assert new_s < np.float32(scale0)
+    if case in ("no_clip", "max_norm_zero", "inf", "nan"):
+        assert new_s == np.float32(scale0)
+
+
+def test_clip_argument_errors(torch):
+    L = A.lib()
+    d = torch.zeros(1, dtype=torch.float64, device="cuda")
+    assert L.adam_clip_grad_scale(None, None, 0.0, None, None, None) == A.ADAM_EINVAL
+    assert L.adam_clip_grad_scale(d.data_ptr(), None, 1.0, None, None, None) == A.ADAM_EINVAL
+    assert L.adam_clip_grad_scale(d.data_ptr(), None, float("nan"), None, None, None) == A.ADAM_EINVAL
+    tl = A.adam_tl_build([], A.make_desc(), stream=0)
+    assert L.adam_grad_sumsq(tl.handle, None, 0, None) == A.ADAM_EINVAL
+    assert L.adam_grad_sumsq(tl.handle, d.data_ptr(), 2, None) == A.ADAM_EINVAL
+    assert L.adam_grad_sumsq(None, d.data_ptr(), 0, None) == A.ADAM_EINVAL
+
+
+def test_whole_capturable_step_in_one_graph(torch, orc):
+    """Two groups (decay and no decay, bf16 grads, bf16 p_out): per step the
+    gradient sum of squares of both groups, the clip / found-inf step, then
+    the capturable update of each group, all recorded in one HIP graph and
+    replayed; an infinite gradient on the third replay skips that step.
+    Each replay equals the oracle fed the same sum of squares."""
+    h1 = host_tensors([40000, 4096, 333], g_dtype="bf16", p_out=True, seed=56)
+    h2 = host_tensors([4096] * 3, g_dtype="bf16", p_out=True, seed=57)
+    d1, d2 = DeviceSet(h1), DeviceSet(h2)
+    t1 = A.adam_tl_build(d1.tensors, desc_for(h1))
+    t2 = A.adam_tl_build(d2.tensors, desc_for(h2))
+    hp1, hr1 = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    hp2, hr2 = hp_pair(0.9, 0.95, 1e-8, 0.0, 1)
+    d_lr = torch.tensor([1.6e-3], dtype=torch.float32, device="cuda")
+    d_scale = torch.tensor([1.0], dtype=torch.float32, device="cuda")
+    d_sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    d_norm = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    max_norm = 0.05
+
+    def step(stream):
+        A.adam_grad_sumsq(t1, d_sumsq, False, stream)
+        A.adam_grad_sumsq(t2, d_sumsq, True, stream)
+        A.adam_clip_grad_scale(d_sumsq, d_scale, max_norm, d_norm, d_noop, stream)
+        A.adam_step_capturable(t1, hp1, d_lr, s1, d_scale, d_noop, stream)
+        A.adam_step_capturable(t2, hp2, d_lr, s2, d_scale, d_noop, stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step(side)
+    torch.cuda.synchronize()
+    assert int(s1.item()) == 0  # capture records, does not run
+
+    r1, r2 = oracle_tensors(copies(h1)), oracle_tensors(copies(h2))
+    st1, st2 = [0], [0]
+    for k in range(5):
+        d_scale.fill_(1.0)  # the optimizer resets its grad scale every iteration
+        if k == 2:
+            d1.tensors[0]["g"][11] = float("inf")
+        graph.replay()
+        torch.cuda.synchronize()
+        sumsq = float(d_sumsq.item())
+        want = orc.grad_sumsq([t.g for t in r1] + [t.g for t in r2])
+        if k == 2:
+            assert sumsq == np.inf and int(d_noop.item()) == 1
+            d1.tensors[0]["g"][11] = 0.0
+            r1[0].g[11] = 0
+        else:
+            assert abs(sumsq - want) <= SUMSQ_RTOL * want
+        norm, new_s, found = orc.clip_grad_scale(sumsq, 1.0, max_norm)
+        assert np.float32(d_norm.item()) == norm or (np.isnan(norm) and np.isnan(d_norm.item()))
+        assert np.float32(d_scale.item()) == new_s
+        orc.group_step(r1, hr1, 1.6e-3, st1, float(new_s), noop=found)
+        orc.group_step(r2, hr2, 1.6e-3, st2, float(new_s), noop=found)
+    assert int(s1.item()) == st1[0] == 4 and int(s2.item()) == st2[0] == 4
+    assert_bitwise(d1.readback(), r1, ctx="group 1")
+    assert_bitwise(d2.readback(), r2, ctx="group 2")
+
+
+def test_grad_sumsq_full_size_201_tensors(torch, orc):
+    """4,215,275,520 fp32 gradients (the benchmark's list): against the exact
+    sum (gradients copied to the host in 1 GiB pieces), repeatable bit for
+    bit, and exactly 4x after doubling every gradient (a power-of-two scale
+    commutes with every rounding)."""
+    w = workloads()["bench201"]
+    bufs = device_flat(w.numel, g_dtype="f32", p_kind="f32", p_out=False, seed=w.seed)
+    views = {k: split_views(v, w.sizes) for k, v in bufs.items()}
+    tensors = [{k: views[k][i] for k in views} for i in range(len(w.sizes))]
+    tl = A.adam_tl_build(tensors, A.make_desc())
+    got = gpu_sumsq(torch, tl)
+    assert gpu_sumsq(torch, tl) == got
+    total = orc.new_accumulator()
+    piece = 1 << 28
+    for lo in range(0, w.numel, piece):
+        host = bufs["g"][lo:lo + piece].cpu().numpy()
+        orc.accumulate_squares(total, [host], threads=16)
+        del host
+    want = orc.accumulator_value(total)
+    assert abs(got - want) <= SUMSQ_RTOL * want, (got, want)
+    bufs["g"].mul_(2.0)
+    assert gpu_sumsq(torch, tl) == 4.0 * got
+    tl.destroy()

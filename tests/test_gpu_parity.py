@@ -118,6 +118,31 @@ def test_shared_offsets_take_the_peeled_vector_path(torch, orc, g_dtype, p_kind,
     assert_bitwise(got, ref, ctx=f"{g_dtype}/{p_kind}/{p_out}/{mode}")
 
 
+def tile_elems():
+    st = A.adam_tl_plan([dict(p=1 << 40, m=2 << 40, v=3 << 40, g=4 << 40, numel=8)], A.make_desc())
+    return st["tile_elems"]
+
+
+@pytest.mark.parametrize("g_dtype,p_kind,p_out", [
+    ("f32", "f32", False), ("bf16", "f32", True), ("bf16", "bf16_rem", False)])
+@pytest.mark.parametrize("layout,chunk", [("aligned", 0), ("aligned", 4096), ("shared", 0)])
+def test_every_tail_length(torch, orc, g_dtype, p_kind, p_out, layout, chunk):
+    """One tensor per tail length: a full tile plus 0..tile-1 elements, so the
+    last tile of every vector body takes every possible ragged length
+    (including the ones whose tail lanes follow the last vector lane)."""
+    tile = tile_elems()
+    sizes = [tile + r for r in range(tile)] + [3 * tile - 1, 3 * tile - 2, 3 * tile - 5]
+    host = host_tensors(sizes, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=61,
+                        m_v_init="random")
+    roles = ("p", "rem", "m", "v", "g", "p_out")
+    offsets = None if layout == "aligned" else [{r: k % 67 for r in roles} for k in range(len(sizes))]
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    got, ref, s, rs = run_both(orc, host, hl, hr, 1.6e-3, 2, desc_kw=dict(chunk_elems=chunk),
+                               offsets=offsets)
+    assert s == rs == 2
+    assert_bitwise(got, ref, ctx=f"{g_dtype}/{p_kind}/{p_out}/{layout}/{chunk}")
+
+
 def test_results_do_not_depend_on_chunk(torch, orc):
     sizes = [70001, 4096 * 5, 123, 9, 65536 * 2]
     host = host_tensors(sizes, g_dtype="bf16", p_out=True, seed=21, m_v_init="random")

@@ -46,6 +46,12 @@ MUTANTS = {
     "remainder_param_out_rne": [("p_out[i] = p[i];", "p_out[i] = oracle_bf16_rne(P_new);")],
     "bf16_grad_index_shift": [("((const uint16_t *)g)[i]", "((const uint16_t *)g)[i ? i - 1 : 0]")],
     "one_minus_beta_wrong": [("float one_minus_beta = 1.0f - beta;", "float one_minus_beta = beta - 1.0f;")],
+    "sumsq_carry_dropped": [("    uint64_t carry = s < lo;\n", "    uint64_t carry = 0;\n")],
+    "sumsq_round_truncates": [("round_up = sticky || (m & 1u);", "round_up = 0;")],
+    "sumsq_ties_away": [("round_up = sticky || (m & 1u);", "round_up = 1;")],
+    "sumsq_square_in_float": [("acc_add_double(a, x * x);", "acc_add_double(a, (double)((float)x * (float)x));")],
+    "sumsq_merge_drops_flags": [("    into->has_inf |= from->has_inf;\n", "")],
+    "sumsq_bit_position_off_by_one": [("int shift = (e - 53) - ACC_LSB_EXP;", "int shift = (e - 52) - ACC_LSB_EXP;")],
 }
 
 

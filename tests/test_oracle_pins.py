@@ -64,6 +64,14 @@ def test_empty_group_counter_matches_pages(oracle_default, golden_dir):
     pins.check_empty_group_counter(oracle_default, _golden_steps(golden_dir))
 
 
+def test_grad_sumsq_is_the_correctly_rounded_sum(oracle_default):
+    pins.check_grad_sumsq(oracle_default)
+
+
+def test_clip_grad_scale_matches_torch_clip(oracle_default):
+    pins.check_clip_grad_scale(oracle_default)
+
+
 def test_host_counter_overflow_wraps_like_int32(oracle_default):
     from oracle import HParams
 
