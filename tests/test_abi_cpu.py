@@ -99,6 +99,19 @@ def test_plan_counts_chunks_and_bytes():
     assert plan(fake_tensors([8]), g="f32", p_out=None)["bytes_per_elem"] == 28
 
 
+def test_every_dtype_set_moves_four_elements_per_lane():
+    """One 4-element group per lane and stream for every dtype set (16-byte
+    fp32 and 8-byte 16-bit accesses): the tile is 4 x block threads, and a
+    bf16 gradient needs only 8-byte alignment for the vector path."""
+    block = plan(fake_tensors([8]))["block_threads"]
+    for kw, flags in ((dict(), {}), (dict(g="bf16"), {}), (dict(p_out="bf16"), dict(out=True)),
+                      (dict(g="bf16", p="bf16_rem"), dict(rem=True)),
+                      (dict(p="bf16_rem", p_out="bf16"), dict(rem=True, out=True))):
+        assert plan(fake_tensors([8], **flags), **kw)["tile_elems"] == 4 * block, kw
+    st = plan(fake_tensors([50], offsets={0: {"g": 8}}), g="bf16")
+    assert st["vector_tensors"] == 1 and st["elements"] == 50
+
+
 def test_plan_marks_unaligned_tensors_for_the_element_path():
     ts = fake_tensors([100, 100, 100], offsets={1: {"m": 4}, 2: {"g": 16}})
     st = plan(ts)

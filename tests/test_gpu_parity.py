@@ -100,8 +100,9 @@ def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
     ("f32", "bf16_rem", True, 1)])
 def test_shared_offsets_take_the_peeled_vector_path(torch, orc, g_dtype, p_kind, p_out, mode):
     """Every stream of a tensor at the same element offset 0..7 (views at one
-    offset into flat buffers): the 0..3 leading elements are peeled and the
-    rest vectorised; results stay bit-identical to the oracle."""
+    offset into flat buffers): the leading elements before the first lane
+    group boundary (or 128-byte line) are peeled and the rest vectorised;
+    results stay bit-identical to the oracle."""
     sizes = list(range(0, 20)) + [1021, 4095, 4099, 8193, 70001]
     host = host_tensors(sizes, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=31,
                         m_v_init="random")
@@ -110,7 +111,8 @@ def test_shared_offsets_take_the_peeled_vector_path(torch, orc, g_dtype, p_kind,
     desc = desc_for(host, chunk_elems=4096)
     dev = DeviceSet(host, offsets)
     st = A.adam_tl_build(dev.tensors, desc).info()
-    assert st["vector_tensors"] == sum(1 for k, n in enumerate(sizes) if n > (4 - k % 4) % 4)
+    lane = st["tile_elems"] // st["block_threads"]
+    assert st["vector_tensors"] == sum(1 for k, n in enumerate(sizes) if n > (lane - k % lane) % lane)
     hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
     got, ref, s, rs = run_both(orc, host, hl, hr, 1.6e-3, 3, grad_scale=0.5,
                                desc_kw=dict(chunk_elems=4096), offsets=offsets)
@@ -118,9 +120,16 @@ def test_shared_offsets_take_the_peeled_vector_path(torch, orc, g_dtype, p_kind,
     assert_bitwise(got, ref, ctx=f"{g_dtype}/{p_kind}/{p_out}/{mode}")
 
 
-def tile_elems():
-    st = A.adam_tl_plan([dict(p=1 << 40, m=2 << 40, v=3 << 40, g=4 << 40, numel=8)], A.make_desc())
-    return st["tile_elems"]
+def tile_elems(g_dtype="f32", p_kind="f32", p_out=False):
+    """Elements per workgroup tile of a list with these dtypes (planned on
+    fake addresses, nothing is dereferenced)."""
+    t = dict(p=1 << 40, m=2 << 40, v=3 << 40, g=4 << 40, numel=8)
+    if p_kind == "bf16_rem":
+        t["rem"] = 5 << 40
+    if p_out:
+        t["p_out"] = 6 << 40
+    desc = A.make_desc(g=g_dtype, p=p_kind, p_out="bf16" if p_out else None)
+    return A.adam_tl_plan([t], desc)["tile_elems"]
 
 
 @pytest.mark.parametrize("g_dtype,p_kind,p_out", [
@@ -130,7 +139,7 @@ def test_every_tail_length(torch, orc, g_dtype, p_kind, p_out, layout, chunk):
     """One tensor per tail length: a full tile plus 0..tile-1 elements, so the
     last tile of every vector body takes every possible ragged length
     (including the ones whose tail lanes follow the last vector lane)."""
-    tile = tile_elems()
+    tile = tile_elems(g_dtype, p_kind, p_out)
     sizes = [tile + r for r in range(tile)] + [3 * tile - 1, 3 * tile - 2, 3 * tile - 5]
     host = host_tensors(sizes, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=61,
                         m_v_init="random")
