@@ -17,8 +17,10 @@ it with ctypes and adds the step-level rules around one call:
 * a group with no elements still advances its counter (TransformerEngine PR
   "Advance FusedAdam step counter for empty param groups", section "Fix").
 
-Arrays are numpy: fp32 as ``float32``, bf16 as raw ``uint16`` bits, the
-remainders as ``int16``.
+Arrays are numpy: fp32 as ``float32``, fp16 as ``float16``, bf16 as raw
+``uint16`` bits, the remainders as ``int16``.  Scaled optimizer state (apex
+distributed_fused_adam.py, ``_local_step_with_scaled_states``) keeps p, m and
+v as bf16 bits or fp16 with three float32 scales per tensor.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` to values fixed by
 the pages or by mathematics (closed forms, exact rational arithmetic,
@@ -55,9 +57,12 @@ class HParams:
 
 @dataclass
 class OracleTensor:
-    """One tensor of a group.  For fp32 params ``p`` is float32 and ``rem`` is
-    None; for remainder params ``p`` is bf16 bits (uint16) and ``rem`` int16.
-    ``g`` is float32 or bf16 bits (uint16).  ``p_out`` is bf16 bits or None."""
+    """One tensor of a group.  For fp32 params ``p`` is float32 and ``rem`` and
+    ``scales`` are None; for remainder params ``p`` is bf16 bits (uint16) and
+    ``rem`` int16; for scaled state ``p``, ``m``, ``v`` are bf16 bits (uint16)
+    or float16 and ``scales`` is float32[3] (param, exp_avg, exp_avg_sq).
+    ``g`` is float32, bf16 bits (uint16) or float16.  ``p_out`` is bf16 bits
+    (uint16), float16 or None."""
 
     p: np.ndarray
     m: np.ndarray
@@ -65,10 +70,26 @@ class OracleTensor:
     g: np.ndarray
     p_out: Optional[np.ndarray] = None
     rem: Optional[np.ndarray] = None
+    scales: Optional[np.ndarray] = None
 
     @property
     def numel(self) -> int:
         return int(self.p.size)
+
+
+# element type codes of adam_oracle.c
+F32, BF16, F16 = 0, 1, 2
+
+
+def type_code(a: np.ndarray) -> int:
+    """float32 -> F32, uint16 (bf16 bits) -> BF16, float16 -> F16."""
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError(f"unsupported element type {a.dtype}")
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -95,11 +116,21 @@ class Oracle:
         lib.oracle_rem_encode_array.restype = None
         lib.oracle_rem_decode_array.argtypes = [vp, vp, vp, i64]
         lib.oracle_rem_decode_array.restype = None
+        lib.oracle_f16_rne_array.argtypes = [vp, vp, i64]
+        lib.oracle_f16_rne_array.restype = None
+        lib.oracle_f16_to_f32_array.argtypes = [vp, vp, i64]
+        lib.oracle_f16_to_f32_array.restype = None
         common = [f32, f32, f32, f32, f32, i32, f32, f32, f32]
-        lib.oracle_adam_f32.argtypes = [vp, vp, vp, vp, i32, vp, i64, *common]
+        lib.oracle_adam_f32.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, *common]
         lib.oracle_adam_f32.restype = None
         lib.oracle_adam_remainder.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, *common]
         lib.oracle_adam_remainder.restype = None
+        lib.oracle_adam_scaled.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, i32, i64, *common]
+        lib.oracle_adam_scaled.restype = ctypes.c_int
+        lib.oracle_scaled_state_limit.argtypes = [i32]
+        lib.oracle_scaled_state_limit.restype = f32
+        lib.oracle_rescale_store.argtypes = [vp, vp, i64, i32]
+        lib.oracle_rescale_store.restype = f32
         lib.oracle_acc_size.argtypes = []
         lib.oracle_acc_size.restype = ctypes.c_size_t
         lib.oracle_acc_clear.argtypes = [vp]
@@ -135,6 +166,44 @@ class Oracle:
         self.lib.oracle_bf16_rne_array(_ptr(x), _ptr(out), x.size)
         return out
 
+    def f16_rne(self, x: np.ndarray) -> np.ndarray:
+        """float32 array -> float16 (round to nearest even, IEEE overflow and
+        subnormals)."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.oracle_f16_rne_array(_ptr(x), _ptr(out), x.size)
+        return out.view(np.float16)
+
+    def f16_to_f32(self, h: np.ndarray) -> np.ndarray:
+        """float16 array -> float32 (exact)."""
+        h = np.ascontiguousarray(h, dtype=np.float16)
+        out = np.empty(h.shape, dtype=np.float32)
+        self.lib.oracle_f16_to_f32_array(_ptr(h), _ptr(out), h.size)
+        return out
+
+    def scaled_state_limit(self, state_dtype) -> np.float32:
+        """Half the largest finite value of the state type (bf16 bits as
+        uint16, or float16), as float32."""
+        code = type_code(np.empty(0, dtype=state_dtype))
+        return np.float32(self.lib.oracle_scaled_state_limit(code))
+
+    def scale_state(self, x: np.ndarray, state_dtype):
+        """float32 values -> (scaled 16-bit values, float32 scale), as apex's
+        _apply_state_scale followed by the copy into the state type."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        assert x.size > 0
+        out = np.empty(x.shape, dtype=np.uint16)
+        code = type_code(np.empty(0, dtype=state_dtype))
+        scale = self.lib.oracle_rescale_store(_ptr(x), _ptr(out), x.size, code)
+        return out.view(state_dtype), np.float32(scale)
+
+    def unscale_state(self, x: np.ndarray, scale) -> np.ndarray:
+        """Scaled 16-bit values -> float32: the copy to float, times the
+        scale (one float multiplication)."""
+        wide = self.f16_to_f32(x) if x.dtype == np.float16 else \
+            (x.astype(np.uint32) << 16).view(np.float32)
+        return (wide * np.float32(scale)).astype(np.float32)
+
     def rem_encode(self, x: np.ndarray):
         """float32 array -> (bf16 bits uint16, remainder int16)."""
         x = np.ascontiguousarray(x, dtype=np.float32)
@@ -160,23 +229,36 @@ class Oracle:
         count = n - lo
         if count <= 0:
             return
-        assert t.g.dtype in (np.float32, np.uint16)
-        g_is_bf16 = 1 if t.g.dtype == np.uint16 else 0
-        m_ptr = _ptr(t.m) + 4 * lo
-        v_ptr = _ptr(t.v) + 4 * lo
-        g_ptr = _ptr(t.g) + t.g.dtype.itemsize * lo
-        out_ptr = None if t.p_out is None else _ptr(t.p_out) + 2 * lo
+        g_type = type_code(t.g)
+        out_type = F32 if t.p_out is None else type_code(t.p_out)
         scal = (float(lr), float(hp.beta1), float(hp.beta2), float(hp.eps),
                 float(hp.weight_decay), int(hp.mode), float(bc1), float(bc2),
                 float(grad_scale))
+        g_ptr = _ptr(t.g) + t.g.dtype.itemsize * lo
+        out_ptr = None if t.p_out is None else _ptr(t.p_out) + 2 * lo
+        if t.scales is not None:
+            # the new scales depend on the whole tensor: no partial ranges
+            assert lo == 0 and n == t.numel, "scaled state is updated whole"
+            st = type_code(t.p)
+            assert st in (BF16, F16) and t.m.dtype == t.p.dtype and t.v.dtype == t.p.dtype
+            assert t.scales.dtype == np.float32 and t.scales.size == 3
+            assert t.p_out is None or type_code(t.p_out) in (BF16, F16)
+            rc = self.lib.oracle_adam_scaled(_ptr(t.p), _ptr(t.m), _ptr(t.v), st, _ptr(t.scales),
+                                             g_ptr, g_type, out_ptr, out_type, count, *scal)
+            if rc != 0:
+                raise MemoryError("oracle_adam_scaled could not allocate its work buffers")
+            return
+        m_ptr = _ptr(t.m) + 4 * lo
+        v_ptr = _ptr(t.v) + 4 * lo
         if t.rem is None:
             assert t.p.dtype == np.float32
             self.lib.oracle_adam_f32(_ptr(t.p) + 4 * lo, m_ptr, v_ptr, g_ptr,
-                                     g_is_bf16, out_ptr, count, *scal)
+                                     g_type, out_ptr, out_type, count, *scal)
         else:
             assert t.p.dtype == np.uint16 and t.rem.dtype == np.int16
+            assert out_type in (F32, BF16), "remainder param-out is the new bf16 param"
             self.lib.oracle_adam_remainder(_ptr(t.p) + 2 * lo, _ptr(t.rem) + 2 * lo,
-                                           m_ptr, v_ptr, g_ptr, g_is_bf16, out_ptr,
+                                           m_ptr, v_ptr, g_ptr, g_type, out_ptr,
                                            count, *scal)
 
     # -- gradient norm and clipping -------------------------------------------
@@ -189,12 +271,12 @@ class Oracle:
 
     def accumulate_squares(self, total, grads: Sequence[np.ndarray], threads: int = 1) -> None:
         """Adds the squares of every element of the gradient arrays (float32,
-        or bf16 bits as uint16) to the accumulator ``total``, exactly.
+        bf16 bits as uint16, or float16) to the accumulator ``total``, exactly.
         ``threads`` > 1 splits the work; the result does not depend on it."""
         jobs = []  # (array, lo, hi)
         for g in grads:
             g = np.ascontiguousarray(g)
-            assert g.dtype in (np.float32, np.uint16)
+            type_code(g)
             n = g.size
             per = max(1, -(-n // max(1, threads)))
             for lo in range(0, n, per):
@@ -204,7 +286,7 @@ class Oracle:
         def run(k):
             g, lo, hi = jobs[k]
             self.lib.oracle_acc_add_squares(accs[k], _ptr(g) + g.dtype.itemsize * lo,
-                                            1 if g.dtype == np.uint16 else 0, hi - lo)
+                                            type_code(g), hi - lo)
 
         if threads > 1 and len(jobs) > 1:
             from concurrent.futures import ThreadPoolExecutor

@@ -16,7 +16,9 @@
  *   [P2] apex distributed_fused_adam.py (master): _bf16_rem_to_fp32 (the
  *        bf16 + int16 remainder encoding), _local_step_with_param_remainders,
  *        step() (step counter handling), _load_state_dict_v2 (remainder =
- *        low int16 half of the fp32 word).
+ *        low int16 half of the fp32 word), _local_step_with_scaled_states
+ *        and _apply_state_scale (per-tensor scaled 16-bit optimizer state),
+ *        _check_params_shard_dtypes (param-sync cast).
  *
  * Precision: the pages compute the update in `float` with `float` state, so
  * every operation here is a single IEEE binary32 operation, rounded to
@@ -38,10 +40,18 @@
  *   - the remainder functor's body is not shown; it is read as decode ->
  *     the float update above -> encode, where encode is the unique inverse
  *     of the decoder _bf16_rem_to_fp32 prints.
+ *   - float -> binary16 casts (fp16 param-out, fp16 scaled state) round to
+ *     nearest even with IEEE overflow to infinity and subnormals kept.
+ *   - scaled state: torch.reciprocal and the float division of the scale are
+ *     correctly rounded float operations.
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
+
+/* Element types of the gradient, param-out and scaled-state buffers. */
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
 
 static float f32_from_bits(uint32_t b)
 {
@@ -143,7 +153,68 @@ void oracle_rem_encode(float x, uint16_t *bf16, int16_t *rem)
     *bf16 = (uint16_t)(high + (r < 0 ? 1u : 0u));
 }
 
+/* float -> IEEE binary16 bits, round to nearest, ties to even, from the
+ * definition of the format: near |x| in [2^e, 2^(e+1)) the binary16 values
+ * are spaced 2^(e-10) apart (e >= -14; below 2^-14 the subnormals are spaced
+ * 2^-24).  |x| divided by that spacing (exact in double) is rounded to an
+ * integer with ties to even (rint in the default rounding mode); a result of
+ * 2^16 or more overflows to infinity.  NaN stays NaN (quiet, sign kept). */
+uint16_t oracle_f16_rne(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7E00u);
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7C00u);
+    double a = fabs((double)x);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);                       /* a in [2^(e-1), 2^e) */
+    int low = e - 1 < -14 ? -14 : e - 1;
+    double spacing = ldexp(1.0, low - 10);
+    double r = rint(a / spacing) * spacing;
+    if (r >= 65536.0)
+        return (uint16_t)(sign | 0x7C00u);
+    if (r < ldexp(1.0, -14))            /* subnormal (or zero): count of 2^-24 */
+        return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+    int re;
+    double f = frexp(r, &re);           /* r = f * 2^re, f in [0.5, 1) */
+    uint16_t exponent = (uint16_t)(re - 1 + 15);
+    uint16_t fraction = (uint16_t)((2.0 * f - 1.0) * 1024.0);
+    return (uint16_t)(sign | (exponent << 10) | fraction);
+}
+
+/* binary16 bits -> float (exact): (-1)^s * 2^(e-15) * (1 + f/1024), or
+ * f * 2^-24 for e == 0; e == 31 is infinity or NaN. */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int negative = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int f = h & 0x3FF;
+    double mag;
+    if (e == 0x1F)
+        mag = f ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)f, -24);
+    else
+        mag = ldexp(1024.0 + f, e - 25);
+    return (float)(negative ? -mag : mag);
+}
+
 /* Array forms, used by the exhaustive encoding tests. */
+void oracle_f16_rne_array(const float *x, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f16_rne(x[i]);
+}
+
+void oracle_f16_to_f32_array(const uint16_t *h, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f16_to_f32(h[i]);
+}
+
 void oracle_bf16_rne_array(const float *x, uint16_t *out, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i)
@@ -223,17 +294,26 @@ static float adam_element(float P, float G, float *M, float *V,
     return P - step;
 }
 
-static float load_grad(const void *g, int32_t g_is_bf16, int64_t i)
+/* Gradient element i as float (g_type: ORACLE_F32, ORACLE_BF16, ORACLE_F16). */
+static float load_grad(const void *g, int32_t g_type, int64_t i)
 {
-    if (g_is_bf16)
-        return oracle_bf16_to_f32(((const uint16_t *)g)[i]);
-    return ((const float *)g)[i];
+    if (g_type == ORACLE_F32)
+        return ((const float *)g)[i];
+    uint16_t h = ((const uint16_t *)g)[i];
+    return g_type == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
 }
 
-/* fp32 params: p, m, v updated in place over n elements; g is float or bf16
- * bits; p_out (nullable) receives round-to-nearest-even bf16 of the new p. */
+/* The param-out cast (out_type ORACLE_BF16 or ORACLE_F16), nearest even. */
+static uint16_t cast_out(float x, int32_t out_type)
+{
+    return out_type == ORACLE_F16 ? oracle_f16_rne(x) : oracle_bf16_rne(x);
+}
+
+/* fp32 params: p, m, v updated in place over n elements; g is float, bf16 or
+ * fp16 (g_type); p_out (nullable) receives the new p cast to bf16 or fp16
+ * (out_type), round to nearest even. */
 void oracle_adam_f32(float *p, float *m, float *v, const void *g,
-                     int32_t g_is_bf16, uint16_t *p_out, int64_t n,
+                     int32_t g_type, uint16_t *p_out, int32_t out_type, int64_t n,
                      float lr, float beta1, float beta2, float eps,
                      float weight_decay, int32_t mode, float bc1, float bc2,
                      float grad_scale)
@@ -243,12 +323,12 @@ void oracle_adam_f32(float *p, float *m, float *v, const void *g,
     for (int64_t i = 0; i < n; ++i) {
         float M = m[i];
         float V = v[i];
-        float P_new = adam_element(p[i], load_grad(g, g_is_bf16, i), &M, &V, &s);
+        float P_new = adam_element(p[i], load_grad(g, g_type, i), &M, &V, &s);
         p[i] = P_new;
         m[i] = M;
         v[i] = V;
         if (p_out)
-            p_out[i] = oracle_bf16_rne(P_new);
+            p_out[i] = cast_out(P_new, out_type);
     }
 }
 
@@ -256,7 +336,7 @@ void oracle_adam_f32(float *p, float *m, float *v, const void *g,
  * is decoded to float, updated exactly as above, and encoded back; p_out
  * (nullable) receives the new bf16 param bits. */
 void oracle_adam_remainder(uint16_t *p, int16_t *rem, float *m, float *v,
-                           const void *g, int32_t g_is_bf16, uint16_t *p_out,
+                           const void *g, int32_t g_type, uint16_t *p_out,
                            int64_t n, float lr, float beta1, float beta2,
                            float eps, float weight_decay, int32_t mode,
                            float bc1, float bc2, float grad_scale)
@@ -267,13 +347,111 @@ void oracle_adam_remainder(uint16_t *p, int16_t *rem, float *m, float *v,
         float P = oracle_rem_decode(p[i], rem[i]);
         float M = m[i];
         float V = v[i];
-        float P_new = adam_element(P, load_grad(g, g_is_bf16, i), &M, &V, &s);
+        float P_new = adam_element(P, load_grad(g, g_type, i), &M, &V, &s);
         oracle_rem_encode(P_new, &p[i], &rem[i]);
         m[i] = M;
         v[i] = V;
         if (p_out)
             p_out[i] = p[i];
     }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Per-tensor scaled 16-bit optimizer state: [P2]                          */
+/* _local_step_with_scaled_states, _apply_state_scale,                     */
+/* _check_params_shard_dtypes.                                             */
+/* ---------------------------------------------------------------------- */
+
+static float state_to_f32(uint16_t h, int32_t type)
+{
+    return type == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
+}
+
+static uint16_t f32_to_state(float x, int32_t type)
+{
+    return type == ORACLE_F16 ? oracle_f16_rne(x) : oracle_bf16_rne(x);
+}
+
+/* Half the largest finite value of the state type (torch.finfo(dtype).max
+ * / 2, exact in float): the magnitude the largest scaled element is mapped
+ * to.  binary16: (2 - 2^-10) * 2^15 / 2; bfloat16: (2 - 2^-7) * 2^127 / 2. */
+float oracle_scaled_state_limit(int32_t type)
+{
+    if (type == ORACLE_F16)
+        return ldexpf(2.0f - ldexpf(1.0f, -10), 14);
+    return ldexpf(2.0f - ldexpf(1.0f, -7), 126);
+}
+
+/* max(-min(x), max(x)) over a float buffer, NaN when any element is NaN (the
+ * minimum and maximum reductions propagate NaN). */
+static float abs_max(const float *x, int64_t n)
+{
+    float lo = x[0], hi = x[0];
+    for (int64_t i = 0; i < n; ++i) {
+        if (isnan(x[i]))
+            return NAN;
+        if (x[i] < lo)
+            lo = x[i];
+        if (x[i] > hi)
+            hi = x[i];
+    }
+    float neg_lo = -lo;
+    return neg_lo > hi ? neg_lo : hi;
+}
+
+/* _apply_state_scale, then the copy into the state type: scale = absmax /
+ * limit, every element multiplied by 1/scale (0 when scale is not positive)
+ * and cast to the state type.  Returns the new scale.  n must be > 0. */
+float oracle_rescale_store(const float *x, uint16_t *out, int64_t n, int32_t type)
+{
+    float absmax = abs_max(x, n);
+    float scale = absmax / oracle_scaled_state_limit(type);
+    float rscale = scale > 0.0f ? 1.0f / scale : 0.0f;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f32_to_state(x[i] * rscale, type);
+    return scale;
+}
+
+/* One step of one tensor with scaled state.  p, m, v hold 16-bit values of
+ * state_type (bf16 or fp16) and scales[0..2] their float scales; all are
+ * updated in place.  In the pages' order: the state is copied to float and
+ * multiplied by its scale; the float update runs with the param as its own
+ * output; the param-sync copy p_out (nullable, bf16 or fp16) is the new float
+ * param cast to its type; then each of param, exp_avg, exp_avg_sq gets a new
+ * scale from its largest magnitude and is stored scaled.  An empty tensor
+ * is left alone (it holds no fragment of the local shard).  Returns 0, or -1
+ * when the float work buffers cannot be allocated. */
+int oracle_adam_scaled(uint16_t *p, uint16_t *m, uint16_t *v, int32_t state_type,
+                       float *scales, const void *g, int32_t g_type,
+                       uint16_t *p_out, int32_t out_type, int64_t n,
+                       float lr, float beta1, float beta2, float eps,
+                       float weight_decay, int32_t mode, float bc1, float bc2,
+                       float grad_scale)
+{
+    if (n <= 0)
+        return 0;
+    float *P = malloc(sizeof(float) * (size_t)n * 3);
+    if (P == NULL)
+        return -1;
+    float *M = P + n;
+    float *V = P + 2 * n;
+    for (int64_t i = 0; i < n; ++i) {
+        P[i] = state_to_f32(p[i], state_type) * scales[0];
+        M[i] = state_to_f32(m[i], state_type) * scales[1];
+        V[i] = state_to_f32(v[i], state_type) * scales[2];
+    }
+    struct oracle_scalars s = {lr, beta1, beta2, eps, weight_decay,
+                               bc1, bc2, grad_scale, mode};
+    for (int64_t i = 0; i < n; ++i)
+        P[i] = adam_element(P[i], load_grad(g, g_type, i), &M[i], &V[i], &s);
+    if (p_out)
+        for (int64_t i = 0; i < n; ++i)
+            p_out[i] = cast_out(P[i], out_type);
+    scales[0] = oracle_rescale_store(P, p, n, state_type);
+    scales[1] = oracle_rescale_store(M, m, n, state_type);
+    scales[2] = oracle_rescale_store(V, v, n, state_type);
+    free(P);
+    return 0;
 }
 
 /* ---------------------------------------------------------------------- */
@@ -344,10 +522,10 @@ static void acc_add_double(struct oracle_acc *a, double x)
     acc_add_bits(a, word, lo, hi);
 }
 
-void oracle_acc_add_squares(struct oracle_acc *a, const void *g, int32_t g_is_bf16, int64_t n)
+void oracle_acc_add_squares(struct oracle_acc *a, const void *g, int32_t g_type, int64_t n)
 {
     for (int64_t i = 0; i < n; ++i) {
-        double x = (double)load_grad(g, g_is_bf16, i);
+        double x = (double)load_grad(g, g_type, i);
         acc_add_double(a, x * x);          /* exact: at most 48 significant bits */
     }
 }

@@ -27,7 +27,19 @@ What pins what:
                               the empty-group reproduction (tests/golden);
 * gradient sum of squares   - math.fsum (a correctly rounded sum) of the
                               squares, closed forms, non-finite inputs;
-* clip / found-inf step     - float64 torch.nn.utils.clip_grad_norm_.
+* clip / found-inf step     - float64 torch.nn.utils.clip_grad_norm_;
+* fp16 casts                - numpy's float32 -> float16 cast (round to
+                              nearest even, IEEE overflow, subnormals) and
+                              its exact float16 -> float32 widening;
+* fp16 gradients / p_out    - the fp32 update of the exactly widened
+                              gradient, numpy's cast of the new param;
+* scaled 16-bit state       - the pages' own torch op sequence for the
+                              unscale / rescale steps (aminmax, maximum, div,
+                              reciprocal, where, mul, dtype casts) around the
+                              pinned fp32 update; closed forms (zero tensors,
+                              power-of-two scales); the largest stored value
+                              sits at half the type's maximum; NaN
+                              propagation.
 """
 from __future__ import annotations
 
@@ -591,6 +603,257 @@ def check_clip_grad_scale(o: Oracle, seed: int = 41):
     assert found == 0 and new_s == np.float32(0.25) and norm == np.float32(1000.0 * 0.25)
 
 
+# ---------------------------------------------------------------------------
+# fp16 casts, fp16 gradients and param-out
+# ---------------------------------------------------------------------------
+
+def special_f16_edges() -> np.ndarray:
+    """float32 bit patterns at the binary16 cast's edges: the overflow
+    threshold 65520 and its neighbours, the largest finite 65504, the normal /
+    subnormal boundary 2^-14, the smallest subnormal 2^-24 and the underflow
+    tie 2^-25, ties with even and odd kept bits in both ranges, signed
+    zeros, infinities, NaNs."""
+    vals = [65504.0, 65519.996, 65520.0, 65520.004, 65535.0, 65536.0, 1e10,
+            2.0 ** -14, 2.0 ** -14 * (1 - 2.0 ** -12), 2.0 ** -24, 2.0 ** -25,
+            2.0 ** -25 * (1 + 2.0 ** -20), 3 * 2.0 ** -25, 5 * 2.0 ** -25, 2.0 ** -26,
+            1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -11 + 2.0 ** -20,
+            2.0 ** -15 + 2.0 ** -25, 2.0 ** -15 + 3 * 2.0 ** -25, 0.1, 1.0 / 3.0, 1e-7]
+    x = np.array(vals + [-v for v in vals], np.float32)
+    extra = np.array([0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x7FC00000,
+                      0xFFC00001, 0x7F800001, 0x00000001, 0x807FFFFF], np.uint32)
+    pats = np.concatenate([x.view(np.uint32), extra])
+    return np.concatenate([pats, pats + 1, pats - 1]).astype(np.uint32)
+
+
+def check_f16_rne(o: Oracle, patterns: np.ndarray):
+    """Finite and infinite inputs: bitwise equal to numpy's float32 ->
+    float16 cast.  NaN: stays NaN with its sign."""
+    x = patterns.astype(np.uint32).view(np.float32)
+    got = o.f16_rne(x).view(np.uint16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], want[~nan])
+    if nan.any():
+        gn = got[nan].astype(np.uint32)
+        assert np.all((gn & 0x7C00) == 0x7C00) and np.all((gn & 0x03FF) != 0)
+        assert np.array_equal(gn >> 15, patterns[nan].astype(np.uint32) >> 31)
+
+
+def check_f16_decode(o: Oracle):
+    """All 65536 binary16 patterns widen exactly, as numpy widens them."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    got = o.f16_to_f32(h)
+    want = h.astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
+def check_f16_codec_quick(o: Oracle):
+    check_f16_rne(o, np.concatenate([special_f16_edges(), sampled_patterns(1 << 18, seed=21)]))
+    check_f16_decode(o)
+
+
+def check_f16_grad_and_param_out(o: Oracle, seed: int = 42):
+    """fp16 gradients are widened exactly: the update equals the fp32 update
+    of the widened gradient, bit for bit (both modes); an fp16 p_out is
+    numpy's cast of the new fp32 param, including values beyond the fp16
+    range (infinity) and below it (subnormals, zero)."""
+    rng = np.random.default_rng(seed)
+    n = 3001
+    p0 = rng.standard_normal(n).astype(np.float32)
+    p0[:8] = [70000.0, -70000.0, 65519.0, 1e-6, -3e-8, 0.0, 2.0 ** -20, 65504.0]
+    g16 = (rng.standard_normal(n) * 1e-3).astype(np.float16)
+    g16[:4] = np.array([6e-8, -6e-8, 1e-5, 60000.0], np.float16)  # subnormal, large
+    g_wide = g16.astype(np.float32)
+    for mode in (0, 1):
+        hp = HParams(0.9, 0.95, 1e-8, 0.1, mode, 1)
+        t16 = OracleTensor(p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), g16.copy(),
+                           np.zeros(n, np.float16))
+        t32 = OracleTensor(p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), g_wide.copy())
+        s16, s32 = [0], [0]
+        for _ in range(3):
+            o.group_step([t16], hp, 1.6e-3, s16, 0.5)
+            o.group_step([t32], hp, 1.6e-3, s32, 0.5)
+            assert np.array_equal(t16.p.view(np.uint32), t32.p.view(np.uint32))
+            assert np.array_equal(t16.v.view(np.uint32), t32.v.view(np.uint32))
+            with np.errstate(over="ignore"):
+                want = t32.p.astype(np.float16)
+            assert np.array_equal(t16.p_out.view(np.uint16), want.view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# Scaled 16-bit optimizer state
+# ---------------------------------------------------------------------------
+
+def _torch_state_dtype(state_dtype):
+    import torch
+
+    return torch.float16 if np.dtype(state_dtype) == np.float16 else torch.bfloat16
+
+
+def _to_numpy_state(t, state_dtype) -> np.ndarray:
+    import torch
+
+    bits = t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    return bits.view(np.float16) if np.dtype(state_dtype) == np.float16 else bits.copy()
+
+
+def _from_numpy_state(a: np.ndarray, state_dtype):
+    import torch
+
+    bits = torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy())
+    return bits.view(_torch_state_dtype(state_dtype))
+
+
+def torch_apply_state_scale(x32: np.ndarray, state_dtype):
+    """The pages' _apply_state_scale followed by the copy into the state
+    dtype, as the torch op sequence they print (CPU, float32)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x32, np.float32).copy())
+    dt = _torch_state_dtype(state_dtype)
+    max_scaled = torch.full([1], torch.finfo(dt).max / 2, dtype=torch.float32)
+    min_val, max_val = torch.aminmax(t)
+    absmax = torch.maximum(-min_val, max_val).to(torch.float32)
+    scale = torch.empty([1], dtype=torch.float32)
+    torch.div(absmax, max_scaled, out=scale)
+    rscale = torch.where(scale > 0, scale.reciprocal(), 0.0)
+    t.mul_(rscale)
+    return _to_numpy_state(t.to(dt), state_dtype), np.float32(scale.item())
+
+
+def torch_unscale(a: np.ndarray, scale, state_dtype) -> np.ndarray:
+    """The pages' unscale: copy to float32, then multiply by the scale."""
+    import torch
+
+    t = _from_numpy_state(a, state_dtype).to(torch.float32)
+    t.mul_(torch.tensor([float(scale)], dtype=torch.float32))
+    return t.numpy().copy()
+
+
+def _scaled_tensor(o: Oracle, rng, n: int, state_dtype, g, out_dtype):
+    """Scaled state from p ~ N(0,1), m, v of mid-training size.  bf16 state
+    takes m, v with magnitudes above 1: the pages' scale maps the largest
+    magnitude to half of bf16's maximum (~1.7e38), so below ~0.5 the float
+    reciprocal of the scale overflows (see the special cases)."""
+    p0 = rng.standard_normal(n).astype(np.float32)
+    if np.dtype(state_dtype) == np.float16:
+        m0 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        v0 = (np.abs(rng.standard_normal(n)) * 1e-6).astype(np.float32)
+    else:
+        m0 = (rng.standard_normal(n) * 4.0).astype(np.float32)
+        v0 = (np.abs(rng.standard_normal(n)) * 4.0 + 1.0).astype(np.float32)
+    parts = [torch_apply_state_scale(x, state_dtype) for x in (p0, m0, v0)]
+    scales = np.array([sc for _, sc in parts], np.float32)
+    p_out = None if out_dtype is None else np.zeros(n, out_dtype)
+    return OracleTensor(parts[0][0], parts[1][0], parts[2][0], g, p_out, None, scales)
+
+
+def check_scaled_state(o: Oracle, seed: int = 43):
+    """Scaled state, both state types: (1) the oracle's scaling of a float
+    buffer equals the pages' torch sequence bit for bit; (2) three steps equal
+    [torch unscale -> the pinned fp32 update -> torch casts for p_out ->
+    torch rescale], bit for bit in p, m, v, the three scales and p_out;
+    (3) the largest stored magnitude is half the type's maximum, rounded;
+    (4) dequantised values are within the type's relative precision of the
+    float32 values they came from."""
+    rng = np.random.default_rng(seed)
+    n = 1537
+    for state_dtype, out_dtype, g_dtype in ((np.uint16, np.uint16, np.float32),
+                                            (np.float16, np.float16, np.uint16),
+                                            (np.uint16, np.float16, np.float16),
+                                            (np.float16, None, np.float32)):
+        limit = o.scaled_state_limit(state_dtype)
+        x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-6, 3)).astype(np.float32)
+        got, sc = o.scale_state(x, state_dtype)
+        want, wsc = torch_apply_state_scale(x, state_dtype)
+        assert sc == wsc and np.array_equal(got.view(np.uint16), want.view(np.uint16))
+        g32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        g = g32 if g_dtype == np.float32 else (
+            g32.astype(np.float16) if g_dtype == np.float16 else torch_bf16_bits(g32))
+        for mode in (0, 1):
+            hp = HParams(0.9, 0.95, 1e-8, 0.1, mode, 1)
+            t = _scaled_tensor(o, rng, n, state_dtype, g.copy(), out_dtype)
+            ref = OracleTensor(t.p.copy(), t.m.copy(), t.v.copy(), g.copy(), None, None, t.scales.copy())
+            st, sr = [0], [0]
+            for _ in range(3):
+                o.group_step([t], hp, 1.6e-3, st, 1.0)
+                # reference: unscale, fp32 update, casts, rescale
+                f = OracleTensor(torch_unscale(ref.p, ref.scales[0], state_dtype),
+                                 torch_unscale(ref.m, ref.scales[1], state_dtype),
+                                 torch_unscale(ref.v, ref.scales[2], state_dtype), g.copy())
+                o.group_step([f], hp, 1.6e-3, sr, 1.0)
+                if out_dtype is not None:
+                    import torch
+
+                    cast = torch.from_numpy(f.p.copy()).to(_torch_state_dtype(out_dtype))
+                    assert np.array_equal(t.p_out.view(np.uint16),
+                                          _to_numpy_state(cast, out_dtype).view(np.uint16))
+                for k, (name, arr) in enumerate((("p", f.p), ("m", f.m), ("v", f.v))):
+                    stored, scale = torch_apply_state_scale(arr, state_dtype)
+                    assert scale == t.scales[k], (name, scale, t.scales[k])
+                    assert np.array_equal(getattr(t, name).view(np.uint16), stored.view(np.uint16)), name
+                    setattr(ref, name, stored)
+                    ref.scales[k] = scale
+                    # largest stored magnitude sits at the limit, within rounding
+                    dec = torch_unscale(stored, 1.0, state_dtype).astype(np.float64)
+                    top = np.max(np.abs(dec))
+                    rel = 2.0 ** -8 if state_dtype == np.uint16 else 2.0 ** -11
+                    assert abs(top - float(limit)) <= 2 * rel * float(limit), (name, top, limit)
+                    # dequantised values track the float values
+                    back = dec * float(scale)
+                    tol = rel * np.abs(arr.astype(np.float64)) + float(scale) * 2.0 ** -24 + 1e-45
+                    if state_dtype == np.float16:  # binary16 subnormals: absolute spacing
+                        tol = tol + float(scale) * 2.0 ** -25
+                    assert np.all(np.abs(back - arr) <= tol * 1.01), name
+
+
+def check_scaled_state_special_cases(o: Oracle):
+    """Closed forms: an all-zero buffer gets scale 0 and stores zeros (and
+    unscales to zeros); a buffer whose largest magnitude is the limit times
+    2^k gets scale 2^k exactly and stores RNE(x / 2^k); a NaN makes the scale
+    NaN and every stored finite value a zero; an infinity makes the scale
+    infinite, the infinity NaN, and every finite value a zero."""
+    for state_dtype in (np.uint16, np.float16):
+        limit = float(o.scaled_state_limit(state_dtype))
+        z, sc = o.scale_state(np.zeros(17, np.float32), state_dtype)
+        assert sc == 0.0 and not np.any(z.view(np.uint16) & 0x7FFF)
+        rng = np.random.default_rng(44)
+        for k in (-30, -3, 0):
+            x = (rng.uniform(-1, 1, 257) * limit * 2.0 ** k).astype(np.float32)
+            x[100] = np.float32(-limit * 2.0 ** k)
+            got, sc = o.scale_state(x, state_dtype)
+            assert sc == np.float32(2.0 ** k), (k, sc)
+            want = (x / np.float32(2.0 ** k)).astype(np.float32)
+            if state_dtype == np.float16:
+                assert np.array_equal(got.view(np.uint16), want.astype(np.float16).view(np.uint16))
+            else:
+                assert np.array_equal(got, torch_bf16_bits(want))
+        # bf16 range: a largest magnitude below ~0.5 gives a subnormal scale
+        # whose float reciprocal overflows, so finite values store as +-inf
+        # (the torch sequence does the same)
+        if state_dtype == np.uint16:
+            x = np.array([1e-3, -2e-4, 0.0, 0.25], np.float32)
+            got, sc = o.scale_state(x, state_dtype)
+            want, wsc = torch_apply_state_scale(x, state_dtype)
+            assert sc == wsc and 0 < sc < np.finfo(np.float32).tiny
+            # 0 * inf is NaN: compare NaN as NaN (payloads differ)
+            assert list(got[[0, 1, 3]]) == list(want[[0, 1, 3]]) == [0x7F80, 0xFF80, 0x7F80]
+            assert (int(got[2]) & 0x7FFF) > 0x7F80 and (int(want[2]) & 0x7FFF) > 0x7F80
+        for bad in (np.nan, np.inf):
+            x = np.array([1.0, -2.0, bad, 0.5], np.float32)
+            got, sc = o.scale_state(x, state_dtype)
+            want_scale_nan = bool(np.isnan(bad))
+            assert np.isnan(sc) if want_scale_nan else sc == np.inf
+            bits = got.view(np.uint16).astype(np.uint32)
+            fin = np.isfinite(x)
+            assert np.all((bits[fin] & 0x7FFF) == 0)  # finite * 0 = signed zero
+            dec = torch_unscale(got[~fin], 1.0, state_dtype)
+            assert np.all(np.isnan(dec))
+
+
 QUICK_CHECKS = (
     "check_bias_corrections_quick",
     "check_first_step_adamw",
@@ -606,6 +869,10 @@ QUICK_CHECKS = (
     "check_noop_and_counter",
     "check_grad_sumsq",
     "check_clip_grad_scale",
+    "check_f16_codec_quick",
+    "check_f16_grad_and_param_out",
+    "check_scaled_state",
+    "check_scaled_state_special_cases",
 )
 
 

@@ -42,7 +42,8 @@ MUTANTS = {
     "decode_sign_fix_dropped": [("(uint16_t)(bf16 - (rem < 0 ? 1u : 0u))", "(uint16_t)(bf16)")],
     "encode_carry_dropped": [("(uint16_t)(high + (r < 0 ? 1u : 0u))", "(uint16_t)(high)")],
     "decode_halves_swapped": [("((uint32_t)high << 16) | (uint32_t)low", "((uint32_t)low << 16) | (uint32_t)high")],
-    "param_out_truncated": [("p_out[i] = oracle_bf16_rne(P_new);", "p_out[i] = (uint16_t)(bits_from_f32(P_new) >> 16);")],
+    "param_out_truncated": [("return out_type == ORACLE_F16 ? oracle_f16_rne(x) : oracle_bf16_rne(x);",
+                             "return out_type == ORACLE_F16 ? oracle_f16_rne(x) : (uint16_t)(bits_from_f32(x) >> 16);")],
     "remainder_param_out_rne": [("p_out[i] = p[i];", "p_out[i] = oracle_bf16_rne(P_new);")],
     "bf16_grad_index_shift": [("((const uint16_t *)g)[i]", "((const uint16_t *)g)[i ? i - 1 : 0]")],
     "one_minus_beta_wrong": [("float one_minus_beta = 1.0f - beta;", "float one_minus_beta = beta - 1.0f;")],
@@ -52,6 +53,30 @@ MUTANTS = {
     "sumsq_square_in_float": [("acc_add_double(a, x * x);", "acc_add_double(a, (double)((float)x * (float)x));")],
     "sumsq_merge_drops_flags": [("    into->has_inf |= from->has_inf;\n", "")],
     "sumsq_bit_position_off_by_one": [("int shift = (e - 53) - ACC_LSB_EXP;", "int shift = (e - 52) - ACC_LSB_EXP;")],
+    "f16_ties_away": [("double r = rint(a / spacing) * spacing;", "double r = round(a / spacing) * spacing;")],
+    "f16_truncates": [("double r = rint(a / spacing) * spacing;", "double r = trunc(a / spacing) * spacing;")],
+    "f16_subnormal_spacing": [("int low = e - 1 < -14 ? -14 : e - 1;", "int low = e - 1 < -15 ? -15 : e - 1;")],
+    "f16_overflow_early": [("if (r >= 65536.0)", "if (r >= 65504.0)")],
+    "f16_decode_bias": [("mag = ldexp(1024.0 + f, e - 25);", "mag = ldexp(1024.0 + f, e - 24);")],
+    "f16_decode_subnormal": [("mag = ldexp((double)f, -24);", "mag = ldexp((double)f, -25);")],
+    "f16_grad_read_as_bf16": [("return g_type == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);",
+                               "return oracle_bf16_to_f32(h);")],
+    "f16_out_cast_as_bf16": [("return out_type == ORACLE_F16 ? oracle_f16_rne(x) : oracle_bf16_rne(x);",
+                              "return oracle_bf16_rne(x);")],
+    "scaled_bf16_limit_not_halved": [("return ldexpf(2.0f - ldexpf(1.0f, -7), 126);",
+                                      "return ldexpf(2.0f - ldexpf(1.0f, -7), 127);")],
+    "scaled_f16_limit_not_halved": [("return ldexpf(2.0f - ldexpf(1.0f, -10), 14);",
+                                     "return ldexpf(2.0f - ldexpf(1.0f, -10), 15);")],
+    "scaled_rscale_not_reciprocal": [("float rscale = scale > 0.0f ? 1.0f / scale : 0.0f;",
+                                      "float rscale = scale > 0.0f ? scale : 0.0f;")],
+    "scaled_absmax_ignores_negatives": [("return neg_lo > hi ? neg_lo : hi;", "return hi;")],
+    "scaled_absmax_drops_nan": [("        if (isnan(x[i]))\n            return NAN;\n", "")],
+    "scaled_unscale_dropped": [("P[i] = state_to_f32(p[i], state_type) * scales[0];",
+                                "P[i] = state_to_f32(p[i], state_type);")],
+    "scaled_moment_scales_swapped": [("M[i] = state_to_f32(m[i], state_type) * scales[1];",
+                                      "M[i] = state_to_f32(m[i], state_type) * scales[2];")],
+    "scaled_param_sync_from_stored": [("p_out[i] = cast_out(P[i], out_type);", "p_out[i] = p[i];")],
+    "scaled_scale_not_returned": [("    scales[1] = oracle_rescale_store(M, m, n, state_type);\n", "")],
 }
 
 

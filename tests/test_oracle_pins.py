@@ -72,6 +72,23 @@ def test_clip_grad_scale_matches_torch_clip(oracle_default):
     pins.check_clip_grad_scale(oracle_default)
 
 
+def test_f16_cast_edges_and_decode(oracle_default):
+    pins.check_f16_rne(oracle_default, pins.special_f16_edges())
+    pins.check_f16_decode(oracle_default)
+
+
+def test_f16_gradients_and_param_out(oracle_default):
+    pins.check_f16_grad_and_param_out(oracle_default)
+
+
+def test_scaled_state_matches_the_pages_torch_sequence(oracle_default):
+    pins.check_scaled_state(oracle_default)
+
+
+def test_scaled_state_special_cases(oracle_default):
+    pins.check_scaled_state_special_cases(oracle_default)
+
+
 def test_host_counter_overflow_wraps_like_int32(oracle_default):
     from oracle import HParams
 
@@ -108,6 +125,12 @@ def _over_all_patterns(fn):
 def test_bf16_rne_exhaustive(oracle_default):
     """All 2^32 float32 bit patterns against torch's cast."""
     _over_all_patterns(lambda pats: pins.check_bf16_rne(oracle_default, pats))
+
+
+@pytest.mark.slow
+def test_f16_rne_exhaustive(oracle_default):
+    """All 2^32 float32 bit patterns against numpy's float32 -> float16 cast."""
+    _over_all_patterns(lambda pats: pins.check_f16_rne(oracle_default, pats))
 
 
 @pytest.mark.slow
