@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_PKG, "libadamw_mi355x.so")
 
 ADAM_OK, ADAM_EINVAL, ADAM_EDTYPE, ADAM_ENOMEM, ADAM_EHIP = 0, -1, -2, -3, -4
-DT_NONE, DT_F32, DT_BF16 = 0, 1, 2
+DT_NONE, DT_F32, DT_BF16, DT_F16 = 0, 1, 2, 3
 
 c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -26,13 +26,13 @@ c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctyp
 class AdamTensor(ctypes.Structure):
     """adam_tensor"""
     _fields_ = [("p", c_vp), ("rem", c_vp), ("m", c_vp), ("v", c_vp), ("g", c_vp),
-                ("p_out", c_vp), ("numel", c_i64)]
+                ("p_out", c_vp), ("scales", c_vp), ("numel", c_i64)]
 
 
 class AdamTlDesc(ctypes.Structure):
     """adam_tl_desc"""
     _fields_ = [("p", c_i32), ("g", c_i32), ("p_out", c_i32), ("with_remainders", c_i32),
-                ("chunk_elems", c_i64), ("reserved0", c_i32), ("reserved1", c_i32)]
+                ("chunk_elems", c_i64), ("scaled_state", c_i32), ("reserved1", c_i32)]
 
 
 class AdamHParams(ctypes.Structure):
@@ -66,7 +66,8 @@ _lib = None
 
 EXPORTED = ("adam_abi_version", "adam_status_string", "adam_tl_plan", "adam_tl_build",
             "adam_tl_destroy", "adam_tl_info", "adam_step", "adam_step_capturable",
-            "adam_step_remainders", "adam_grad_sumsq", "adam_clip_grad_scale")
+            "adam_step_remainders", "adam_step_remainders_capturable", "adam_step_scaled",
+            "adam_grad_sumsq", "adam_clip_grad_scale")
 
 
 def lib():
@@ -98,13 +99,17 @@ def lib():
     L.adam_step.restype = c_i32
     L.adam_step_remainders.argtypes = L.adam_step.argtypes
     L.adam_step_remainders.restype = c_i32
+    L.adam_step_scaled.argtypes = L.adam_step.argtypes
+    L.adam_step_scaled.restype = c_i32
     L.adam_step_capturable.argtypes = [c_vp, ctypes.POINTER(AdamHParams), c_vp, c_vp, c_vp, c_vp, c_vp]
     L.adam_step_capturable.restype = c_i32
+    L.adam_step_remainders_capturable.argtypes = L.adam_step_capturable.argtypes
+    L.adam_step_remainders_capturable.restype = c_i32
     L.adam_grad_sumsq.argtypes = [c_vp, c_vp, c_i32, c_vp]
     L.adam_grad_sumsq.restype = c_i32
     L.adam_clip_grad_scale.argtypes = [c_vp, c_vp, c_f32, c_vp, c_vp, c_vp]
     L.adam_clip_grad_scale.restype = c_i32
-    if L.adam_abi_version() != 1:
+    if L.adam_abi_version() != 2:
         raise ImportError("libadamw_mi355x.so has an unexpected ABI version")
     _lib = L
     return L
@@ -156,34 +161,40 @@ def _tensor_array(tensors: Sequence, desc: AdamTlDesc):
     try:
         import torch
 
-        f32, bf16, i16 = torch.float32, torch.bfloat16, torch.int16
-        torch_dtypes = {DT_F32: (f32,), DT_BF16: (bf16, i16)}
+        f32, bf16, f16, i16 = torch.float32, torch.bfloat16, torch.float16, torch.int16
+        # 16-bit buffers may also be int16 views of the raw bits
+        torch_dtypes = {DT_F32: (f32,), DT_BF16: (bf16, i16), DT_F16: (f16, i16)}
     except ImportError:  # raw addresses only
         pass
+    mv = desc.p if desc.scaled_state == 1 else DT_F32
     for i, t in enumerate(tensors):
         n = _numel(t)
         if torch_dtypes is not None:
             _check_tensor(_get(t, "p"), "p", torch_dtypes.get(desc.p, ()))
-            _check_tensor(_get(t, "m"), "m", torch_dtypes[DT_F32])
-            _check_tensor(_get(t, "v"), "v", torch_dtypes[DT_F32])
+            _check_tensor(_get(t, "m"), "m", torch_dtypes[mv])
+            _check_tensor(_get(t, "v"), "v", torch_dtypes[mv])
             _check_tensor(_get(t, "g"), "g", torch_dtypes.get(desc.g, ()))
             if _get(t, "p_out") is not None:
-                _check_tensor(_get(t, "p_out"), "p_out", torch_dtypes[DT_BF16])
+                _check_tensor(_get(t, "p_out"), "p_out", torch_dtypes.get(desc.p_out, ()))
             if _get(t, "rem") is not None:
-                _check_tensor(_get(t, "rem"), "rem", torch_dtypes[DT_BF16])
+                _check_tensor(_get(t, "rem"), "rem", (torch.int16,))
+            if _get(t, "scales") is not None:
+                _check_tensor(_get(t, "scales"), "scales", torch_dtypes[DT_F32])
         arr[i] = AdamTensor(_addr(_get(t, "p")), _addr(_get(t, "rem")), _addr(_get(t, "m")),
-                            _addr(_get(t, "v")), _addr(_get(t, "g")), _addr(_get(t, "p_out")), n)
+                            _addr(_get(t, "v")), _addr(_get(t, "g")), _addr(_get(t, "p_out")),
+                            _addr(_get(t, "scales")), n)
     return arr
 
 
 def make_desc(*, g="f32", p="f32", p_out=None, chunk_elems=0) -> AdamTlDesc:
-    """Descriptor from short names: g in {"f32","bf16"}, p in {"f32","bf16_rem"},
-    p_out in {None, "bf16"}."""
-    gd = {"f32": DT_F32, "bf16": DT_BF16}[g]
-    rem = 1 if p == "bf16_rem" else 0
-    pd = DT_BF16 if rem else {"f32": DT_F32}[p]
-    od = {None: DT_NONE, "bf16": DT_BF16}[p_out]
-    return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), 0, 0)
+    """Descriptor from short names: g in {"f32", "bf16", "f16"}; p in {"f32",
+    "bf16_rem" (bf16 + int16 remainders), "bf16_scaled", "f16_scaled" (scaled
+    16-bit p, m, v)}; p_out in {None, "bf16", "f16"}."""
+    gd = {"f32": DT_F32, "bf16": DT_BF16, "f16": DT_F16}[g]
+    pd, rem, scaled = {"f32": (DT_F32, 0, 0), "bf16_rem": (DT_BF16, 1, 0),
+                       "bf16_scaled": (DT_BF16, 0, 1), "f16_scaled": (DT_F16, 0, 1)}[p]
+    od = {None: DT_NONE, "bf16": DT_BF16, "f16": DT_F16}[p_out]
+    return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), scaled, 0)
 
 
 def _stream(stream) -> Optional[int]:
@@ -241,8 +252,8 @@ class TensorList:
 
 def adam_tl_build(tensors: Sequence, desc: AdamTlDesc, stream=None) -> TensorList:
     """Builds a handle for one group (see include/adam.h).  ``tensors`` holds
-    dicts or objects with p, m, v, g and optional rem / p_out (torch tensors
-    or int device addresses plus ``numel``)."""
+    dicts or objects with p, m, v, g and optional rem / p_out / scales (torch
+    tensors or int device addresses plus ``numel``)."""
     arr = _tensor_array(tensors, desc)
     out = c_vp()
     s = _stream(stream) if len(tensors) and any(_numel(t) for t in tensors) else (stream or 0)
@@ -286,6 +297,14 @@ def adam_step_remainders(tl: TensorList, hp: AdamHParams, lr: float, step: HostS
                                                   stream)), "adam_step_remainders")
 
 
+def adam_step_scaled(tl: TensorList, hp: AdamHParams, lr: float, step: HostStep,
+                     grad_scale: float = 1.0, d_grad_scale=None, stream=None) -> None:
+    """Non-capturable step of a scaled 16-bit-state handle (each tensor's
+    ``scales`` are read and replaced)."""
+    _check(lib().adam_step_scaled(*_step_args(tl, hp, lr, step, grad_scale, d_grad_scale, stream)),
+           "adam_step_scaled")
+
+
 def adam_step_capturable(tl: TensorList, hp: AdamHParams, d_lr, d_step, d_grad_scale=None,
                          d_noop=None, stream=None) -> None:
     """Capturable step: lr (float32), step (int32), grad scale (float32) and
@@ -293,6 +312,16 @@ def adam_step_capturable(tl: TensorList, hp: AdamHParams, d_lr, d_step, d_grad_s
     _check(lib().adam_step_capturable(tl.handle, ctypes.byref(hp), _addr(d_lr), _addr(d_step),
                                       _addr(d_grad_scale), _addr(d_noop), _stream(stream)),
            "adam_step_capturable")
+
+
+def adam_step_remainders_capturable(tl: TensorList, hp: AdamHParams, d_lr, d_step,
+                                    d_grad_scale=None, d_noop=None, stream=None) -> None:
+    """Capturable step of a bf16 + int16-remainder handle (device scalars as
+    adam_step_capturable)."""
+    _check(lib().adam_step_remainders_capturable(tl.handle, ctypes.byref(hp), _addr(d_lr),
+                                                 _addr(d_step), _addr(d_grad_scale), _addr(d_noop),
+                                                 _stream(stream)),
+           "adam_step_remainders_capturable")
 
 
 def adam_grad_sumsq(tl: TensorList, d_sumsq, accumulate: bool = False, stream=None) -> None:

@@ -4,16 +4,16 @@
 // What is computed is defined by the apex patch "Enhance Distributed Fused
 // Adam (#1794)" (DistAdamCapturableFunctor::local_step and operator()) and by
 // apex distributed_fused_adam.py (step(), _bf16_rem_to_fp32, grad_norm,
-// clip_grad_norm); the header states it in full.  How it runs is this file's
-// own design:
+// clip_grad_norm, _local_step_with_scaled_states, _apply_state_scale); the
+// header states it in full.  How it runs is this file's own design:
 //
 //  * The host turns a tensor list into a table of 64-byte work items.  Each
 //    item is a run of at most `chunk` elements (a power of two) of one tensor
 //    with every stream pointer already advanced to the run's start.
 //  * One launch covers the whole list with one 128-thread workgroup (two
 //    waves) per 512-element tile.  Each lane moves exactly one 4-element
-//    group per stream (16-byte fp32, 8-byte bf16 / int16 accesses), so a
-//    wave's access is 1 KiB (or 512 B) of contiguous memory.  Measured on
+//    group per stream (16-byte fp32, 8-byte bf16 / fp16 / int16 accesses), so
+//    a wave's access is 1 KiB (or 512 B) of contiguous memory.  Measured on
 //    MI355X: 8-element lanes (16-byte accesses of the 16-bit streams, two
 //    adjacent 16-byte accesses of the fp32 ones) run 10-25% slower on every
 //    list with a 16-bit stream.  Workgroup b reads item t >> shift of tile
@@ -32,7 +32,7 @@
 //  * Records start on a 128-byte boundary in every stream when one element
 //    index gets there for all of them (true for views at equal offsets into
 //    flat buffers, the usual layout), else where every stream is aligned for
-//    its lane access: a tensor's first record carries `head`, the 0..63
+//    its 4-element access: a tensor's first record carries `head`, the 0..63
 //    leading elements before that point, which tile 0 of the record updates
 //    element by element at negative indices.  Line-aligned tiles keep two
 //    workgroups from writing parts of one cache line (measured on ragged
@@ -41,15 +41,22 @@
 //    coalesced, narrower accesses); the ragged tail of a tile is finished
 //    element by element.
 //  * Per-step scalars are kernel arguments (non-capturable).  The capturable
-//    step first runs a one-lane prologue that reads the device lr, step,
+//    steps first run a one-lane prologue that reads the device lr, step,
 //    grad scale and noop flag, advances the step (unless noop == 1), and
 //    writes the resolved scalars, bias corrections included, to a 64-byte
 //    block beside the work table; every tile then reads that one block.
+//  * Scaled 16-bit state needs each buffer's largest magnitude after the
+//    update before any of it can be stored, so it takes two passes over the
+//    same tiles: the first computes the update in registers and folds
+//    per-tensor maxima (one atomic maximum per workgroup and buffer, skipped
+//    when the stored maximum is already larger); the second recomputes the
+//    identical update and stores it with the new scales.  A one-lane-per-
+//    tensor kernel then writes the scales.
 //  * Arithmetic follows the header's expressions operation for operation in
 //    binary32 (the library is built with -ffp-contract=off; division and
 //    square root are the compiler's correctly rounded sequences; fp32
 //    denormals are kept), so results match a scalar C evaluation bit for bit
-//    and do not depend on chunking, lane width or alignment.
+//    and do not depend on chunking or alignment.
 
 #include <hip/hip_runtime.h>
 
@@ -58,6 +65,7 @@
 
 #include <algorithm>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "adam.h"
@@ -87,10 +95,22 @@ constexpr int64_t kMaxNumel = int64_t(1) << 56;
 constexpr int64_t kMaxGrid = int64_t(1) << 31;
 constexpr int64_t kMaxHead = 63;            // a 2-byte stream reaches a 128-byte boundary within 63 elements
 constexpr int kRunElems = ADAM_RUN_ELEMS;   // elements each XCD updates before the next XCD's run
+constexpr uint32_t kRun = uint32_t(kRunElems / kTile);
 constexpr uint32_t kNormRun = ADAM_NORM_RUN_ELEMS / kTile;  // tiles per reduction workgroup
 static_assert(kBlock > kMaxHead, "tile 0 updates the head with one element per lane");
+static_assert(kBlock % 64 == 0, "whole waves");
 static_assert(kMinChunk % kTile == 0 && kRunElems % kTile == 0 && ADAM_NORM_RUN_ELEMS % kTile == 0,
               "records and runs hold whole tiles");
+
+// Element types: the adam_dtype values.
+constexpr int kNone = ADAM_DT_NONE;
+constexpr int kF32 = ADAM_DT_F32;
+constexpr int kBF16 = ADAM_DT_BF16;
+constexpr int kF16 = ADAM_DT_F16;
+
+// How params are stored (non-scaled update kernels).
+constexpr int kParamF32 = 0;  // fp32 params
+constexpr int kParamRem = 1;  // bf16 params + int16 remainders
 
 enum : uint32_t { kItemVector = 1u };
 
@@ -98,15 +118,15 @@ enum : uint32_t { kItemVector = 1u };
 // first element; absent streams are null.
 struct alignas(64) WorkItem {
     void *p;
-    int16_t *rem;
-    float *m;
-    float *v;
+    void *aux;       // int16 remainders (remainder mode), or the tensor's float[3] scales (scaled state)
+    void *m;
+    void *v;
     const void *g;
     void *p_out;
     int32_t n;       // elements in the run, 1 .. chunk
     uint32_t flags;  // kItemVector: every stream allows 4-element accesses
     int32_t head;    // elements just before the run, updated by its tile 0 (0..63)
-    int32_t unused;
+    int32_t tensor;  // ordinal of the tensor among the non-empty ones
 };
 static_assert(sizeof(WorkItem) == 64, "work item must be one 64-byte record");
 
@@ -193,6 +213,78 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x)
     const uint32_t b = __float_as_uint(x);
     if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x40u;
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// binary16 bits (round to nearest, ties to even) of a float, in integer
+// steps.  Normal results: the exponent is rebiased by 127 - 15 = 112 and the
+// 13 dropped fraction bits are rounded like the bf16 case (a carry may ripple
+// into the exponent).  Magnitudes from 65520 (the midpoint between the
+// largest finite 65504 and 2^16, which rounds to even, i.e. up) overflow to
+// infinity.  Below 2^-14 the result is a subnormal count of 2^-24: the 24-bit
+// significand shifted right by 126 - exponent, rounded to nearest even on
+// the shifted-out bits; 2^-25 and below give zero.  NaN keeps sign and top
+// payload and is made quiet.
+__device__ __forceinline__ uint32_t f16_bits_rne(float x)
+{
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t sign = (b >> 16) & 0x8000u;
+    const uint32_t a = b & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7E00u | ((a >> 13) & 0x3FFu);
+    if (a >= 0x477FF000u) return sign | 0x7C00u;
+    if (a >= 0x38800000u) {
+        const uint32_t r = a - 0x38000000u;
+        return sign | ((r + 0xFFFu + ((r >> 13) & 1u)) >> 13);
+    }
+    if (a <= 0x33000000u) return sign;
+    const uint32_t shift = 126u - (a >> 23);  // 14 .. 24
+    const uint32_t sig = (a & 0x7FFFFFu) | 0x800000u;
+    const uint32_t q = sig >> shift;
+    const uint32_t rest = sig & ((1u << shift) - 1u);
+    const uint32_t half = 1u << (shift - 1u);
+    return sign | (q + ((rest > half || (rest == half && (q & 1u))) ? 1u : 0u));
+}
+
+// binary16 bits -> float, exact: normal values rebias the exponent by 112;
+// subnormals (f * 2^-24) are normalised so their leading one becomes the
+// implicit bit; exponent 31 is infinity or NaN.
+__device__ __forceinline__ float f16_to_f32(uint32_t h)
+{
+    const uint32_t sign = (h & 0x8000u) << 16;
+    const uint32_t e = (h >> 10) & 0x1Fu;
+    const uint32_t f = h & 0x3FFu;
+    uint32_t bits;
+    if (e == 0x1Fu) {
+        bits = sign | 0x7F800000u | (f << 13);
+    } else if (e != 0u) {
+        bits = sign | ((e + 112u) << 23) | (f << 13);
+    } else if (f == 0u) {
+        bits = sign;
+    } else {
+        const uint32_t s = uint32_t(__builtin_clz(f)) - 21u;  // 1 .. 10: moves the leading one to bit 10
+        bits = sign | ((113u - s) << 23) | (((f << s) & 0x3FFu) << 13);
+    }
+    return __uint_as_float(bits);
+}
+
+// 16-bit storage types: bits -> float, float -> bits.
+template <int T>
+__device__ __forceinline__ float widen16(uint32_t h)
+{
+    static_assert(T == kBF16 || T == kF16, "16-bit type");
+    if constexpr (T == kBF16)
+        return __uint_as_float(h << 16);
+    else
+        return f16_to_f32(h);
+}
+
+template <int T>
+__device__ __forceinline__ uint32_t narrow16(float x)
+{
+    static_assert(T == kBF16 || T == kF16, "16-bit type");
+    if constexpr (T == kBF16)
+        return bf16_bits_rne(x);
+    else
+        return f16_bits_rne(x);
 }
 
 // Remainder encoding.  The fp32 master word is the bf16 half shifted up plus
@@ -282,14 +374,42 @@ __device__ __forceinline__ void store_f32x4(void *base, int gi, const float *x)
     store_stream<f32x4>(base, gi, f32x4{x[0], x[1], x[2], x[3]});
 }
 
+// Gradients of type GT (fp32, bf16 or fp16) as float: a lane group, or one.
+template <int GT>
+__device__ __forceinline__ void load_grad4(const void *g, int gi, float *x)
+{
+    if constexpr (GT == kF32) {
+        load_f32x4(g, gi, x);
+    } else {
+        uint32_t h[kLane];
+        load_u16x4(g, gi, h);
+#pragma unroll
+        for (int k = 0; k < kLane; ++k) x[k] = widen16<GT>(h[k]);
+    }
+}
+
+template <int GT>
+__device__ __forceinline__ float load_grad1(const void *g, int i)
+{
+    if constexpr (GT == kF32)
+        return load_one<float>(g, i);
+    else
+        return widen16<GT>(load_one<uint16_t>(g, i));
+}
+
+// ---------------------------------------------------------------------------
+// The update kernel (fp32 params or bf16 params + remainders)
+// ---------------------------------------------------------------------------
+
 // Kernel configuration (compile-time).
-template <bool G_BF16, bool P_REM, bool OUT, int MODE, bool CAPT>
+template <int GT, int PK, int OT, int MODE, bool CAPT>
 struct Config {
-    static constexpr bool g_bf16 = G_BF16;
-    static constexpr bool p_rem = P_REM;
-    static constexpr bool out = OUT;
+    static constexpr int gt = GT;     // gradient type
+    static constexpr int pk = PK;     // kParamF32 or kParamRem
+    static constexpr int ot = OT;     // param-out type, kNone if absent
     static constexpr int mode = MODE;
     static constexpr bool capturable = CAPT;
+    static_assert(PK == kParamF32 || OT != kF16, "remainder param-out is the new bf16 param");
 };
 
 // The four consecutive elements of lane group gi, updated in registers:
@@ -300,18 +420,11 @@ __device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Co
     float p[kLane], m[kLane], v[kLane], g[kLane];
     load_f32x4(w.m, gi, m);
     load_f32x4(w.v, gi, v);
-    if constexpr (C::g_bf16) {
-        uint32_t gb[kLane];
-        load_u16x4(w.g, gi, gb);
-#pragma unroll
-        for (int k = 0; k < kLane; ++k) g[k] = __uint_as_float(gb[k] << 16);
-    } else {
-        load_f32x4(w.g, gi, g);
-    }
-    if constexpr (C::p_rem) {
+    load_grad4<C::gt>(w.g, gi, g);
+    if constexpr (C::pk == kParamRem) {
         uint32_t h[kLane], r[kLane];
         load_u16x4(w.p, gi, h);
-        load_u16x4(w.rem, gi, r);
+        load_u16x4(w.aux, gi, r);
 #pragma unroll
         for (int k = 0; k < kLane; ++k) p[k] = master_from(h[k], r[k]);
     } else {
@@ -322,19 +435,19 @@ __device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Co
 
     store_f32x4(w.m, gi, m);
     store_f32x4(w.v, gi, v);
-    if constexpr (C::p_rem) {
+    if constexpr (C::pk == kParamRem) {
         uint32_t h[kLane], r[kLane];
 #pragma unroll
         for (int k = 0; k < kLane; ++k) master_to(p[k], h[k], r[k]);
         store_u16x4(w.p, gi, h);
-        store_u16x4(w.rem, gi, r);
-        if constexpr (C::out) store_u16x4(w.p_out, gi, h);
+        store_u16x4(w.aux, gi, r);
+        if constexpr (C::ot != kNone) store_u16x4(w.p_out, gi, h);
     } else {
         store_f32x4(w.p, gi, p);
-        if constexpr (C::out) {
+        if constexpr (C::ot != kNone) {
             uint32_t o[kLane];
 #pragma unroll
-            for (int k = 0; k < kLane; ++k) o[k] = bf16_bits_rne(p[k]);
+            for (int k = 0; k < kLane; ++k) o[k] = narrow16<C::ot>(p[k]);
             store_u16x4(w.p_out, gi, o);
         }
     }
@@ -344,25 +457,21 @@ __device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Co
 template <class C>
 __device__ __forceinline__ void update_single(const WorkItem &w, int i, const Coeffs &c)
 {
-    float g;
-    if constexpr (C::g_bf16)
-        g = __uint_as_float(uint32_t(load_one<uint16_t>(w.g, i)) << 16);
-    else
-        g = load_one<float>(w.g, i);
+    const float g = load_grad1<C::gt>(w.g, i);
     float m = load_one<float>(w.m, i);
     float v = load_one<float>(w.v, i);
-    if constexpr (C::p_rem) {
-        const float p = master_from(load_one<uint16_t>(w.p, i), load_one<uint16_t>(w.rem, i));
+    if constexpr (C::pk == kParamRem) {
+        const float p = master_from(load_one<uint16_t>(w.p, i), load_one<uint16_t>(w.aux, i));
         const float pn = update_element<C::mode>(p, g, m, v, c);
         uint32_t h, r;
         master_to(pn, h, r);
         store_one<uint16_t>(w.p, i, uint16_t(h));
-        store_one<uint16_t>(w.rem, i, uint16_t(r));
-        if constexpr (C::out) store_one<uint16_t>(w.p_out, i, uint16_t(h));
+        store_one<uint16_t>(w.aux, i, uint16_t(r));
+        if constexpr (C::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(h));
     } else {
         const float pn = update_element<C::mode>(load_one<float>(w.p, i), g, m, v, c);
         store_one<float>(w.p, i, pn);
-        if constexpr (C::out) store_one<uint16_t>(w.p_out, i, uint16_t(bf16_bits_rne(pn)));
+        if constexpr (C::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<C::ot>(pn)));
     }
     store_one<float>(w.m, i, m);
     store_one<float>(w.v, i, v);
@@ -387,18 +496,35 @@ __device__ __forceinline__ uint32_t tile_of_block(uint32_t b, uint32_t grid)
     return b;
 }
 
+// The per-workgroup constants of a non-capturable step.
+__device__ __forceinline__ Coeffs host_coeffs(const StepArgs &a)
+{
+    Coeffs c;
+    c.lr = a.lr;
+    c.scale = a.d_grad_scale != nullptr ? *a.d_grad_scale : a.grad_scale;
+    c.bc1 = a.bc1;
+    c.bc2 = a.bc2;
+    c.beta1 = a.beta1;
+    c.keep1 = 1.0f - a.beta1;
+    c.beta2 = a.beta2;
+    c.keep2 = 1.0f - a.beta2;
+    c.eps = a.eps;
+    c.wd = a.weight_decay;
+    return c;
+}
+
 // The update: workgroup b handles tile t = tile_of_block(b): tile
 // (t & mask) of work item (t >> shift).
 template <class C>
 __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict__ items,
                                                        uint32_t shift, StepArgs a)
 {
-    const uint32_t b = tile_of_block<uint32_t(kRunElems / kTile)>(blockIdx.x, gridDim.x);
+    const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
     const WorkItem w = items[b >> shift];
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
     if (start >= w.n) return;  // past the end of a tensor's last item
 
-    Coeffs c;
+    Coeffs c = host_coeffs(a);
     if constexpr (C::capturable) {
         const StepBlock s = *a.block;
         if (s.skip) return;
@@ -406,18 +532,7 @@ __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict
         c.scale = s.scale;
         c.bc1 = s.bc1;
         c.bc2 = s.bc2;
-    } else {
-        c.lr = a.lr;
-        c.scale = a.d_grad_scale != nullptr ? *a.d_grad_scale : a.grad_scale;
-        c.bc1 = a.bc1;
-        c.bc2 = a.bc2;
     }
-    c.beta1 = a.beta1;
-    c.keep1 = 1.0f - a.beta1;
-    c.beta2 = a.beta2;
-    c.keep2 = 1.0f - a.beta2;
-    c.eps = a.eps;
-    c.wd = a.weight_decay;
 
     const int n = min(kTile, w.n - start);
     const int tid = threadIdx.x;
@@ -454,11 +569,193 @@ __global__ void adam_capture_prologue(StepBlock *block, const float *d_lr, int32
 }
 
 // ---------------------------------------------------------------------------
+// Scaled 16-bit state (apex distributed_fused_adam.py,
+// _local_step_with_scaled_states and _apply_state_scale).  p, m, v of type ST
+// times the tensor's three float scales are the fp32 values; the step
+// updates those and stores them again with new scales.
+// ---------------------------------------------------------------------------
+
+// Half the largest finite value of the state type, as a float.
+template <int ST>
+__host__ __device__ constexpr float scaled_limit()
+{
+    // bfloat16: (2 - 2^-7) * 2^127 / 2 (bits 0x7EFF0000);  binary16: 65504 / 2
+    return ST == kBF16 ? 1.69476569462576773e38f : 32752.0f;
+}
+
+template <int ST, int GT, int OT, int MODE, int PASS>
+struct ScaledConfig {
+    static constexpr int st = ST;      // state type of p, m, v
+    static constexpr int gt = GT;
+    static constexpr int ot = OT;
+    static constexpr int mode = MODE;
+    static constexpr int pass = PASS;  // 0: fold maxima; 1: store
+};
+
+// Magnitude bits of a float: ordering them as unsigned integers orders the
+// magnitudes, with every NaN above infinity.
+__device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
+
+// The reciprocal scale that maps a buffer with largest magnitude `amax` to
+// the state type: 1 / (amax / limit), or 0 when that scale is not positive
+// (also NaN).
+template <int ST>
+__device__ __forceinline__ float rscale_of(uint32_t amax)
+{
+    const float scale = __uint_as_float(amax) / scaled_limit<ST>();
+    return scale > 0.0f ? 1.0f / scale : 0.0f;
+}
+
+// One lane group: unscale, update; then fold maxima (pass 0) or store (pass 1).
+template <class S>
+__device__ __forceinline__ void scaled_group(const WorkItem &w, int gi, const Coeffs &c,
+                                             const float *sc, const float *r, uint32_t *mx)
+{
+    uint32_t hp[kLane], hm[kLane], hv[kLane];
+    float p[kLane], m[kLane], v[kLane], g[kLane];
+    load_u16x4(w.p, gi, hp);
+    load_u16x4(w.m, gi, hm);
+    load_u16x4(w.v, gi, hv);
+    load_grad4<S::gt>(w.g, gi, g);
+#pragma unroll
+    for (int k = 0; k < kLane; ++k) {
+        p[k] = widen16<S::st>(hp[k]) * sc[0];
+        m[k] = widen16<S::st>(hm[k]) * sc[1];
+        v[k] = widen16<S::st>(hv[k]) * sc[2];
+        p[k] = update_element<S::mode>(p[k], g[k], m[k], v[k], c);
+    }
+    if constexpr (S::pass == 0) {
+#pragma unroll
+        for (int k = 0; k < kLane; ++k) {
+            mx[0] = max(mx[0], abs_bits(p[k]));
+            mx[1] = max(mx[1], abs_bits(m[k]));
+            mx[2] = max(mx[2], abs_bits(v[k]));
+        }
+    } else {
+        if constexpr (S::ot != kNone) {
+            uint32_t o[kLane];
+#pragma unroll
+            for (int k = 0; k < kLane; ++k) o[k] = narrow16<S::ot>(p[k]);
+            store_u16x4(w.p_out, gi, o);
+        }
+#pragma unroll
+        for (int k = 0; k < kLane; ++k) {
+            hp[k] = narrow16<S::st>(p[k] * r[0]);
+            hm[k] = narrow16<S::st>(m[k] * r[1]);
+            hv[k] = narrow16<S::st>(v[k] * r[2]);
+        }
+        store_u16x4(w.p, gi, hp);
+        store_u16x4(w.m, gi, hm);
+        store_u16x4(w.v, gi, hv);
+    }
+}
+
+template <class S>
+__device__ __forceinline__ void scaled_single(const WorkItem &w, int i, const Coeffs &c,
+                                              const float *sc, const float *r, uint32_t *mx)
+{
+    const float g = load_grad1<S::gt>(w.g, i);
+    float p = widen16<S::st>(load_one<uint16_t>(w.p, i)) * sc[0];
+    float m = widen16<S::st>(load_one<uint16_t>(w.m, i)) * sc[1];
+    float v = widen16<S::st>(load_one<uint16_t>(w.v, i)) * sc[2];
+    p = update_element<S::mode>(p, g, m, v, c);
+    if constexpr (S::pass == 0) {
+        mx[0] = max(mx[0], abs_bits(p));
+        mx[1] = max(mx[1], abs_bits(m));
+        mx[2] = max(mx[2], abs_bits(v));
+    } else {
+        if constexpr (S::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<S::ot>(p)));
+        store_one<uint16_t>(w.p, i, uint16_t(narrow16<S::st>(p * r[0])));
+        store_one<uint16_t>(w.m, i, uint16_t(narrow16<S::st>(m * r[1])));
+        store_one<uint16_t>(w.v, i, uint16_t(narrow16<S::st>(v * r[2])));
+    }
+}
+
+// Device-coherent load of one word (the maxima are folded by every XCD).
+__device__ __forceinline__ uint32_t load_agent(const uint32_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One pass over the tiles of a scaled-state list (same tile map as the
+// update).  amax holds three magnitude maxima (p, m, v) per tensor: pass 0
+// folds into them, pass 1 reads them.
+template <class S>
+__global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__restrict__ items,
+                                                            uint32_t shift, StepArgs a,
+                                                            uint32_t *__restrict__ amax)
+{
+    const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
+    const WorkItem w = items[b >> shift];
+    const int start = int(b & ((1u << shift) - 1u)) * kTile;
+    if (start >= w.n) return;  // uniform across the workgroup
+
+    const Coeffs c = host_coeffs(a);
+    const float *scales = static_cast<const float *>(w.aux);
+    const float sc[3] = {scales[0], scales[1], scales[2]};
+    uint32_t *slot = amax + 3 * w.tensor;
+    float r[3] = {0.0f, 0.0f, 0.0f};
+    if constexpr (S::pass == 1) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) r[j] = rscale_of<S::st>(load_agent(slot + j));
+    }
+    uint32_t mx[3] = {0u, 0u, 0u};
+
+    const int n = min(kTile, w.n - start);
+    const int tid = threadIdx.x;
+    if (w.flags & kItemVector) {
+        if (start == 0 && tid < w.head) scaled_single<S>(w, tid - w.head, c, sc, r, mx);
+        const int groups = n / kLane;
+        if (tid < groups) scaled_group<S>(w, start / kLane + tid, c, sc, r, mx);
+        if (tid < n - groups * kLane) scaled_single<S>(w, start + groups * kLane + tid, c, sc, r, mx);
+    } else {
+        for (int i = tid; i < n; i += kBlock) scaled_single<S>(w, start + i, c, sc, r, mx);
+    }
+
+    if constexpr (S::pass == 0) {
+        // workgroup maxima, then one atomic maximum per buffer (skipped when
+        // the tensor's maximum is already at least as large)
+        __shared__ uint32_t wave_max[3][kBlock / 64];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            uint32_t x = mx[j];
+            for (int off = 32; off > 0; off >>= 1) x = max(x, uint32_t(__shfl_xor(int(x), off, 64)));
+            if (tid % 64 == 0) wave_max[j][tid / 64] = x;
+        }
+        __syncthreads();
+        if (tid < 3) {
+            uint32_t x = 0u;
+            for (int k = 0; k < kBlock / 64; ++k) x = max(x, wave_max[tid][k]);
+            if (x > load_agent(slot + tid)) atomicMax(slot + tid, x);
+        }
+    }
+}
+
+// Zeroes the per-tensor maxima (device-coherent stores).
+__global__ void adam_scaled_clear(uint32_t *amax, uint32_t count)
+{
+    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
+        __hip_atomic_store(amax + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One lane per tensor: the new scales, amax / limit.
+template <int ST>
+__global__ void adam_scaled_finish(float *const *__restrict__ scale_ptrs,
+                                   const uint32_t *__restrict__ amax, uint32_t tensors)
+{
+    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= tensors) return;
+    float *s = scale_ptrs[k];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(load_agent(amax + 3 * k + j)) / scaled_limit<ST>();
+}
+
+// ---------------------------------------------------------------------------
 // Gradient sum of squares and the clip / found-inf step (apex
 // distributed_fused_adam.py: grad_norm, clip_grad_norm, the found-inf check
-// of step()).  Squares of float or bf16 gradients are exact in double; every
-// workgroup adds its squares in a fixed order, partial sums are folded in a
-// fixed order, so the result does not depend on scheduling.
+// of step()).  Squares of float, bf16 or fp16 gradients are exact in double;
+// every workgroup adds its squares in a fixed order, partial sums are folded
+// in a fixed order, so the result does not depend on scheduling.
 // ---------------------------------------------------------------------------
 constexpr int kFoldBlock = 256;
 constexpr int kNormUnroll = 4;  // 16-byte loads in flight per lane
@@ -477,32 +774,22 @@ __device__ __forceinline__ double block_sum(double x)
     return total;  // meaningful in thread 0
 }
 
-// One gradient element as float.
-template <bool G_BF16>
-__device__ __forceinline__ float grad_at(const WorkItem &w, int i)
-{
-    if constexpr (G_BF16)
-        return __uint_as_float(uint32_t(load_one<uint16_t>(w.g, i)) << 16);
-    else
-        return load_one<float>(w.g, i);
-}
-
-// The squares of the gradients in one 16-byte word (8 bf16 or 4 fp32), added
-// to acc in element order.
-template <bool G_BF16>
+// The squares of the gradients in one 16-byte word (8 bf16 / fp16 or 4 fp32),
+// added to acc in element order.
+template <int GT>
 __device__ __forceinline__ double add_squares16(double acc, u32x4 q)
 {
     const uint32_t x[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        if constexpr (G_BF16) {
-            const double lo = __uint_as_float(x[k] << 16);
-            const double hi = __uint_as_float(x[k] & 0xFFFF0000u);
-            acc += lo * lo;
-            acc += hi * hi;
-        } else {
+        if constexpr (GT == kF32) {
             const double f = __uint_as_float(x[k]);
             acc += f * f;
+        } else {
+            const double lo = widen16<GT>(x[k] & 0xFFFFu);
+            const double hi = widen16<GT>(x[k] >> 16);
+            acc += lo * lo;
+            acc += hi * hi;
         }
     }
     return acc;
@@ -517,14 +804,14 @@ __device__ __forceinline__ double add_squares16(double acc, u32x4 q)
 // loads on bf16 gradients).  The 0..7 elements before the first 16-byte
 // boundary and after the last whole word go element by element; the update's
 // alignment of the other streams does not matter here.
-template <bool G_BF16>
+template <int GT>
 __global__ __launch_bounds__(kBlock) void grad_sumsq_partial(const WorkItem *__restrict__ items,
                                                               uint32_t shift, uint32_t tiles,
                                                               uint32_t run,
                                                               double *__restrict__ partials)
 {
-    constexpr int GS = G_BF16 ? 2 : 4;  // bytes per gradient element
-    constexpr int W = 16 / GS;          // gradient elements per 16-byte word
+    constexpr int GS = GT == kF32 ? 4 : 2;  // bytes per gradient element
+    constexpr int W = 16 / GS;              // gradient elements per 16-byte word
     const uint32_t first = blockIdx.x * run;
     const uint32_t last = min(first + run, tiles);
     const int tid = threadIdx.x;
@@ -539,14 +826,14 @@ __global__ __launch_bounds__(kBlock) void grad_sumsq_partial(const WorkItem *__r
         t = t_end;
         if (e0 >= e1) continue;  // tiles past the end of a tensor's last record
         if ((w.flags & kItemVector) && e0 == 0 && tid < w.head) {
-            const double x = grad_at<G_BF16>(w, tid - w.head);
+            const double x = load_grad1<GT>(w.g, tid - w.head);
             acc += x * x;
         }
         // e0 is a whole number of tiles, so element e0 has the record's
         // alignment modulo 16 bytes
         const int lead = min(e1 - e0, int(((16u - (uintptr_t(w.g) & 15u)) & 15u) / GS));
         if (tid < lead) {
-            const double x = grad_at<G_BF16>(w, e0 + tid);
+            const double x = load_grad1<GT>(w.g, e0 + tid);
             acc += x * x;
         }
         const int words = (e1 - e0 - lead) / W;
@@ -559,10 +846,10 @@ __global__ __launch_bounds__(kBlock) void grad_sumsq_partial(const WorkItem *__r
                 q[u] = vi < words ? load_stream<u32x4>(base, vi) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int u = 0; u < kNormUnroll; ++u) acc = add_squares16<G_BF16>(acc, q[u]);
+            for (int u = 0; u < kNormUnroll; ++u) acc = add_squares16<GT>(acc, q[u]);
         }
         for (int i = e0 + lead + words * W + tid; i < e1; i += kBlock) {
-            const double x = grad_at<G_BF16>(w, i);
+            const double x = load_grad1<GT>(w.g, i);
             acc += x * x;
         }
     }
@@ -601,44 +888,87 @@ __global__ void clip_grad_scale_kernel(const double *d_sumsq, float *d_grad_scal
 }
 
 // ---------------------------------------------------------------------------
-// Host side
+// Host side: kernel tables
 // ---------------------------------------------------------------------------
 
-typedef void (*KernelFn)(const WorkItem *, uint32_t, StepArgs);
+typedef void (*UpdateFn)(const WorkItem *, uint32_t, StepArgs);
+typedef void (*ScaledFn)(const WorkItem *, uint32_t, StepArgs, uint32_t *);
 
-// Kernel table index: g_bf16 | p_rem << 1 | out << 2 | mode << 3 | capturable << 4.
+constexpr int kGradTypes[3] = {kF32, kBF16, kF16};
+constexpr int kOutTypes[3] = {kNone, kBF16, kF16};
+constexpr int kStateTypes[2] = {kBF16, kF16};
+
+// Update table index: g + 3 * (param kind + 2 * (out + 3 * (mode + 2 * capturable))),
+// with g and out positions in kGradTypes / kOutTypes.
 template <int I>
-constexpr KernelFn kernel_at()
+constexpr UpdateFn update_at()
 {
-    return adam_update<Config<(I & 1) != 0, (I & 2) != 0, (I & 4) != 0, (I >> 3) & 1, (I & 16) != 0>>;
+    constexpr int g = kGradTypes[I % 3];
+    constexpr int pk = (I / 3) % 2;
+    constexpr int ot = kOutTypes[(I / 6) % 3];
+    constexpr int mode = (I / 18) % 2;
+    constexpr bool capt = (I / 36) != 0;
+    if constexpr (pk == kParamRem && ot == kF16)
+        return nullptr;  // refused by the planner
+    else
+        return adam_update<Config<g, pk, ot, mode, capt>>;
+}
+
+// Scaled table index: g + 3 * (out + 3 * (state + 2 * (mode + 2 * pass))).
+template <int I>
+constexpr ScaledFn scaled_at()
+{
+    constexpr int g = kGradTypes[I % 3];
+    constexpr int ot = kOutTypes[(I / 3) % 3];
+    constexpr int st = kStateTypes[(I / 9) % 2];
+    constexpr int mode = (I / 18) % 2;
+    constexpr int pass = I / 36;
+    return adam_scaled_pass<ScaledConfig<st, g, ot, mode, pass>>;
 }
 
 template <int... I>
-struct KernelTable {
-    static constexpr KernelFn fns[sizeof...(I)] = {kernel_at<I>()...};
+struct UpdateTable {
+    static constexpr UpdateFn fns[sizeof...(I)] = {update_at<I>()...};
 };
-using AllKernels = KernelTable<0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19,
-                               20, 21, 22, 23, 24, 25, 26, 27, 28, 29, 30, 31>;
+template <int... I>
+struct ScaledTable {
+    static constexpr ScaledFn fns[sizeof...(I)] = {scaled_at<I>()...};
+};
 
-inline int kernel_index(bool g_bf16, bool p_rem, bool out, int mode, bool capturable)
+template <int... I>
+UpdateTable<I...> update_table(std::integer_sequence<int, I...>);
+template <int... I>
+ScaledTable<I...> scaled_table(std::integer_sequence<int, I...>);
+
+using UpdateKernels = decltype(update_table(std::make_integer_sequence<int, 72>()));
+using ScaledKernels = decltype(scaled_table(std::make_integer_sequence<int, 72>()));
+
+int type_pos(const int *types, int n, int t)
 {
-    return int(g_bf16) | int(p_rem) << 1 | int(out) << 2 | (mode & 1) << 3 | int(capturable) << 4;
+    for (int i = 0; i < n; ++i)
+        if (types[i] == t) return i;
+    return -1;
 }
+
+// ---------------------------------------------------------------------------
+// Host side: planning
+// ---------------------------------------------------------------------------
 
 struct Plan {
     adam_tl_stats stats;
     uint32_t shift;
     std::vector<WorkItem> items;
+    std::vector<float *> scale_ptrs;  // scaled state: per non-empty tensor
 };
 
 bool valid_dtype_set(const adam_tl_desc &d)
 {
-    const bool g_ok = d.g == ADAM_DT_F32 || d.g == ADAM_DT_BF16;
-    const bool out_ok = d.p_out == ADAM_DT_NONE || d.p_out == ADAM_DT_BF16;
-    if (!g_ok || !out_ok) return false;
-    if (d.with_remainders == 1) return d.p == ADAM_DT_BF16;
-    if (d.with_remainders == 0) return d.p == ADAM_DT_F32;
-    return false;
+    const bool g_ok = d.g == ADAM_DT_F32 || d.g == ADAM_DT_BF16 || d.g == ADAM_DT_F16;
+    const bool out16 = d.p_out == ADAM_DT_BF16 || d.p_out == ADAM_DT_F16;
+    if (!g_ok || !(d.p_out == ADAM_DT_NONE || out16)) return false;
+    if (d.with_remainders == 1) return d.p == ADAM_DT_BF16 && d.p_out != ADAM_DT_F16;
+    if (d.scaled_state == 1) return d.p == ADAM_DT_BF16 || d.p == ADAM_DT_F16;
+    return d.p == ADAM_DT_F32;
 }
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -681,23 +1011,27 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
               bool keep_items)
 {
     if (desc == nullptr || count < 0 || (count > 0 && tensors == nullptr)) return ADAM_EINVAL;
-    if (desc->reserved0 != 0 || desc->reserved1 != 0) return ADAM_EINVAL;
+    if (desc->reserved1 != 0) return ADAM_EINVAL;
     if (desc->with_remainders != 0 && desc->with_remainders != 1) return ADAM_EINVAL;
+    if (desc->scaled_state != 0 && desc->scaled_state != 1) return ADAM_EINVAL;
+    if (desc->with_remainders == 1 && desc->scaled_state == 1) return ADAM_EINVAL;
     if (!valid_dtype_set(*desc)) return ADAM_EDTYPE;
     if (desc->chunk_elems != 0 &&
         (!is_pow2(desc->chunk_elems) || desc->chunk_elems < kMinChunk || desc->chunk_elems > kMaxChunk))
         return ADAM_EINVAL;
 
     const bool rem = desc->with_remainders == 1;
-    const bool out = desc->p_out == ADAM_DT_BF16;
-    const bool g_bf16 = desc->g == ADAM_DT_BF16;
-    const uintptr_t p_size = rem ? 2 : 4;
-    const uintptr_t g_size = g_bf16 ? 2 : 4;
+    const bool scaled = desc->scaled_state == 1;
+    const bool out = desc->p_out != ADAM_DT_NONE;
+    const uintptr_t p_size = desc->p == ADAM_DT_F32 ? 4 : 2;
+    const uintptr_t mv_size = scaled ? 2 : 4;
+    const uintptr_t g_size = desc->g == ADAM_DT_F32 ? 4 : 2;
     const int64_t tile = kTile;
 
     adam_tl_stats st = {};
     st.tensors = count;
-    st.bytes_per_elem = int32_t(2 * (p_size + (rem ? 2 : 0) + 4 + 4) + g_size + (out ? 2 : 0));
+    st.bytes_per_elem =
+        int32_t(2 * (p_size + (rem ? 2 : 0) + 2 * mv_size) + g_size + (out ? 2 : 0));
     st.block_threads = kBlock;
     st.tile_elems = int32_t(tile);
     st.device = -1;
@@ -705,24 +1039,26 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
     std::vector<Span> spans;
     std::vector<int64_t> sizes;  // elements covered by records (a vector body excludes its head)
     std::vector<int32_t> heads;  // head elements of a vector tensor, -1 for the element path
-    spans.reserve(size_t(count) * 6);
+    spans.reserve(size_t(count) * 7);
     for (int64_t k = 0; k < count; ++k) {
         const adam_tensor &t = tensors[k];
         if (t.numel < 0 || t.numel > kMaxNumel) return ADAM_EINVAL;
         if (t.numel == 0) continue;
         if (t.p == nullptr || t.m == nullptr || t.v == nullptr || t.g == nullptr) return ADAM_EINVAL;
-        if ((t.rem != nullptr) != rem || (t.p_out != nullptr) != out) return ADAM_EINVAL;
+        if ((t.rem != nullptr) != rem || (t.p_out != nullptr) != out || (t.scales != nullptr) != scaled)
+            return ADAM_EINVAL;
         const uintptr_t n = uintptr_t(t.numel);
         spans.push_back({uintptr_t(t.p), uintptr_t(t.p) + n * p_size, false});
-        spans.push_back({uintptr_t(t.m), uintptr_t(t.m) + n * 4, false});
-        spans.push_back({uintptr_t(t.v), uintptr_t(t.v) + n * 4, false});
+        spans.push_back({uintptr_t(t.m), uintptr_t(t.m) + n * mv_size, false});
+        spans.push_back({uintptr_t(t.v), uintptr_t(t.v) + n * mv_size, false});
         spans.push_back({uintptr_t(t.g), uintptr_t(t.g) + n * g_size, true});
         if (rem) spans.push_back({uintptr_t(t.rem), uintptr_t(t.rem) + n * 2, false});
         if (out) spans.push_back({uintptr_t(t.p_out), uintptr_t(t.p_out) + n * 2, false});
+        if (scaled) spans.push_back({uintptr_t(t.scales), uintptr_t(t.scales) + 3 * sizeof(float), false});
         // every stream must be naturally aligned for its element type
-        if (uintptr_t(t.p) % p_size || uintptr_t(t.m) % 4 || uintptr_t(t.v) % 4 ||
+        if (uintptr_t(t.p) % p_size || uintptr_t(t.m) % mv_size || uintptr_t(t.v) % mv_size ||
             uintptr_t(t.g) % g_size || (rem && uintptr_t(t.rem) % 2) ||
-            (out && uintptr_t(t.p_out) % 2))
+            (out && uintptr_t(t.p_out) % 2) || (scaled && uintptr_t(t.scales) % 4))
             return ADAM_EINVAL;
         // The head: the fewest leading elements after which every stream sits
         // on a 128-byte boundary, else on the boundary of its 4-element access
@@ -732,7 +1068,7 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
                 const uintptr_t need = line ? 128u : uintptr_t(kLane) * size;
                 return (uintptr_t(ptr) + uintptr_t(e) * size) % need == 0;
             };
-            return ok(t.p, p_size) && ok(t.m, 4) && ok(t.v, 4) && ok(t.g, g_size) &&
+            return ok(t.p, p_size) && ok(t.m, mv_size) && ok(t.v, mv_size) && ok(t.g, g_size) &&
                    (!rem || ok(t.rem, 2)) && (!out || ok(t.p_out, 2));
         };
         int64_t head = -1;
@@ -748,6 +1084,7 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
         heads.push_back(vec ? int32_t(head) : -1);
     }
     if (spans_conflict(spans)) return ADAM_EINVAL;
+    if (st.nonempty >= (int64_t(1) << 31) / 3) return ADAM_EINVAL;
 
     const int64_t chunk = desc->chunk_elems != 0 ? desc->chunk_elems : auto_chunk(sizes, tile);
     uint32_t shift = 0;
@@ -765,21 +1102,24 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
     for (int64_t k = 0; k < count; ++k) {
         const adam_tensor &t = tensors[k];
         if (t.numel == 0) continue;
+        const int32_t ordinal = int32_t(j);
         const int32_t head = heads[j];
         const int64_t body = sizes[j++];
         const int64_t first = head > 0 ? head : 0;  // element index where records start
+        if (scaled) plan.scale_ptrs.push_back(t.scales);
         for (int64_t off = 0; off < body; off += chunk) {
             const int64_t e = first + off;
             WorkItem w = {};
             w.p = static_cast<char *>(t.p) + e * int64_t(p_size);
-            w.rem = rem ? t.rem + e : nullptr;
-            w.m = t.m + e;
-            w.v = t.v + e;
+            w.aux = rem ? static_cast<void *>(t.rem + e) : scaled ? static_cast<void *>(t.scales) : nullptr;
+            w.m = static_cast<char *>(t.m) + e * int64_t(mv_size);
+            w.v = static_cast<char *>(t.v) + e * int64_t(mv_size);
             w.g = static_cast<const char *>(t.g) + e * int64_t(g_size);
             w.p_out = out ? static_cast<char *>(t.p_out) + e * 2 : nullptr;
             w.n = int32_t(std::min(chunk, body - off));
             w.flags = head >= 0 ? kItemVector : 0u;
             w.head = off == 0 && head > 0 ? head : 0;
+            w.tensor = ordinal;
             plan.items.push_back(w);
         }
     }
@@ -811,35 +1151,65 @@ bool valid_hparams(const adam_hparams *hp)
            (hp->bias_correction == 0 || hp->bias_correction == 1);
 }
 
+// What kind of storage a handle updates; each step entry point takes one.
+enum class Kind { Plain, Remainders, Scaled };
+
 }  // namespace
 
 struct adam_tl {
     adam_tl_stats stats;
     uint32_t shift;
-    bool remainders;
-    bool g_bf16;
-    bool out;
-    WorkItem *d_items;   // device table, null when there is no work
-    StepBlock *d_block;  // device scalar block of the capturable step (after the table)
-    double *d_partials;  // reduction partial sums (after the block), one per kNormRun tiles
+    Kind kind;
+    int g;                 // adam_dtype of the gradients
+    int p;                 // adam_dtype of the params (the state type when scaled)
+    int out;               // adam_dtype of p_out, ADAM_DT_NONE if absent
+    WorkItem *d_items;     // device table, null when there is no work
+    StepBlock *d_block;    // device scalar block of the capturable steps (after the table)
+    double *d_partials;    // reduction partial sums (after the block), one per kNormRun tiles
     uint32_t n_partials;
+    float **d_scale_ptrs;  // scaled state: each non-empty tensor's scales (after the partials)
+    uint32_t *d_amax;      // scaled state: three magnitude maxima per non-empty tensor (last)
+    uint32_t n_tensors;    // non-empty tensors
 };
 
 namespace {
 
 int launch_update(const adam_tl *tl, int mode, bool capturable, const StepArgs &args, hipStream_t stream)
 {
-    const int idx = kernel_index(tl->g_bf16, tl->remainders, tl->out, mode, capturable);
-    hipLaunchKernelGGL(AllKernels::fns[idx], dim3(uint32_t(tl->stats.grid_blocks)), dim3(kBlock), 0,
-                       stream, tl->d_items, tl->shift, args);
+    const int idx = type_pos(kGradTypes, 3, tl->g) +
+                    3 * ((tl->kind == Kind::Remainders ? kParamRem : kParamF32) +
+                         2 * (type_pos(kOutTypes, 3, tl->out) + 3 * (mode + 2 * int(capturable))));
+    const UpdateFn fn = UpdateKernels::fns[idx];
+    if (fn == nullptr) return ADAM_EDTYPE;
+    hipLaunchKernelGGL(fn, dim3(uint32_t(tl->stats.grid_blocks)), dim3(kBlock), 0, stream,
+                       tl->d_items, tl->shift, args);
+    return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
+}
+
+int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t stream)
+{
+    const uint32_t slots = 3 * tl->n_tensors;
+    hipLaunchKernelGGL(adam_scaled_clear, dim3(std::min<uint32_t>((slots + 255) / 256, 1024)), dim3(256),
+                       0, stream, tl->d_amax, slots);
+    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
+    const int base = type_pos(kGradTypes, 3, tl->g) +
+                     3 * (type_pos(kOutTypes, 3, tl->out) + 3 * (type_pos(kStateTypes, 2, tl->p) + 2 * mode));
+    for (int pass = 0; pass < 2; ++pass) {
+        hipLaunchKernelGGL(ScaledKernels::fns[base + 36 * pass], dim3(uint32_t(tl->stats.grid_blocks)),
+                           dim3(kBlock), 0, stream, tl->d_items, tl->shift, args, tl->d_amax);
+        if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
+    }
+    auto finish = tl->p == kBF16 ? adam_scaled_finish<kBF16> : adam_scaled_finish<kF16>;
+    hipLaunchKernelGGL(finish, dim3((tl->n_tensors + 255) / 256), dim3(256), 0, stream,
+                       tl->d_scale_ptrs, tl->d_amax, tl->n_tensors);
     return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
 }
 
 int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
-              const float *d_grad_scale, hipStream_t stream, bool want_remainders)
+              const float *d_grad_scale, hipStream_t stream, Kind want)
 {
     if (tl == nullptr || step_io == nullptr || !valid_hparams(hp)) return ADAM_EINVAL;
-    if (tl->remainders != want_remainders) return ADAM_EINVAL;
+    if (tl->kind != want) return ADAM_EINVAL;
     const int32_t before = *step_io;
     if (before < 0 || before == INT32_MAX) return ADAM_EINVAL;
     const int32_t t = before + 1;
@@ -855,10 +1225,37 @@ int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
     a.d_grad_scale = d_grad_scale;
     corrections(hp->beta1, hp->beta2, t, hp->bias_correction, a.bc1, a.bc2);
     DeviceGuard guard(tl->stats.device);
-    int rc = guard.status == hipSuccess ? launch_update(tl, hp->mode, false, a, stream) : ADAM_EHIP;
+    int rc = ADAM_EHIP;
+    if (guard.status == hipSuccess)
+        rc = want == Kind::Scaled ? launch_scaled(tl, hp->mode, a, stream)
+                                  : launch_update(tl, hp->mode, false, a, stream);
     if (rc != ADAM_OK) *step_io = before;
     return rc;
 }
+
+int capturable_step(const adam_tl *tl, const adam_hparams *hp, const float *d_lr, int32_t *d_step,
+                    const float *d_grad_scale, const int32_t *d_noop, hipStream_t stream, Kind want)
+{
+    if (tl == nullptr || d_lr == nullptr || d_step == nullptr || !valid_hparams(hp)) return ADAM_EINVAL;
+    if (tl->kind != want) return ADAM_EINVAL;
+    int device = tl->stats.device;
+    if (device < 0 && hipGetDevice(&device) != hipSuccess) return ADAM_EHIP;
+    DeviceGuard guard(device);
+    if (guard.status != hipSuccess) return ADAM_EHIP;
+    hipLaunchKernelGGL(adam_capture_prologue, dim3(1), dim3(64), 0, stream, tl->d_block, d_lr, d_step,
+                       d_grad_scale, d_noop, hp->beta1, hp->beta2, hp->bias_correction);
+    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
+    if (tl->stats.chunks == 0) return ADAM_OK;
+    StepArgs a = {};
+    a.beta1 = hp->beta1;
+    a.beta2 = hp->beta2;
+    a.eps = hp->eps;
+    a.weight_decay = hp->weight_decay;
+    a.block = tl->d_block;
+    return launch_update(tl, hp->mode, true, a, stream);
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
@@ -911,13 +1308,19 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     if (tl == nullptr) return ADAM_ENOMEM;
     tl->stats = plan.stats;
     tl->shift = plan.shift;
-    tl->remainders = desc->with_remainders == 1;
-    tl->g_bf16 = desc->g == ADAM_DT_BF16;
-    tl->out = desc->p_out == ADAM_DT_BF16;
+    tl->kind = desc->with_remainders == 1 ? Kind::Remainders
+               : desc->scaled_state == 1  ? Kind::Scaled
+                                          : Kind::Plain;
+    tl->g = desc->g;
+    tl->p = desc->p;
+    tl->out = desc->p_out;
     tl->d_items = nullptr;
     tl->d_block = nullptr;
     tl->d_partials = nullptr;
     tl->n_partials = 0;
+    tl->d_scale_ptrs = nullptr;
+    tl->d_amax = nullptr;
+    tl->n_tensors = uint32_t(plan.stats.nonempty);
     if (plan.items.empty()) {  // nothing to launch: no device state at all
         *out = tl;
         return ADAM_OK;
@@ -929,22 +1332,35 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
         return ADAM_EHIP;
     }
     tl->stats.device = device;
-    const size_t table_bytes = plan.items.size() * sizeof(WorkItem);
     tl->n_partials = uint32_t((tl->stats.grid_blocks + kNormRun - 1) / kNormRun);
+    // layout: [work table][scalar block][partial sums][scale pointers][maxima]
+    const size_t table_bytes = plan.items.size() * sizeof(WorkItem);
+    const size_t block_off = table_bytes;
+    const size_t partials_off = block_off + sizeof(StepBlock);
+    const size_t ptrs_off = align_up(partials_off + tl->n_partials * sizeof(double), 8);
+    const size_t amax_off = ptrs_off + plan.scale_ptrs.size() * sizeof(float *);
+    const size_t total = amax_off + (tl->kind == Kind::Scaled ? 3 * sizeof(uint32_t) * tl->n_tensors : 0);
     void *mem = nullptr;
-    if (hipMalloc(&mem, table_bytes + sizeof(StepBlock) + tl->n_partials * sizeof(double)) !=
-        hipSuccess) {
+    if (hipMalloc(&mem, total) != hipSuccess) {
         (void)hipGetLastError();
         delete tl;
         return ADAM_ENOMEM;
     }
-    tl->d_items = static_cast<WorkItem *>(mem);
-    tl->d_block = reinterpret_cast<StepBlock *>(static_cast<char *>(mem) + table_bytes);
-    tl->d_partials =
-        reinterpret_cast<double *>(static_cast<char *>(mem) + table_bytes + sizeof(StepBlock));
-    if (hipMemcpyAsync(tl->d_items, plan.items.data(), table_bytes, hipMemcpyHostToDevice, stream) !=
-            hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess) {
+    char *base = static_cast<char *>(mem);
+    tl->d_items = reinterpret_cast<WorkItem *>(base);
+    tl->d_block = reinterpret_cast<StepBlock *>(base + block_off);
+    tl->d_partials = reinterpret_cast<double *>(base + partials_off);
+    if (tl->kind == Kind::Scaled) {
+        tl->d_scale_ptrs = reinterpret_cast<float **>(base + ptrs_off);
+        tl->d_amax = reinterpret_cast<uint32_t *>(base + amax_off);
+    }
+    bool ok = hipMemcpyAsync(tl->d_items, plan.items.data(), table_bytes, hipMemcpyHostToDevice,
+                             stream) == hipSuccess;
+    if (ok && tl->kind == Kind::Scaled)
+        ok = hipMemcpyAsync(tl->d_scale_ptrs, plan.scale_ptrs.data(),
+                            plan.scale_ptrs.size() * sizeof(float *), hipMemcpyHostToDevice,
+                            stream) == hipSuccess;
+    if (!ok || hipStreamSynchronize(stream) != hipSuccess) {
         (void)hipFree(mem);
         delete tl;
         return ADAM_EHIP;
@@ -973,35 +1389,32 @@ int adam_tl_info(const adam_tl *tl, adam_tl_stats *stats)
 int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
               const float *d_grad_scale, hipStream_t stream)
 {
-    return host_step(tl, hp, lr, step_io, grad_scale, d_grad_scale, stream, false);
+    return host_step(tl, hp, lr, step_io, grad_scale, d_grad_scale, stream, Kind::Plain);
 }
 
 int adam_step_remainders(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
                          float grad_scale, const float *d_grad_scale, hipStream_t stream)
 {
-    return host_step(tl, hp, lr, step_io, grad_scale, d_grad_scale, stream, true);
+    return host_step(tl, hp, lr, step_io, grad_scale, d_grad_scale, stream, Kind::Remainders);
+}
+
+int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
+                     float grad_scale, const float *d_grad_scale, hipStream_t stream)
+{
+    return host_step(tl, hp, lr, step_io, grad_scale, d_grad_scale, stream, Kind::Scaled);
 }
 
 int adam_step_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr, int32_t *d_step,
                          const float *d_grad_scale, const int32_t *d_noop, hipStream_t stream)
 {
-    if (tl == nullptr || d_lr == nullptr || d_step == nullptr || !valid_hparams(hp)) return ADAM_EINVAL;
-    if (tl->remainders) return ADAM_EINVAL;
-    int device = tl->stats.device;
-    if (device < 0 && hipGetDevice(&device) != hipSuccess) return ADAM_EHIP;
-    DeviceGuard guard(device);
-    if (guard.status != hipSuccess) return ADAM_EHIP;
-    hipLaunchKernelGGL(adam_capture_prologue, dim3(1), dim3(64), 0, stream, tl->d_block, d_lr, d_step,
-                       d_grad_scale, d_noop, hp->beta1, hp->beta2, hp->bias_correction);
-    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
-    if (tl->stats.chunks == 0) return ADAM_OK;
-    StepArgs a = {};
-    a.beta1 = hp->beta1;
-    a.beta2 = hp->beta2;
-    a.eps = hp->eps;
-    a.weight_decay = hp->weight_decay;
-    a.block = tl->d_block;
-    return launch_update(tl, hp->mode, true, a, stream);
+    return capturable_step(tl, hp, d_lr, d_step, d_grad_scale, d_noop, stream, Kind::Plain);
+}
+
+int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
+                                    int32_t *d_step, const float *d_grad_scale,
+                                    const int32_t *d_noop, hipStream_t stream)
+{
+    return capturable_step(tl, hp, d_lr, d_step, d_grad_scale, d_noop, stream, Kind::Remainders);
 }
 
 int adam_grad_sumsq(const adam_tl *tl, double *d_sumsq, int32_t accumulate, hipStream_t stream)
@@ -1012,7 +1425,9 @@ int adam_grad_sumsq(const adam_tl *tl, double *d_sumsq, int32_t accumulate, hipS
     DeviceGuard guard(device);
     if (guard.status != hipSuccess) return ADAM_EHIP;
     if (tl->n_partials > 0) {
-        auto fn = tl->g_bf16 ? grad_sumsq_partial<true> : grad_sumsq_partial<false>;
+        auto fn = tl->g == kF32    ? grad_sumsq_partial<kF32>
+                  : tl->g == kBF16 ? grad_sumsq_partial<kBF16>
+                                   : grad_sumsq_partial<kF16>;
         hipLaunchKernelGGL(fn, dim3(tl->n_partials), dim3(kBlock), 0, stream, tl->d_items, tl->shift,
                            uint32_t(tl->stats.grid_blocks), kNormRun, tl->d_partials);
         if (hipGetLastError() != hipSuccess) return ADAM_EHIP;

@@ -25,6 +25,15 @@
  * float.  The library therefore reproduces a scalar C evaluation of these
  * expressions bit for bit.
  *
+ * Two more storage schemes around the same fp32 update:
+ *   - remainders (apex _bf16_rem_to_fp32): bf16 params plus int16 low halves
+ *     hold the fp32 master exactly;
+ *   - scaled 16-bit state (apex distributed_fused_adam.py,
+ *     _local_step_with_scaled_states and _apply_state_scale): p, m and v are
+ *     stored as bf16 or fp16 values times a per-tensor fp32 scale each; the
+ *     step unscales them to fp32, updates, and stores them again with new
+ *     scales taken from each buffer's largest magnitude.
+ *
  * Conventions for every call below:
  *   - Pointers marked "device" point to GPU memory on the device that was
  *     current when the handle was built; "host" pointers to CPU memory.
@@ -34,7 +43,9 @@
  *   - Work is enqueued on `stream` (0 = the null stream) and runs
  *     asynchronously; faults inside a kernel surface at the caller's next
  *     synchronisation.
- *   - bf16 buffers hold raw bfloat16 bit patterns (uint16_t).
+ *   - bf16 buffers hold raw bfloat16 bit patterns (uint16_t); fp16 buffers
+ *     hold IEEE binary16 bit patterns.  Casts from fp32 round to nearest
+ *     even (fp16: overflow to infinity, subnormals kept); NaN stays NaN.
  */
 #ifndef ADAMW_MI355X_ADAM_H
 #define ADAMW_MI355X_ADAM_H
@@ -46,7 +57,7 @@
 extern "C" {
 #endif
 
-#define ADAM_ABI_VERSION 1
+#define ADAM_ABI_VERSION 2
 
 typedef enum {
     ADAM_OK = 0,
@@ -59,7 +70,8 @@ typedef enum {
 typedef enum {
     ADAM_DT_NONE = 0, /* buffer absent (p_out only) */
     ADAM_DT_F32 = 1,
-    ADAM_DT_BF16 = 2
+    ADAM_DT_BF16 = 2,
+    ADAM_DT_F16 = 3
 } adam_dtype;
 
 /* One tensor of a group: five (six with remainders) flat, dense arrays of
@@ -67,28 +79,35 @@ typedef enum {
  * g is only read; p_out is only written.  The layout is the apex tensor-list
  * order [p, m, v, g, p_out] (remainder mode: [p, rem, m, v, g, p_out]). */
 typedef struct {
-    void *p;          /* device: float (ADAM_DT_F32) or bf16 bits (remainder mode) */
+    void *p;          /* device: float; bf16 bits (remainder mode); bf16 or fp16
+                         (scaled state, the handle's p dtype)                     */
     int16_t *rem;     /* device: int16 remainders (remainder mode), else NULL      */
-    float *m;         /* device: first moment, float                               */
-    float *v;         /* device: second moment, float                              */
-    const void *g;    /* device: gradient, float or bf16 bits                      */
-    void *p_out;      /* device: bf16 copy of the new param, or NULL               */
+    void *m;          /* device: first moment: float, or p's 16-bit type (scaled)  */
+    void *v;          /* device: second moment: float, or p's 16-bit type (scaled) */
+    const void *g;    /* device: gradient: float, bf16 or fp16 bits                */
+    void *p_out;      /* device: bf16 or fp16 copy of the new param, or NULL       */
+    float *scales;    /* device: scaled state only: float[3] = the scales of p, m,
+                         v (stored value x scale = fp32 value), read and replaced
+                         by each step; NULL otherwise                             */
     int64_t numel;    /* >= 0; a tensor with numel == 0 may have NULL pointers     */
 } adam_tensor;
 
 /* The dtypes shared by every tensor of one handle, and the work-table
  * granularity. */
 typedef struct {
-    adam_dtype p;            /* ADAM_DT_F32, or ADAM_DT_BF16 with remainders     */
-    adam_dtype g;            /* ADAM_DT_F32 or ADAM_DT_BF16                      */
-    adam_dtype p_out;        /* ADAM_DT_NONE or ADAM_DT_BF16                     */
+    adam_dtype p;            /* ADAM_DT_F32; ADAM_DT_BF16 with remainders;
+                                ADAM_DT_BF16 or ADAM_DT_F16 with scaled state  */
+    adam_dtype g;            /* ADAM_DT_F32, ADAM_DT_BF16 or ADAM_DT_F16         */
+    adam_dtype p_out;        /* ADAM_DT_NONE, ADAM_DT_BF16 or ADAM_DT_F16 (not
+                                F16 with remainders)                            */
     int32_t with_remainders; /* 1: p is bf16 and rem holds the low fp32 halves  */
     int64_t chunk_elems;     /* elements per work-table record: 0 = automatic
                                 (the largest power of two <= 65536 that wastes
                                 under 1% of workgroups on ragged tensor ends);
                                 else a power of two from 1024 to 2^30.  Results
                                 do not depend on it.                           */
-    int32_t reserved0;       /* must be 0                                       */
+    int32_t scaled_state;    /* 1: p, m, v are p's 16-bit type with per-tensor
+                                scales (adam_tensor.scales); 0: no             */
     int32_t reserved1;       /* must be 0                                       */
 } adam_tl_desc;
 
@@ -130,19 +149,24 @@ const char *adam_status_string(int status);
  * HIP call, no device allocation); fills *stats (device = -1).
  * Errors: ADAM_EINVAL for a NULL desc/stats, count < 0, NULL `tensors` with
  * count > 0, numel < 0, a NULL required pointer in a non-empty tensor, a
- * pointer given where the dtype says none, a bad chunk_elems, reserved != 0,
- * or two buffers that overlap (gradients may overlap other gradients; no
- * other pair may share a byte); ADAM_EDTYPE for an unsupported dtype set.
- * Supported sets: p F32, g F32|BF16, p_out NONE|BF16, no remainders; or
- * p BF16 with remainders, g F32|BF16, p_out NONE|BF16 (apex: bf16 params
- * need fp32 optimizer state for the remainder scheme). */
+ * pointer given where the dtype says none, a bad chunk_elems, reserved1 != 0,
+ * with_remainders or scaled_state not 0/1 or both 1, or two buffers that
+ * overlap (gradients may overlap other gradients; no other pair may share a
+ * byte; a tensor's scales are written too); ADAM_EDTYPE for an unsupported
+ * dtype set.  Supported sets (g F32|BF16|F16 in each):
+ *   - fp32 master: p F32, p_out NONE|BF16|F16;
+ *   - remainders: p BF16, p_out NONE|BF16 (apex: bf16 params need fp32
+ *     optimizer state for the remainder scheme; p_out is the new bf16);
+ *   - scaled state: p BF16|F16 (m and v the same type), p_out NONE|BF16|F16
+ *     (apex: the param-sync buffer is a 16-bit type). */
 int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
                  adam_tl_stats *stats);
 
 /* Builds a handle for one group: validates as adam_tl_plan, then copies the
  * work table (one 64-byte record per chunk, plus a 64-byte scalar block used
- * by adam_step_capturable) to the current device, using `stream`, and waits
- * for that copy.  `tensors` (host array of `count`) is
+ * by the capturable steps, partial-sum scratch for adam_grad_sumsq, and for
+ * scaled state one 12-byte maximum record per tensor) to the current device,
+ * using `stream`, and waits for that copy.  `tensors` (host array of `count`) is
  * not retained; the device buffers it names must stay allocated and in place
  * for the handle's life.  On success *out owns device memory; release it with
  * adam_tl_destroy.  A list whose elements sum to 0 gives a valid handle that
@@ -167,7 +191,7 @@ int adam_tl_info(const adam_tl *tl, adam_tl_stats *stats);
  *               tensor).
  * On ADAM_EHIP from the launch the counter is restored.  Errors: ADAM_EINVAL
  * (NULL tl/hp/step_io, mode not 0/1, bias_correction not 0/1, a remainder
- * handle). */
+ * or scaled-state handle). */
 int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
               float grad_scale, const float *d_grad_scale, hipStream_t stream);
 
@@ -185,8 +209,8 @@ int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
  * the counter) and then the update, which reads the resolved scalars from
  * the handle's scalar block; capturable steps of one handle must therefore
  * be ordered (one stream, or synchronised streams).
- * Errors: ADAM_EINVAL (NULL tl/hp/d_lr/d_step, bad mode/flag, remainder
- * handle); ADAM_EHIP. */
+ * Errors: ADAM_EINVAL (NULL tl/hp/d_lr/d_step, bad mode/flag, a remainder
+ * or scaled-state handle); ADAM_EHIP. */
 int adam_step_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
                          int32_t *d_step, const float *d_grad_scale, const int32_t *d_noop,
                          hipStream_t stream);
@@ -198,15 +222,50 @@ int adam_step_capturable(const adam_tl *tl, const adam_hparams *hp, const float 
  * fp32 word; bf16 = high 16 bits, plus one when that remainder is negative
  * as an int16, mod 2^16: a round to nearest with ties away from zero).
  * p_out, if present, receives the new bf16 param bits.  Arguments and errors
- * as adam_step; ADAM_EINVAL for an fp32-param handle. */
+ * as adam_step; ADAM_EINVAL for a handle that is not in remainder mode. */
 int adam_step_remainders(const adam_tl *tl, const adam_hparams *hp, float lr,
                          int32_t *step_io, float grad_scale, const float *d_grad_scale,
                          hipStream_t stream);
 
+/* Capturable step on a remainder handle: the arithmetic and encoding of
+ * adam_step_remainders with the device scalars, noop flag and counter rules
+ * of adam_step_capturable (apex refuses remainders with its capturable
+ * option; nothing in the update needs host scalars, so this library offers
+ * both).  Errors as adam_step_capturable; ADAM_EINVAL for a handle that is
+ * not in remainder mode. */
+int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
+                                    int32_t *d_step, const float *d_grad_scale,
+                                    const int32_t *d_noop, hipStream_t stream);
+
+/* Non-capturable step on a scaled-state handle (apex distributed_fused_adam.py
+ * _local_step_with_scaled_states, _apply_state_scale and
+ * _check_params_shard_dtypes).  Per tensor, with S = scales[0..2] and T the
+ * state type (bf16 or fp16):
+ *   P = float(p) * S[0],  M = float(m) * S[1],  V = float(v) * S[2]
+ *   (P, M, V) <- the fp32 update above, with lr, counter and grad scale as
+ *                in adam_step
+ *   p_out     = P cast to p_out's type (param-sync copy), if present
+ *   for (X, x, k) in (P, p, 0), (M, m, 1), (V, v, 2):
+ *     amax = max |X| over the tensor (NaN if any element is NaN)
+ *     S[k] = amax / L,   L = half the largest finite T (bf16 ~1.69e38,
+ *                        fp16 32752), a correctly rounded float division
+ *     r    = S[k] > 0 ? 1/S[k] : 0   (correctly rounded)
+ *     x    = T(X * r)                (float product, then round to nearest even)
+ * Note: with bf16 state a tensor whose largest magnitude is below about 0.5
+ * gets a subnormal scale whose reciprocal overflows, so its values store as
+ * +-inf (0 becomes NaN) -- the pages' formula does this; fp16 state does not.
+ * Empty tensors keep their scales.  The call enqueues four kernels (clear the
+ * per-tensor maxima, a pass that computes the update and the maxima, a pass
+ * that recomputes it and stores, a per-tensor pass that writes the new
+ * scales); steps of one handle must be ordered.  Arguments and errors as
+ * adam_step; ADAM_EINVAL for a handle without scaled state. */
+int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
+                     float grad_scale, const float *d_grad_scale, hipStream_t stream);
+
 /* Sum of squares of every gradient element of a handle: the local part of
  * the global gradient norm that apex's distributed_fused_adam.py computes in
  * grad_norm (per-bucket L2 norms of the gradient shards, squared and summed,
- * then all-reduced across ranks).  Each square of a float or bf16 gradient is
+ * then all-reduced across ranks).  Each square of a float, bf16 or fp16 gradient is
  * exact in double; the sum is accumulated in double with a fixed order of
  * additions, so repeated calls give identical bits.
  *   d_sumsq     device double: *d_sumsq = (accumulate ? *d_sumsq : 0) + sum.

@@ -11,7 +11,7 @@ import adamw_optimizer_step_tensor_amd as A
 from oracle import HParams, OracleTensor
 from workloads import HostTensor
 
-ROLES = ("p", "rem", "m", "v", "g", "p_out")
+ROLES = ("p", "rem", "m", "v", "g", "p_out", "scales")
 
 
 def torch_mod():
@@ -24,12 +24,10 @@ def np_to_dev(a: np.ndarray, role: str, offset: int = 0, pad: int = 8):
     """Device copy of a host array placed ``offset`` elements into a fresh
     allocation (to test unaligned bases)."""
     torch = torch_mod()
-    if a.dtype == np.float32:
+    if a.dtype in (np.float32, np.float16, np.int16):
         t = torch.from_numpy(a)
     elif a.dtype == np.uint16:
         t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
-    elif a.dtype == np.int16:
-        t = torch.from_numpy(a)
     else:
         raise TypeError(a.dtype)
     buf = torch.zeros(a.size + offset + pad, dtype=t.dtype, device="cuda")
@@ -65,7 +63,7 @@ class DeviceSet:
         for d in self.tensors:
             vals = {r: (dev_to_np(d[r]) if r in d else None) for r in ROLES}
             out.append(HostTensor(vals["p"], vals["m"], vals["v"], vals["g"], vals["p_out"],
-                                  vals["rem"]))
+                                  vals["rem"], vals["scales"]))
         return out
 
     def set_grad(self, i: int, idx: int, value: float):
@@ -74,14 +72,15 @@ class DeviceSet:
 
 
 def oracle_tensors(host: Sequence[HostTensor]) -> List[OracleTensor]:
-    return [OracleTensor(h.p, h.m, h.v, h.g, h.p_out, h.rem) for h in host]
+    return [OracleTensor(h.p, h.m, h.v, h.g, h.p_out, h.rem, h.scales) for h in host]
 
 
 def copies(host: Sequence[HostTensor]) -> List[HostTensor]:
     return [h.copy() for h in host]
 
 
-def assert_bitwise(got: Sequence[HostTensor], want: Sequence[HostTensor], roles=("p", "rem", "m", "v", "p_out"),
+def assert_bitwise(got: Sequence[HostTensor], want: Sequence[HostTensor],
+                   roles=("p", "rem", "m", "v", "p_out", "scales"),
                    ctx=""):
     """Bit-for-bit equality; NaNs compare as NaN regardless of payload (the
     CPU and the GPU make different default NaN bits)."""
@@ -94,7 +93,10 @@ def assert_bitwise(got: Sequence[HostTensor], want: Sequence[HostTensor], roles=
             if a.dtype == np.float32:
                 nan = np.isnan(a) & np.isnan(b)
                 bad = (a.view(np.uint32) != b.view(np.uint32)) & ~nan
-            elif r == "p_out" or (r == "p" and a.dtype == np.uint16):
+            elif a.dtype == np.float16:
+                nan = np.isnan(a) & np.isnan(b)
+                bad = (a.view(np.uint16) != b.view(np.uint16)) & ~nan
+            elif a.dtype == np.uint16:  # bf16 bits
                 fa = (a.astype(np.uint32) << 16).view(np.float32)
                 fb = (b.astype(np.uint32) << 16).view(np.float32)
                 nan = np.isnan(fa) & np.isnan(fb)
@@ -124,8 +126,19 @@ def hp_pair(beta1=0.9, beta2=0.999, eps=1e-8, wd=0.0, mode=1, bc=1):
     return A.AdamHParams(beta1, beta2, eps, wd, mode, bc), HParams(beta1, beta2, eps, wd, mode, bc)
 
 
+def _short(a: Optional[np.ndarray]) -> Optional[str]:
+    if a is None:
+        return None
+    return {np.dtype(np.float32): "f32", np.dtype(np.uint16): "bf16",
+            np.dtype(np.float16): "f16"}[a.dtype]
+
+
 def desc_for(host: Sequence[HostTensor], **kw):
     h = host[0]
-    return A.make_desc(g="bf16" if h.g.dtype == np.uint16 else "f32",
-                       p="bf16_rem" if h.rem is not None else "f32",
-                       p_out="bf16" if h.p_out is not None else None, **kw)
+    if h.rem is not None:
+        p = "bf16_rem"
+    elif h.scales is not None:
+        p = _short(h.p) + "_scaled"
+    else:
+        p = "f32"
+    return A.make_desc(g=_short(h.g), p=p, p_out=_short(h.p_out), **kw)

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (adam_\w+)$", out, flags=re.M))
     assert set(names) <= exported
-    assert L.adam_abi_version() == 1
+    assert L.adam_abi_version() == 2
 
 
 def test_status_strings():
@@ -49,14 +49,15 @@ def fake(i, k, offset=0):
     return BASE + (i * 8 + k) * STRIDE + offset
 
 
-def fake_tensors(sizes, *, rem=False, out=False, offsets=None):
+def fake_tensors(sizes, *, rem=False, out=False, scaled=False, offsets=None):
     ts = []
     for i, n in enumerate(sizes):
         off = (offsets or {}).get(i, {})
         ts.append(dict(p=fake(i, 0, off.get("p", 0)), m=fake(i, 1, off.get("m", 0)),
                        v=fake(i, 2, off.get("v", 0)), g=fake(i, 3, off.get("g", 0)),
                        rem=fake(i, 4, off.get("rem", 0)) if rem else None,
-                       p_out=fake(i, 5, off.get("p_out", 0)) if out else None, numel=n))
+                       p_out=fake(i, 5, off.get("p_out", 0)) if out else None,
+                       scales=fake(i, 6, off.get("scales", 0)) if scaled else None, numel=n))
     return ts
 
 
@@ -168,23 +169,51 @@ def test_plan_rejects_bad_arguments():
 def test_plan_rejects_unsupported_dtypes():
     ts = fake_tensors([64])
     desc = A.make_desc()
-    for p, g, o, r in [(A.DT_BF16, A.DT_F32, A.DT_NONE, 0), (A.DT_F32, A.DT_NONE, A.DT_NONE, 0),
-                       (A.DT_F32, A.DT_F32, A.DT_F32, 0), (A.DT_F32, A.DT_F32, A.DT_NONE, 1),
-                       (7, A.DT_F32, A.DT_NONE, 0)]:
-        d = A.AdamTlDesc(p, g, o, r, 0, 0, 0)
+    # (p, g, p_out, with_remainders, scaled_state)
+    for p, g, o, r, sc in [(A.DT_BF16, A.DT_F32, A.DT_NONE, 0, 0), (A.DT_F32, A.DT_NONE, A.DT_NONE, 0, 0),
+                           (A.DT_F32, A.DT_F32, A.DT_F32, 0, 0), (A.DT_F32, A.DT_F32, A.DT_NONE, 1, 0),
+                           (7, A.DT_F32, A.DT_NONE, 0, 0), (A.DT_F32, 7, A.DT_NONE, 0, 0),
+                           (A.DT_BF16, A.DT_BF16, A.DT_F16, 1, 0),   # remainder p_out is bf16
+                           (A.DT_F32, A.DT_F32, A.DT_NONE, 0, 1),    # scaled state is 16-bit
+                           (A.DT_F16, A.DT_F32, A.DT_NONE, 1, 0)]:   # remainders are bf16
+        d = A.AdamTlDesc(p, g, o, r, 0, sc, 0)
         arr = A._tensor_array(ts, desc)
         st = A.AdamTlStats()
-        assert A.lib().adam_tl_plan(arr, 1, ctypes.byref(d), ctypes.byref(st)) == A.ADAM_EDTYPE
-    d = A.AdamTlDesc(A.DT_F32, A.DT_F32, A.DT_NONE, 2, 0, 0, 0)
+        assert A.lib().adam_tl_plan(arr, 1, ctypes.byref(d), ctypes.byref(st)) == A.ADAM_EDTYPE, (p, g, o, r, sc)
     st = A.AdamTlStats()
-    assert A.lib().adam_tl_plan(A._tensor_array(ts, desc), 1, ctypes.byref(d),
-                                ctypes.byref(st)) == A.ADAM_EINVAL
-    for r0, r1 in ((5, 0), (0, 1)):  # reserved fields must be 0
-        d = A.AdamTlDesc(A.DT_F32, A.DT_F32, A.DT_NONE, 0, 0, r0, r1)
+    for r, sc, r1 in ((2, 0, 0), (0, 2, 0), (1, 1, 0), (0, 0, 1)):  # flags 0/1, not both; reserved 0
+        d = A.AdamTlDesc(A.DT_BF16, A.DT_F32, A.DT_NONE, r, 0, sc, r1)
         assert A.lib().adam_tl_plan(A._tensor_array(ts, desc), 1, ctypes.byref(d),
-                                    ctypes.byref(st)) == A.ADAM_EINVAL
+                                    ctypes.byref(st)) == A.ADAM_EINVAL, (r, sc, r1)
     assert A.lib().adam_tl_plan(None, 1, ctypes.byref(d), ctypes.byref(st)) == A.ADAM_EINVAL
     assert A.lib().adam_tl_plan(None, 0, None, ctypes.byref(st)) == A.ADAM_EINVAL
+
+
+def test_fp16_and_scaled_state_plans():
+    """fp16 gradients and param-out in every scheme that allows them; scaled
+    state needs each tensor's scales (12 bytes, written) and moves 16-bit p,
+    m, v: 16 B/elem with bf16 gradients and a param-sync copy."""
+    assert plan(fake_tensors([8]), g="f16")["bytes_per_elem"] == 26
+    assert plan(fake_tensors([8], out=True), g="f16", p_out="f16")["bytes_per_elem"] == 28
+    assert plan(fake_tensors([8], rem=True), g="f16", p="bf16_rem")["bytes_per_elem"] == 26
+    for p in ("bf16_scaled", "f16_scaled"):
+        assert plan(fake_tensors([8], scaled=True), g="bf16", p=p)["bytes_per_elem"] == 14
+        assert plan(fake_tensors([8], scaled=True, out=True), g="bf16", p=p,
+                    p_out="f16")["bytes_per_elem"] == 16
+        assert plan(fake_tensors([8], scaled=True), g="f32", p=p)["bytes_per_elem"] == 16
+        assert status_of(fake_tensors([8]), g="bf16", p=p) == A.ADAM_EINVAL  # no scales
+    assert status_of(fake_tensors([8], scaled=True)) == A.ADAM_EINVAL  # scales without scaled state
+    assert status_of(fake_tensors([8], rem=True, out=True), g="bf16", p="bf16_rem",
+                     p_out="f16") == A.ADAM_EDTYPE
+    # a tensor's scales are written: they may not overlap a buffer
+    ts = fake_tensors([100, 100], scaled=True)
+    ts[1]["scales"] = ts[0]["m"] + 2 * 40
+    assert status_of(ts, g="bf16", p="f16_scaled") == A.ADAM_EINVAL
+    ts = fake_tensors([100], scaled=True, offsets={0: {"scales": 2}})  # misaligned floats
+    assert status_of(ts, g="bf16", p="f16_scaled") == A.ADAM_EINVAL
+    # 16-bit m and v: 8-byte alignment is enough for the vector path
+    ts = fake_tensors([100], scaled=True, offsets={0: {"p": 8, "m": 8, "v": 8, "g": 8}})
+    assert plan(ts, g="bf16", p="f16_scaled")["vector_tensors"] == 1
 
 
 def test_plan_rejects_overlapping_buffers():
@@ -221,6 +250,10 @@ def test_empty_handle_advances_host_counter_without_a_gpu():
     step = A.HostStep(5)
     A.adam_step_remainders(tl, A.AdamHParams(), 1e-3, step, stream=0)
     assert step.value == 6
+    tl = A.adam_tl_build([], A.make_desc(p="f16_scaled", g="bf16", p_out="f16"), stream=0)
+    step = A.HostStep(7)
+    A.adam_step_scaled(tl, A.AdamHParams(), 1e-3, step, stream=0)
+    assert step.value == 8
 
 
 def test_step_argument_errors_leave_the_counter():
@@ -249,6 +282,19 @@ def test_step_argument_errors_leave_the_counter():
     trem = A.adam_tl_build([], A.make_desc(p="bf16_rem"), stream=0)
     assert L.adam_step_capturable(trem.handle, ctypes.byref(hp), 256, 512, None, None,
                                   None) == A.ADAM_EINVAL
+    assert L.adam_step_remainders_capturable(tl.handle, ctypes.byref(hp), 256, 512, None, None,
+                                             None) == A.ADAM_EINVAL
+    assert L.adam_step_remainders_capturable(trem.handle, ctypes.byref(hp), None, 512, None, None,
+                                             None) == A.ADAM_EINVAL
+    tsc = A.adam_tl_build([], A.make_desc(p="bf16_scaled"), stream=0)
+    for handle in (tl.handle, trem.handle):
+        assert L.adam_step_scaled(handle, ctypes.byref(hp), 1e-3, ctypes.byref(s), 1.0, None,
+                                  None) == A.ADAM_EINVAL
+    assert L.adam_step(tsc.handle, ctypes.byref(hp), 1e-3, ctypes.byref(s), 1.0, None,
+                       None) == A.ADAM_EINVAL
+    assert L.adam_step_capturable(tsc.handle, ctypes.byref(hp), 256, 512, None, None,
+                                  None) == A.ADAM_EINVAL
+    assert s.value == 0
     out = ctypes.c_void_p()
     assert L.adam_tl_build(None, 0, None, None, ctypes.byref(out)) == A.ADAM_EINVAL
     assert L.adam_tl_build(None, 0, ctypes.byref(A.make_desc()), None, None) == A.ADAM_EINVAL

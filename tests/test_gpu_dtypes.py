@@ -1,0 +1,253 @@
+"""GPU parity of the rest of the dtype matrix and of scaled optimizer state,
+through the C ABI against the oracle: fp16 gradients and fp16 param-out,
+the capturable remainder step, and per-tensor scaled 16-bit p / m / v
+(apex distributed_fused_adam.py, _local_step_with_scaled_states and
+_apply_state_scale).  Bit-for-bit, NaN compared as NaN."""
+import numpy as np
+import pytest
+
+import adamw_optimizer_step_tensor_amd as A
+import oracle
+from gpu_helpers import (DeviceSet, assert_bitwise, assert_within_tolerance, copies, desc_for,
+                         hp_pair, oracle_tensors, torch_mod)
+from workloads import host_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    A.lib()
+    return t
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def run_steps(orc, host, hl, hr, lr, steps, *, grad_scale=1.0, desc_kw=None, offsets=None):
+    """`steps` non-capturable steps on the GPU (the step call the handle's
+    storage needs) and on the oracle from the same inputs."""
+    torch = torch_mod()
+    ref = copies(host)
+    dev = DeviceSet(host, offsets)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host, **(desc_kw or {})))
+    h = host[0]
+    fn = A.adam_step_scaled if h.scales is not None else \
+        A.adam_step_remainders if h.rem is not None else A.adam_step
+    step, ref_step = A.HostStep(0), [0]
+    ot = oracle_tensors(ref)
+    for _ in range(steps):
+        fn(tl, hl, lr, step, grad_scale)
+        orc.group_step(ot, hr, lr, ref_step, grad_scale)
+    torch.cuda.synchronize()
+    got = dev.readback()
+    tl.destroy()
+    assert step.value == ref_step[0] == steps
+    return got, ref
+
+
+SIZES = [0, 1, 3, 4, 5, 63, 64, 65, 511, 512, 513, 4095, 4097, 20001, 70001]
+
+
+# ---------------------------------------------------------------------------
+# fp16 gradients and param-out
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p_kind,p_out,mode", [("f32", "f16", 1), ("f32", "f16", 0),
+                                               ("f32", "bf16", 1), ("bf16_rem", True, 1)])
+def test_fp16_gradients_match_the_oracle(torch, orc, p_kind, p_out, mode):
+    """fp16 gradients (with subnormal, large and signed-zero values) into fp32
+    or remainder params; fp16 param-out includes params beyond the fp16 range
+    (infinity), at the overflow threshold, and subnormal in fp16."""
+    host = host_tensors(SIZES, g_dtype="f16", p_kind=p_kind, p_out=p_out, seed=71,
+                        m_v_init="random")
+    big = host[-1]
+    big.g[:6] = np.array([6e-8, -6e-8, 1e-5, 60000.0, -0.0, 3e-5], np.float16)
+    if p_kind == "f32":
+        big.p[:8] = np.array([70000.0, -70000.0, 65519.0, 65520.0, 1e-6, -3e-8, 2.0 ** -20, 65504.0],
+                             np.float32)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 4, grad_scale=0.5, desc_kw=dict(chunk_elems=4096))
+    assert_within_tolerance(got, ref)
+    assert_bitwise(got, ref, ctx=f"{p_kind}/{p_out}/{mode}")
+
+
+def test_fp16_param_out_is_the_cast_of_the_new_param(torch, orc):
+    host = host_tensors([30000, 77], g_dtype="bf16", p_out="f16", seed=72)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
+    assert_bitwise(got, ref)
+    for t in got:
+        assert np.array_equal(t.p_out.view(np.uint16), t.p.astype(np.float16).view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# Capturable remainder step
+# ---------------------------------------------------------------------------
+
+def _device_scalars(torch, lr=1.6e-3, scale=1.0, step0=0):
+    return (torch.tensor([lr], dtype=torch.float32, device="cuda"),
+            torch.tensor([step0], dtype=torch.int32, device="cuda"),
+            torch.tensor([scale], dtype=torch.float32, device="cuda"),
+            torch.zeros(1, dtype=torch.int32, device="cuda"))
+
+
+@pytest.mark.parametrize("g_dtype,p_out", [("bf16", True), ("f32", False), ("f16", True)])
+def test_remainders_capturable_equals_noncapturable_and_oracle(torch, orc, g_dtype, p_out):
+    host = host_tensors([20000, 4097, 64, 3], g_dtype=g_dtype, p_kind="bf16_rem", p_out=p_out,
+                        seed=73, m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    d_lr, d_step, d_s, d_noop = _device_scalars(torch, scale=0.5)
+    for _ in range(5):
+        A.adam_step_remainders_capturable(tl, hl, d_lr, d_step, d_s, d_noop)
+    torch.cuda.synchronize()
+    assert int(d_step.item()) == 5
+    got_c = dev.readback()
+    got_n, ref = run_steps(orc, host, hl, hr, 1.6e-3, 5, grad_scale=0.5)
+    assert_bitwise(got_c, got_n, ctx="capturable vs non-capturable")
+    assert_bitwise(got_c, ref, ctx="capturable vs oracle")
+
+
+def test_remainders_capturable_noop_and_graph_replay(torch, orc):
+    """The noop flag leaves bf16 params, remainders, moments, p_out and the
+    counter untouched; a captured step replayed with a changing device lr
+    equals the oracle's steps."""
+    host = host_tensors([50000, 4096, 13], g_dtype="bf16", p_kind="bf16_rem", p_out=True, seed=74,
+                        m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    d_lr, d_step, d_s, d_noop = _device_scalars(torch)
+    for d in dev.tensors:
+        d["p_out"].fill_(7.0)
+    before = dev.readback()
+    d_noop.fill_(1)
+    A.adam_step_remainders_capturable(tl, hl, d_lr, d_step, d_s, d_noop)
+    torch.cuda.synchronize()
+    assert int(d_step.item()) == 0
+    after = dev.readback()
+    for b, a in zip(before, after):
+        for r in ("p", "rem", "m", "v", "p_out"):
+            assert np.array_equal(getattr(b, r).view(np.uint8), getattr(a, r).view(np.uint8)), r
+    d_noop.fill_(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        A.adam_step_remainders_capturable(tl, hl, d_lr, d_step, d_s, d_noop)
+    torch.cuda.synchronize()
+    lrs = [1e-3, 2e-3, 5e-4]
+    for lr in lrs:
+        d_lr.fill_(lr)
+        graph.replay()
+        torch.cuda.synchronize()
+    assert int(d_step.item()) == 3
+    ref = copies(host)
+    ot = oracle_tensors(ref)
+    st = [0]
+    for lr in lrs:
+        orc.group_step(ot, hr, lr, st, 1.0, noop=0)
+    assert_bitwise(dev.readback(), ref, ctx="graph vs oracle")
+
+
+# ---------------------------------------------------------------------------
+# Scaled 16-bit optimizer state
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p_kind,g_dtype,p_out,mode", [
+    ("f16_scaled", "bf16", "bf16", 1), ("f16_scaled", "f32", None, 0), ("f16_scaled", "f16", "f16", 1),
+    ("bf16_scaled", "bf16", "f16", 1), ("bf16_scaled", "f32", "bf16", 0)])
+@pytest.mark.parametrize("chunk", [0, 1024])
+def test_scaled_state_matches_the_oracle(torch, orc, p_kind, g_dtype, p_out, mode, chunk):
+    """Several steps from a mid-training state: p, m, v (16-bit), the three
+    scales of every tensor and the param-sync copy, bit for bit.  Tensors span
+    many work items (so the per-tensor maxima fold across workgroups), ragged
+    tails and empty tensors (whose scales stay)."""
+    init = "large" if p_kind == "bf16_scaled" else "random"
+    g_std = 1.0 if p_kind == "bf16_scaled" else 1e-3
+    host = host_tensors(SIZES, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=75,
+                        m_v_init=init, g_std=g_std)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 4, desc_kw=dict(chunk_elems=chunk))
+    assert_bitwise(got, ref, ctx=f"{p_kind}/{g_dtype}/{p_out}/{mode}/{chunk}")
+    for t in got[1:]:
+        assert np.all(np.isfinite(t.scales)) and np.all(t.scales > 0)
+
+
+def test_scaled_state_from_zero_moments(torch, orc):
+    """A fresh optimizer: m = v = 0 with scales 0 (the pages initialise the
+    scales to zero); the first steps must give the oracle's scales."""
+    host = host_tensors([100000, 4096, 7], g_dtype="bf16", p_kind="f16_scaled", p_out="bf16",
+                        seed=76, m_v_init="zero")
+    assert all(h.scales[1] == 0 and h.scales[2] == 0 for h in host)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 3)
+    assert_bitwise(got, ref)
+
+
+def test_scaled_state_bf16_small_values_overflow_like_the_oracle(torch, orc):
+    """bf16 state with moments far below 0.5: the pages' scale is subnormal,
+    its reciprocal overflows, and the stored values become +-inf (zeros
+    NaN); the library reproduces exactly that."""
+    host = host_tensors([5000, 300], g_dtype="bf16", p_kind="bf16_scaled", seed=77,
+                        m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 1)
+    assert_bitwise(got, ref)
+    m = (got[0].m.astype(np.uint32) << 16).view(np.float32)
+    assert np.isinf(m).sum() > 0
+
+
+def test_scaled_state_nonfinite_gradient(torch, orc):
+    """A NaN gradient makes that tensor's three scales NaN and its stored
+    values zeros or NaN; an infinite one makes the param scale infinite.
+    Other tensors are unaffected."""
+    host = host_tensors([4096, 3000, 700], g_dtype="f32", p_kind="f16_scaled", seed=78,
+                        m_v_init="random")
+    host[0].g[100] = np.nan
+    host[1].g[5] = np.inf
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 1)
+    assert_bitwise(got, ref)
+    assert np.all(np.isnan(got[0].scales))
+    assert np.all(np.isfinite(got[2].scales))
+
+
+def test_scaled_state_does_not_depend_on_layout(torch, orc):
+    """Shared element offsets (peeled heads), unaligned per-stream offsets
+    (element path) and chunk sizes give the same bits."""
+    sizes = [70001, 4099, 1021, 17]
+    host = host_tensors(sizes, g_dtype="bf16", p_kind="f16_scaled", p_out="f16", seed=79,
+                        m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    roles = ("p", "m", "v", "g", "p_out", "scales")
+    results = []
+    for offsets, chunk in ((None, 0), ([{r: k % 8 for r in roles} for k in range(4)], 4096),
+                           ([{"p": 1, "m": 2, "v": 3, "g": 0, "p_out": 5, "scales": 1}] * 4, 1024)):
+        got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 3, desc_kw=dict(chunk_elems=chunk),
+                             offsets=offsets)
+        assert_bitwise(got, ref, ctx=f"{chunk}")
+        results.append(got)
+    for r in results[1:]:
+        assert_bitwise(r, results[0])
+
+
+def test_scaled_state_sumsq_and_clip_apply(torch, orc):
+    """The gradient reduction reads a scaled-state handle's gradients like
+    any other (fp16 gradients here)."""
+    host = host_tensors([70001, 333], g_dtype="f16", p_kind="f16_scaled", seed=80)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    d = torch.zeros(1, dtype=torch.float64, device="cuda")
+    A.adam_grad_sumsq(tl, d)
+    torch.cuda.synchronize()
+    want = orc.grad_sumsq([h.g for h in host])
+    assert abs(float(d.item()) - want) <= 1e-12 * want
+    tl.destroy()

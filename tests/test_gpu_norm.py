@@ -56,7 +56,8 @@ def gpu_sumsq(torch, tl, accumulate=False, start=0.0):
 
 @pytest.mark.parametrize("g_dtype,p_kind,layout", [
     ("f32", "f32", "aligned"), ("bf16", "f32", "shared"), ("f32", "f32", "random"),
-    ("bf16", "bf16_rem", "shared"), ("bf16", "f32", "random")])
+    ("bf16", "bf16_rem", "shared"), ("bf16", "f32", "random"), ("f16", "f32", "random"),
+    ("f16", "f16_scaled", "shared")])
 def test_grad_sumsq_matches_the_exact_sum(torch, orc, g_dtype, p_kind, layout):
     rng = np.random.default_rng(zlib.crc32(f"{g_dtype}{p_kind}{layout}".encode()))
     host = host_tensors(SIZES, g_dtype=g_dtype, p_kind=p_kind, seed=51)
@@ -81,7 +82,7 @@ def test_grad_sumsq_matches_the_exact_sum(torch, orc, g_dtype, p_kind, layout):
     tl.destroy()
 
 
-@pytest.mark.parametrize("g_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("g_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("layout,chunk", [("aligned", 0), ("aligned", 4096), ("shared", 0)])
 def test_grad_sumsq_every_tail_length(torch, orc, g_dtype, layout, chunk):
     st = A.adam_tl_plan([dict(p=1 << 40, m=2 << 40, v=3 << 40, g=4 << 40, numel=8)],

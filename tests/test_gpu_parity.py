@@ -41,6 +41,8 @@ def run_both(orc, host, hp_lib, hp_ref, lr, steps, *, grad_scale=1.0, desc_kw=No
     tl = A.adam_tl_build(dev.tensors, desc)
     rem = host[0].rem is not None if remainder is None else remainder
     fn = A.adam_step_remainders if rem else A.adam_step
+    if host[0].scales is not None:
+        fn = A.adam_step_scaled
     step = A.HostStep(0)
     ref_step = [0]
     ot = oracle_tensors(ref)
@@ -73,7 +75,9 @@ SWEEP_SIZES = list(range(0, 68)) + [4095, 4096, 4097, 4096 * 3 + 5, 10000, 65537
 @pytest.mark.parametrize("g_dtype,p_kind,p_out,mode", [
     ("f32", "f32", False, 0), ("f32", "f32", False, 1), ("bf16", "f32", False, 1),
     ("bf16", "f32", True, 0), ("f32", "f32", True, 1), ("bf16", "bf16_rem", False, 1),
-    ("f32", "bf16_rem", True, 0), ("bf16", "bf16_rem", True, 1)])
+    ("f32", "bf16_rem", True, 0), ("bf16", "bf16_rem", True, 1), ("f16", "f32", "f16", 1),
+    ("f16", "bf16_rem", True, 0), ("bf16", "f16_scaled", "f16", 1), ("f32", "f16_scaled", False, 0),
+    ("f16", "bf16_scaled", "bf16", 1)])
 def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
     """Every size 0..67 plus sizes around and across work-item boundaries, with
     each buffer of each tensor at its own element offset 0..7 (so some tensors
@@ -81,7 +85,7 @@ def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
     bitwise against the oracle."""
     rng = np.random.default_rng(zlib.crc32(f"{g_dtype}{p_kind}{p_out}{mode}".encode()))
     host = host_tensors(SWEEP_SIZES, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=7,
-                        m_v_init="random")
+                        m_v_init="large" if p_kind == "bf16_scaled" else "random")
     offsets = []
     for i in range(len(SWEEP_SIZES)):
         if i % 3 == 0:
@@ -97,7 +101,7 @@ def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
 
 @pytest.mark.parametrize("g_dtype,p_kind,p_out,mode", [
     ("f32", "f32", False, 1), ("bf16", "f32", True, 0), ("bf16", "bf16_rem", False, 1),
-    ("f32", "bf16_rem", True, 1)])
+    ("f32", "bf16_rem", True, 1), ("f16", "f32", "f16", 1), ("bf16", "f16_scaled", "bf16", 0)])
 def test_shared_offsets_take_the_peeled_vector_path(torch, orc, g_dtype, p_kind, p_out, mode):
     """Every stream of a tensor at the same element offset 0..7 (views at one
     offset into flat buffers): the leading elements before the first lane
@@ -126,14 +130,17 @@ def tile_elems(g_dtype="f32", p_kind="f32", p_out=False):
     t = dict(p=1 << 40, m=2 << 40, v=3 << 40, g=4 << 40, numel=8)
     if p_kind == "bf16_rem":
         t["rem"] = 5 << 40
+    if p_kind.endswith("_scaled"):
+        t["scales"] = 7 << 40
     if p_out:
         t["p_out"] = 6 << 40
-    desc = A.make_desc(g=g_dtype, p=p_kind, p_out="bf16" if p_out else None)
+    desc = A.make_desc(g=g_dtype, p=p_kind, p_out=("bf16" if p_out is True else p_out) or None)
     return A.adam_tl_plan([t], desc)["tile_elems"]
 
 
 @pytest.mark.parametrize("g_dtype,p_kind,p_out", [
-    ("f32", "f32", False), ("bf16", "f32", True), ("bf16", "bf16_rem", False)])
+    ("f32", "f32", False), ("bf16", "f32", True), ("bf16", "bf16_rem", False), ("f16", "f32", "f16"),
+    ("bf16", "f16_scaled", "f16")])
 @pytest.mark.parametrize("layout,chunk", [("aligned", 0), ("aligned", 4096), ("shared", 0)])
 def test_every_tail_length(torch, orc, g_dtype, p_kind, p_out, layout, chunk):
     """One tensor per tail length: a full tile plus 0..tile-1 elements, so the

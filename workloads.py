@@ -178,28 +178,56 @@ def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 @dataclass
 class HostTensor:
-    p: np.ndarray                     # float32, or bf16 bits (uint16)
-    m: np.ndarray                     # float32
-    v: np.ndarray                     # float32
-    g: np.ndarray                     # float32, or bf16 bits (uint16)
-    p_out: Optional[np.ndarray] = None
-    rem: Optional[np.ndarray] = None  # int16
+    p: np.ndarray                        # float32, bf16 bits (uint16) or float16 (scaled)
+    m: np.ndarray                        # float32, or p's 16-bit type (scaled)
+    v: np.ndarray                        # float32, or p's 16-bit type (scaled)
+    g: np.ndarray                        # float32, bf16 bits (uint16) or float16
+    p_out: Optional[np.ndarray] = None   # bf16 bits (uint16) or float16
+    rem: Optional[np.ndarray] = None     # int16
+    scales: Optional[np.ndarray] = None  # float32[3] (scaled state)
 
     def copy(self) -> "HostTensor":
         c = lambda a: None if a is None else a.copy()
         return HostTensor(c(self.p), c(self.m), c(self.v), c(self.g), c(self.p_out),
-                          c(self.rem))
+                          c(self.rem), c(self.scales))
+
+
+# Scaled-state inputs: stored = T(x * 2^k), scale = 2^-k, with k per buffer
+# chosen so that the drawn magnitudes sit well inside fp16's range (bf16
+# shares fp32's range and takes k = 0).  Any (stored, scale) pair is a valid
+# state; these are not the method's own scaling.
+_F16_SHIFT = {"p": 12, "m": 22, "v": 32}
+
+
+def _to_state(x: np.ndarray, state: str, role: str):
+    k = _F16_SHIFT[role] if state == "f16" else 0
+    y = (x.astype(np.float64) * 2.0 ** k).astype(np.float32)
+    stored = y.astype(np.float16) if state == "f16" else _to_bf16_bits(y)
+    return stored, np.float32(2.0 ** -k)
+
+
+def _out_type(p_out) -> Optional[str]:
+    """p_out option: False/None (absent), True or "bf16", or "f16"."""
+    if p_out is None or p_out is False:
+        return None
+    return "bf16" if p_out is True else p_out
 
 
 def host_tensors(sizes: Sequence[int], *, g_dtype: str = "f32", p_kind: str = "f32",
-                 p_out: bool = False, seed: int = 0, g_std: float = 1e-3,
+                 p_out=False, seed: int = 0, g_std: float = 1e-3,
                  g_multiplier: float = 1.0, m_v_init: str = "zero") -> List[HostTensor]:
-    """p ~ N(0,1), g ~ N(0,1)*g_std*g_multiplier.  m = v = 0 by default;
+    """p ~ N(0,1), g ~ N(0,1)*g_std*g_multiplier (g_dtype "f32", "bf16" or
+    "f16", cast by library conversions).  m = v = 0 by default;
     ``m_v_init="random"`` draws m ~ N(0,1)*1e-3 and v ~ |N(0,1)|*1e-6 (a
-    state part-way through training).  Remainder params: bf16 p drawn as the
-    cast of N(0,1) and the int16 remainder uniform over all 65536 values, so
-    every (bf16, remainder) pair is a valid master weight."""
+    state part-way through training); ``"large"`` draws m ~ N(0,1)*4 and
+    v ~ |N(0,1)|*4 + 1.  Remainder params (p_kind "bf16_rem"): bf16 p drawn as
+    the cast of N(0,1) and the int16 remainder uniform over all 65536 values,
+    so every (bf16, remainder) pair is a valid master weight.  Scaled state
+    (p_kind "bf16_scaled" / "f16_scaled"): p, m, v stored as T(x * 2^k) with
+    scale 2^-k (zero moments get scale 0, as a fresh optimizer has them).
+    p_out: False, True / "bf16", or "f16"."""
     rng = np.random.default_rng(seed)
+    out_type = _out_type(p_out)
     out = []
     for n in sizes:
         p32 = rng.standard_normal(n, dtype=np.float32)
@@ -208,18 +236,31 @@ def host_tensors(sizes: Sequence[int], *, g_dtype: str = "f32", p_kind: str = "f
         if m_v_init == "zero":
             m = np.zeros(n, np.float32)
             v = np.zeros(n, np.float32)
+        elif m_v_init == "large":
+            m = (rng.standard_normal(n, dtype=np.float32) * np.float32(4.0)).astype(np.float32)
+            v = (np.abs(rng.standard_normal(n, dtype=np.float32)) * np.float32(4.0)
+                 + np.float32(1.0)).astype(np.float32)
         else:
             m = (rng.standard_normal(n, dtype=np.float32) * np.float32(1e-3)).astype(np.float32)
             v = (np.abs(rng.standard_normal(n, dtype=np.float32)) * np.float32(1e-6)).astype(np.float32)
-        g = g32 if g_dtype == "f32" else _to_bf16_bits(g32)
-        rem = None
+        g = {"f32": lambda x: x, "bf16": _to_bf16_bits,
+             "f16": lambda x: x.astype(np.float16)}[g_dtype](g32)
+        rem = scales = None
         if p_kind == "f32":
             p = p32
-        else:
+        elif p_kind == "bf16_rem":
             p = _to_bf16_bits(p32)
             rem = rng.integers(-32768, 32768, size=n, dtype=np.int64).astype(np.int16)
-        po = np.zeros(n, np.uint16) if p_out else None
-        out.append(HostTensor(p, m, v, g, po, rem))
+        else:
+            state = {"bf16_scaled": "bf16", "f16_scaled": "f16"}[p_kind]
+            p, sp = _to_state(p32, state, "p")
+            m, sm = _to_state(m, state, "m")
+            v, sv = _to_state(v, state, "v")
+            if m_v_init == "zero":
+                sm = sv = np.float32(0.0)
+            scales = np.array([sp, sm, sv], np.float32)
+        po = None if out_type is None else np.zeros(n, np.float16 if out_type == "f16" else np.uint16)
+        out.append(HostTensor(p, m, v, g, po, rem, scales))
     return out
 
 
@@ -228,34 +269,44 @@ def host_tensors(sizes: Sequence[int], *, g_dtype: str = "f32", p_kind: str = "f
 # ---------------------------------------------------------------------------
 
 
-def device_flat(total: int, *, g_dtype: str, p_kind: str, p_out: bool, seed: int,
+def device_flat(total: int, *, g_dtype: str, p_kind: str, p_out, seed: int,
                 device="cuda", g_std: float = 1e-3, g_multiplier: float = 1.0,
                 chunk: int = 1 << 28):
     """Flat device buffers for ``total`` elements, drawn with torch's CUDA
     generator in chunks: p ~ N(0,1), g ~ N(0,1)*g_std*g_multiplier, m = v = 0.
-    Returns a dict of torch tensors (bf16 kept as torch.bfloat16; remainders
-    as torch.int16)."""
+    Returns a dict of torch tensors (bf16 kept as torch.bfloat16, fp16 as
+    torch.float16; remainders as torch.int16).  Scaled state stores p as
+    T(p * 2^k) (k from the scaled-state recipe); the caller keeps the scales
+    ([2^-k, 0, 0] per tensor, see ``scaled_p_scale``)."""
     import torch
 
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
     bufs = {}
+    scaled = p_kind in ("bf16_scaled", "f16_scaled")
     if p_kind == "f32":
         bufs["p"] = torch.empty(total, dtype=torch.float32, device=device)
-    else:
+    elif p_kind == "bf16_rem":
         bufs["p"] = torch.empty(total, dtype=torch.bfloat16, device=device)
         bufs["rem"] = torch.empty(total, dtype=torch.int16, device=device)
-    bufs["m"] = torch.zeros(total, dtype=torch.float32, device=device)
-    bufs["v"] = torch.zeros(total, dtype=torch.float32, device=device)
-    bufs["g"] = torch.empty(total, dtype=torch.float32 if g_dtype == "f32" else torch.bfloat16,
-                            device=device)
-    if p_out:
-        bufs["p_out"] = torch.zeros(total, dtype=torch.bfloat16, device=device)
+    else:
+        bufs["p"] = torch.empty(total, dtype=tdt[p_kind.split("_")[0]], device=device)
+    mv = bufs["p"].dtype if scaled else torch.float32
+    bufs["m"] = torch.zeros(total, dtype=mv, device=device)
+    bufs["v"] = torch.zeros(total, dtype=mv, device=device)
+    bufs["g"] = torch.empty(total, dtype=tdt[g_dtype], device=device)
+    out_type = _out_type(p_out)
+    if out_type is not None:
+        bufs["p_out"] = torch.zeros(total, dtype=tdt[out_type], device=device)
     scale = float(g_std * g_multiplier)
+    p_mul = 1.0 / scaled_p_scale(p_kind) if scaled else 1.0
     for lo in range(0, total, chunk):
         hi = min(total, lo + chunk)
         n = hi - lo
         tmp = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
+        if p_mul != 1.0:
+            tmp.mul_(p_mul)
         bufs["p"][lo:hi].copy_(tmp)
         tmp = torch.randn(n, generator=gen, device=device, dtype=torch.float32)
         tmp.mul_(scale)
@@ -266,6 +317,11 @@ def device_flat(total: int, *, g_dtype: str, p_kind: str, p_out: bool, seed: int
             bufs["rem"][lo:hi].copy_(r)
         del tmp
     return bufs
+
+
+def scaled_p_scale(p_kind: str) -> float:
+    """The param scale of ``device_flat``'s scaled-state p (a power of two)."""
+    return 2.0 ** -_F16_SHIFT["p"] if p_kind == "f16_scaled" else 1.0
 
 
 def split_views(buf, sizes: Sequence[int]):
