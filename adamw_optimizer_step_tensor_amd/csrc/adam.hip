@@ -47,11 +47,12 @@
 //    block beside the work table; every tile then reads that one block.
 //  * Scaled 16-bit state needs each buffer's largest magnitude after the
 //    update before any of it can be stored, so it takes two passes over the
-//    same tiles: the first computes the update in registers and folds
-//    per-tensor maxima (one atomic maximum per workgroup and buffer, skipped
-//    when the stored maximum is already larger); the second recomputes the
-//    identical update and stores it with the new scales.  A one-lane-per-
-//    tensor kernel then writes the scales.
+//    same tiles: the first computes the update in registers and writes each
+//    tile's three magnitude maxima; one workgroup per tensor folds its tiles'
+//    maxima; the second pass recomputes the identical update and stores it
+//    with the new scales; a one-lane-per-tensor kernel then writes the
+//    scales.  (Folding with one atomic maximum per workgroup instead was
+//    measured 8x slower: a tensor's ~1000 workgroups contend for one word.)
 //  * Arithmetic follows the header's expressions operation for operation in
 //    binary32 (the library is built with -ffp-contract=off; division and
 //    square root are the compiler's correctly rounded sequences; fp32
@@ -215,55 +216,25 @@ __device__ __forceinline__ uint32_t bf16_bits_rne(float x)
     return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
 }
 
-// binary16 bits (round to nearest, ties to even) of a float, in integer
-// steps.  Normal results: the exponent is rebiased by 127 - 15 = 112 and the
-// 13 dropped fraction bits are rounded like the bf16 case (a carry may ripple
-// into the exponent).  Magnitudes from 65520 (the midpoint between the
-// largest finite 65504 and 2^16, which rounds to even, i.e. up) overflow to
-// infinity.  Below 2^-14 the result is a subnormal count of 2^-24: the 24-bit
-// significand shifted right by 126 - exponent, rounded to nearest even on
-// the shifted-out bits; 2^-25 and below give zero.  NaN keeps sign and top
-// payload and is made quiet.
+// binary16 bits of a float and back, with the hardware conversions: the
+// kernels run in round-to-nearest-even with fp16 and fp32 subnormals kept
+// (the code object's default float mode), so float -> fp16 is the IEEE
+// nearest-even cast (overflow to infinity, subnormal results kept, NaN stays
+// NaN) and fp16 -> float is exact.  One instruction each, where an integer
+// implementation costs 10-15: the scaled-state passes are ALU-bound.
+// The empty register constraint keeps the compiler from folding the float
+// operation that produced x into the conversion: gfx950's mixed-precision
+// multiply-add would round the exact product once, straight to fp16, where
+// the method rounds it to float first (measured: 1 element in ~10^6 differs).
 __device__ __forceinline__ uint32_t f16_bits_rne(float x)
 {
-    const uint32_t b = __float_as_uint(x);
-    const uint32_t sign = (b >> 16) & 0x8000u;
-    const uint32_t a = b & 0x7FFFFFFFu;
-    if (a > 0x7F800000u) return sign | 0x7E00u | ((a >> 13) & 0x3FFu);
-    if (a >= 0x477FF000u) return sign | 0x7C00u;
-    if (a >= 0x38800000u) {
-        const uint32_t r = a - 0x38000000u;
-        return sign | ((r + 0xFFFu + ((r >> 13) & 1u)) >> 13);
-    }
-    if (a <= 0x33000000u) return sign;
-    const uint32_t shift = 126u - (a >> 23);  // 14 .. 24
-    const uint32_t sig = (a & 0x7FFFFFu) | 0x800000u;
-    const uint32_t q = sig >> shift;
-    const uint32_t rest = sig & ((1u << shift) - 1u);
-    const uint32_t half = 1u << (shift - 1u);
-    return sign | (q + ((rest > half || (rest == half && (q & 1u))) ? 1u : 0u));
+    asm volatile("" : "+v"(x));
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
 }
 
-// binary16 bits -> float, exact: normal values rebias the exponent by 112;
-// subnormals (f * 2^-24) are normalised so their leading one becomes the
-// implicit bit; exponent 31 is infinity or NaN.
 __device__ __forceinline__ float f16_to_f32(uint32_t h)
 {
-    const uint32_t sign = (h & 0x8000u) << 16;
-    const uint32_t e = (h >> 10) & 0x1Fu;
-    const uint32_t f = h & 0x3FFu;
-    uint32_t bits;
-    if (e == 0x1Fu) {
-        bits = sign | 0x7F800000u | (f << 13);
-    } else if (e != 0u) {
-        bits = sign | ((e + 112u) << 23) | (f << 13);
-    } else if (f == 0u) {
-        bits = sign;
-    } else {
-        const uint32_t s = uint32_t(__builtin_clz(f)) - 21u;  // 1 .. 10: moves the leading one to bit 10
-        bits = sign | ((113u - s) << 23) | (((f << s) & 0x3FFu) << 13);
-    }
-    return __uint_as_float(bits);
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
 // 16-bit storage types: bits -> float, float -> bits.
@@ -671,38 +642,37 @@ __device__ __forceinline__ void scaled_single(const WorkItem &w, int i, const Co
     }
 }
 
-// Device-coherent load of one word (the maxima are folded by every XCD).
-__device__ __forceinline__ uint32_t load_agent(const uint32_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // One pass over the tiles of a scaled-state list (same tile map as the
-// update).  amax holds three magnitude maxima (p, m, v) per tensor: pass 0
-// folds into them, pass 1 reads them.
+// update).  Pass 0 writes the three magnitude maxima (p, m, v) of tile t to
+// maxima[3t .. 3t+2] (zeros for a tile past its record's end); pass 1 reads
+// the folded maxima of its tensor from maxima[3k ..] of `folded`.
 template <class S>
 __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__restrict__ items,
                                                             uint32_t shift, StepArgs a,
-                                                            uint32_t *__restrict__ amax)
+                                                            uint32_t *__restrict__ maxima)
 {
     const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
     const WorkItem w = items[b >> shift];
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
-    if (start >= w.n) return;  // uniform across the workgroup
+    const int tid = threadIdx.x;
+    if (start >= w.n) {  // uniform across the workgroup
+        if constexpr (S::pass == 0) {
+            if (tid < 3) maxima[3 * b + tid] = 0u;
+        }
+        return;
+    }
 
     const Coeffs c = host_coeffs(a);
     const float *scales = static_cast<const float *>(w.aux);
     const float sc[3] = {scales[0], scales[1], scales[2]};
-    uint32_t *slot = amax + 3 * w.tensor;
     float r[3] = {0.0f, 0.0f, 0.0f};
     if constexpr (S::pass == 1) {
 #pragma unroll
-        for (int j = 0; j < 3; ++j) r[j] = rscale_of<S::st>(load_agent(slot + j));
+        for (int j = 0; j < 3; ++j) r[j] = rscale_of<S::st>(maxima[3 * w.tensor + j]);
     }
     uint32_t mx[3] = {0u, 0u, 0u};
 
     const int n = min(kTile, w.n - start);
-    const int tid = threadIdx.x;
     if (w.flags & kItemVector) {
         if (start == 0 && tid < w.head) scaled_single<S>(w, tid - w.head, c, sc, r, mx);
         const int groups = n / kLane;
@@ -713,8 +683,7 @@ __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__res
     }
 
     if constexpr (S::pass == 0) {
-        // workgroup maxima, then one atomic maximum per buffer (skipped when
-        // the tensor's maximum is already at least as large)
+        // the workgroup's maxima, one word per buffer
         __shared__ uint32_t wave_max[3][kBlock / 64];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -726,28 +695,49 @@ __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__res
         if (tid < 3) {
             uint32_t x = 0u;
             for (int k = 0; k < kBlock / 64; ++k) x = max(x, wave_max[tid][k]);
-            if (x > load_agent(slot + tid)) atomicMax(slot + tid, x);
+            maxima[3 * b + tid] = x;
         }
     }
 }
 
-// Zeroes the per-tensor maxima (device-coherent stores).
-__global__ void adam_scaled_clear(uint32_t *amax, uint32_t count)
+constexpr int kFoldMaxBlock = 256;
+
+// One workgroup per tensor: the maxima of its tiles [tiles[2k], tiles[2k+1])
+// folded into folded[3k .. 3k+2].
+__global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t *__restrict__ tile_maxima,
+                                                                  const uint32_t *__restrict__ tiles,
+                                                                  uint32_t *__restrict__ folded)
 {
-    for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += gridDim.x * blockDim.x)
-        __hip_atomic_store(amax + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t k = blockIdx.x;
+    const uint32_t lo = tiles[2 * k], hi = tiles[2 * k + 1];
+    uint32_t x[3] = {0u, 0u, 0u};
+    for (uint32_t t = lo + threadIdx.x; t < hi; t += kFoldMaxBlock)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) x[j] = max(x[j], tile_maxima[3 * t + j]);
+    __shared__ uint32_t wave_max[3][kFoldMaxBlock / 64];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        for (int off = 32; off > 0; off >>= 1) x[j] = max(x[j], uint32_t(__shfl_xor(int(x[j]), off, 64)));
+        if (threadIdx.x % 64 == 0) wave_max[j][threadIdx.x / 64] = x[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        uint32_t m = 0u;
+        for (int i = 0; i < kFoldMaxBlock / 64; ++i) m = max(m, wave_max[threadIdx.x][i]);
+        folded[3 * k + threadIdx.x] = m;
+    }
 }
 
 // One lane per tensor: the new scales, amax / limit.
 template <int ST>
 __global__ void adam_scaled_finish(float *const *__restrict__ scale_ptrs,
-                                   const uint32_t *__restrict__ amax, uint32_t tensors)
+                                   const uint32_t *__restrict__ folded, uint32_t tensors)
 {
     const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= tensors) return;
     float *s = scale_ptrs[k];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(load_agent(amax + 3 * k + j)) / scaled_limit<ST>();
+    for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(folded[3 * k + j]) / scaled_limit<ST>();
 }
 
 // ---------------------------------------------------------------------------
@@ -959,6 +949,7 @@ struct Plan {
     uint32_t shift;
     std::vector<WorkItem> items;
     std::vector<float *> scale_ptrs;  // scaled state: per non-empty tensor
+    std::vector<uint32_t> tile_ranges;  // scaled state: [first, end) tiles per non-empty tensor
 };
 
 bool valid_dtype_set(const adam_tl_desc &d)
@@ -1106,7 +1097,12 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
         const int32_t head = heads[j];
         const int64_t body = sizes[j++];
         const int64_t first = head > 0 ? head : 0;  // element index where records start
-        if (scaled) plan.scale_ptrs.push_back(t.scales);
+        if (scaled) {
+            const int64_t records = (body + chunk - 1) / chunk;
+            plan.scale_ptrs.push_back(t.scales);
+            plan.tile_ranges.push_back(uint32_t(int64_t(plan.items.size()) << shift));
+            plan.tile_ranges.push_back(uint32_t((int64_t(plan.items.size()) + records) << shift));
+        }
         for (int64_t off = 0; off < body; off += chunk) {
             const int64_t e = first + off;
             WorkItem w = {};
@@ -1168,7 +1164,9 @@ struct adam_tl {
     double *d_partials;    // reduction partial sums (after the block), one per kNormRun tiles
     uint32_t n_partials;
     float **d_scale_ptrs;  // scaled state: each non-empty tensor's scales (after the partials)
-    uint32_t *d_amax;      // scaled state: three magnitude maxima per non-empty tensor (last)
+    uint32_t *d_tiles;     // scaled state: [first, end) tile range per non-empty tensor
+    uint32_t *d_tile_max;  // scaled state: three magnitude maxima per tile
+    uint32_t *d_folded;    // scaled state: three magnitude maxima per non-empty tensor
     uint32_t n_tensors;    // non-empty tensors
 };
 
@@ -1188,20 +1186,21 @@ int launch_update(const adam_tl *tl, int mode, bool capturable, const StepArgs &
 
 int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t stream)
 {
-    const uint32_t slots = 3 * tl->n_tensors;
-    hipLaunchKernelGGL(adam_scaled_clear, dim3(std::min<uint32_t>((slots + 255) / 256, 1024)), dim3(256),
-                       0, stream, tl->d_amax, slots);
-    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     const int base = type_pos(kGradTypes, 3, tl->g) +
                      3 * (type_pos(kOutTypes, 3, tl->out) + 3 * (type_pos(kStateTypes, 2, tl->p) + 2 * mode));
-    for (int pass = 0; pass < 2; ++pass) {
-        hipLaunchKernelGGL(ScaledKernels::fns[base + 36 * pass], dim3(uint32_t(tl->stats.grid_blocks)),
-                           dim3(kBlock), 0, stream, tl->d_items, tl->shift, args, tl->d_amax);
-        if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
-    }
+    const dim3 grid(uint32_t(tl->stats.grid_blocks));
+    hipLaunchKernelGGL(ScaledKernels::fns[base], grid, dim3(kBlock), 0, stream, tl->d_items, tl->shift,
+                       args, tl->d_tile_max);
+    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
+    hipLaunchKernelGGL(adam_scaled_fold, dim3(tl->n_tensors), dim3(kFoldMaxBlock), 0, stream,
+                       tl->d_tile_max, tl->d_tiles, tl->d_folded);
+    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
+    hipLaunchKernelGGL(ScaledKernels::fns[base + 36], grid, dim3(kBlock), 0, stream, tl->d_items, tl->shift,
+                       args, tl->d_folded);
+    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     auto finish = tl->p == kBF16 ? adam_scaled_finish<kBF16> : adam_scaled_finish<kF16>;
     hipLaunchKernelGGL(finish, dim3((tl->n_tensors + 255) / 256), dim3(256), 0, stream,
-                       tl->d_scale_ptrs, tl->d_amax, tl->n_tensors);
+                       tl->d_scale_ptrs, tl->d_folded, tl->n_tensors);
     return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
 }
 
@@ -1319,7 +1318,9 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     tl->d_partials = nullptr;
     tl->n_partials = 0;
     tl->d_scale_ptrs = nullptr;
-    tl->d_amax = nullptr;
+    tl->d_tiles = nullptr;
+    tl->d_tile_max = nullptr;
+    tl->d_folded = nullptr;
     tl->n_tensors = uint32_t(plan.stats.nonempty);
     if (plan.items.empty()) {  // nothing to launch: no device state at all
         *out = tl;
@@ -1333,13 +1334,18 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     }
     tl->stats.device = device;
     tl->n_partials = uint32_t((tl->stats.grid_blocks + kNormRun - 1) / kNormRun);
-    // layout: [work table][scalar block][partial sums][scale pointers][maxima]
+    // layout: [work table][scalar block][partial sums][scale pointers]
+    //         [tile ranges][per-tile maxima][per-tensor maxima]
+    const bool scaled = tl->kind == Kind::Scaled;
     const size_t table_bytes = plan.items.size() * sizeof(WorkItem);
     const size_t block_off = table_bytes;
     const size_t partials_off = block_off + sizeof(StepBlock);
     const size_t ptrs_off = align_up(partials_off + tl->n_partials * sizeof(double), 8);
-    const size_t amax_off = ptrs_off + plan.scale_ptrs.size() * sizeof(float *);
-    const size_t total = amax_off + (tl->kind == Kind::Scaled ? 3 * sizeof(uint32_t) * tl->n_tensors : 0);
+    const size_t tiles_off = ptrs_off + plan.scale_ptrs.size() * sizeof(float *);
+    const size_t tile_max_off = tiles_off + plan.tile_ranges.size() * sizeof(uint32_t);
+    const size_t folded_off =
+        tile_max_off + (scaled ? 3 * sizeof(uint32_t) * size_t(tl->stats.grid_blocks) : 0);
+    const size_t total = folded_off + (scaled ? 3 * sizeof(uint32_t) * tl->n_tensors : 0);
     void *mem = nullptr;
     if (hipMalloc(&mem, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -1350,15 +1356,20 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     tl->d_items = reinterpret_cast<WorkItem *>(base);
     tl->d_block = reinterpret_cast<StepBlock *>(base + block_off);
     tl->d_partials = reinterpret_cast<double *>(base + partials_off);
-    if (tl->kind == Kind::Scaled) {
+    if (scaled) {
         tl->d_scale_ptrs = reinterpret_cast<float **>(base + ptrs_off);
-        tl->d_amax = reinterpret_cast<uint32_t *>(base + amax_off);
+        tl->d_tiles = reinterpret_cast<uint32_t *>(base + tiles_off);
+        tl->d_tile_max = reinterpret_cast<uint32_t *>(base + tile_max_off);
+        tl->d_folded = reinterpret_cast<uint32_t *>(base + folded_off);
     }
     bool ok = hipMemcpyAsync(tl->d_items, plan.items.data(), table_bytes, hipMemcpyHostToDevice,
                              stream) == hipSuccess;
-    if (ok && tl->kind == Kind::Scaled)
+    if (ok && scaled)
         ok = hipMemcpyAsync(tl->d_scale_ptrs, plan.scale_ptrs.data(),
                             plan.scale_ptrs.size() * sizeof(float *), hipMemcpyHostToDevice,
+                            stream) == hipSuccess &&
+             hipMemcpyAsync(tl->d_tiles, plan.tile_ranges.data(),
+                            plan.tile_ranges.size() * sizeof(uint32_t), hipMemcpyHostToDevice,
                             stream) == hipSuccess;
     if (!ok || hipStreamSynchronize(stream) != hipSuccess) {
         (void)hipFree(mem);

@@ -84,17 +84,19 @@ def _short(name: str) -> str:
     import re
 
     n = name.replace("(anonymous namespace)::", "")
-    if "adam_update" in n:
-        cfg = n[n.index("Config<") + 7:n.index(">")]
-        return f"adam_update<{cfg}>"
+    for kernel, cfg_name in (("adam_update", "Config<"), ("adam_scaled_pass", "ScaledConfig<")):
+        if kernel in n and cfg_name in n:
+            i = n.index(cfg_name) + len(cfg_name)
+            return f"{kernel}<{n[i:n.index('>', i)]}>"
     base = re.split(r"[<(]", n.replace("void ", ""), maxsplit=1)[0]
     m = re.search(r"(\w+Functor)<", n)
     return base + (f"[{m.group(1)}]" if m else "")
 
 
 def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> None:
-    """Writes profiles/adam_update_<workload>_{kernel_trace,pmc}.txt and
-    updates profiles/traffic.json from rocprofv3 CSV output.
+    """Writes profiles/<kernel>_<workload>_{kernel_trace,pmc}.txt (kernel
+    adam_update, or adam_scaled for scaled state) and updates
+    profiles/traffic.json from rocprofv3 CSV output.
 
     Durations of the update kernel come from the per-dispatch trace, grouped
     by kernel configuration and grid size (the largest grid is the workload's
@@ -110,6 +112,11 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
     cmds = {k: v.format(w=w.name) for k, v in PROFILE_COMMANDS.items()}
     n0 = sum(w.sizes)
     algo = n0 * w.bytes_per_elem
+    scaled = w.p_kind.endswith("_scaled")
+    prefix = "adam_scaled" if scaled else "adam_update"
+
+    def main_kernel(name):
+        return name.startswith("adam_update") or name.startswith("adam_scaled_pass")
 
     # kernel trace: all kernels (stats), then the update kernel per dispatch
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
@@ -124,19 +131,26 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
     per = {}
     for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
         name = _short(r["Kernel_Name"])
-        if name.startswith("adam_update"):
+        if main_kernel(name):
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
             per.setdefault((name, int(r["Grid_Size_X"])), []).append(dur)
     big = max(g for _, g in per)
-    lines += ["", "update kernel per dispatch (main group = the largest grid):",
+    lines += ["", ("scaled-state passes" if scaled else "update kernel") +
+              " per dispatch (main group = the largest grid):",
               f"{'kernel':46s} {'grid threads':>13s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} "
               f"{'max ms':>9s} {'GB/s(avg)':>10s}"]
     for (name, grid), durs in sorted(per.items()):
         avg = statistics.mean(durs)
-        gbps = f"{algo / (avg * 1e-3) / 1e9:10.1f}" if grid == big else ""
+        gbps = f"{algo / (avg * 1e-3) / 1e9:10.1f}" if grid == big and not scaled else ""
         lines.append(f"{name:46s} {grid:13d} {len(durs):5d} {avg:9.3f} {min(durs):9.3f} "
                      f"{max(durs):9.3f} {gbps}")
-    trace_path = os.path.join(ROOT, "profiles", f"adam_update_{w.name}_kernel_trace.txt")
+    if scaled:
+        # both passes of the main group make one step (the clear and scales
+        # kernels are a few microseconds)
+        passes = [statistics.mean(d) for (name, grid), d in per.items() if grid == big]
+        lines.append(f"both passes of one step: {sum(passes):.3f} ms; algorithmic bytes per step "
+                     f"{algo / 1e9:.3f} GB -> {algo / (sum(passes) * 1e-3) / 1e9:.1f} GB/s")
+    trace_path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_kernel_trace.txt")
     with open(trace_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -145,7 +159,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
         agg = {}
         for r in csv.DictReader(open(os.path.join(path, "run_counter_collection.csv"))):
             name = _short(r["Kernel_Name"])
-            if name.startswith("adam_update") and int(r["Grid_Size"]) != big:
+            if main_kernel(name) and int(r["Grid_Size"]) != big:
                 name += " (small group)"
             agg.setdefault(name, []).append(float(r["Counter_Value"]))
         return agg
@@ -153,14 +167,19 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
     fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
     cal = [k for k in fetch if "AUnaryFunctor" in k]
     assert cal, "calibration kernel (elementwise multiply) not found"
-    known_kib = w.numel * 4 / 1024  # fp32 temporary of all elements, read once and written once
+    # fp32 temporaries of all elements, read once and written once: the
+    # gradient's, and for scaled fp16 state also the param's
+    from workloads import scaled_p_scale
+
+    draws = 2 if scaled and scaled_p_scale(w.p_kind) != 1.0 else 1
+    known_kib = draws * w.numel * 4 / 1024
     f_factor = known_kib / sum(fetch[cal[0]])
     w_factor = known_kib / sum(write[cal[0]])
-    upd = [k for k in fetch if k.startswith("adam_update") and not k.endswith("(small group)")]
-    assert len(upd) == 1, upd
-    k = upd[0]
-    fetch_kib = statistics.mean(fetch[k])
-    write_kib = statistics.mean(write[k])
+    upd = [k for k in fetch if main_kernel(k) and not k.endswith("(small group)")]
+    assert len(upd) == (2 if scaled else 1), upd
+    fetch_kib = sum(statistics.mean(fetch[k]) for k in upd)
+    write_kib = sum(statistics.mean(write[k]) for k in upd)
+    k = " + ".join(upd)
     traffic = (fetch_kib * f_factor + write_kib * w_factor) * 1024
     lines = [f"rocprofv3 counters: workload {w.name}, kernel {k} (main group, {n0:,} elements)",
              f"command (read): {cmds['fetch']}", f"command (write): {cmds['write']}",
@@ -172,14 +191,20 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
                      f"{statistics.mean(write.get(name, [0])):14.1f}")
     lines += ["",
               f"calibration: {cal[0]} reads and writes {known_kib:,.0f} KiB in total",
-              f"  (the gradient scaling while inputs are drawn); counters summed over its dispatches give",
+              f"  (scaling the drawn fp32 temporaries: the gradient's, and the param's for scaled fp16 state);",
+              f"  counters summed over its dispatches give",
               f"  FETCH factor {f_factor:.4f}, WRITE factor {w_factor:.4f}",
-              f"update kernel per launch: read {fetch_kib * f_factor * 1024 / 1e9:.3f} GB, "
+              f"{'both passes per step' if scaled else 'update kernel per launch'}: "
+              f"read {fetch_kib * f_factor * 1024 / 1e9:.3f} GB, "
               f"write {write_kib * w_factor * 1024 / 1e9:.3f} GB, total {traffic / 1e9:.3f} GB",
               f"algorithmic bytes per launch: {algo / 1e9:.3f} GB ({n0:,} elements x {w.bytes_per_elem} B); "
               f"measured / algorithmic = {traffic / algo:.4f}",
               f"kernel source sha256[:16] = {source_hash()}"]
-    pmc_path = os.path.join(ROOT, "profiles", f"adam_update_{w.name}_pmc.txt")
+    if scaled:
+        lines.append("scaled state reads p, m, v and g twice (the maxima pass, then the store pass "
+                     "recomputes the update): the second read is counted whether the Infinity Cache "
+                     "or HBM serves it")
+    pmc_path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_pmc.txt")
     with open(pmc_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     try:
@@ -210,6 +235,8 @@ def cpu_baseline(w, sample_elems: int, sample_steps: int) -> dict:
 
     o = oracle.default()
     cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    if w.p_kind.endswith("_scaled"):
+        sample_elems //= 8  # the scaled-state oracle is ~8x slower per element
     sizes = []
     for n in w.sizes:
         sizes.append(n)
@@ -217,19 +244,27 @@ def cpu_baseline(w, sample_elems: int, sample_steps: int) -> dict:
             break
     host = host_tensors(sizes, g_dtype=w.g_dtype, p_kind=w.p_kind, p_out=w.p_out, seed=w.seed,
                         g_multiplier=w.grad_multiplier)
-    cat = lambda role: (None if getattr(host[0], role) is None
-                        else np.concatenate([getattr(h, role) for h in host]))
-    t = oracle.OracleTensor(cat("p"), cat("m"), cat("v"), cat("g"), cat("p_out"), cat("rem"))
-    del host
-    n = t.numel
     hp = oracle.HParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
-    bounds = [(i * n // cores, (i + 1) * n // cores) for i in range(cores)]
+    if host[0].scales is not None:
+        # scaled state: each tensor's new scales need all of it, so the
+        # threads take whole tensors
+        ts = [oracle.OracleTensor(h.p, h.m, h.v, h.g, h.p_out, None, h.scales) for h in host]
+        n = sum(t.numel for t in ts)
+        jobs = [lambda bc1, bc2, t=t: o.update_tensor(t, hp, w.lr, bc1, bc2, w.grad_scale) for t in ts]
+    else:
+        cat = lambda role: (None if getattr(host[0], role) is None
+                            else np.concatenate([getattr(h, role) for h in host]))
+        t = oracle.OracleTensor(cat("p"), cat("m"), cat("v"), cat("g"), cat("p_out"), cat("rem"))
+        n = t.numel
+        bounds = [(i * n // cores, (i + 1) * n // cores) for i in range(cores)]
+        jobs = [lambda bc1, bc2, b=b: o.update_tensor(t, hp, w.lr, bc1, bc2, w.grad_scale, b[0], b[1])
+                for b in bounds]
+    del host
     t0 = time.perf_counter()
     with ThreadPoolExecutor(cores) as ex:
         for step in range(1, sample_steps + 1):
             bc1, bc2 = o.bias_corrections(w.beta1, w.beta2, step, 1)
-            list(ex.map(lambda b: o.update_tensor(t, hp, w.lr, bc1, bc2, w.grad_scale, b[0], b[1]),
-                        bounds))
+            list(ex.map(lambda job: job(bc1, bc2), jobs))
     dt = time.perf_counter() - t0
     gbps = n * sample_steps * w.bytes_per_elem / dt / 1e9
     cpu_model = ""
@@ -279,7 +314,7 @@ def main() -> int:
     import torch
 
     import adamw_optimizer_step_tensor_amd as A
-    from workloads import device_flat, split_views, workloads
+    from workloads import device_flat, scaled_p_scale, split_views, workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -298,14 +333,24 @@ def main() -> int:
     log(f"inputs drawn on the GPU in {time.perf_counter() - t0:.1f} s")
 
     # one handle per group, views into the flat buffers
+    scaled = w.p_kind.endswith("_scaled")
+    p_out = ("bf16" if w.p_out is True else w.p_out) or None
     handles = []
+    scale_bufs = []
     off = 0
     for sizes, wd in groups:
         n = sum(sizes)
         views = {k: split_views(v[off:off + n], sizes) for k, v in bufs.items()}
         tensors = [{k: views[k][i] for k in views} for i in range(len(sizes))]
-        desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out="bf16" if w.p_out else None,
-                           chunk_elems=args.chunk_elems)
+        if scaled:
+            # per-tensor scales of p, m, v: the drawn p's power-of-two scale;
+            # zero moments carry scale 0 (a fresh optimizer)
+            sc = torch.zeros((len(sizes), 3), dtype=torch.float32, device="cuda")
+            sc[:, 0] = scaled_p_scale(w.p_kind)
+            scale_bufs.append(sc)
+            for i, t in enumerate(tensors):
+                t["scales"] = sc[i]
+        desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out, chunk_elems=args.chunk_elems)
         tl = A.adam_tl_build(tensors, desc)
         hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
         # each group keeps its own counter, host and device
@@ -316,7 +361,7 @@ def main() -> int:
         f"{info['grid_blocks']} workgroups of {info['block_threads']} threads, "
         f"{info['tile_elems']} elements each")
 
-    step_fn = A.adam_step_remainders if w.p_kind == "bf16_rem" else A.adam_step
+    step_fn = {"bf16_rem": A.adam_step_remainders, "f32": A.adam_step}.get(w.p_kind, A.adam_step_scaled)
     stream = torch.cuda.current_stream()
     d_scale = torch.tensor([w.grad_scale], dtype=torch.float32, device="cuda")
 
@@ -381,10 +426,13 @@ def main() -> int:
         "data": "synthetic (p~N(0,1), g~N(0,1)*1e-3, m=v=0; drawn on the GPU)",
         "config": {
             "workload": f"{w.name}: {len(w.sizes)} tensors, {total:,} elements, "
-                        f"p {w.p_kind}, g {w.g_dtype}, m/v f32, p_out {'bf16' if w.p_out else 'none'}, "
+                        f"p {w.p_kind}, g {w.g_dtype}, m/v {'scaled 16-bit' if scaled else 'f32'}, "
+                        f"p_out {p_out or 'none'}, "
                         f"{'AdamW' if w.mode else 'L2'}, lr {w.lr}, betas ({w.beta1}, {w.beta2}), "
                         f"eps {w.eps}, wd {w.weight_decay}",
-            "path": f"{step_fn.__name__} (non-capturable), one launch per group per step",
+            "path": f"{step_fn.__name__} (non-capturable), "
+                    + ("four launches per group per step (maxima pass, per-tensor fold, store pass, scales)"
+                       if scaled else "one launch per group per step"),
             "bytes_per_elem": w.bytes_per_elem,
             "chunk_elems": info["chunk_elems"],
             "grid_blocks": info["grid_blocks"],
@@ -395,8 +443,10 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"adam_update (p {w.p_kind}, g {w.g_dtype}, m/v f32, p_out "
-                      f"{'bf16' if w.p_out else 'none'}, {'AdamW' if w.mode else 'L2'}, non-capturable)",
+            "kernel": (f"adam_scaled_pass x2 + clear + scales (the whole scaled step of the main group; "
+                       f"p {w.p_kind}, g {w.g_dtype}, p_out {p_out or 'none'})" if scaled else
+                       f"adam_update (p {w.p_kind}, g {w.g_dtype}, m/v f32, p_out "
+                       f"{p_out or 'none'}, {'AdamW' if w.mode else 'L2'}, non-capturable)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -408,14 +458,15 @@ def main() -> int:
     }
 
     # --- capturable, eager and graph -----------------------------------------
-    if not args.no_capturable and w.p_kind == "f32":
+    cap_fn = {"f32": A.adam_step_capturable, "bf16_rem": A.adam_step_remainders_capturable}.get(w.p_kind)
+    if not args.no_capturable and cap_fn is not None:
         d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
         d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
 
         def one_step_cap(ev=None, s=stream):
             for i, (tl, hp, _, _, d_step) in enumerate(handles):
                 launch_timed(ev if i == 0 else None,
-                             lambda: A.adam_step_capturable(tl, hp, d_lr, d_step, d_scale, d_noop, s))
+                             lambda: cap_fn(tl, hp, d_lr, d_step, d_scale, d_noop, s))
 
         for _ in range(args.warmup):
             one_step_cap()
@@ -460,7 +511,7 @@ def main() -> int:
                              lambda: A.adam_grad_sumsq(tl, d_sumsq, i > 0, s))
             A.adam_clip_grad_scale(d_sumsq, d_full_scale, max_norm, d_norm, d_noop, s)
             for tl, hp, _, _, d_step in handles:
-                A.adam_step_capturable(tl, hp, d_lr, d_step, d_full_scale, d_noop, s)
+                cap_fn(tl, hp, d_lr, d_step, d_full_scale, d_noop, s)
 
         for _ in range(args.warmup):
             one_full_step()
@@ -491,7 +542,7 @@ def main() -> int:
 
     for h in handles:
         h[0].destroy()
-    del bufs
+    del bufs, scale_bufs
     torch.cuda.empty_cache()
 
     if not args.no_cpu:

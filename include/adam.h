@@ -165,7 +165,8 @@ int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *
 /* Builds a handle for one group: validates as adam_tl_plan, then copies the
  * work table (one 64-byte record per chunk, plus a 64-byte scalar block used
  * by the capturable steps, partial-sum scratch for adam_grad_sumsq, and for
- * scaled state one 12-byte maximum record per tensor) to the current device,
+ * scaled state 12 bytes of maxima per 512-element tile and per tensor) to the
+ * current device,
  * using `stream`, and waits for that copy.  `tensors` (host array of `count`) is
  * not retained; the device buffers it names must stay allocated and in place
  * for the handle's life.  On success *out owns device memory; release it with
@@ -254,11 +255,12 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
  * Note: with bf16 state a tensor whose largest magnitude is below about 0.5
  * gets a subnormal scale whose reciprocal overflows, so its values store as
  * +-inf (0 becomes NaN) -- the pages' formula does this; fp16 state does not.
- * Empty tensors keep their scales.  The call enqueues four kernels (clear the
- * per-tensor maxima, a pass that computes the update and the maxima, a pass
- * that recomputes it and stores, a per-tensor pass that writes the new
- * scales); steps of one handle must be ordered.  Arguments and errors as
- * adam_step; ADAM_EINVAL for a handle without scaled state. */
+ * Empty tensors keep their scales.  The call enqueues four kernels (a pass
+ * that computes the update and each tile's maxima, a fold of those maxima
+ * per tensor, a pass that recomputes the update and stores it, a per-tensor
+ * kernel that writes the new scales); steps of one handle must be ordered.
+ * Arguments and errors as adam_step; ADAM_EINVAL for a handle without
+ * scaled state. */
 int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
                      float grad_scale, const float *d_grad_scale, hipStream_t stream);
 

@@ -86,6 +86,45 @@ def test_fp16_param_out_is_the_cast_of_the_new_param(torch, orc):
         assert np.array_equal(t.p_out.view(np.uint16), t.p.astype(np.float16).view(np.uint16))
 
 
+def test_fp16_casts_through_the_update(torch, orc):
+    """The fp16 conversions over many inputs, through the update itself.
+    (1) p_out: with g = m = v = 0, lr = 0 and no decay the new param is the
+    old one (finite p), so p_out is the fp16 cast of 2^24 random float32
+    patterns from the cast's whole range (2^-26 .. 2^17 in magnitude) plus its
+    edges; it must equal numpy's cast.  (2) gradients: with beta1 = 0 and
+    grad scale 1 the new first moment is the widened gradient, for all 65536
+    fp16 patterns.  Both also match the oracle bit for bit."""
+    rng = np.random.default_rng(81)
+    lo, hi = np.float32(2.0 ** -26).view(np.uint32), np.float32(2.0 ** 17).view(np.uint32)
+    pats = rng.integers(int(lo), int(hi), size=1 << 24, dtype=np.int64).astype(np.uint32)
+    pats[: 1 << 23] |= np.uint32(0x80000000)
+    edges = np.array([65504.0, 65519.996, 65520.0, 65536.0, 2.0 ** -14, 2.0 ** -24, 2.0 ** -25,
+                      3 * 2.0 ** -25, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 0.0, -0.0], np.float32)
+    p = np.concatenate([pats.view(np.float32), edges, -edges])
+    n = p.size
+    from workloads import HostTensor
+
+    host = [HostTensor(p.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32),
+                       np.zeros(n, np.float16), np.zeros(n, np.float16))]
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.0, 1)
+    got, ref = run_steps(orc, host, hl, hr, 0.0, 1)
+    assert_bitwise(got, ref)
+    assert np.array_equal(got[0].p.view(np.uint32), p.view(np.uint32))
+    with np.errstate(over="ignore"):
+        want = p.astype(np.float16)
+    assert np.array_equal(got[0].p_out.view(np.uint16), want.view(np.uint16))
+    # gradients: every fp16 pattern
+    g = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    host = [HostTensor(np.zeros(65536, np.float32), np.zeros(65536, np.float32),
+                       np.zeros(65536, np.float32), g.copy())]
+    hl, hr = hp_pair(0.0, 0.95, 1e-8, 0.0, 1)
+    got, ref = run_steps(orc, host, hl, hr, 0.0, 1)
+    assert_bitwise(got, ref)
+    wide = g.astype(np.float32)
+    ok = ~np.isnan(wide) & (wide != 0)
+    assert np.array_equal(got[0].m[ok].view(np.uint32), wide[ok].view(np.uint32))
+
+
 # ---------------------------------------------------------------------------
 # Capturable remainder step
 # ---------------------------------------------------------------------------

@@ -58,10 +58,15 @@ def group_tensors(bufs, sizes, off):
     return [{k: views[k][i] for k in views} for i in range(len(sizes))]
 
 
-def oracle_sample(host, pos, has_out, rem):
+def out_type(w):
+    return ("bf16" if w.p_out is True else w.p_out) or None
+
+
+def oracle_sample(host, pos, out, rem):
     return oracle.OracleTensor(p=host["p"].copy(), m=host["m"].copy(), v=host["v"].copy(),
                                g=host["g"].copy(),
-                               p_out=np.zeros(len(pos), np.uint16) if has_out else None,
+                               p_out=None if not out else np.zeros(len(pos), np.float16 if out == "f16"
+                                                                   else np.uint16),
                                rem=host["rem"].copy() if rem else None)
 
 
@@ -70,6 +75,8 @@ def compare(got, ref, roles):
         a, b = got[r], getattr(ref, r)
         if a.dtype == np.float32:
             same = (a.view(np.uint32) == b.view(np.uint32)) | (np.isnan(a) & np.isnan(b))
+        elif a.dtype == np.float16:
+            same = (a.view(np.uint16) == b.view(np.uint16)) | (np.isnan(a) & np.isnan(b))
         else:
             same = a == b
         assert same.all(), f"{r}: {int((~same).sum())} of {a.size} sampled elements differ"
@@ -94,12 +101,12 @@ def run_sampled(torch, wname, steps, *, capturable=False, noop_every=0, seed=0,
         pos_dev = torch.from_numpy(pos).to("cuda")
         host = {r: gather(torch, bufs[r], pos_dev) for r in roles}
         tl = A.adam_tl_build(group_tensors(bufs, sizes, off),
-                             A.make_desc(g=w.g_dtype, p=w.p_kind, p_out="bf16" if w.p_out else None))
+                             A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=out_type(w)))
         hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
         hr = oracle.HParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
         handles.append(dict(tl=tl, hp=hp, hr=hr, step=A.HostStep(0),
                             d_step=torch.zeros(1, dtype=torch.int32, device="cuda"), ref_step=[0]))
-        samples.append(dict(pos=pos, pos_dev=pos_dev, ref=oracle_sample(host, pos, w.p_out, rem)))
+        samples.append(dict(pos=pos, pos_dev=pos_dev, ref=oracle_sample(host, pos, out_type(w), rem)))
         off += n
     d_scale = torch.tensor([w.grad_scale], dtype=torch.float32, device="cuda")
     d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
@@ -179,6 +186,56 @@ def test_remainders_hundred_steps_with_empty_group(torch):
         A.adam_step_remainders(empty, A.AdamHParams(), 1e-3, empty_step)
     assert empty_step.value == 100
     del bufs
+
+
+def test_zero_shard_fp16_capturable_with_noop(torch):
+    """The ZeRO shard with fp16 gradients and an fp16 param-sync copy,
+    capturable, noop on every 5th step."""
+    run_sampled(torch, "zero1e9_f16", 10, capturable=True, noop_every=5, seed=8)
+
+
+def test_scaled_state_zero_shard(torch):
+    """1e9 elements of scaled fp16 p, m, v in 2048 buckets, bf16 gradients,
+    bf16 param-sync copy, five steps from a fresh state.  The new scales of a
+    tensor depend on all of it, so the samples are whole tensors (first,
+    middle, last and five random buckets): their initial state goes to the
+    host, the oracle steps them, and values, scales and p_out must match."""
+    w = workloads()["scaled1e9"]
+    from workloads import scaled_p_scale
+
+    bufs = device_flat(w.numel, g_dtype=w.g_dtype, p_kind=w.p_kind, p_out=w.p_out, seed=w.seed)
+    sizes = w.sizes
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    scales = torch.zeros((len(sizes), 3), dtype=torch.float32, device="cuda")
+    scales[:, 0] = scaled_p_scale(w.p_kind)
+    tensors = group_tensors(bufs, sizes, 0)
+    for i, t in enumerate(tensors):
+        t["scales"] = scales[i]
+    rng = np.random.default_rng(9)
+    picks = sorted({0, len(sizes) // 2, len(sizes) - 1, *rng.integers(0, len(sizes), 5).tolist()})
+    torch.cuda.synchronize()
+    refs = []
+    for k in picks:
+        lo, hi = int(offs[k]), int(offs[k + 1])
+        host = {r: dev_to_np(bufs[r][lo:hi]) for r in ("p", "m", "v", "g")}
+        refs.append(oracle.OracleTensor(host["p"], host["m"], host["v"], host["g"],
+                                        np.zeros(hi - lo, np.uint16), None,
+                                        dev_to_np(scales[k]).astype(np.float32)))
+    tl = A.adam_tl_build(tensors, A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=out_type(w)))
+    hp = A.AdamHParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
+    hr = oracle.HParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
+    step, ref_step = A.HostStep(0), [0]
+    for _ in range(5):
+        A.adam_step_scaled(tl, hp, w.lr, step)
+        oracle.default().group_step(refs, hr, w.lr, ref_step, 1.0)
+    torch.cuda.synchronize()
+    assert step.value == ref_step[0] == 5
+    for k, ref in zip(picks, refs):
+        lo, hi = int(offs[k]), int(offs[k + 1])
+        got = {r: dev_to_np(bufs[r][lo:hi]) for r in ("p", "m", "v", "p_out")}
+        got["scales"] = dev_to_np(scales[k])
+        compare(got, ref, ("p", "m", "v", "p_out", "scales"))
+    tl.destroy()
 
 
 def test_single_tensor_beyond_2_pow_31_elements(torch):

@@ -31,3 +31,27 @@ def test_host_tensors_distributions():
     assert h.rem.min() < -30000 and h.rem.max() > 30000
     h2 = host_tensors([100000], seed=3)[0]
     assert 0.98 < h2.p.std() < 1.02 and h2.p.dtype == np.float32
+
+
+def test_fp16_and_scaled_workloads():
+    w = workloads()
+    assert w["zero1e9_f16"].bytes_per_elem == 28 and w["zero1e9_f16"].sizes == w["zero1e9"].sizes
+    s = w["scaled1e9"]
+    assert s.bytes_per_elem == 16 and s.numel == 1_000_000_000 and s.p_kind == "f16_scaled"
+
+
+def test_scaled_state_inputs_decode_to_the_drawn_values():
+    """Scaled-state inputs: stored x 2^-k reproduces the drawn float32
+    values to the state type's precision; zero moments carry scale 0."""
+    h = host_tensors([50000], g_dtype="f16", p_kind="f16_scaled", p_out="f16", seed=5,
+                     m_v_init="random")[0]
+    h32 = host_tensors([50000], g_dtype="f32", seed=5, m_v_init="random")[0]
+    assert h.p.dtype == np.float16 and h.m.dtype == np.float16 and h.g.dtype == np.float16
+    assert h.p_out.dtype == np.float16 and h.scales.dtype == np.float32
+    for stored, scale, x in ((h.p, h.scales[0], h32.p), (h.m, h.scales[1], h32.m),
+                             (h.v, h.scales[2], h32.v)):
+        back = stored.astype(np.float64) * float(scale)
+        assert np.all(np.abs(back - x) <= 2.0 ** -11 * np.abs(x) + float(scale) * 2.0 ** -24)
+        assert np.isfinite(stored).all()
+    z = host_tensors([100], p_kind="bf16_scaled", seed=1)[0]
+    assert z.scales[1] == 0 and z.scales[2] == 0 and z.p.dtype == np.uint16

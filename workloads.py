@@ -13,7 +13,9 @@ Shapes and value distributions follow the pages' workloads:
   run that issue reports on, which is not available here;
 * a ZeRO-style local shard cut into buckets (apex distributed_fused_adam.py,
   bucket sizes rounded to the 128-byte alignment of the grad-sync dtype);
-* bf16 params with int16 remainders.
+* bf16 params with int16 remainders;
+* per-tensor scaled 16-bit optimizer state (apex distributed_fused_adam.py,
+  ``with_scaled_states``) on the ZeRO shard's buckets.
 
 Host arrays are numpy (bf16 as raw uint16 bits).  Large inputs are drawn on
 the GPU with torch's generator (see ``device_*`` helpers) so no 100 GB host
@@ -37,9 +39,9 @@ import numpy as np
 class Workload:
     name: str
     sizes: Tuple[int, ...]                 # elements per tensor (group 0)
-    g_dtype: str                           # "f32" or "bf16"
-    p_kind: str                            # "f32" or "bf16_rem"
-    p_out: bool                            # bf16 param-out copy
+    g_dtype: str                           # "f32", "bf16" or "f16"
+    p_kind: str                            # "f32", "bf16_rem", "bf16_scaled" or "f16_scaled"
+    p_out: object                          # False, True / "bf16", or "f16": param-out copy
     lr: float
     beta1: float
     beta2: float
@@ -59,10 +61,12 @@ class Workload:
     def bytes_per_elem(self) -> int:
         """Algorithmic HBM bytes per element: every state word is read once and
         written once; the gradient is read once."""
-        p = 4 if self.p_kind == "f32" else 4  # fp32 p, or bf16 p + int16 rem
+        scaled = self.p_kind.endswith("_scaled")
+        p = 2 if scaled else 4  # fp32 p, bf16 p + int16 rem, or a scaled 16-bit p
+        mv = 2 if scaled else 4
         g = 4 if self.g_dtype == "f32" else 2
-        read = p + 4 + 4 + g
-        write = p + 4 + 4 + (2 if self.p_out else 0)
+        read = p + 2 * mv + g
+        write = p + 2 * mv + (2 if self.p_out else 0)
         return read + write
 
 
@@ -159,6 +163,15 @@ def workloads() -> dict:
                            "bf16", "bf16_rem", False,
                            lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
                            weight_decay=0.1, mode=1, seed=5),
+        # the ZeRO shard with fp16 gradients and an fp16 param-sync copy
+        "zero1e9_f16": Workload("zero1e9_f16", zero_bucket_sizes(), "f16", "f32", "f16",
+                                lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                                weight_decay=0.1, mode=1, seed=6),
+        # the ZeRO shard with scaled fp16 p, m, v, bf16 gradients and a bf16
+        # param-sync copy: 16 B/elem
+        "scaled1e9": Workload("scaled1e9", zero_bucket_sizes(), "bf16", "f16_scaled", "bf16",
+                              lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                              weight_decay=0.1, mode=1, seed=7),
     }
 
 
