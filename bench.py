@@ -75,7 +75,59 @@ PROFILE_COMMANDS = {
              "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
     "summary": "python bench.py --summarize-profiles --workload {w} --trace-dir gpurun_out/trace_{w} "
                "--fetch-dir gpurun_out/pmc_fetch_{w} --write-dir gpurun_out/pmc_write_{w}",
+    "valu": "cd /tmp && rocprofv3 --pmc SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVES GRBM_GUI_ACTIVE "
+            "--output-format csv -d <repo>/gpurun_out/pmc_valu_{w} -o run -- python3 <repo>/bench.py "
+            "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+    "valu_summary": "python bench.py --summarize-valu --workload {w} --valu-dir gpurun_out/pmc_valu_{w}",
 }
+
+CU_NUM = 256
+XCD_NUM = 8
+
+
+def summarize_valu(w, valu_dir: str) -> None:
+    """Writes profiles/<kernel>_<workload>_valu.txt: VALU instructions per
+    element and VALU activity of the main group's kernels, from one rocprofv3
+    --pmc pass (SQ_INSTS_VALU, SQ_ACTIVE_INST_VALU, SQ_WAVES, GRBM_GUI_ACTIVE;
+    the CSV sums each over shader engines and XCDs).  "VALU busy" is
+    rocprofv3's VALUBusy expression, 100 * SQ_ACTIVE_INST_VALU / CUs /
+    GRBM_GUI_ACTIVE of one XCD (the summed value / 8)."""
+    import csv
+
+    cmds = {k: v.format(w=w.name) for k, v in PROFILE_COMMANDS.items()}
+    n0 = sum(w.sizes)
+    scaled = w.p_kind.endswith("_scaled")
+    prefix = "adam_scaled" if scaled else "adam_update"
+    vals = {}  # (kernel, dispatch) -> {counter: value}
+    grids = {}
+    for r in csv.DictReader(open(os.path.join(valu_dir, "run_counter_collection.csv"))):
+        name = _short(r["Kernel_Name"])
+        key = (name, r["Dispatch_Id"])
+        vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        grids[key] = int(r["Grid_Size"])
+    big = max(g for (n, _), g in grids.items() if n.startswith(("adam_update", "adam_scaled_pass")))
+    per = {}
+    for key, c in vals.items():
+        if grids[key] == big and key[0].startswith(("adam_update", "adam_scaled_pass")):
+            per.setdefault(key[0], []).append(c)
+    lines = [f"rocprofv3 VALU counters: workload {w.name}, main group ({n0:,} elements)",
+             f"command: {cmds['valu']}", f"summary: {cmds['valu_summary']}", "",
+             f"{'kernel':40s} {'n':>3s} {'VALU insts/elem':>16s} {'VALU busy %':>12s} {'waves':>12s}"]
+    for name, cs in sorted(per.items()):
+        insts = statistics.mean(c["SQ_INSTS_VALU"] for c in cs)
+        active = statistics.mean(c["SQ_ACTIVE_INST_VALU"] for c in cs)
+        gui = statistics.mean(c["GRBM_GUI_ACTIVE"] for c in cs) / XCD_NUM  # per-XCD cycles
+        waves = statistics.mean(c["SQ_WAVES"] for c in cs)
+        busy = 100.0 * active / CU_NUM / gui
+        lines.append(f"{name:40s} {len(cs):3d} {insts * 64 / n0:16.1f} {busy:12.1f} {waves:12.0f}")
+    lines += ["", "VALU insts/elem = SQ_INSTS_VALU (wave-level instructions) x 64 lanes / elements.",
+              "VALU busy is rocprofv3's VALUBusy expression; on this part it is not capped at 100%",
+              "(its quad-cycle normalisation), so compare kernels with each other: the same",
+              "expression for a memory-bound kernel and an ALU-bound one differs by ~3x."]
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_valu.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def _short(name: str) -> str:
@@ -298,12 +350,20 @@ def main() -> int:
     ap.add_argument("--trace-dir")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
+    ap.add_argument("--summarize-valu", action="store_true",
+                    help="write profiles/ VALU summary from a rocprofv3 counter directory (no GPU)")
+    ap.add_argument("--valu-dir")
     args = ap.parse_args()
 
     if args.summarize_profiles:
         from workloads import workloads
 
         summarize_profiles(workloads()[args.workload], args.trace_dir, args.fetch_dir, args.write_dir)
+        return 0
+    if args.summarize_valu:
+        from workloads import workloads
+
+        summarize_valu(workloads()[args.workload], args.valu_dir)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
