@@ -122,7 +122,9 @@ def run_sampled(torch, wname, steps, *, capturable=False, noop_every=0, seed=0,
             if k == noop_every:  # full-buffer check once
                 before = {r: bufs[r].clone() for r in out_roles}
         for h in handles:
-            if capturable:
+            if capturable and rem:
+                A.adam_step_remainders_capturable(h["tl"], h["hp"], d_lr, h["d_step"], d_scale, d_noop)
+            elif capturable:
                 A.adam_step_capturable(h["tl"], h["hp"], d_lr, h["d_step"], d_scale, d_noop)
             elif rem:
                 A.adam_step_remainders(h["tl"], h["hp"], w.lr, h["step"], 1.0, d_scale)
@@ -236,6 +238,12 @@ def test_scaled_state_zero_shard(torch):
         got["scales"] = dev_to_np(scales[k])
         compare(got, ref, ("p", "m", "v", "p_out", "scales"))
     tl.destroy()
+
+
+def test_remainders_capturable_with_noop(torch):
+    """The remainder workload through the capturable remainder step, noop on
+    every 4th step."""
+    run_sampled(torch, "rem5e8", 12, capturable=True, noop_every=4, seed=10, whole_limit=1_000_000)
 
 
 def test_single_tensor_beyond_2_pow_31_elements(torch):

@@ -170,14 +170,17 @@ def test_clip_argument_errors(torch):
     assert L.adam_grad_sumsq(None, d.data_ptr(), 0, None) == A.ADAM_EINVAL
 
 
-def test_whole_capturable_step_in_one_graph(torch, orc):
-    """Two groups (decay and no decay, bf16 grads, bf16 p_out): per step the
-    gradient sum of squares of both groups, the clip / found-inf step, then
-    the capturable update of each group, all recorded in one HIP graph and
-    replayed; an infinite gradient on the third replay skips that step.
-    Each replay equals the oracle fed the same sum of squares."""
-    h1 = host_tensors([40000, 4096, 333], g_dtype="bf16", p_out=True, seed=56)
-    h2 = host_tensors([4096] * 3, g_dtype="bf16", p_out=True, seed=57)
+@pytest.mark.parametrize("g_dtype,p_kind,p_out", [("bf16", "f32", "bf16"), ("bf16", "bf16_rem", "bf16"),
+                                                 ("f16", "f32", "f16")])
+def test_whole_capturable_step_in_one_graph(torch, orc, g_dtype, p_kind, p_out):
+    """Two groups (decay and no decay): per step the gradient sum of squares
+    of both groups, the clip / found-inf step, then the capturable update of
+    each group (fp32 master or bf16 + remainders), all recorded in one HIP
+    graph and replayed; an infinite gradient on the third replay skips that
+    step.  Each replay equals the oracle fed the same sum of squares."""
+    h1 = host_tensors([40000, 4096, 333], g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=56)
+    h2 = host_tensors([4096] * 3, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=57)
+    cap = A.adam_step_remainders_capturable if p_kind == "bf16_rem" else A.adam_step_capturable
     d1, d2 = DeviceSet(h1), DeviceSet(h2)
     t1 = A.adam_tl_build(d1.tensors, desc_for(h1))
     t2 = A.adam_tl_build(d2.tensors, desc_for(h2))
@@ -196,8 +199,8 @@ def test_whole_capturable_step_in_one_graph(torch, orc):
         A.adam_grad_sumsq(t1, d_sumsq, False, stream)
         A.adam_grad_sumsq(t2, d_sumsq, True, stream)
         A.adam_clip_grad_scale(d_sumsq, d_scale, max_norm, d_norm, d_noop, stream)
-        A.adam_step_capturable(t1, hp1, d_lr, s1, d_scale, d_noop, stream)
-        A.adam_step_capturable(t2, hp2, d_lr, s2, d_scale, d_noop, stream)
+        cap(t1, hp1, d_lr, s1, d_scale, d_noop, stream)
+        cap(t2, hp2, d_lr, s2, d_scale, d_noop, stream)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
