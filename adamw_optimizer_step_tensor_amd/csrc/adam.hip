@@ -55,9 +55,11 @@
 //    measured 8x slower: a tensor's ~1000 workgroups contend for one word.)
 //  * Arithmetic follows the header's expressions operation for operation in
 //    binary32 (the library is built with -ffp-contract=off; division and
-//    square root are the compiler's correctly rounded sequences; fp32
-//    denormals are kept), so results match a scalar C evaluation bit for bit
-//    and do not depend on chunking or alignment.
+//    square root are correctly rounded -- the compiler's sequences, or for
+//    the two divisions by the step's bias corrections a double reciprocal
+//    product proven to give the same bits; fp32 denormals are kept), so
+//    results match a scalar C evaluation bit for bit and do not depend on
+//    chunking or alignment.
 
 #include <hip/hip_runtime.h>
 
@@ -133,12 +135,14 @@ static_assert(sizeof(WorkItem) == 64, "work item must be one 64-byte record");
 
 // Scalars of one capturable step, resolved on the device by the prologue.
 struct alignas(64) StepBlock {
+    double rbc1, rbc2;  // 1/bc1, 1/bc2 rounded to double
     float lr, scale, bc1, bc2;
-    int32_t skip;  // the noop flag was 1: the update does nothing
-    int32_t t;     // step used by this update
+    int32_t skip;       // the noop flag was 1: the update does nothing
+    int32_t t;          // step used by this update
 };
 
 struct StepArgs {
+    double rbc1, rbc2;  // 1/bc1, 1/bc2 rounded to double
     float lr, beta1, beta2, eps, weight_decay, bc1, bc2, grad_scale;
     const float *d_grad_scale;  // nullable: read on the device instead of grad_scale
     const StepBlock *block;     // capturable only
@@ -146,6 +150,7 @@ struct StepArgs {
 
 // Per-workgroup constants of the update.
 struct Coeffs {
+    double rbc1, rbc2;
     float lr, beta1, keep1, beta2, keep2, eps, wd, bc1, bc2, scale;
 };
 
@@ -182,13 +187,44 @@ __host__ __device__ inline void corrections(float beta1, float beta2, int32_t t,
     }
 }
 
+// The corrections and their double reciprocals (see quotient_by below).
+__host__ __device__ inline void step_corrections(float beta1, float beta2, int32_t t, int32_t on,
+                                                 float &bc1, float &bc2, double &rbc1, double &rbc2)
+{
+    corrections(beta1, beta2, t, on, bc1, bc2);
+    rbc1 = 1.0 / double(bc1);
+    rbc2 = 1.0 / double(bc2);
+}
+
 // ---------------------------------------------------------------------------
 // Element arithmetic
 // ---------------------------------------------------------------------------
 
+// The float quotient x / y for a y shared by every element, given r, the
+// double nearest 1/y: float(double(x) * r).  This is x / y rounded to float,
+// bit for bit, for every float x.  The double product is within 2^-52
+// (relative) of x / y, while a quotient of two floats is never within 2^-49
+// of a float rounding midpoint: a midpoint m has a 25-bit odd significand, so
+// x - m*y is a non-zero multiple of 2^k with |m*y| < 2^(k+49) (and x / y is
+// never exactly a midpoint); so both round to the same float.  Zeros,
+// infinities, NaN, subnormal quotients and overflow follow from IEEE double
+// arithmetic and the double -> float conversion.  Checked against float
+// division for all 2^32 x and 36 divisors (bias corrections at several
+// steps and betas, 1, values next to 0.5 and 1, a subnormal).  A convert, a
+// double multiply and a convert replace the ~12-cycle division expansion:
+// the ALU-bound scaled-state passes use it (10% faster); the HBM-bound
+// update keeps the float division (the product form measured 1% slower
+// there, both give the same bits).
+__device__ __forceinline__ float quotient_by(float x, double r)
+{
+    return float(double(x) * r);
+}
+
 // One element of the update.  MODE 0: decay joins the gradient (L2);
 // MODE 1: decay joins the update (AdamW) using the param before the step.
-template <int MODE>
+// RECIP: divide by the bias corrections through their double reciprocals
+// (same bits, fewer instructions).
+template <int MODE, bool RECIP = false>
 __device__ __forceinline__ float update_element(float p, float g, float &m, float &v,
                                                 const Coeffs &c)
 {
@@ -196,8 +232,8 @@ __device__ __forceinline__ float update_element(float p, float g, float &m, floa
     if constexpr (MODE == 0) x = x + c.wd * p;
     const float m1 = c.beta1 * m + c.keep1 * x;
     const float v1 = c.beta2 * v + c.keep2 * (x * x);
-    const float m_hat = m1 / c.bc1;
-    const float v_hat = v1 / c.bc2;
+    const float m_hat = RECIP ? quotient_by(m1, c.rbc1) : m1 / c.bc1;
+    const float v_hat = RECIP ? quotient_by(v1, c.rbc2) : v1 / c.bc2;
     float u = m_hat / (sqrtf(v_hat) + c.eps);
     if constexpr (MODE == 1) u = u + c.wd * p;
     m = m1;
@@ -474,6 +510,8 @@ __device__ __forceinline__ Coeffs host_coeffs(const StepArgs &a)
     Coeffs c;
     c.lr = a.lr;
     c.scale = a.d_grad_scale != nullptr ? *a.d_grad_scale : a.grad_scale;
+    c.rbc1 = a.rbc1;
+    c.rbc2 = a.rbc2;
     c.bc1 = a.bc1;
     c.bc2 = a.bc2;
     c.beta1 = a.beta1;
@@ -502,6 +540,8 @@ __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict
         if (s.skip) return;
         c.lr = s.lr;
         c.scale = s.scale;
+        c.rbc1 = s.rbc1;
+        c.rbc2 = s.rbc2;
         c.bc1 = s.bc1;
         c.bc2 = s.bc2;
     }
@@ -536,7 +576,7 @@ __global__ void adam_capture_prologue(StepBlock *block, const float *d_lr, int32
     s.t = t;
     s.lr = *d_lr;
     s.scale = d_grad_scale != nullptr ? *d_grad_scale : 1.0f;
-    corrections(beta1, beta2, t, bias_correction, s.bc1, s.bc2);
+    step_corrections(beta1, beta2, t, bias_correction, s.bc1, s.bc2, s.rbc1, s.rbc2);
     *block = s;
 }
 
@@ -594,7 +634,7 @@ __device__ __forceinline__ void scaled_group(const WorkItem &w, int gi, const Co
         p[k] = widen16<S::st>(hp[k]) * sc[0];
         m[k] = widen16<S::st>(hm[k]) * sc[1];
         v[k] = widen16<S::st>(hv[k]) * sc[2];
-        p[k] = update_element<S::mode>(p[k], g[k], m[k], v[k], c);
+        p[k] = update_element<S::mode, true>(p[k], g[k], m[k], v[k], c);
     }
     if constexpr (S::pass == 0) {
 #pragma unroll
@@ -630,7 +670,7 @@ __device__ __forceinline__ void scaled_single(const WorkItem &w, int i, const Co
     float p = widen16<S::st>(load_one<uint16_t>(w.p, i)) * sc[0];
     float m = widen16<S::st>(load_one<uint16_t>(w.m, i)) * sc[1];
     float v = widen16<S::st>(load_one<uint16_t>(w.v, i)) * sc[2];
-    p = update_element<S::mode>(p, g, m, v, c);
+    p = update_element<S::mode, true>(p, g, m, v, c);
     if constexpr (S::pass == 0) {
         mx[0] = max(mx[0], abs_bits(p));
         mx[1] = max(mx[1], abs_bits(m));
@@ -1223,7 +1263,7 @@ int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
     a.weight_decay = hp->weight_decay;
     a.grad_scale = grad_scale;
     a.d_grad_scale = d_grad_scale;
-    corrections(hp->beta1, hp->beta2, t, hp->bias_correction, a.bc1, a.bc2);
+    step_corrections(hp->beta1, hp->beta2, t, hp->bias_correction, a.bc1, a.bc2, a.rbc1, a.rbc2);
     DeviceGuard guard(tl->stats.device);
     int rc = ADAM_EHIP;
     if (guard.status == hipSuccess)

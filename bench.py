@@ -49,8 +49,17 @@ def log(msg: str) -> None:
 
 
 def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the kernel source's code: comments and
+    whitespace are dropped first, so a change to the comments alone does not
+    invalidate the recorded counter figures."""
+    import re
+
+    with open(KERNEL_SOURCE) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    code = " ".join(text.split())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
