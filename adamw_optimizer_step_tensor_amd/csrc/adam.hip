@@ -64,7 +64,6 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
-#include <string.h>
 
 #include <algorithm>
 #include <new>
@@ -698,7 +697,7 @@ __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__res
     const int tid = threadIdx.x;
     if (start >= w.n) {  // uniform across the workgroup
         if constexpr (S::pass == 0) {
-            if (tid < 3) maxima[3 * b + tid] = 0u;
+            if (tid < 3) maxima[3 * size_t(b) + tid] = 0u;
         }
         return;
     }
@@ -736,7 +735,7 @@ __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__res
         if (tid < 3) {
             uint32_t x = 0u;
             for (int k = 0; k < kBlock / 64; ++k) x = max(x, wave_max[tid][k]);
-            maxima[3 * b + tid] = x;
+            maxima[3 * size_t(b) + tid] = x;
         }
     }
 }
@@ -754,7 +753,7 @@ __global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t
     uint32_t x[3] = {0u, 0u, 0u};
     for (uint32_t t = lo + threadIdx.x; t < hi; t += kFoldMaxBlock)
 #pragma unroll
-        for (int j = 0; j < 3; ++j) x[j] = max(x[j], tile_maxima[3 * t + j]);
+        for (int j = 0; j < 3; ++j) x[j] = max(x[j], tile_maxima[3 * size_t(t) + j]);
     __shared__ uint32_t wave_max[3][kFoldMaxBlock / 64];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
