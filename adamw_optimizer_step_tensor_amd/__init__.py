@@ -7,6 +7,33 @@ carry the same names and turn torch tensors (or raw device addresses) into
 the C structs.  PyTorch provides device memory and streams, nothing else.
 There is no fallback: if the library is missing, importing the binding's
 functions raises.
+
+Typical use (one handle per parameter group, built once; buffers must stay
+allocated and in place)::
+
+    import torch
+    import adamw_optimizer_step_tensor_amd as A
+
+    tensors = [dict(p=p, m=m, v=v, g=g) for p, m, v, g in group]     # fp32 p/m/v, bf16 g
+    tl = A.adam_tl_build(tensors, A.make_desc(g="bf16"))
+    hp = A.AdamHParams(beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, mode=1)
+    step = A.HostStep(0)
+    A.adam_step(tl, hp, 1.6e-3, step)                                  # host lr and counter
+
+    # capturable: every scalar on the device, recordable into a HIP graph
+    d_lr = torch.tensor([1.6e-3], device="cuda")
+    d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_sumsq = torch.zeros(1, dtype=torch.float64, device="cuda")
+    d_scale = torch.ones(1, device="cuda")
+    A.adam_grad_sumsq(tl, d_sumsq)                                     # local grad-norm^2
+    A.adam_clip_grad_scale(d_sumsq, d_scale, max_norm=1.0, d_noop=d_noop)
+    A.adam_step_capturable(tl, hp, d_lr, d_step, d_scale, d_noop)
+
+Remainder storage uses ``make_desc(p="bf16_rem")`` with an int16 ``rem`` per
+tensor and ``adam_step_remainders`` (or ``..._capturable``); scaled 16-bit
+state uses ``make_desc(p="f16_scaled")`` (or ``"bf16_scaled"``) with a
+float32[3] ``scales`` per tensor and ``adam_step_scaled``.
 """
 from __future__ import annotations
 
