@@ -47,10 +47,13 @@
 //    block beside the work table; every tile then reads that one block.
 //  * Scaled 16-bit state needs each buffer's largest magnitude after the
 //    update before any of it can be stored, so it takes two passes over the
-//    same tiles: the first computes the update in registers and writes each
-//    tile's three magnitude maxima; one workgroup per tensor folds its tiles'
-//    maxima; the second pass recomputes the identical update and stores it
-//    with the new scales; a one-lane-per-tensor kernel then writes the
+//    same tiles: the first (one wave per tile) computes the update in
+//    registers and writes each tile's three magnitude maxima, taking the
+//    param through the hardware square root and reciprocal with an error
+//    bound and recomputing exactly only the elements that can hold the
+//    maximum; one workgroup per tensor folds its tiles' maxima and derives
+//    the reciprocal scales; the second pass recomputes the exact update and
+//    stores it with those; a one-lane-per-tensor kernel then writes the
 //    scales.  (Folding with one atomic maximum per workgroup instead was
 //    measured 8x slower: a tensor's ~1000 workgroups contend for one word.)
 //  * Arithmetic follows the header's expressions operation for operation in
@@ -219,25 +222,42 @@ __device__ __forceinline__ float quotient_by(float x, double r)
     return float(double(x) * r);
 }
 
-// One element of the update.  MODE 0: decay joins the gradient (L2);
-// MODE 1: decay joins the update (AdamW) using the param before the step.
-// RECIP: divide by the bias corrections through their double reciprocals
-// (same bits, fewer instructions).
+// One element of the update, in two halves.  MODE 0: decay joins the
+// gradient (L2); MODE 1: decay joins the update (AdamW) using the param
+// before the step.  RECIP: divide by the bias corrections through their
+// double reciprocals (same bits, fewer instructions).
+//
+// moments: the new m and v (in place) and the bias-corrected m_hat, v_hat.
 template <int MODE, bool RECIP = false>
-__device__ __forceinline__ float update_element(float p, float g, float &m, float &v,
-                                                const Coeffs &c)
+__device__ __forceinline__ void moments(float p, float g, float &m, float &v, const Coeffs &c,
+                                        float &m_hat, float &v_hat)
 {
     float x = g * c.scale;
     if constexpr (MODE == 0) x = x + c.wd * p;
     const float m1 = c.beta1 * m + c.keep1 * x;
     const float v1 = c.beta2 * v + c.keep2 * (x * x);
-    const float m_hat = RECIP ? quotient_by(m1, c.rbc1) : m1 / c.bc1;
-    const float v_hat = RECIP ? quotient_by(v1, c.rbc2) : v1 / c.bc2;
-    float u = m_hat / (sqrtf(v_hat) + c.eps);
-    if constexpr (MODE == 1) u = u + c.wd * p;
+    m_hat = RECIP ? quotient_by(m1, c.rbc1) : m1 / c.bc1;
+    v_hat = RECIP ? quotient_by(v1, c.rbc2) : v1 / c.bc2;
     m = m1;
     v = v1;
+}
+
+// param_from: the new param from the param before the step and m_hat, v_hat.
+template <int MODE>
+__device__ __forceinline__ float param_from(float p, float m_hat, float v_hat, const Coeffs &c)
+{
+    float u = m_hat / (sqrtf(v_hat) + c.eps);
+    if constexpr (MODE == 1) u = u + c.wd * p;
     return p - c.lr * u;
+}
+
+template <int MODE, bool RECIP = false>
+__device__ __forceinline__ float update_element(float p, float g, float &m, float &v,
+                                                const Coeffs &c)
+{
+    float m_hat, v_hat;
+    moments<MODE, RECIP>(p, g, m, v, c, m_hat, v_hat);
+    return param_from<MODE>(p, m_hat, v_hat, c);
 }
 
 // bf16 bits (round to nearest, ties to even) of a float: adding 0x7FFF plus
@@ -617,10 +637,11 @@ __device__ __forceinline__ float rscale_of(uint32_t amax)
     return scale > 0.0f ? 1.0f / scale : 0.0f;
 }
 
-// One lane group: unscale, update; then fold maxima (pass 0) or store (pass 1).
+// One lane group of the store pass: unscale, update, store with the new
+// reciprocal scales r.
 template <class S>
 __device__ __forceinline__ void scaled_group(const WorkItem &w, int gi, const Coeffs &c,
-                                             const float *sc, const float *r, uint32_t *mx)
+                                             const float *sc, const float *r)
 {
     uint32_t hp[kLane], hm[kLane], hv[kLane];
     float p[kLane], m[kLane], v[kLane], g[kLane];
@@ -635,32 +656,25 @@ __device__ __forceinline__ void scaled_group(const WorkItem &w, int gi, const Co
         v[k] = widen16<S::st>(hv[k]) * sc[2];
         p[k] = update_element<S::mode, true>(p[k], g[k], m[k], v[k], c);
     }
-    if constexpr (S::pass == 0) {
+    if constexpr (S::ot != kNone) {
+        uint32_t o[kLane];
 #pragma unroll
-        for (int k = 0; k < kLane; ++k) {
-            mx[0] = max(mx[0], abs_bits(p[k]));
-            mx[1] = max(mx[1], abs_bits(m[k]));
-            mx[2] = max(mx[2], abs_bits(v[k]));
-        }
-    } else {
-        if constexpr (S::ot != kNone) {
-            uint32_t o[kLane];
-#pragma unroll
-            for (int k = 0; k < kLane; ++k) o[k] = narrow16<S::ot>(p[k]);
-            store_u16x4(w.p_out, gi, o);
-        }
-#pragma unroll
-        for (int k = 0; k < kLane; ++k) {
-            hp[k] = narrow16<S::st>(p[k] * r[0]);
-            hm[k] = narrow16<S::st>(m[k] * r[1]);
-            hv[k] = narrow16<S::st>(v[k] * r[2]);
-        }
-        store_u16x4(w.p, gi, hp);
-        store_u16x4(w.m, gi, hm);
-        store_u16x4(w.v, gi, hv);
+        for (int k = 0; k < kLane; ++k) o[k] = narrow16<S::ot>(p[k]);
+        store_u16x4(w.p_out, gi, o);
     }
+#pragma unroll
+    for (int k = 0; k < kLane; ++k) {
+        hp[k] = narrow16<S::st>(p[k] * r[0]);
+        hm[k] = narrow16<S::st>(m[k] * r[1]);
+        hv[k] = narrow16<S::st>(v[k] * r[2]);
+    }
+    store_u16x4(w.p, gi, hp);
+    store_u16x4(w.m, gi, hm);
+    store_u16x4(w.v, gi, hv);
 }
 
+// One element, exact: fold its magnitudes into mx (maxima pass) or store it
+// (store pass).
 template <class S>
 __device__ __forceinline__ void scaled_single(const WorkItem &w, int i, const Coeffs &c,
                                               const float *sc, const float *r, uint32_t *mx)
@@ -682,68 +696,183 @@ __device__ __forceinline__ void scaled_single(const WorkItem &w, int i, const Co
     }
 }
 
-// One pass over the tiles of a scaled-state list (same tile map as the
-// update).  Pass 0 writes the three magnitude maxima (p, m, v) of tile t to
-// maxima[3t .. 3t+2] (zeros for a tile past its record's end); pass 1 reads
-// the folded maxima of its tensor from maxima[3k ..] of `folded`.
+// Largest of x over the 64 lanes of the wave, returned to every lane; every
+// lane must be active.  Data-parallel-primitive moves: shifts right by 1, 2,
+// 4 and 8 lanes within each row of 16 leave the row's maximum in its lane 15;
+// broadcasting lane 15 into the next row (rows 1 and 3) and lane 31 into
+// rows 2 and 3 leaves the wave's maximum in lane 63, the lane read at the
+// end.  A lane with no source reads 0, the identity of unsigned max; lanes
+// of the rows a broadcast skips hold values that lane 63 never reads.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t x)
+{
+    return max(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), CTRL, ROWS, 0xf, true)));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t x)
+{
+    x = dpp_max<0x111, 0xf>(x);  // row_shr:1
+    x = dpp_max<0x112, 0xf>(x);  // row_shr:2
+    x = dpp_max<0x114, 0xf>(x);  // row_shr:4
+    x = dpp_max<0x118, 0xf>(x);  // row_shr:8
+    x = dpp_max<0x142, 0xa>(x);  // row_bcast:15
+    x = dpp_max<0x143, 0xc>(x);  // row_bcast:31
+    return uint32_t(__builtin_amdgcn_readlane(int(x), 63));
+}
+
+// The maxima pass over a tile's lane groups: lane l takes groups gi0 + l +
+// 64 j (j < G) that are below `groups`; every lane of the wave calls it.
+// m, v and their maxima are exact.  The param is first computed with the
+// hardware square root and reciprocal, which are within 0.78 ulp of the exact
+// values for every normal input (checked over all floats; subnormal inputs
+// flush).  With rho = 2^-24, mu = 2^-150 and 2^-22 taken as their relative
+// error, the exact chain
+//   q = RN(m_hat / RN(RN(sqrt v_hat) + eps)),  u = q (+ RN(wd p)),
+//   t = RN(lr u),  p' = RN(p - t)
+// and the approximate one (q~ = RN(m_hat * rcp(RN(sqrt~ v_hat + eps))), then
+// the same roundings) differ by
+//   |q~ - q|   <= 0.84 * 2^-20 |q~| + 3 mu   (eps >= 0 keeps the root's
+//                                             relative error in the sum)
+//   |p~ - p'|  <= 1.01 (|lr| |q~ - q| + 4.2 rho |t~|) + 2.01 rho |p~|
+//                 + 10 mu (|lr| + 1)
+// so E = 2^-19 |lr| max|q~| + 2^-21 max|t~| + 2^-22 max|p~| + 2^-140 (|lr|+1),
+// over the wave, bounds every element's error with a factor 2 to spare (which
+// also covers rounding in E and in the cut).  The element with the largest
+// exact magnitude has |p~| >= max|p~| - 2E, and any element below
+// max|p~| - 2.5 E has an exact magnitude below that one's; so the exact
+// maximum is the maximum over the elements at or above the cut, each
+// recomputed exactly.  The bound assumes finite values clear of overflow and
+// a normal (or zero) v_hat: a wave with a subnormal v_hat, or |q~|, |u~|, |t~|
+// or |p~| not below 2^126 (NaN included), recomputes all its elements, as
+// does every wave when `approx` is off (eps < 0 or >= 2^125, |lr| >= 2^126).
+template <class S, int G>
+__device__ __forceinline__ void scaled_group_max(const WorkItem &w, int gi0, int groups, const Coeffs &c,
+                                                 const float *sc, bool approx, uint32_t *mx)
+{
+    const int lane = threadIdx.x % 64;
+    float p[G][kLane], m_hat[G][kLane], v_hat[G][kLane], pa[G][kLane];
+    uint32_t pbits = 0u;
+    float qmax = 0.0f, umax = 0.0f, tmax = 0.0f;
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        if (lane + 64 * j >= groups) continue;
+        const int gi = gi0 + lane + 64 * j;
+        uint32_t hp[kLane], hm[kLane], hv[kLane];
+        float g[kLane];
+        load_u16x4(w.p, gi, hp);
+        load_u16x4(w.m, gi, hm);
+        load_u16x4(w.v, gi, hv);
+        load_grad4<S::gt>(w.g, gi, g);
+#pragma unroll
+        for (int k = 0; k < kLane; ++k) {
+            p[j][k] = widen16<S::st>(hp[k]) * sc[0];
+            float m = widen16<S::st>(hm[k]) * sc[1];
+            float v = widen16<S::st>(hv[k]) * sc[2];
+            moments<S::mode, true>(p[j][k], g[k], m, v, c, m_hat[j][k], v_hat[j][k]);
+            mx[1] = max(mx[1], abs_bits(m));
+            mx[2] = max(mx[2], abs_bits(v));
+            ok = ok && !__builtin_isfpclass(v_hat[j][k], __FPCLASS_POSSUBNORMAL);
+            const float q = m_hat[j][k] * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(v_hat[j][k]) + c.eps);
+            float u = q;
+            if constexpr (S::mode == 1) u = q + c.wd * p[j][k];
+            const float t = c.lr * u;
+            pa[j][k] = p[j][k] - t;
+            qmax = fmaxf(qmax, fabsf(q));
+            umax = fmaxf(umax, fabsf(u));
+            tmax = fmaxf(tmax, fabsf(t));
+            pbits = max(pbits, abs_bits(pa[j][k]));
+        }
+    }
+    ok = ok && pbits < 0x7E800000u && qmax < 0x1p126f && umax < 0x1p126f && tmax < 0x1p126f;
+    const float alr = fabsf(c.lr);
+    const float e = 0x1p-19f * alr * qmax + 0x1p-21f * tmax + 0x1p-22f * __uint_as_float(pbits) +
+                    0x1p-140f * (alr + 1.0f);
+    const float top = __uint_as_float(wave_max(pbits));
+    const float we = __uint_as_float(wave_max(__float_as_uint(e)));
+    const bool all = !(approx && __all(ok) && we < 0x1p126f);
+    const float cut = top - 2.5f * we;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        if (lane + 64 * j >= groups) continue;
+#pragma unroll
+        for (int k = 0; k < kLane; ++k)
+            if (all || fabsf(pa[j][k]) >= cut)
+                mx[0] = max(mx[0], abs_bits(param_from<S::mode>(p[j][k], m_hat[j][k], v_hat[j][k], c)));
+    }
+}
+
+// The maxima pass: one wave per tile (same tile map as the update), two lane
+// groups per lane.  Writes the three magnitude maxima (p, m, v) of tile t to
+// maxima[3t .. 3t+2], zeros for a tile past its record's end.
+constexpr int kMaxBlock = 64;
+
+template <class S>
+__global__ __launch_bounds__(kMaxBlock) void adam_scaled_maxima(const WorkItem *__restrict__ items,
+                                                                 uint32_t shift, StepArgs a,
+                                                                 uint32_t *__restrict__ maxima)
+{
+    static_assert(kTile == 2 * kLane * kMaxBlock, "two lane groups per lane");
+    const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
+    const WorkItem w = items[b >> shift];
+    const int start = int(b & ((1u << shift) - 1u)) * kTile;
+    const int tid = threadIdx.x;
+    uint32_t mx[3] = {0u, 0u, 0u};
+    if (start < w.n) {  // uniform across the wave
+        const Coeffs c = host_coeffs(a);
+        const float *scales = static_cast<const float *>(w.aux);
+        const float sc[3] = {scales[0], scales[1], scales[2]};
+        const int n = min(kTile, w.n - start);
+        if (w.flags & kItemVector) {
+            if (start == 0 && tid < w.head) scaled_single<S>(w, tid - w.head, c, sc, nullptr, mx);
+            const int groups = n / kLane;
+            const bool approx = c.eps >= 0.0f && c.eps < 0x1p125f && fabsf(c.lr) < 0x1p126f;
+            scaled_group_max<S, 2>(w, start / kLane, groups, c, sc, approx, mx);
+            if (tid < n - groups * kLane) scaled_single<S>(w, start + groups * kLane + tid, c, sc, nullptr, mx);
+        } else {
+            for (int i = tid; i < n; i += kMaxBlock) scaled_single<S>(w, start + i, c, sc, nullptr, mx);
+        }
+    }
+    const uint32_t x0 = wave_max(mx[0]), x1 = wave_max(mx[1]), x2 = wave_max(mx[2]);
+    if (tid < 3) maxima[3 * size_t(b) + tid] = tid == 0 ? x0 : tid == 1 ? x1 : x2;
+}
+
+// The store pass over the tiles of a scaled-state list (same tile map as the
+// update): reads the reciprocal scales of its tensor from folded[6k + 3 ..].
 template <class S>
 __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__restrict__ items,
                                                             uint32_t shift, StepArgs a,
-                                                            uint32_t *__restrict__ maxima)
+                                                            uint32_t *__restrict__ folded)
 {
     const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
     const WorkItem w = items[b >> shift];
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
     const int tid = threadIdx.x;
-    if (start >= w.n) {  // uniform across the workgroup
-        if constexpr (S::pass == 0) {
-            if (tid < 3) maxima[3 * size_t(b) + tid] = 0u;
-        }
-        return;
-    }
+    if (start >= w.n) return;  // uniform across the workgroup
 
     const Coeffs c = host_coeffs(a);
     const float *scales = static_cast<const float *>(w.aux);
     const float sc[3] = {scales[0], scales[1], scales[2]};
-    float r[3] = {0.0f, 0.0f, 0.0f};
-    if constexpr (S::pass == 1) {
-#pragma unroll
-        for (int j = 0; j < 3; ++j) r[j] = rscale_of<S::st>(maxima[3 * w.tensor + j]);
-    }
-    uint32_t mx[3] = {0u, 0u, 0u};
+    const uint32_t *f = folded + 6 * size_t(w.tensor) + 3;
+    const float r[3] = {__uint_as_float(f[0]), __uint_as_float(f[1]), __uint_as_float(f[2])};
 
     const int n = min(kTile, w.n - start);
     if (w.flags & kItemVector) {
-        if (start == 0 && tid < w.head) scaled_single<S>(w, tid - w.head, c, sc, r, mx);
+        if (start == 0 && tid < w.head) scaled_single<S>(w, tid - w.head, c, sc, r, nullptr);
         const int groups = n / kLane;
-        if (tid < groups) scaled_group<S>(w, start / kLane + tid, c, sc, r, mx);
-        if (tid < n - groups * kLane) scaled_single<S>(w, start + groups * kLane + tid, c, sc, r, mx);
+        if (tid < groups) scaled_group<S>(w, start / kLane + tid, c, sc, r);
+        if (tid < n - groups * kLane) scaled_single<S>(w, start + groups * kLane + tid, c, sc, r, nullptr);
     } else {
-        for (int i = tid; i < n; i += kBlock) scaled_single<S>(w, start + i, c, sc, r, mx);
-    }
-
-    if constexpr (S::pass == 0) {
-        // the workgroup's maxima, one word per buffer
-        __shared__ uint32_t wave_max[3][kBlock / 64];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            uint32_t x = mx[j];
-            for (int off = 32; off > 0; off >>= 1) x = max(x, uint32_t(__shfl_xor(int(x), off, 64)));
-            if (tid % 64 == 0) wave_max[j][tid / 64] = x;
-        }
-        __syncthreads();
-        if (tid < 3) {
-            uint32_t x = 0u;
-            for (int k = 0; k < kBlock / 64; ++k) x = max(x, wave_max[tid][k]);
-            maxima[3 * size_t(b) + tid] = x;
-        }
+        for (int i = tid; i < n; i += kBlock) scaled_single<S>(w, start + i, c, sc, r, nullptr);
     }
 }
 
 constexpr int kFoldMaxBlock = 256;
 
 // One workgroup per tensor: the maxima of its tiles [tiles[2k], tiles[2k+1])
-// folded into folded[3k .. 3k+2].
+// folded into folded[6k .. 6k+2], and the reciprocal scales the store pass
+// applies into folded[6k+3 .. 6k+5] (float bits).
+template <int ST>
 __global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t *__restrict__ tile_maxima,
                                                                   const uint32_t *__restrict__ tiles,
                                                                   uint32_t *__restrict__ folded)
@@ -754,17 +883,18 @@ __global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t
     for (uint32_t t = lo + threadIdx.x; t < hi; t += kFoldMaxBlock)
 #pragma unroll
         for (int j = 0; j < 3; ++j) x[j] = max(x[j], tile_maxima[3 * size_t(t) + j]);
-    __shared__ uint32_t wave_max[3][kFoldMaxBlock / 64];
+    __shared__ uint32_t wave_maxima[3][kFoldMaxBlock / 64];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-        for (int off = 32; off > 0; off >>= 1) x[j] = max(x[j], uint32_t(__shfl_xor(int(x[j]), off, 64)));
-        if (threadIdx.x % 64 == 0) wave_max[j][threadIdx.x / 64] = x[j];
+        const uint32_t m = wave_max(x[j]);
+        if (threadIdx.x % 64 == 0) wave_maxima[j][threadIdx.x / 64] = m;
     }
     __syncthreads();
     if (threadIdx.x < 3) {
         uint32_t m = 0u;
-        for (int i = 0; i < kFoldMaxBlock / 64; ++i) m = max(m, wave_max[threadIdx.x][i]);
-        folded[3 * k + threadIdx.x] = m;
+        for (int i = 0; i < kFoldMaxBlock / 64; ++i) m = max(m, wave_maxima[threadIdx.x][i]);
+        folded[6 * size_t(k) + threadIdx.x] = m;
+        folded[6 * size_t(k) + 3 + threadIdx.x] = __float_as_uint(rscale_of<ST>(m));
     }
 }
 
@@ -777,7 +907,7 @@ __global__ void adam_scaled_finish(float *const *__restrict__ scale_ptrs,
     if (k >= tensors) return;
     float *s = scale_ptrs[k];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(folded[3 * k + j]) / scaled_limit<ST>();
+    for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(folded[6 * size_t(k) + j]) / scaled_limit<ST>();
 }
 
 // ---------------------------------------------------------------------------
@@ -953,7 +1083,10 @@ constexpr ScaledFn scaled_at()
     constexpr int st = kStateTypes[(I / 9) % 2];
     constexpr int mode = (I / 18) % 2;
     constexpr int pass = I / 36;
-    return adam_scaled_pass<ScaledConfig<st, g, ot, mode, pass>>;
+    if constexpr (pass == 0)
+        return adam_scaled_maxima<ScaledConfig<st, g, ot, mode, 0>>;
+    else
+        return adam_scaled_pass<ScaledConfig<st, g, ot, mode, 1>>;
 }
 
 template <int... I>
@@ -1206,7 +1339,7 @@ struct adam_tl {
     float **d_scale_ptrs;  // scaled state: each non-empty tensor's scales (after the partials)
     uint32_t *d_tiles;     // scaled state: [first, end) tile range per non-empty tensor
     uint32_t *d_tile_max;  // scaled state: three magnitude maxima per tile
-    uint32_t *d_folded;    // scaled state: three magnitude maxima per non-empty tensor
+    uint32_t *d_folded;    // scaled state: three magnitude maxima, then three reciprocal scales, per non-empty tensor
     uint32_t n_tensors;    // non-empty tensors
 };
 
@@ -1229,10 +1362,11 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
     const int base = type_pos(kGradTypes, 3, tl->g) +
                      3 * (type_pos(kOutTypes, 3, tl->out) + 3 * (type_pos(kStateTypes, 2, tl->p) + 2 * mode));
     const dim3 grid(uint32_t(tl->stats.grid_blocks));
-    hipLaunchKernelGGL(ScaledKernels::fns[base], grid, dim3(kBlock), 0, stream, tl->d_items, tl->shift,
+    hipLaunchKernelGGL(ScaledKernels::fns[base], grid, dim3(kMaxBlock), 0, stream, tl->d_items, tl->shift,
                        args, tl->d_tile_max);
     if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
-    hipLaunchKernelGGL(adam_scaled_fold, dim3(tl->n_tensors), dim3(kFoldMaxBlock), 0, stream,
+    auto fold = tl->p == kBF16 ? adam_scaled_fold<kBF16> : adam_scaled_fold<kF16>;
+    hipLaunchKernelGGL(fold, dim3(tl->n_tensors), dim3(kFoldMaxBlock), 0, stream,
                        tl->d_tile_max, tl->d_tiles, tl->d_folded);
     if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     hipLaunchKernelGGL(ScaledKernels::fns[base + 36], grid, dim3(kBlock), 0, stream, tl->d_items, tl->shift,
@@ -1385,7 +1519,7 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     const size_t tile_max_off = tiles_off + plan.tile_ranges.size() * sizeof(uint32_t);
     const size_t folded_off =
         tile_max_off + (scaled ? 3 * sizeof(uint32_t) * size_t(tl->stats.grid_blocks) : 0);
-    const size_t total = folded_off + (scaled ? 3 * sizeof(uint32_t) * tl->n_tensors : 0);
+    const size_t total = folded_off + (scaled ? 6 * sizeof(uint32_t) * tl->n_tensors : 0);
     void *mem = nullptr;
     if (hipMalloc(&mem, total) != hipSuccess) {
         (void)hipGetLastError();

@@ -256,9 +256,10 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
  * gets a subnormal scale whose reciprocal overflows, so its values store as
  * +-inf (0 becomes NaN) -- the pages' formula does this; fp16 state does not.
  * Empty tensors keep their scales.  The call enqueues four kernels (a pass
- * that computes the update and each tile's maxima, a fold of those maxima
- * per tensor, a pass that recomputes the update and stores it, a per-tensor
- * kernel that writes the new scales); steps of one handle must be ordered.
+ * that computes each tile's maxima of the updated buffers, a fold of those
+ * maxima per tensor, a pass that recomputes the update and stores it, a
+ * per-tensor kernel that writes the new scales); steps of one handle must be
+ * ordered.
  * Arguments and errors as adam_step; ADAM_EINVAL for a handle without
  * scaled state. */
 int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,

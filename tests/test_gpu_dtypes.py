@@ -290,3 +290,94 @@ def test_scaled_state_sumsq_and_clip_apply(torch, orc):
     want = orc.grad_sumsq([h.g for h in host])
     assert abs(float(d.item()) - want) <= 1e-12 * want
     tl.destroy()
+
+
+# ---------------------------------------------------------------------------
+# The maxima pass: approximate params with an error bound, exact recompute of
+# the elements that can hold the maximum, and the cases that take the exact
+# path for a whole wave or call
+# ---------------------------------------------------------------------------
+
+def _f16_scaled(sizes, seed, **kw):
+    kw.setdefault("g_dtype", "bf16")
+    kw.setdefault("m_v_init", "random")
+    return host_tensors(sizes, p_kind="f16_scaled", p_out="f16", seed=seed, **kw)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_scaled_maxima_with_ties(torch, orc, mode):
+    """Many elements at or next to the largest magnitude: a tensor with every
+    element equal, one with equal params and gradients one ulp apart, and one
+    whose params take three values.  Each of those elements must be
+    recomputed exactly; the scales and stored values match the oracle."""
+    rng = np.random.default_rng(84)
+    host = _f16_scaled([70001, 4096, 3000], 81, g_dtype="f32")
+    t = host[0]
+    for a in (t.p, t.m, t.v, t.g):
+        a[:] = a[17]
+    t = host[1]
+    t.p[:] = t.p[5]
+    t.m[:] = t.m[5]
+    t.v[:] = t.v[5]
+    base = np.float32(2.5e-3)
+    t.g[:] = np.where(rng.random(t.g.size) < 0.5, base, np.nextafter(base, np.float32(1.0)))
+    t = host[2]
+    t.p[:] = rng.choice(t.p[:3], size=t.p.size)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 3)
+    assert_bitwise(got, ref, ctx=f"mode {mode}")
+
+
+@pytest.mark.parametrize("eps,lr,label", [
+    (0.0, 1.6e-3, "eps zero (zero moments give 0/0)"),
+    (-1e-8, 1.6e-3, "negative eps (no approximation in the call)"),
+    (1e30, 1.6e-3, "large eps"),
+    (1e38, 1.6e-3, "eps beyond 2^125 (no approximation in the call)"),
+    (1e-8, 1e30, "lr large enough to overflow the update"),
+    (1e-8, 0.0, "lr zero"),
+    (1e-8, -1e-3, "negative lr"),
+])
+def test_scaled_maxima_hyperparameter_edges(torch, orc, eps, lr, label):
+    """Hyperparameters at the edges of the bound's assumptions (and past
+    them), with some elements of zero moments and zero gradient."""
+    host = _f16_scaled([70001, 513, 4096], 82)
+    for t in host[1:]:
+        t.m[:40] = 0
+        t.v[:40] = 0
+        t.g[:40] = 0
+    hl, hr = hp_pair(0.9, 0.95, eps, 0.1, 1)
+    got, ref = run_steps(orc, host, hl, hr, lr, 2)
+    assert_bitwise(got, ref, ctx=label)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_scaled_maxima_subnormal_second_moment(torch, orc, mode):
+    """Gradients of ~1e-21 make v_hat subnormal, where the hardware square
+    root flushes to zero: the waves holding such elements are recomputed
+    exactly (the first tensor throughout, the second at every 97th element)."""
+    host = _f16_scaled([70001, 4096], 83, g_dtype="f32", m_v_init="zero", g_std=1e-21)
+    t = host[1]
+    t.g[:] = np.random.default_rng(85).standard_normal(t.g.size).astype(np.float32) * np.float32(1e-3)
+    t.g[::97] = np.float32(3e-21)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
+    assert_bitwise(got, ref, ctx=f"mode {mode}")
+
+
+@pytest.mark.parametrize("p_kind", ["f16_scaled", "bf16_scaled"])
+def test_scaled_maxima_wide_magnitudes(torch, orc, p_kind):
+    """Stored params drawn over every finite 16-bit pattern (fp16 subnormals to
+    65504; bf16 over all its binades) with large moments: the maxima are
+    decided among values of very different sizes, some overflowing."""
+    rng = np.random.default_rng(86)
+    host = host_tensors([70001, 4096, 1000], p_kind=p_kind, p_out="f16", seed=87, g_dtype="f32",
+                        m_v_init="large", g_std=1.0)
+    for t in host:
+        finite = 0x7C00 if p_kind == "f16_scaled" else 0x7F80
+        bits = rng.integers(0, finite, size=t.p.size).astype(np.uint16) | \
+            (rng.integers(0, 2, size=t.p.size).astype(np.uint16) << 15)
+        t.p[:] = bits.view(t.p.dtype)
+    for mode in (0, 1):
+        hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+        got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
+        assert_bitwise(got, ref, ctx=f"{p_kind} mode {mode}")
