@@ -90,6 +90,10 @@ PROFILE_COMMANDS = {
     "valu_summary": "python bench.py --summarize-valu --workload {w} --valu-dir gpurun_out/pmc_valu_{w}",
 }
 
+# the kernels that stream the elements: the update, and the scaled-state
+# maxima and store passes
+MAIN_KERNELS = ("adam_update", "adam_scaled_maxima", "adam_scaled_pass")
+
 CU_NUM = 256
 XCD_NUM = 8
 
@@ -113,11 +117,11 @@ def summarize_valu(w, valu_dir: str) -> None:
         name = _short(r["Kernel_Name"])
         key = (name, r["Dispatch_Id"])
         vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
-        grids[key] = int(r["Grid_Size"])
-    big = max(g for (n, _), g in grids.items() if n.startswith(("adam_update", "adam_scaled_pass")))
+        grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+    big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
     per = {}
     for key, c in vals.items():
-        if grids[key] == big and key[0].startswith(("adam_update", "adam_scaled_pass")):
+        if grids[key] == big and key[0].startswith(MAIN_KERNELS):
             per.setdefault(key[0], []).append(c)
     lines = [f"rocprofv3 VALU counters: workload {w.name}, main group ({n0:,} elements)",
              f"command: {cmds['valu']}", f"summary: {cmds['valu_summary']}", "",
@@ -145,7 +149,8 @@ def _short(name: str) -> str:
     import re
 
     n = name.replace("(anonymous namespace)::", "")
-    for kernel, cfg_name in (("adam_update", "Config<"), ("adam_scaled_pass", "ScaledConfig<")):
+    for kernel, cfg_name in (("adam_update", "Config<"), ("adam_scaled_maxima", "ScaledConfig<"),
+                             ("adam_scaled_pass", "ScaledConfig<")):
         if kernel in n and cfg_name in n:
             i = n.index(cfg_name) + len(cfg_name)
             return f"{kernel}<{n[i:n.index('>', i)]}>"
@@ -177,7 +182,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
     prefix = "adam_scaled" if scaled else "adam_update"
 
     def main_kernel(name):
-        return name.startswith("adam_update") or name.startswith("adam_scaled_pass")
+        return name.startswith(MAIN_KERNELS)
 
     # kernel trace: all kernels (stats), then the update kernel per dispatch
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
@@ -194,11 +199,11 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
         name = _short(r["Kernel_Name"])
         if main_kernel(name):
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
-            per.setdefault((name, int(r["Grid_Size_X"])), []).append(dur)
+            per.setdefault((name, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])), []).append(dur)
     big = max(g for _, g in per)
     lines += ["", ("scaled-state passes" if scaled else "update kernel") +
               " per dispatch (main group = the largest grid):",
-              f"{'kernel':46s} {'grid threads':>13s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} "
+              f"{'kernel':46s} {'workgroups':>13s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} "
               f"{'max ms':>9s} {'GB/s(avg)':>10s}"]
     for (name, grid), durs in sorted(per.items()):
         avg = statistics.mean(durs)
@@ -206,7 +211,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
         lines.append(f"{name:46s} {grid:13d} {len(durs):5d} {avg:9.3f} {min(durs):9.3f} "
                      f"{max(durs):9.3f} {gbps}")
     if scaled:
-        # both passes of the main group make one step (the clear and scales
+        # both passes of the main group make one step (the fold and scales
         # kernels are a few microseconds)
         passes = [statistics.mean(d) for (name, grid), d in per.items() if grid == big]
         lines.append(f"both passes of one step: {sum(passes):.3f} ms; algorithmic bytes per step "
@@ -220,7 +225,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
         agg = {}
         for r in csv.DictReader(open(os.path.join(path, "run_counter_collection.csv"))):
             name = _short(r["Kernel_Name"])
-            if main_kernel(name) and int(r["Grid_Size"]) != big:
+            if main_kernel(name) and int(r["Grid_Size"]) // int(r["Workgroup_Size"]) != big:
                 name += " (small group)"
             agg.setdefault(name, []).append(float(r["Counter_Value"]))
         return agg
@@ -512,7 +517,7 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"adam_scaled_pass x2 + clear + scales (the whole scaled step of the main group; "
+            "kernel": (f"adam_scaled_maxima + fold + adam_scaled_pass + scales (the whole scaled step of the main group; "
                        f"p {w.p_kind}, g {w.g_dtype}, p_out {p_out or 'none'})" if scaled else
                        f"adam_update (p {w.p_kind}, g {w.g_dtype}, m/v f32, p_out "
                        f"{p_out or 'none'}, {'AdamW' if w.mode else 'L2'}, non-capturable)"),
