@@ -88,6 +88,10 @@ PROFILE_COMMANDS = {
             "--output-format csv -d <repo>/gpurun_out/pmc_valu_{w} -o run -- python3 <repo>/bench.py "
             "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
     "valu_summary": "python bench.py --summarize-valu --workload {w} --valu-dir gpurun_out/pmc_valu_{w}",
+    "occupancy": "cd /tmp && rocprofv3 --pmc MeanOccupancyPerCU OccupancyPercent --output-format csv "
+                 "-d <repo>/gpurun_out/pmc_occ_{w} -o run -- python3 <repo>/bench.py --workload {w} "
+                 "--steps 3 --warmup 1 --no-cpu --no-capturable",
+    "occupancy_summary": "python bench.py --summarize-occupancy --workload {w} --occupancy-dir gpurun_out/pmc_occ_{w}",
 }
 
 # the kernels that stream the elements: the update, and the scaled-state
@@ -138,6 +142,45 @@ def summarize_valu(w, valu_dir: str) -> None:
               "(its quad-cycle normalisation), so compare kernels with each other: the same",
               "expression for a memory-bound kernel and an ALU-bound one differs by ~3x."]
     path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_valu.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_occupancy(w, occ_dir: str) -> None:
+    """Writes profiles/<kernel>_<workload>_occupancy.txt: the mean resident
+    waves per CU of the main group's kernels and that as a percentage of the
+    32-wave maximum, from rocprofv3's derived metrics MeanOccupancyPerCU
+    (accumulated SQ_LEVEL_WAVES / GRBM_GUI_ACTIVE / CUs) and OccupancyPercent
+    (SQ_WAVE_CYCLES based), one --pmc pass."""
+    import csv
+
+    cmds = {k: v.format(w=w.name) for k, v in PROFILE_COMMANDS.items()}
+    n0 = sum(w.sizes)
+    prefix = "adam_scaled" if w.p_kind.endswith("_scaled") else "adam_update"
+    vals, grids, regs = {}, {}, {}
+    for r in csv.DictReader(open(os.path.join(occ_dir, "run_counter_collection.csv"))):
+        name = _short(r["Kernel_Name"])
+        key = (name, r["Dispatch_Id"])
+        vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+        regs[name] = (int(r["Workgroup_Size"]), int(r["VGPR_Count"]), int(r["SGPR_Count"]), int(r["LDS_Block_Size"]))
+    big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
+    per = {}
+    for key, c in vals.items():
+        if grids[key] == big and key[0].startswith(MAIN_KERNELS):
+            per.setdefault(key[0], []).append(c)
+    lines = [f"rocprofv3 occupancy: workload {w.name}, main group ({n0:,} elements, {big:,} workgroups)",
+             f"command: {cmds['occupancy']}", f"summary: {cmds['occupancy_summary']}", "",
+             f"{'kernel':40s} {'n':>3s} {'waves/CU':>9s} {'% of 32':>8s} {'wg size':>8s} {'VGPRs':>6s} {'SGPRs':>6s} {'LDS':>6s}"]
+    for name, cs in sorted(per.items()):
+        occ = statistics.mean(c["MeanOccupancyPerCU"] for c in cs)
+        pct = statistics.mean(c["OccupancyPercent"] for c in cs)
+        wg, vg, sg, lds = regs[name]
+        lines.append(f"{name:40s} {len(cs):3d} {occ:9.2f} {pct:8.1f} {wg:8d} {vg:6d} {sg:6d} {lds:6d}")
+    lines += ["", "waves/CU: mean resident waves per compute unit over the kernel (4 SIMDs, at most",
+              "8 waves each); VGPRs as rocprofv3 reports them for the code object."]
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_occupancy.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -367,6 +410,9 @@ def main() -> int:
     ap.add_argument("--summarize-valu", action="store_true",
                     help="write profiles/ VALU summary from a rocprofv3 counter directory (no GPU)")
     ap.add_argument("--valu-dir")
+    ap.add_argument("--summarize-occupancy", action="store_true",
+                    help="write profiles/ occupancy summary from a rocprofv3 counter directory (no GPU)")
+    ap.add_argument("--occupancy-dir")
     args = ap.parse_args()
 
     if args.summarize_profiles:
@@ -378,6 +424,11 @@ def main() -> int:
         from workloads import workloads
 
         summarize_valu(workloads()[args.workload], args.valu_dir)
+        return 0
+    if args.summarize_occupancy:
+        from workloads import workloads
+
+        summarize_occupancy(workloads()[args.workload], args.occupancy_dir)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
