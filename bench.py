@@ -92,6 +92,15 @@ PROFILE_COMMANDS = {
                  "-d <repo>/gpurun_out/pmc_occ_{w} -o run -- python3 <repo>/bench.py --workload {w} "
                  "--steps 3 --warmup 1 --no-cpu --no-capturable",
     "occupancy_summary": "python bench.py --summarize-occupancy --workload {w} --occupancy-dir gpurun_out/pmc_occ_{w}",
+    "dram_req": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_WRREQ_sum "
+                "TCC_EA0_WRREQ_64B_sum --output-format csv -d <repo>/gpurun_out/pmc_dreq_{w} -o run -- "
+                "python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+    "dram_stall": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_WRREQ_LEVEL_sum "
+                  "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum GRBM_GUI_ACTIVE "
+                  "--output-format csv -d <repo>/gpurun_out/pmc_dstall_{w} -o run -- python3 <repo>/bench.py "
+                  "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+    "dram_summary": "python bench.py --summarize-dram --workload {w} --dram-req-dir gpurun_out/pmc_dreq_{w} "
+                    "--dram-stall-dir gpurun_out/pmc_dstall_{w}",
 }
 
 # the kernels that stream the elements: the update, and the scaled-state
@@ -181,6 +190,69 @@ def summarize_occupancy(w, occ_dir: str) -> None:
     lines += ["", "waves/CU: mean resident waves per compute unit over the kernel (4 SIMDs, at most",
               "8 waves each); VGPRs as rocprofv3 reports them for the code object."]
     path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_occupancy.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+TCC_CHANNELS = 128  # L2 channels over the 8 XCDs
+
+
+def summarize_dram(w, req_dir: str, stall_dir: str) -> None:
+    """Writes profiles/<kernel>_<workload>_dram.txt: the main kernel's memory
+    requests as the L2 sends them to the fabric, from two rocprofv3 --pmc
+    passes: request counts by size (TCC_EA0_RDREQ / _128B, TCC_EA0_WRREQ /
+    _64B, summed over the L2 channels), and occupancy of the request queues
+    (TCC_EA0_RDREQ_LEVEL / WRREQ_LEVEL: outstanding requests summed per
+    cycle) with the cycles a request waited for a DRAM credit
+    (TCC_EA0_*_DRAM_CREDIT_STALL), against GRBM_GUI_ACTIVE."""
+    import csv
+
+    cmds = {k: v.format(w=w.name) for k, v in PROFILE_COMMANDS.items()}
+    n0 = sum(w.sizes)
+    prefix = "adam_scaled" if w.p_kind.endswith("_scaled") else "adam_update"
+
+    def load(d):
+        vals, grids = {}, {}
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            key = (_short(r["Kernel_Name"]), r["Dispatch_Id"])
+            vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+        big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
+        per = {}
+        for key, c in vals.items():
+            if grids[key] == big and key[0].startswith(MAIN_KERNELS):
+                per.setdefault(key[0], []).append(c)
+        return per
+
+    req, stall = load(req_dir), load(stall_dir)
+    lines = [f"rocprofv3 memory requests: workload {w.name}, main group ({n0:,} elements, "
+             f"{w.bytes_per_elem} B/elem algorithmic)",
+             f"command (requests): {cmds['dram_req']}", f"command (queues): {cmds['dram_stall']}",
+             f"summary: {cmds['dram_summary']}", ""]
+    for name in sorted(req):
+        rq = {k: statistics.mean(c[k] for c in req[name]) for k in req[name][0]}
+        st = {k: statistics.mean(c[k] for c in stall[name]) for k in stall[name][0]}
+        rd, rd128 = rq["TCC_EA0_RDREQ_sum"], rq["TCC_EA0_RDREQ_128B_sum"]
+        wr, wr64 = rq["TCC_EA0_WRREQ_sum"], rq["TCC_EA0_WRREQ_64B_sum"]
+        cycles = st["GRBM_GUI_ACTIVE"] / XCD_NUM  # per-XCD cycles of the dispatch
+        lines += [f"{name}:",
+                  f"  read requests {rd:,.0f}, of them 128-byte {rd128:,.0f} ({100 * rd128 / rd:.2f}%)",
+                  f"  write requests {wr:,.0f}, of them 64-byte {wr64:,.0f} ({100 * wr64 / wr:.2f}%)",
+                  f"  bytes per element implied (128 B reads + 64 B writes, the rest 64 / 32 B): "
+                  f"{(128 * rd128 + 64 * (rd - rd128) + 64 * wr64 + 32 * (wr - wr64)) / n0:.3f}",
+                  f"  mean outstanding requests over the GPU: reads {st['TCC_EA0_RDREQ_LEVEL_sum'] / cycles:,.0f}, "
+                  f"writes {st['TCC_EA0_WRREQ_LEVEL_sum'] / cycles:,.0f}",
+                  f"  mean read request lifetime (Little): {st['TCC_EA0_RDREQ_LEVEL_sum'] / rd:,.0f} cycles; "
+                  f"write: {st['TCC_EA0_WRREQ_LEVEL_sum'] / wr:,.0f} cycles",
+                  f"  DRAM credit stalls, % of channel-cycles: reads "
+                  f"{100 * st['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / (cycles * TCC_CHANNELS):.1f}, "
+                  f"writes {100 * st['TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum'] / (cycles * TCC_CHANNELS):.1f}",
+                  ""]
+    lines += ["Counters are summed over the L2 channels (128); GRBM_GUI_ACTIVE is summed over the",
+              "8 XCDs and divided by 8 here.  A request's lifetime is its time in the L2-to-fabric",
+              "queue until the data returns (reads) or the write is acknowledged."]
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_dram.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -413,6 +485,10 @@ def main() -> int:
     ap.add_argument("--summarize-occupancy", action="store_true",
                     help="write profiles/ occupancy summary from a rocprofv3 counter directory (no GPU)")
     ap.add_argument("--occupancy-dir")
+    ap.add_argument("--summarize-dram", action="store_true",
+                    help="write profiles/ memory-request summary from two rocprofv3 counter directories (no GPU)")
+    ap.add_argument("--dram-req-dir")
+    ap.add_argument("--dram-stall-dir")
     args = ap.parse_args()
 
     if args.summarize_profiles:
@@ -429,6 +505,11 @@ def main() -> int:
         from workloads import workloads
 
         summarize_occupancy(workloads()[args.workload], args.occupancy_dir)
+        return 0
+    if args.summarize_dram:
+        from workloads import workloads
+
+        summarize_dram(workloads()[args.workload], args.dram_req_dir, args.dram_stall_dir)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
