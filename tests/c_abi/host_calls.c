@@ -1,0 +1,50 @@
+/* A C99 client of the library: includes adam.h as a C translation unit and
+ * makes the calls that need no GPU (plan, a handle over an empty list, the
+ * host step counter of that handle, status strings).  Exit status 0 when
+ * every call behaves as the header states, else the number of the first
+ * failed check. */
+#include <stdio.h>
+#include <string.h>
+
+#include "adam.h"
+
+int main(void)
+{
+    adam_tensor t[2];
+    adam_tl_desc d;
+    adam_tl_stats st;
+    adam_tl *tl = NULL;
+    adam_hparams hp = {0.9f, 0.999f, 1e-8f, 0.01f, 1, 1};
+    int32_t step = 0;
+
+    memset(t, 0, sizeof t);
+    memset(&d, 0, sizeof d);
+    d.p = ADAM_DT_F32;
+    d.g = ADAM_DT_BF16;
+    d.p_out = ADAM_DT_NONE;
+    /* planning reads only the pointer values, never the memory */
+    t[0].p = (void *)0x100000;
+    t[0].m = (void *)0x200000;
+    t[0].v = (void *)0x300000;
+    t[0].g = (const void *)0x400000;
+    t[0].numel = 4096;
+
+    if (adam_abi_version() != ADAM_ABI_VERSION) return 1;
+    if (adam_tl_plan(t, 2, &d, &st) != ADAM_OK) return 2;
+    if (st.elements != 4096 || st.nonempty != 1 || st.tensors != 2 || st.bytes_per_elem != 26) return 3;
+    if (adam_tl_plan(t, 1, NULL, &st) != ADAM_EINVAL) return 4;
+    d.g = ADAM_DT_NONE;
+    if (adam_tl_plan(t, 1, &d, &st) != ADAM_EDTYPE) return 5;
+    d.g = ADAM_DT_BF16;
+    if (adam_tl_build(t, 0, &d, 0, &tl) != ADAM_OK || tl == NULL) return 6;
+    if (adam_step(tl, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_OK || step != 1) return 7;
+    if (adam_step(tl, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_OK || step != 2) return 8;
+    hp.mode = 2;
+    if (adam_step(tl, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_EINVAL || step != 2) return 9;
+    if (adam_step_remainders(tl, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_EINVAL) return 10;
+    adam_tl_destroy(tl);
+    adam_tl_destroy(NULL);
+    if (strcmp(adam_status_string(ADAM_EDTYPE), adam_status_string(ADAM_OK)) == 0) return 11;
+    puts("ok");
+    return 0;
+}
