@@ -5,8 +5,9 @@ shared element offset per tensor, or independent offsets per stream),
 hyperparameters (L2 or AdamW, bias correction on or off, betas near 1 or
 not, eps, weight decay, lr, grad scale on the host or the device), a chunk
 size and a number of steps, then runs the library (capturable where the
-storage allows it and the case says so) and the oracle from the same inputs
-and compares every output bit for bit (NaN as NaN)."""
+storage allows it and the case says so, with the noop flag raised on random
+steps) and the oracle from the same inputs and compares every output bit
+for bit (NaN as NaN) and the step counter."""
 import numpy as np
 import pytest
 
@@ -17,7 +18,7 @@ from workloads import host_tensors
 
 pytestmark = pytest.mark.gpu
 
-CASES = 48
+CASES = 96
 
 STORAGE = [  # (p_kind, allowed gradient types, allowed param-out)
     ("f32", ("f32", "bf16", "f16"), (None, "bf16", "f16")),
@@ -63,10 +64,11 @@ def draw_case(k):
     chunk = int(rng.choice([0, 1024, 4096, 65536]))
     steps = int(rng.integers(1, 5))
     capturable = p_kind in ("f32", "bf16_rem") and bool(rng.random() < 0.4)
+    noops = [int(rng.random() < 0.3) for _ in range(steps)] if capturable else [0] * steps
     return dict(p_kind=p_kind, g_dtype=g_dtype, p_out=p_out, sizes=sizes, layout=layout, mode=mode,
                 bias_correction=bias_correction, beta1=beta1, beta2=beta2, eps=eps, wd=wd, lr=lr,
                 grad_scale=grad_scale, device_scale=device_scale, chunk=chunk, steps=steps,
-                capturable=capturable, seed=2000 + k, rng=rng)
+                capturable=capturable, noops=noops, seed=2000 + k, rng=rng)
 
 
 @pytest.mark.parametrize("k", range(CASES))
@@ -98,12 +100,14 @@ def test_random_case(torch, orc, k):
     if c["capturable"]:
         d_lr = torch.tensor([c["lr"]], dtype=torch.float32, device="cuda")
         d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
+        d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
         fn = A.adam_step_remainders_capturable if c["p_kind"] == "bf16_rem" else A.adam_step_capturable
-        for _ in range(c["steps"]):
-            fn(tl, hp, d_lr, d_step, d_scale, None)
-            orc.group_step(ot, hr, c["lr"], ref_step, c["grad_scale"], noop=0)
+        for noop in c["noops"]:
+            d_noop.fill_(noop)
+            fn(tl, hp, d_lr, d_step, d_scale, d_noop)
+            orc.group_step(ot, hr, c["lr"], ref_step, c["grad_scale"], noop=noop)
         torch.cuda.synchronize()
-        assert int(d_step.item()) == ref_step[0] == c["steps"]
+        assert int(d_step.item()) == ref_step[0] == c["steps"] - sum(c["noops"])
     else:
         fn = {"f32": A.adam_step, "bf16_rem": A.adam_step_remainders}.get(c["p_kind"], A.adam_step_scaled)
         step = A.HostStep(0)
