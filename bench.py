@@ -75,32 +75,34 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+# The commands behind profiles/: <repo> is the repository root, <out> any
+# writable directory the rocprofv3 CSV output goes to.
 PROFILE_COMMANDS = {
-    "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/trace_{w} "
+    "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_{w} "
              "-o run -- python3 <repo>/bench.py --workload {w} --steps 10 --warmup 2 --no-cpu",
-    "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <repo>/gpurun_out/pmc_fetch_{w} "
+    "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_{w} "
              "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
-    "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <repo>/gpurun_out/pmc_write_{w} "
+    "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_{w} "
              "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
-    "summary": "python bench.py --summarize-profiles --workload {w} --trace-dir gpurun_out/trace_{w} "
-               "--fetch-dir gpurun_out/pmc_fetch_{w} --write-dir gpurun_out/pmc_write_{w}",
+    "summary": "python bench.py --summarize-profiles --workload {w} --trace-dir <out>/trace_{w} "
+               "--fetch-dir <out>/pmc_fetch_{w} --write-dir <out>/pmc_write_{w}",
     "valu": "cd /tmp && rocprofv3 --pmc SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVES GRBM_GUI_ACTIVE "
-            "--output-format csv -d <repo>/gpurun_out/pmc_valu_{w} -o run -- python3 <repo>/bench.py "
+            "--output-format csv -d <out>/pmc_valu_{w} -o run -- python3 <repo>/bench.py "
             "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
-    "valu_summary": "python bench.py --summarize-valu --workload {w} --valu-dir gpurun_out/pmc_valu_{w}",
+    "valu_summary": "python bench.py --summarize-valu --workload {w} --valu-dir <out>/pmc_valu_{w}",
     "occupancy": "cd /tmp && rocprofv3 --pmc MeanOccupancyPerCU OccupancyPercent --output-format csv "
-                 "-d <repo>/gpurun_out/pmc_occ_{w} -o run -- python3 <repo>/bench.py --workload {w} "
+                 "-d <out>/pmc_occ_{w} -o run -- python3 <repo>/bench.py --workload {w} "
                  "--steps 3 --warmup 1 --no-cpu --no-capturable",
-    "occupancy_summary": "python bench.py --summarize-occupancy --workload {w} --occupancy-dir gpurun_out/pmc_occ_{w}",
+    "occupancy_summary": "python bench.py --summarize-occupancy --workload {w} --occupancy-dir <out>/pmc_occ_{w}",
     "dram_req": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_WRREQ_sum "
-                "TCC_EA0_WRREQ_64B_sum --output-format csv -d <repo>/gpurun_out/pmc_dreq_{w} -o run -- "
+                "TCC_EA0_WRREQ_64B_sum --output-format csv -d <out>/pmc_dreq_{w} -o run -- "
                 "python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
     "dram_stall": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_WRREQ_LEVEL_sum "
                   "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum GRBM_GUI_ACTIVE "
-                  "--output-format csv -d <repo>/gpurun_out/pmc_dstall_{w} -o run -- python3 <repo>/bench.py "
+                  "--output-format csv -d <out>/pmc_dstall_{w} -o run -- python3 <repo>/bench.py "
                   "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
-    "dram_summary": "python bench.py --summarize-dram --workload {w} --dram-req-dir gpurun_out/pmc_dreq_{w} "
-                    "--dram-stall-dir gpurun_out/pmc_dstall_{w}",
+    "dram_summary": "python bench.py --summarize-dram --workload {w} --dram-req-dir <out>/pmc_dreq_{w} "
+                    "--dram-stall-dir <out>/pmc_dstall_{w}",
 }
 
 # the kernels that stream the elements: the update, and the scaled-state

@@ -27,7 +27,7 @@
  * reassociation, no flush-to-zero).  On x86-64 `float` arithmetic is SSE, so
  * there is no excess precision.
  *
- * Readings where the pages leave a step open (listed again in the design doc):
+ * Readings where the pages leave a step open:
  *   - lerp(beta, x, m) is used but never defined; it is read as the Adam
  *     moment average beta*m + (1-beta)*x: two rounded products and a rounded
  *     sum, with 1-beta itself rounded in float.
