@@ -33,7 +33,7 @@ allocated and in place)::
 Remainder storage uses ``make_desc(p="bf16_rem")`` with an int16 ``rem`` per
 tensor and ``adam_step_remainders`` (or ``..._capturable``); scaled 16-bit
 state uses ``make_desc(p="f16_scaled")`` (or ``"bf16_scaled"``) with a
-float32[3] ``scales`` per tensor and ``adam_step_scaled``.
+float32[3] ``scales`` per tensor and ``adam_step_scaled`` (or ``..._capturable``).
 """
 from __future__ import annotations
 
@@ -94,7 +94,7 @@ _lib = None
 EXPORTED = ("adam_abi_version", "adam_status_string", "adam_tl_plan", "adam_tl_build",
             "adam_tl_destroy", "adam_tl_info", "adam_step", "adam_step_capturable",
             "adam_step_remainders", "adam_step_remainders_capturable", "adam_step_scaled",
-            "adam_grad_sumsq", "adam_clip_grad_scale")
+            "adam_step_scaled_capturable", "adam_grad_sumsq", "adam_clip_grad_scale")
 
 
 def lib():
@@ -132,11 +132,13 @@ def lib():
     L.adam_step_capturable.restype = c_i32
     L.adam_step_remainders_capturable.argtypes = L.adam_step_capturable.argtypes
     L.adam_step_remainders_capturable.restype = c_i32
+    L.adam_step_scaled_capturable.argtypes = L.adam_step_capturable.argtypes
+    L.adam_step_scaled_capturable.restype = c_i32
     L.adam_grad_sumsq.argtypes = [c_vp, c_vp, c_i32, c_vp]
     L.adam_grad_sumsq.restype = c_i32
     L.adam_clip_grad_scale.argtypes = [c_vp, c_vp, c_f32, c_vp, c_vp, c_vp]
     L.adam_clip_grad_scale.restype = c_i32
-    if L.adam_abi_version() != 2:
+    if L.adam_abi_version() != 3:
         raise ImportError("libadamw_mi355x.so has an unexpected ABI version")
     _lib = L
     return L
@@ -349,6 +351,15 @@ def adam_step_remainders_capturable(tl: TensorList, hp: AdamHParams, d_lr, d_ste
                                                  _addr(d_step), _addr(d_grad_scale), _addr(d_noop),
                                                  _stream(stream)),
            "adam_step_remainders_capturable")
+
+
+def adam_step_scaled_capturable(tl: TensorList, hp: AdamHParams, d_lr, d_step,
+                                d_grad_scale=None, d_noop=None, stream=None) -> None:
+    """Capturable step of a scaled-state handle (device scalars as
+    adam_step_capturable; a noop step leaves values and scales)."""
+    _check(lib().adam_step_scaled_capturable(tl.handle, ctypes.byref(hp), _addr(d_lr), _addr(d_step),
+                                             _addr(d_grad_scale), _addr(d_noop), _stream(stream)),
+           "adam_step_scaled_capturable")
 
 
 def adam_grad_sumsq(tl: TensorList, d_sumsq, accumulate: bool = False, stream=None) -> None:

@@ -542,6 +542,25 @@ __device__ __forceinline__ Coeffs host_coeffs(const StepArgs &a)
     return c;
 }
 
+// The constants of a step of the scaled-state kernels: from the host
+// arguments, or, when the step is capturable (a.block set), from the block
+// the prologue resolved.  False when that block says the step is a noop.
+__device__ __forceinline__ bool step_coeffs(const StepArgs &a, Coeffs &c)
+{
+    c = host_coeffs(a);
+    if (a.block != nullptr) {
+        const StepBlock s = *a.block;
+        if (s.skip) return false;
+        c.lr = s.lr;
+        c.scale = s.scale;
+        c.rbc1 = s.rbc1;
+        c.rbc2 = s.rbc2;
+        c.bc1 = s.bc1;
+        c.bc2 = s.bc2;
+    }
+    return true;
+}
+
 // The update: workgroup b handles tile t = tile_of_block(b): tile
 // (t & mask) of work item (t >> shift).
 template <class C>
@@ -813,13 +832,14 @@ __global__ __launch_bounds__(kMaxBlock) void adam_scaled_maxima(const WorkItem *
                                                                  uint32_t *__restrict__ maxima)
 {
     static_assert(kTile == 2 * kLane * kMaxBlock, "two lane groups per lane");
+    Coeffs c;
+    if (!step_coeffs(a, c)) return;  // a noop step changes nothing (the fold skips too)
     const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
     const WorkItem w = items[b >> shift];
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
     const int tid = threadIdx.x;
     uint32_t mx[3] = {0u, 0u, 0u};
     if (start < w.n) {  // uniform across the wave
-        const Coeffs c = host_coeffs(a);
         const float *scales = static_cast<const float *>(w.aux);
         const float sc[3] = {scales[0], scales[1], scales[2]};
         const int n = min(kTile, w.n - start);
@@ -849,8 +869,9 @@ __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__res
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
     const int tid = threadIdx.x;
     if (start >= w.n) return;  // uniform across the workgroup
+    Coeffs c;
+    if (!step_coeffs(a, c)) return;
 
-    const Coeffs c = host_coeffs(a);
     const float *scales = static_cast<const float *>(w.aux);
     const float sc[3] = {scales[0], scales[1], scales[2]};
     const uint32_t *f = folded + 6 * size_t(w.tensor) + 3;
@@ -871,12 +892,15 @@ constexpr int kFoldMaxBlock = 256;
 
 // One workgroup per tensor: the maxima of its tiles [tiles[2k], tiles[2k+1])
 // folded into folded[6k .. 6k+2], and the reciprocal scales the store pass
-// applies into folded[6k+3 .. 6k+5] (float bits).
+// applies into folded[6k+3 .. 6k+5] (float bits).  `block` (capturable
+// steps, else null): nothing to do when it marks the step a noop.
 template <int ST>
 __global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t *__restrict__ tile_maxima,
                                                                   const uint32_t *__restrict__ tiles,
-                                                                  uint32_t *__restrict__ folded)
+                                                                  uint32_t *__restrict__ folded,
+                                                                  const StepBlock *__restrict__ block)
 {
+    if (block != nullptr && block->skip) return;
     const uint32_t k = blockIdx.x;
     const uint32_t lo = tiles[2 * k], hi = tiles[2 * k + 1];
     uint32_t x[3] = {0u, 0u, 0u};
@@ -898,11 +922,13 @@ __global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t
     }
 }
 
-// One lane per tensor: the new scales, amax / limit.
+// One lane per tensor: the new scales, amax / limit (none for a noop step).
 template <int ST>
 __global__ void adam_scaled_finish(float *const *__restrict__ scale_ptrs,
-                                   const uint32_t *__restrict__ folded, uint32_t tensors)
+                                   const uint32_t *__restrict__ folded, uint32_t tensors,
+                                   const StepBlock *__restrict__ block)
 {
+    if (block != nullptr && block->skip) return;
     const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k >= tensors) return;
     float *s = scale_ptrs[k];
@@ -1367,14 +1393,14 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
     if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     auto fold = tl->p == kBF16 ? adam_scaled_fold<kBF16> : adam_scaled_fold<kF16>;
     hipLaunchKernelGGL(fold, dim3(tl->n_tensors), dim3(kFoldMaxBlock), 0, stream,
-                       tl->d_tile_max, tl->d_tiles, tl->d_folded);
+                       tl->d_tile_max, tl->d_tiles, tl->d_folded, args.block);
     if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     hipLaunchKernelGGL(ScaledKernels::fns[base + 36], grid, dim3(kBlock), 0, stream, tl->d_items, tl->shift,
                        args, tl->d_folded);
     if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     auto finish = tl->p == kBF16 ? adam_scaled_finish<kBF16> : adam_scaled_finish<kF16>;
     hipLaunchKernelGGL(finish, dim3((tl->n_tensors + 255) / 256), dim3(256), 0, stream,
-                       tl->d_scale_ptrs, tl->d_folded, tl->n_tensors);
+                       tl->d_scale_ptrs, tl->d_folded, tl->n_tensors, args.block);
     return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
 }
 
@@ -1425,7 +1451,8 @@ int capturable_step(const adam_tl *tl, const adam_hparams *hp, const float *d_lr
     a.eps = hp->eps;
     a.weight_decay = hp->weight_decay;
     a.block = tl->d_block;
-    return launch_update(tl, hp->mode, true, a, stream);
+    return want == Kind::Scaled ? launch_scaled(tl, hp->mode, a, stream)
+                                : launch_update(tl, hp->mode, true, a, stream);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1600,6 +1627,12 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
                                     const int32_t *d_noop, hipStream_t stream)
 {
     return capturable_step(tl, hp, d_lr, d_step, d_grad_scale, d_noop, stream, Kind::Remainders);
+}
+
+int adam_step_scaled_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr, int32_t *d_step,
+                                const float *d_grad_scale, const int32_t *d_noop, hipStream_t stream)
+{
+    return capturable_step(tl, hp, d_lr, d_step, d_grad_scale, d_noop, stream, Kind::Scaled);
 }
 
 int adam_grad_sumsq(const adam_tl *tl, double *d_sumsq, int32_t accumulate, hipStream_t stream)

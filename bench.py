@@ -666,7 +666,9 @@ def main() -> int:
     }
 
     # --- capturable, eager and graph -----------------------------------------
-    cap_fn = {"f32": A.adam_step_capturable, "bf16_rem": A.adam_step_remainders_capturable}.get(w.p_kind)
+    cap_fn = {"f32": A.adam_step_capturable, "bf16_rem": A.adam_step_remainders_capturable,
+              "bf16_scaled": A.adam_step_scaled_capturable,
+              "f16_scaled": A.adam_step_scaled_capturable}[w.p_kind]
     if not args.no_capturable and cap_fn is not None:
         d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
         d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")

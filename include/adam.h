@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define ADAM_ABI_VERSION 2
+#define ADAM_ABI_VERSION 3
 
 typedef enum {
     ADAM_OK = 0,
@@ -264,6 +264,17 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
  * scaled state. */
 int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
                      float grad_scale, const float *d_grad_scale, hipStream_t stream);
+
+/* Capturable step on a scaled-state handle: the arithmetic, maxima and new
+ * scales of adam_step_scaled with the device scalars, noop flag and counter
+ * rules of adam_step_capturable (apex refuses scaled state with its
+ * capturable option; the per-tensor fold runs on the device between the two
+ * passes, so nothing needs the host).  A noop step (*d_noop == 1) writes no
+ * buffer, no scale and not the counter.  Errors as adam_step_capturable;
+ * ADAM_EINVAL for a handle without scaled state. */
+int adam_step_scaled_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
+                                int32_t *d_step, const float *d_grad_scale, const int32_t *d_noop,
+                                hipStream_t stream);
 
 /* Sum of squares of every gradient element of a handle: the local part of
  * the global gradient norm that apex's distributed_fused_adam.py computes in

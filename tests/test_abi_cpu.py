@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (adam_\w+)$", out, flags=re.M))
     assert set(names) <= exported
-    assert L.adam_abi_version() == 2
+    assert L.adam_abi_version() == 3
 
 
 def test_status_strings():
@@ -294,6 +294,15 @@ def test_step_argument_errors_leave_the_counter():
                        None) == A.ADAM_EINVAL
     assert L.adam_step_capturable(tsc.handle, ctypes.byref(hp), 256, 512, None, None,
                                   None) == A.ADAM_EINVAL
+    for handle in (tl.handle, trem.handle):
+        assert L.adam_step_scaled_capturable(handle, ctypes.byref(hp), 256, 512, None, None,
+                                             None) == A.ADAM_EINVAL
+    assert L.adam_step_scaled_capturable(tsc.handle, ctypes.byref(hp), None, 512, None, None,
+                                         None) == A.ADAM_EINVAL
+    assert L.adam_step_scaled_capturable(tsc.handle, ctypes.byref(hp), 256, None, None, None,
+                                         None) == A.ADAM_EINVAL
+    assert L.adam_step_scaled_capturable(tsc.handle, ctypes.byref(A.AdamHParams(mode=3)), 256, 512, None,
+                                         None, None) == A.ADAM_EINVAL
     assert s.value == 0
     out = ctypes.c_void_p()
     assert L.adam_tl_build(None, 0, None, None, ctypes.byref(out)) == A.ADAM_EINVAL

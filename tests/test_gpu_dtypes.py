@@ -381,3 +381,83 @@ def test_scaled_maxima_wide_magnitudes(torch, orc, p_kind):
         hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
         got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
         assert_bitwise(got, ref, ctx=f"{p_kind} mode {mode}")
+
+
+
+# ---------------------------------------------------------------------------
+# The capturable scaled-state step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p_kind,g_dtype,p_out,mode", [("f16_scaled", "bf16", "bf16", 1),
+                                                       ("bf16_scaled", "f32", "f16", 0)])
+def test_scaled_capturable_equals_noncapturable_and_oracle(torch, orc, p_kind, g_dtype, p_out, mode):
+    """Device lr (changed every step), grad scale and counter, with the noop
+    flag raised on two of six steps: values and scales equal the oracle's
+    (which skips those steps), the counter counts the steps that ran, and the
+    non-capturable step over the same steps gives the same bits."""
+    init = "large" if p_kind == "bf16_scaled" else "random"
+    g_std = 1.0 if p_kind == "bf16_scaled" else 1e-3
+    host = host_tensors(SIZES, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=88, m_v_init=init,
+                        g_std=g_std)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    ref = copies(host)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    d_lr = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_scale = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plan = [(1e-3, 0), (2e-3, 1), (1.6e-3, 0), (5e-4, 0), (1e-3, 1), (3e-3, 0)]
+    ot, st = oracle_tensors(ref), [0]
+    for lr, noop in plan:
+        d_lr.fill_(lr)
+        d_noop.fill_(noop)
+        A.adam_step_scaled_capturable(tl, hl, d_lr, d_step, d_scale, d_noop)
+        orc.group_step(ot, hr, lr, st, 0.5, noop=noop)
+    torch.cuda.synchronize()
+    assert int(d_step.item()) == st[0] == 4
+    got = dev.readback()
+    tl.destroy()
+    assert_bitwise(got, ref, ctx=f"{p_kind}/{mode}")
+
+    dev2 = DeviceSet(host)
+    tl2 = A.adam_tl_build(dev2.tensors, desc_for(host))
+    step = A.HostStep(0)
+    for lr, noop in plan:
+        if not noop:
+            A.adam_step_scaled(tl2, hl, lr, step, 0.5)
+    torch.cuda.synchronize()
+    assert_bitwise(dev2.readback(), got, ctx="non-capturable")
+    tl2.destroy()
+
+
+def test_scaled_capturable_graph_replay(torch, orc):
+    """One capturable scaled step recorded in a HIP graph and replayed four
+    times, lr changed and the noop flag raised between replays: each
+    replay's values and scales follow the oracle."""
+    host = host_tensors([70001, 4096, 513], g_dtype="bf16", p_kind="f16_scaled", p_out="f16", seed=89,
+                        m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    d_lr = torch.tensor([1e-3], dtype=torch.float32, device="cuda")
+    d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        A.adam_step_scaled_capturable(tl, hl, d_lr, d_step, None, d_noop)
+    torch.cuda.synchronize()
+    assert int(d_step.item()) == 0
+    ref = copies(host)
+    ot, st = oracle_tensors(ref), [0]
+    for lr, noop in [(1e-3, 0), (2e-3, 1), (5e-4, 0), (1.6e-3, 0)]:
+        d_lr.fill_(lr)
+        d_noop.fill_(noop)
+        graph.replay()
+        torch.cuda.synchronize()
+        orc.group_step(ot, hr, lr, st, 1.0, noop=noop)
+        assert_bitwise(dev.readback(), ref, ctx=f"replay lr {lr} noop {noop}")
+    assert int(d_step.item()) == st[0] == 3
+    tl.destroy()

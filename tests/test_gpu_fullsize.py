@@ -196,9 +196,11 @@ def test_zero_shard_fp16_capturable_with_noop(torch):
     run_sampled(torch, "zero1e9_f16", 10, capturable=True, noop_every=5, seed=8)
 
 
-def test_scaled_state_zero_shard(torch):
+@pytest.mark.parametrize("capturable", [False, True])
+def test_scaled_state_zero_shard(torch, capturable):
     """1e9 elements of scaled fp16 p, m, v in 2048 buckets, bf16 gradients,
-    bf16 param-sync copy, five steps from a fresh state.  The new scales of a
+    bf16 param-sync copy, five steps from a fresh state (capturable: six
+    calls from device scalars, the fourth a noop).  The new scales of a
     tensor depend on all of it, so the samples are whole tensors (first,
     middle, last and five random buckets): their initial state goes to the
     host, the oracle steps them, and values, scales and p_out must match."""
@@ -227,11 +229,22 @@ def test_scaled_state_zero_shard(torch):
     hp = A.AdamHParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
     hr = oracle.HParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
     step, ref_step = A.HostStep(0), [0]
-    for _ in range(5):
-        A.adam_step_scaled(tl, hp, w.lr, step)
-        oracle.default().group_step(refs, hr, w.lr, ref_step, 1.0)
-    torch.cuda.synchronize()
-    assert step.value == ref_step[0] == 5
+    if capturable:
+        d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
+        d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
+        d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+        for k in range(6):
+            d_noop.fill_(1 if k == 3 else 0)
+            A.adam_step_scaled_capturable(tl, hp, d_lr, d_step, None, d_noop)
+            oracle.default().group_step(refs, hr, w.lr, ref_step, 1.0, noop=1 if k == 3 else 0)
+        torch.cuda.synchronize()
+        assert int(d_step.item()) == ref_step[0] == 5
+    else:
+        for _ in range(5):
+            A.adam_step_scaled(tl, hp, w.lr, step)
+            oracle.default().group_step(refs, hr, w.lr, ref_step, 1.0)
+        torch.cuda.synchronize()
+        assert step.value == ref_step[0] == 5
     for k, ref in zip(picks, refs):
         lo, hi = int(offs[k]), int(offs[k + 1])
         got = {r: dev_to_np(bufs[r][lo:hi]) for r in ("p", "m", "v", "p_out")}

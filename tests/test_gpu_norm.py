@@ -171,16 +171,18 @@ def test_clip_argument_errors(torch):
 
 
 @pytest.mark.parametrize("g_dtype,p_kind,p_out", [("bf16", "f32", "bf16"), ("bf16", "bf16_rem", "bf16"),
-                                                 ("f16", "f32", "f16")])
+                                                 ("f16", "f32", "f16"), ("bf16", "f16_scaled", "f16")])
 def test_whole_capturable_step_in_one_graph(torch, orc, g_dtype, p_kind, p_out):
     """Two groups (decay and no decay): per step the gradient sum of squares
     of both groups, the clip / found-inf step, then the capturable update of
-    each group (fp32 master or bf16 + remainders), all recorded in one HIP
-    graph and replayed; an infinite gradient on the third replay skips that
-    step.  Each replay equals the oracle fed the same sum of squares."""
+    each group (fp32 master, bf16 + remainders, or scaled fp16 state), all
+    recorded in one HIP graph and replayed; an infinite gradient on the third
+    replay skips that step.  Each replay equals the oracle fed the same sum
+    of squares."""
     h1 = host_tensors([40000, 4096, 333], g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=56)
     h2 = host_tensors([4096] * 3, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=57)
-    cap = A.adam_step_remainders_capturable if p_kind == "bf16_rem" else A.adam_step_capturable
+    cap = {"bf16_rem": A.adam_step_remainders_capturable,
+           "f16_scaled": A.adam_step_scaled_capturable}.get(p_kind, A.adam_step_capturable)
     d1, d2 = DeviceSet(h1), DeviceSet(h2)
     t1 = A.adam_tl_build(d1.tensors, desc_for(h1))
     t2 = A.adam_tl_build(d2.tensors, desc_for(h2))
