@@ -132,7 +132,8 @@ typedef struct {
     int64_t vector_tensors;  /* tensors whose buffers all allow 4-element vectors */
     int64_t grid_blocks;     /* workgroups per launch of the update kernel        */
     int32_t tile_elems;      /* elements per workgroup (one tile)                 */
-    int32_t block_threads;   /* threads per workgroup                             */
+    int32_t block_threads;   /* threads per workgroup of the update (the scaled-
+                                state maxima pass runs one 64-lane wave per tile) */
     int32_t bytes_per_elem;  /* algorithmic HBM bytes per element (read + write)  */
     int32_t device;          /* HIP device of the handle (-1 from adam_tl_plan)   */
 } adam_tl_stats;
@@ -165,8 +166,8 @@ int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *
 /* Builds a handle for one group: validates as adam_tl_plan, then copies the
  * work table (one 64-byte record per chunk, plus a 64-byte scalar block used
  * by the capturable steps, partial-sum scratch for adam_grad_sumsq, and for
- * scaled state 12 bytes of maxima per 512-element tile and per tensor) to the
- * current device,
+ * scaled state 12 bytes of maxima per 512-element tile and 24 bytes of maxima
+ * and reciprocal scales per tensor) to the current device,
  * using `stream`, and waits for that copy.  `tensors` (host array of `count`) is
  * not retained; the device buffers it names must stay allocated and in place
  * for the handle's life.  On success *out owns device memory; release it with
