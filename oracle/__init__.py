@@ -57,12 +57,15 @@ class HParams:
 
 @dataclass
 class OracleTensor:
-    """One tensor of a group.  For fp32 params ``p`` is float32 and ``rem`` and
-    ``scales`` are None; for remainder params ``p`` is bf16 bits (uint16) and
-    ``rem`` int16; for scaled state ``p``, ``m``, ``v`` are bf16 bits (uint16)
-    or float16 and ``scales`` is float32[3] (param, exp_avg, exp_avg_sq).
-    ``g`` is float32, bf16 bits (uint16) or float16.  ``p_out`` is bf16 bits
-    (uint16), float16 or None."""
+    """One tensor of a group.  For fp32 params ``p``, ``m``, ``v`` are float32
+    and ``rem`` and ``scales`` are None; for 16-bit state ``p``, ``m``, ``v``
+    are all bf16 bits (uint16) or all float16, without ``rem`` or
+    ``scales``; for remainder params ``p`` is bf16 bits (uint16), ``rem``
+    int16 and ``m``, ``v`` float32; for scaled state ``p``, ``m``, ``v`` are
+    bf16 bits (uint16) or float16 and ``scales`` is float32[3] (param,
+    exp_avg, exp_avg_sq).  ``g`` is float32, bf16 bits (uint16) or float16.
+    ``p_out`` is float32 (fp32 or 16-bit state only), bf16 bits (uint16),
+    float16 or None."""
 
     p: np.ndarray
     m: np.ndarray
@@ -123,6 +126,8 @@ class Oracle:
         common = [f32, f32, f32, f32, f32, i32, f32, f32, f32]
         lib.oracle_adam_f32.argtypes = [vp, vp, vp, vp, i32, vp, i32, i64, *common]
         lib.oracle_adam_f32.restype = None
+        lib.oracle_adam_state16.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i64, *common]
+        lib.oracle_adam_state16.restype = None
         lib.oracle_adam_remainder.argtypes = [vp, vp, vp, vp, vp, i32, vp, i64, *common]
         lib.oracle_adam_remainder.restype = None
         lib.oracle_adam_scaled.argtypes = [vp, vp, vp, i32, vp, vp, i32, vp, i32, i64, *common]
@@ -235,7 +240,7 @@ class Oracle:
                 float(hp.weight_decay), int(hp.mode), float(bc1), float(bc2),
                 float(grad_scale))
         g_ptr = _ptr(t.g) + t.g.dtype.itemsize * lo
-        out_ptr = None if t.p_out is None else _ptr(t.p_out) + 2 * lo
+        out_ptr = None if t.p_out is None else _ptr(t.p_out) + t.p_out.dtype.itemsize * lo
         if t.scales is not None:
             # the new scales depend on the whole tensor: no partial ranges
             assert lo == 0 and n == t.numel, "scaled state is updated whole"
@@ -248,15 +253,22 @@ class Oracle:
             if rc != 0:
                 raise MemoryError("oracle_adam_scaled could not allocate its work buffers")
             return
+        if t.rem is None and t.p.dtype != np.float32:
+            # 16-bit state: p, m and v of one 16-bit type
+            st = type_code(t.p)
+            assert st in (BF16, F16) and t.m.dtype == t.p.dtype and t.v.dtype == t.p.dtype
+            self.lib.oracle_adam_state16(_ptr(t.p) + 2 * lo, _ptr(t.m) + 2 * lo, _ptr(t.v) + 2 * lo, st,
+                                         g_ptr, g_type, out_ptr, out_type, count, *scal)
+            return
         m_ptr = _ptr(t.m) + 4 * lo
         v_ptr = _ptr(t.v) + 4 * lo
         if t.rem is None:
-            assert t.p.dtype == np.float32
+            assert t.p.dtype == np.float32 and t.m.dtype == np.float32 and t.v.dtype == np.float32
             self.lib.oracle_adam_f32(_ptr(t.p) + 4 * lo, m_ptr, v_ptr, g_ptr,
                                      g_type, out_ptr, out_type, count, *scal)
         else:
             assert t.p.dtype == np.uint16 and t.rem.dtype == np.int16
-            assert out_type in (F32, BF16), "remainder param-out is the new bf16 param"
+            assert t.p_out is None or out_type == BF16, "remainder param-out is the new bf16 param"
             self.lib.oracle_adam_remainder(_ptr(t.p) + 2 * lo, _ptr(t.rem) + 2 * lo,
                                            m_ptr, v_ptr, g_ptr, g_type, out_ptr,
                                            count, *scal)

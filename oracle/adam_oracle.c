@@ -44,6 +44,10 @@
  *     nearest even with IEEE overflow to infinity and subnormals kept.
  *   - scaled state: torch.reciprocal and the float division of the scale are
  *     correctly rounded float operations.
+ *   - a 16-bit state type T (bf16 or fp16 params and moments): the functor's
+ *     update of its T arrays (`p -= lr * update`, `m = next_m`, ...) is read
+ *     as the float result rounded once to T, nearest even; the param-out
+ *     cast starts from the new T value.
  */
 #include <math.h>
 #include <stdint.h>
@@ -309,11 +313,34 @@ static uint16_t cast_out(float x, int32_t out_type)
     return out_type == ORACLE_F16 ? oracle_f16_rne(x) : oracle_bf16_rne(x);
 }
 
+/* The param-out store ([P1] operator(): the new param cast to PARAM_OUT_T):
+ * out_type ORACLE_F32 stores the float, ORACLE_BF16 / ORACLE_F16 its
+ * nearest-even 16-bit value. */
+static void store_out(void *p_out, int64_t i, float x, int32_t out_type)
+{
+    if (out_type == ORACLE_F32)
+        ((float *)p_out)[i] = x;
+    else
+        ((uint16_t *)p_out)[i] = cast_out(x, out_type);
+}
+
+/* A 16-bit value of the state type (ORACLE_BF16 or ORACLE_F16) as float
+ * (exact), and a float rounded to that type (nearest even). */
+static float state_to_f32(uint16_t h, int32_t type)
+{
+    return type == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
+}
+
+static uint16_t f32_to_state(float x, int32_t type)
+{
+    return type == ORACLE_F16 ? oracle_f16_rne(x) : oracle_bf16_rne(x);
+}
+
 /* fp32 params: p, m, v updated in place over n elements; g is float, bf16 or
- * fp16 (g_type); p_out (nullable) receives the new p cast to bf16 or fp16
+ * fp16 (g_type); p_out (nullable) receives the new p as float, bf16 or fp16
  * (out_type), round to nearest even. */
 void oracle_adam_f32(float *p, float *m, float *v, const void *g,
-                     int32_t g_type, uint16_t *p_out, int32_t out_type, int64_t n,
+                     int32_t g_type, void *p_out, int32_t out_type, int64_t n,
                      float lr, float beta1, float beta2, float eps,
                      float weight_decay, int32_t mode, float bc1, float bc2,
                      float grad_scale)
@@ -328,7 +355,37 @@ void oracle_adam_f32(float *p, float *m, float *v, const void *g,
         m[i] = M;
         v[i] = V;
         if (p_out)
-            p_out[i] = cast_out(P_new, out_type);
+            store_out(p_out, i, P_new, out_type);
+    }
+}
+
+/* 16-bit state: [P1] operator() takes the type T of the param and both
+ * moments from the param tensor list (float, half or bfloat16; apex's
+ * optimizer passes its state dtype as T).  For T = bf16 or fp16
+ * (state_type) p, m and v hold T values: each is widened to float (exact),
+ * updated as above, and assigned back to T (round to nearest even, once, as
+ * the functor's stores of its float results into T arrays do); p_out
+ * (nullable) receives the static_cast of the new param, which the functor
+ * takes from its T array, so from the rounded T value (out_type float, bf16
+ * or fp16). */
+void oracle_adam_state16(uint16_t *p, uint16_t *m, uint16_t *v, int32_t state_type,
+                         const void *g, int32_t g_type, void *p_out, int32_t out_type,
+                         int64_t n, float lr, float beta1, float beta2, float eps,
+                         float weight_decay, int32_t mode, float bc1, float bc2,
+                         float grad_scale)
+{
+    struct oracle_scalars s = {lr, beta1, beta2, eps, weight_decay,
+                               bc1, bc2, grad_scale, mode};
+    for (int64_t i = 0; i < n; ++i) {
+        float P = state_to_f32(p[i], state_type);
+        float M = state_to_f32(m[i], state_type);
+        float V = state_to_f32(v[i], state_type);
+        float P_new = adam_element(P, load_grad(g, g_type, i), &M, &V, &s);
+        m[i] = f32_to_state(M, state_type);
+        v[i] = f32_to_state(V, state_type);
+        p[i] = f32_to_state(P_new, state_type);
+        if (p_out)
+            store_out(p_out, i, state_to_f32(p[i], state_type), out_type);
     }
 }
 
@@ -361,16 +418,6 @@ void oracle_adam_remainder(uint16_t *p, int16_t *rem, float *m, float *v,
 /* _local_step_with_scaled_states, _apply_state_scale,                     */
 /* _check_params_shard_dtypes.                                             */
 /* ---------------------------------------------------------------------- */
-
-static float state_to_f32(uint16_t h, int32_t type)
-{
-    return type == ORACLE_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
-}
-
-static uint16_t f32_to_state(float x, int32_t type)
-{
-    return type == ORACLE_F16 ? oracle_f16_rne(x) : oracle_bf16_rne(x);
-}
 
 /* Half the largest finite value of the state type (torch.finfo(dtype).max
  * / 2, exact in float): the magnitude the largest scaled element is mapped

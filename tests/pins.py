@@ -33,6 +33,10 @@ What pins what:
                               its exact float16 -> float32 widening;
 * fp16 gradients / p_out    - the fp32 update of the exactly widened
                               gradient, numpy's cast of the new param;
+* fp32 param-out            - the new param itself;
+* 16-bit state (T bf16/fp16) - the pinned fp32 update of the widened values,
+                              rounded to T by torch's / numpy's casts; the
+                              param-out the library cast of the new T value;
 * scaled 16-bit state       - the pages' own torch op sequence for the
                               unscale / rescale steps (aminmax, maximum, div,
                               reciprocal, where, mul, dtype casts) around the
@@ -683,6 +687,96 @@ def check_f16_grad_and_param_out(o: Oracle, seed: int = 42):
             assert np.array_equal(t16.p_out.view(np.uint16), want.view(np.uint16))
 
 
+def check_f32_param_out(o: Oracle, seed: int = 45):
+    """An fp32 param-out of fp32 params is the new param itself, bit for bit
+    (the functor's cast to a float PARAM_OUT_T is the identity)."""
+    rng = np.random.default_rng(seed)
+    n = 1001
+    p0 = rng.standard_normal(n).astype(np.float32)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    for mode in (0, 1):
+        hp = HParams(0.9, 0.95, 1e-8, 0.1, mode, 1)
+        t = OracleTensor(p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), g,
+                         np.zeros(n, np.float32))
+        st = [0]
+        for _ in range(2):
+            o.group_step([t], hp, 1.6e-3, st, 1.0)
+            assert np.array_equal(t.p_out.view(np.uint32), t.p.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# 16-bit optimizer state (the state type T of the pages' functor = bf16/fp16)
+# ---------------------------------------------------------------------------
+
+def _library_round(x32: np.ndarray, kind: str) -> np.ndarray:
+    """float32 -> bf16 bits (torch's CPU cast) or float16 (numpy's cast),
+    both round to nearest even."""
+    if kind == "f16":
+        with np.errstate(over="ignore"):
+            return np.ascontiguousarray(x32, np.float32).astype(np.float16)
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x32, np.float32).copy()).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _library_widen(a: np.ndarray, kind: str) -> np.ndarray:
+    if kind == "f16":
+        return a.astype(np.float32)
+    return (a.astype(np.uint32) << 16).view(np.float32)
+
+
+def _bits16(a: np.ndarray) -> np.ndarray:
+    return a.view(np.uint16) if a.dtype == np.float16 else a
+
+
+def check_state16_update(o: Oracle, seed: int = 44):
+    """16-bit state: p, m, v of one type T (bf16 or fp16) step as the pinned
+    fp32 update of their widened values, with p, m and v then rounded to T by
+    a library conversion (torch's float32 -> bfloat16, numpy's float32 ->
+    float16); the param-out is the library cast of the new T param (an fp32
+    param-out its exact widening).  Three steps, both modes, every gradient
+    and param-out type; params include fp16 values next to its overflow
+    threshold and subnormal second moments."""
+    rng = np.random.default_rng(seed)
+    n = 509
+    for st in ("bf16", "f16"):
+        p32 = rng.standard_normal(n).astype(np.float32)
+        if st == "f16":
+            p32[:4] = [65504.0, -65504.0, 65000.0, 6.1e-5]
+        p0 = _library_round(p32, st)
+        m0 = _library_round((rng.standard_normal(n) * 1e-3).astype(np.float32), st)
+        v0 = _library_round((np.abs(rng.standard_normal(n)) * 1e-6).astype(np.float32), st)
+        for g_kind in ("f32", "bf16", "f16"):
+            g32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+            g = g32 if g_kind == "f32" else _library_round(g32, g_kind)
+            for out in (None, "f32", "bf16", "f16"):
+                for mode in (0, 1):
+                    hp = HParams(0.9, 0.95, 1e-8, 0.1, mode, 1)
+                    p_out = None if out is None else np.zeros(
+                        n, {"f32": np.float32, "bf16": np.uint16, "f16": np.float16}[out])
+                    t16 = OracleTensor(p0.copy(), m0.copy(), v0.copy(), g, p_out)
+                    t32 = OracleTensor(_library_widen(p0, st), _library_widen(m0, st),
+                                       _library_widen(v0, st), g)
+                    s16, s32 = [0], [0]
+                    for _ in range(3):
+                        o.group_step([t16], hp, 1.6e-3, s16, 0.5)
+                        o.group_step([t32], hp, 1.6e-3, s32, 0.5)
+                        for name in ("p", "m", "v"):
+                            want = _library_round(getattr(t32, name), st)
+                            assert np.array_equal(_bits16(getattr(t16, name)), _bits16(want)), \
+                                (st, g_kind, out, mode, name)
+                            setattr(t32, name, _library_widen(want, st))
+                        if out is not None:
+                            wide = _library_widen(t16.p, st)
+                            if out == "f32":
+                                assert np.array_equal(t16.p_out.view(np.uint32), wide.view(np.uint32))
+                            else:
+                                want_out = _library_round(wide, out)
+                                assert np.array_equal(_bits16(t16.p_out), _bits16(want_out)), \
+                                    (st, g_kind, out, mode, "p_out")
+
+
 # ---------------------------------------------------------------------------
 # Scaled 16-bit optimizer state
 # ---------------------------------------------------------------------------
@@ -873,6 +967,8 @@ QUICK_CHECKS = (
     "check_f16_grad_and_param_out",
     "check_scaled_state",
     "check_scaled_state_special_cases",
+    "check_f32_param_out",
+    "check_state16_update",
 )
 
 

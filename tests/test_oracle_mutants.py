@@ -76,6 +76,15 @@ MUTANTS = {
     "scaled_moment_scales_swapped": [("M[i] = state_to_f32(m[i], state_type) * scales[1];",
                                       "M[i] = state_to_f32(m[i], state_type) * scales[2];")],
     "scaled_param_sync_from_stored": [("p_out[i] = cast_out(P[i], out_type);", "p_out[i] = p[i];")],
+    "state16_moment_rounded_as_bf16": [("m[i] = f32_to_state(M, state_type);",
+                                        "m[i] = f32_to_state(M, ORACLE_BF16);")],
+    "state16_second_moment_from_first": [("float V = state_to_f32(v[i], state_type);",
+                                          "float V = state_to_f32(m[i], state_type);")],
+    "state16_param_not_rounded": [("p[i] = f32_to_state(P_new, state_type);",
+                                   "p[i] = f32_to_state(P, state_type);")],
+    "state16_param_out_from_float": [("store_out(p_out, i, state_to_f32(p[i], state_type), out_type);",
+                                      "store_out(p_out, i, P_new, out_type);")],
+    "f32_param_out_dropped": [("((float *)p_out)[i] = x;", "((float *)p_out)[i] = 0.0f;")],
     "scaled_scale_not_returned": [("    scales[1] = oracle_rescale_store(M, m, n, state_type);\n", "")],
 }
 

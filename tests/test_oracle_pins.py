@@ -85,6 +85,14 @@ def test_scaled_state_matches_the_pages_torch_sequence(oracle_default):
     pins.check_scaled_state(oracle_default)
 
 
+def test_f32_param_out_is_the_new_param(oracle_default):
+    pins.check_f32_param_out(oracle_default)
+
+
+def test_state16_update_is_the_rounded_fp32_update(oracle_default):
+    pins.check_state16_update(oracle_default)
+
+
 def test_scaled_state_special_cases(oracle_default):
     pins.check_scaled_state_special_cases(oracle_default)
 
