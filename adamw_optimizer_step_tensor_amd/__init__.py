@@ -138,7 +138,7 @@ def lib():
     L.adam_grad_sumsq.restype = c_i32
     L.adam_clip_grad_scale.argtypes = [c_vp, c_vp, c_f32, c_vp, c_vp, c_vp]
     L.adam_clip_grad_scale.restype = c_i32
-    if L.adam_abi_version() != 3:
+    if L.adam_abi_version() != 4:
         raise ImportError("libadamw_mi355x.so has an unexpected ABI version")
     _lib = L
     return L
@@ -195,7 +195,7 @@ def _tensor_array(tensors: Sequence, desc: AdamTlDesc):
         torch_dtypes = {DT_F32: (f32,), DT_BF16: (bf16, i16), DT_F16: (f16, i16)}
     except ImportError:  # raw addresses only
         pass
-    mv = desc.p if desc.scaled_state == 1 else DT_F32
+    mv = DT_F32 if desc.p == DT_F32 or desc.with_remainders == 1 else desc.p
     for i, t in enumerate(tensors):
         n = _numel(t)
         if torch_dtypes is not None:
@@ -217,12 +217,14 @@ def _tensor_array(tensors: Sequence, desc: AdamTlDesc):
 
 def make_desc(*, g="f32", p="f32", p_out=None, chunk_elems=0) -> AdamTlDesc:
     """Descriptor from short names: g in {"f32", "bf16", "f16"}; p in {"f32",
-    "bf16_rem" (bf16 + int16 remainders), "bf16_scaled", "f16_scaled" (scaled
-    16-bit p, m, v)}; p_out in {None, "bf16", "f16"}."""
+    "bf16", "f16" (16-bit p, m, v), "bf16_rem" (bf16 + int16 remainders, fp32
+    m, v), "bf16_scaled", "f16_scaled" (scaled 16-bit p, m, v)}; p_out in
+    {None, "f32", "bf16", "f16"}."""
     gd = {"f32": DT_F32, "bf16": DT_BF16, "f16": DT_F16}[g]
-    pd, rem, scaled = {"f32": (DT_F32, 0, 0), "bf16_rem": (DT_BF16, 1, 0),
+    pd, rem, scaled = {"f32": (DT_F32, 0, 0), "bf16": (DT_BF16, 0, 0), "f16": (DT_F16, 0, 0),
+                       "bf16_rem": (DT_BF16, 1, 0),
                        "bf16_scaled": (DT_BF16, 0, 1), "f16_scaled": (DT_F16, 0, 1)}[p]
-    od = {None: DT_NONE, "bf16": DT_BF16, "f16": DT_F16}[p_out]
+    od = {None: DT_NONE, "f32": DT_F32, "bf16": DT_BF16, "f16": DT_F16}[p_out]
     return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), scaled, 0)
 
 

@@ -113,9 +113,11 @@ constexpr int kF32 = ADAM_DT_F32;
 constexpr int kBF16 = ADAM_DT_BF16;
 constexpr int kF16 = ADAM_DT_F16;
 
-// How params are stored (non-scaled update kernels).
-constexpr int kParamF32 = 0;  // fp32 params
-constexpr int kParamRem = 1;  // bf16 params + int16 remainders
+// How params and moments are stored (non-scaled update kernels).
+constexpr int kParamF32 = 0;   // fp32 p, m, v
+constexpr int kParamRem = 1;   // bf16 params + int16 remainders, fp32 m, v
+constexpr int kParamBF16 = 2;  // bf16 p, m, v (16-bit state)
+constexpr int kParamF16 = 3;   // fp16 p, m, v (16-bit state)
 
 enum : uint32_t { kItemVector = 1u };
 
@@ -432,12 +434,27 @@ __device__ __forceinline__ float load_grad1(const void *g, int i)
 template <int GT, int PK, int OT, int MODE, bool CAPT>
 struct Config {
     static constexpr int gt = GT;     // gradient type
-    static constexpr int pk = PK;     // kParamF32 or kParamRem
+    static constexpr int pk = PK;     // kParamF32, kParamRem, kParamBF16 or kParamF16
     static constexpr int ot = OT;     // param-out type, kNone if absent
     static constexpr int mode = MODE;
     static constexpr bool capturable = CAPT;
-    static_assert(PK == kParamF32 || OT != kF16, "remainder param-out is the new bf16 param");
+    // the 16-bit type of p, m, v (16-bit state), else kNone
+    static constexpr int st = PK == kParamBF16 ? kBF16 : PK == kParamF16 ? kF16 : kNone;
+    static_assert(PK != kParamRem || OT == kNone || OT == kBF16, "remainder param-out is the new bf16 param");
 };
+
+// The param-out of a new param x (float), or for 16-bit state of the new
+// stored bits h of type ST: the cast of that value to OT.
+template <int OT, int ST>
+__device__ __forceinline__ uint32_t out16(float x, uint32_t h)
+{
+    if constexpr (ST == kNone)
+        return narrow16<OT>(x);
+    else if constexpr (OT == ST)
+        return h;
+    else
+        return narrow16<OT>(widen16<ST>(h));
+}
 
 // The four consecutive elements of lane group gi, updated in registers:
 // every load is issued before any arithmetic.
@@ -445,36 +462,72 @@ template <class C>
 __device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Coeffs &c)
 {
     float p[kLane], m[kLane], v[kLane], g[kLane];
-    load_f32x4(w.m, gi, m);
-    load_f32x4(w.v, gi, v);
+    uint32_t hp[kLane], hm[kLane], hv[kLane];
+    if constexpr (C::st != kNone) {
+        load_u16x4(w.m, gi, hm);
+        load_u16x4(w.v, gi, hv);
+    } else {
+        load_f32x4(w.m, gi, m);
+        load_f32x4(w.v, gi, v);
+    }
     load_grad4<C::gt>(w.g, gi, g);
     if constexpr (C::pk == kParamRem) {
-        uint32_t h[kLane], r[kLane];
-        load_u16x4(w.p, gi, h);
+        uint32_t r[kLane];
+        load_u16x4(w.p, gi, hp);
         load_u16x4(w.aux, gi, r);
 #pragma unroll
-        for (int k = 0; k < kLane; ++k) p[k] = master_from(h[k], r[k]);
+        for (int k = 0; k < kLane; ++k) p[k] = master_from(hp[k], r[k]);
+    } else if constexpr (C::st != kNone) {
+        load_u16x4(w.p, gi, hp);
+#pragma unroll
+        for (int k = 0; k < kLane; ++k) {
+            p[k] = widen16<C::st>(hp[k]);
+            m[k] = widen16<C::st>(hm[k]);
+            v[k] = widen16<C::st>(hv[k]);
+        }
     } else {
         load_f32x4(w.p, gi, p);
     }
 #pragma unroll
     for (int k = 0; k < kLane; ++k) p[k] = update_element<C::mode>(p[k], g[k], m[k], v[k], c);
 
-    store_f32x4(w.m, gi, m);
-    store_f32x4(w.v, gi, v);
-    if constexpr (C::pk == kParamRem) {
-        uint32_t h[kLane], r[kLane];
+    if constexpr (C::st != kNone) {
 #pragma unroll
-        for (int k = 0; k < kLane; ++k) master_to(p[k], h[k], r[k]);
-        store_u16x4(w.p, gi, h);
-        store_u16x4(w.aux, gi, r);
-        if constexpr (C::ot != kNone) store_u16x4(w.p_out, gi, h);
+        for (int k = 0; k < kLane; ++k) {
+            hm[k] = narrow16<C::st>(m[k]);
+            hv[k] = narrow16<C::st>(v[k]);
+            hp[k] = narrow16<C::st>(p[k]);
+        }
+        store_u16x4(w.m, gi, hm);
+        store_u16x4(w.v, gi, hv);
+        store_u16x4(w.p, gi, hp);
     } else {
-        store_f32x4(w.p, gi, p);
-        if constexpr (C::ot != kNone) {
+        store_f32x4(w.m, gi, m);
+        store_f32x4(w.v, gi, v);
+    }
+    if constexpr (C::pk == kParamRem) {
+        uint32_t r[kLane];
+#pragma unroll
+        for (int k = 0; k < kLane; ++k) master_to(p[k], hp[k], r[k]);
+        store_u16x4(w.p, gi, hp);
+        store_u16x4(w.aux, gi, r);
+        if constexpr (C::ot != kNone) store_u16x4(w.p_out, gi, hp);
+    } else {
+        if constexpr (C::pk == kParamF32) store_f32x4(w.p, gi, p);
+        if constexpr (C::ot == kF32) {
+            float o[kLane];
+#pragma unroll
+            for (int k = 0; k < kLane; ++k) {
+                if constexpr (C::st == kNone)
+                    o[k] = p[k];
+                else
+                    o[k] = widen16<C::st>(hp[k]);
+            }
+            store_f32x4(w.p_out, gi, o);
+        } else if constexpr (C::ot != kNone) {
             uint32_t o[kLane];
 #pragma unroll
-            for (int k = 0; k < kLane; ++k) o[k] = narrow16<C::ot>(p[k]);
+            for (int k = 0; k < kLane; ++k) o[k] = out16<C::ot, C::st>(p[k], hp[k]);
             store_u16x4(w.p_out, gi, o);
         }
     }
@@ -485,9 +538,9 @@ template <class C>
 __device__ __forceinline__ void update_single(const WorkItem &w, int i, const Coeffs &c)
 {
     const float g = load_grad1<C::gt>(w.g, i);
-    float m = load_one<float>(w.m, i);
-    float v = load_one<float>(w.v, i);
     if constexpr (C::pk == kParamRem) {
+        float m = load_one<float>(w.m, i);
+        float v = load_one<float>(w.v, i);
         const float p = master_from(load_one<uint16_t>(w.p, i), load_one<uint16_t>(w.aux, i));
         const float pn = update_element<C::mode>(p, g, m, v, c);
         uint32_t h, r;
@@ -495,13 +548,32 @@ __device__ __forceinline__ void update_single(const WorkItem &w, int i, const Co
         store_one<uint16_t>(w.p, i, uint16_t(h));
         store_one<uint16_t>(w.aux, i, uint16_t(r));
         if constexpr (C::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(h));
+        store_one<float>(w.m, i, m);
+        store_one<float>(w.v, i, v);
+    } else if constexpr (C::st != kNone) {
+        float m = widen16<C::st>(load_one<uint16_t>(w.m, i));
+        float v = widen16<C::st>(load_one<uint16_t>(w.v, i));
+        const float pn = update_element<C::mode>(widen16<C::st>(load_one<uint16_t>(w.p, i)), g, m, v, c);
+        const uint32_t h = narrow16<C::st>(pn);
+        store_one<uint16_t>(w.m, i, uint16_t(narrow16<C::st>(m)));
+        store_one<uint16_t>(w.v, i, uint16_t(narrow16<C::st>(v)));
+        store_one<uint16_t>(w.p, i, uint16_t(h));
+        if constexpr (C::ot == kF32)
+            store_one<float>(w.p_out, i, widen16<C::st>(h));
+        else if constexpr (C::ot != kNone)
+            store_one<uint16_t>(w.p_out, i, uint16_t(out16<C::ot, C::st>(pn, h)));
     } else {
+        float m = load_one<float>(w.m, i);
+        float v = load_one<float>(w.v, i);
         const float pn = update_element<C::mode>(load_one<float>(w.p, i), g, m, v, c);
         store_one<float>(w.p, i, pn);
-        if constexpr (C::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<C::ot>(pn)));
+        if constexpr (C::ot == kF32)
+            store_one<float>(w.p_out, i, pn);
+        else if constexpr (C::ot != kNone)
+            store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<C::ot>(pn)));
+        store_one<float>(w.m, i, m);
+        store_one<float>(w.v, i, v);
     }
-    store_one<float>(w.m, i, m);
-    store_one<float>(w.v, i, v);
 }
 
 // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
@@ -1081,20 +1153,21 @@ typedef void (*UpdateFn)(const WorkItem *, uint32_t, StepArgs);
 typedef void (*ScaledFn)(const WorkItem *, uint32_t, StepArgs, uint32_t *);
 
 constexpr int kGradTypes[3] = {kF32, kBF16, kF16};
-constexpr int kOutTypes[3] = {kNone, kBF16, kF16};
+constexpr int kOutTypes[3] = {kNone, kBF16, kF16};              // scaled state
+constexpr int kUpdateOutTypes[4] = {kNone, kBF16, kF16, kF32};  // update kernels
 constexpr int kStateTypes[2] = {kBF16, kF16};
 
-// Update table index: g + 3 * (param kind + 2 * (out + 3 * (mode + 2 * capturable))),
-// with g and out positions in kGradTypes / kOutTypes.
+// Update table index: g + 3 * (param kind + 4 * (out + 4 * (mode + 2 * capturable))),
+// with g and out positions in kGradTypes / kUpdateOutTypes.
 template <int I>
 constexpr UpdateFn update_at()
 {
     constexpr int g = kGradTypes[I % 3];
-    constexpr int pk = (I / 3) % 2;
-    constexpr int ot = kOutTypes[(I / 6) % 3];
-    constexpr int mode = (I / 18) % 2;
-    constexpr bool capt = (I / 36) != 0;
-    if constexpr (pk == kParamRem && ot == kF16)
+    constexpr int pk = (I / 3) % 4;
+    constexpr int ot = kUpdateOutTypes[(I / 12) % 4];
+    constexpr int mode = (I / 48) % 2;
+    constexpr bool capt = (I / 96) != 0;
+    if constexpr (pk == kParamRem && ot != kNone && ot != kBF16)
         return nullptr;  // refused by the planner
     else
         return adam_update<Config<g, pk, ot, mode, capt>>;
@@ -1129,7 +1202,7 @@ UpdateTable<I...> update_table(std::integer_sequence<int, I...>);
 template <int... I>
 ScaledTable<I...> scaled_table(std::integer_sequence<int, I...>);
 
-using UpdateKernels = decltype(update_table(std::make_integer_sequence<int, 72>()));
+using UpdateKernels = decltype(update_table(std::make_integer_sequence<int, 192>()));
 using ScaledKernels = decltype(scaled_table(std::make_integer_sequence<int, 72>()));
 
 int type_pos(const int *types, int n, int t)
@@ -1154,11 +1227,12 @@ struct Plan {
 bool valid_dtype_set(const adam_tl_desc &d)
 {
     const bool g_ok = d.g == ADAM_DT_F32 || d.g == ADAM_DT_BF16 || d.g == ADAM_DT_F16;
+    const bool p16 = d.p == ADAM_DT_BF16 || d.p == ADAM_DT_F16;
     const bool out16 = d.p_out == ADAM_DT_BF16 || d.p_out == ADAM_DT_F16;
-    if (!g_ok || !(d.p_out == ADAM_DT_NONE || out16)) return false;
-    if (d.with_remainders == 1) return d.p == ADAM_DT_BF16 && d.p_out != ADAM_DT_F16;
-    if (d.scaled_state == 1) return d.p == ADAM_DT_BF16 || d.p == ADAM_DT_F16;
-    return d.p == ADAM_DT_F32;
+    if (!g_ok || !(d.p_out == ADAM_DT_NONE || out16 || d.p_out == ADAM_DT_F32)) return false;
+    if (d.with_remainders == 1) return d.p == ADAM_DT_BF16 && (d.p_out == ADAM_DT_NONE || d.p_out == ADAM_DT_BF16);
+    if (d.scaled_state == 1) return p16 && d.p_out != ADAM_DT_F32;
+    return d.p == ADAM_DT_F32 || p16;
 }
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -1214,14 +1288,15 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
     const bool scaled = desc->scaled_state == 1;
     const bool out = desc->p_out != ADAM_DT_NONE;
     const uintptr_t p_size = desc->p == ADAM_DT_F32 ? 4 : 2;
-    const uintptr_t mv_size = scaled ? 2 : 4;
+    const uintptr_t mv_size = desc->p != ADAM_DT_F32 && !rem ? 2 : 4;  // 16-bit or scaled state
     const uintptr_t g_size = desc->g == ADAM_DT_F32 ? 4 : 2;
+    const uintptr_t out_size = desc->p_out == ADAM_DT_F32 ? 4 : 2;
     const int64_t tile = kTile;
 
     adam_tl_stats st = {};
     st.tensors = count;
     st.bytes_per_elem =
-        int32_t(2 * (p_size + (rem ? 2 : 0) + 2 * mv_size) + g_size + (out ? 2 : 0));
+        int32_t(2 * (p_size + (rem ? 2 : 0) + 2 * mv_size) + g_size + (out ? out_size : 0));
     st.block_threads = kBlock;
     st.tile_elems = int32_t(tile);
     st.device = -1;
@@ -1243,12 +1318,12 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
         spans.push_back({uintptr_t(t.v), uintptr_t(t.v) + n * mv_size, false});
         spans.push_back({uintptr_t(t.g), uintptr_t(t.g) + n * g_size, true});
         if (rem) spans.push_back({uintptr_t(t.rem), uintptr_t(t.rem) + n * 2, false});
-        if (out) spans.push_back({uintptr_t(t.p_out), uintptr_t(t.p_out) + n * 2, false});
+        if (out) spans.push_back({uintptr_t(t.p_out), uintptr_t(t.p_out) + n * out_size, false});
         if (scaled) spans.push_back({uintptr_t(t.scales), uintptr_t(t.scales) + 3 * sizeof(float), false});
         // every stream must be naturally aligned for its element type
         if (uintptr_t(t.p) % p_size || uintptr_t(t.m) % mv_size || uintptr_t(t.v) % mv_size ||
             uintptr_t(t.g) % g_size || (rem && uintptr_t(t.rem) % 2) ||
-            (out && uintptr_t(t.p_out) % 2) || (scaled && uintptr_t(t.scales) % 4))
+            (out && uintptr_t(t.p_out) % out_size) || (scaled && uintptr_t(t.scales) % 4))
             return ADAM_EINVAL;
         // The head: the fewest leading elements after which every stream sits
         // on a 128-byte boundary, else on the boundary of its 4-element access
@@ -1259,7 +1334,7 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
                 return (uintptr_t(ptr) + uintptr_t(e) * size) % need == 0;
             };
             return ok(t.p, p_size) && ok(t.m, mv_size) && ok(t.v, mv_size) && ok(t.g, g_size) &&
-                   (!rem || ok(t.rem, 2)) && (!out || ok(t.p_out, 2));
+                   (!rem || ok(t.rem, 2)) && (!out || ok(t.p_out, out_size));
         };
         int64_t head = -1;
         for (int64_t e = 0; e <= kMaxHead && e < t.numel && head < 0; ++e)
@@ -1310,7 +1385,7 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
             w.m = static_cast<char *>(t.m) + e * int64_t(mv_size);
             w.v = static_cast<char *>(t.v) + e * int64_t(mv_size);
             w.g = static_cast<const char *>(t.g) + e * int64_t(g_size);
-            w.p_out = out ? static_cast<char *>(t.p_out) + e * 2 : nullptr;
+            w.p_out = out ? static_cast<char *>(t.p_out) + e * int64_t(out_size) : nullptr;
             w.n = int32_t(std::min(chunk, body - off));
             w.flags = head >= 0 ? kItemVector : 0u;
             w.head = off == 0 && head > 0 ? head : 0;
@@ -1373,9 +1448,12 @@ namespace {
 
 int launch_update(const adam_tl *tl, int mode, bool capturable, const StepArgs &args, hipStream_t stream)
 {
+    const int pk = tl->kind == Kind::Remainders ? kParamRem
+                   : tl->p == kBF16             ? kParamBF16
+                   : tl->p == kF16              ? kParamF16
+                                                : kParamF32;
     const int idx = type_pos(kGradTypes, 3, tl->g) +
-                    3 * ((tl->kind == Kind::Remainders ? kParamRem : kParamF32) +
-                         2 * (type_pos(kOutTypes, 3, tl->out) + 3 * (mode + 2 * int(capturable))));
+                    3 * (pk + 4 * (type_pos(kUpdateOutTypes, 4, tl->out) + 4 * (mode + 2 * int(capturable))));
     const UpdateFn fn = UpdateKernels::fns[idx];
     if (fn == nullptr) return ADAM_EDTYPE;
     hipLaunchKernelGGL(fn, dim3(uint32_t(tl->stats.grid_blocks)), dim3(kBlock), 0, stream,

@@ -542,6 +542,7 @@ def main() -> int:
 
     # one handle per group, views into the flat buffers
     scaled = w.p_kind.endswith("_scaled")
+    mv_desc = "scaled 16-bit" if scaled else w.p_kind if w.p_kind in ("bf16", "f16") else "f32"
     p_out = ("bf16" if w.p_out is True else w.p_out) or None
     handles = []
     scale_bufs = []
@@ -569,7 +570,8 @@ def main() -> int:
         f"{info['grid_blocks']} workgroups of {info['block_threads']} threads, "
         f"{info['tile_elems']} elements each")
 
-    step_fn = {"bf16_rem": A.adam_step_remainders, "f32": A.adam_step}.get(w.p_kind, A.adam_step_scaled)
+    step_fn = {"bf16_rem": A.adam_step_remainders, "bf16_scaled": A.adam_step_scaled,
+               "f16_scaled": A.adam_step_scaled}.get(w.p_kind, A.adam_step)
     stream = torch.cuda.current_stream()
     d_scale = torch.tensor([w.grad_scale], dtype=torch.float32, device="cuda")
 
@@ -634,7 +636,7 @@ def main() -> int:
         "data": "synthetic (p~N(0,1), g~N(0,1)*1e-3, m=v=0; drawn on the GPU)",
         "config": {
             "workload": f"{w.name}: {len(w.sizes)} tensors, {total:,} elements, "
-                        f"p {w.p_kind}, g {w.g_dtype}, m/v {'scaled 16-bit' if scaled else 'f32'}, "
+                        f"p {w.p_kind}, g {w.g_dtype}, m/v {mv_desc}, "
                         f"p_out {p_out or 'none'}, "
                         f"{'AdamW' if w.mode else 'L2'}, lr {w.lr}, betas ({w.beta1}, {w.beta2}), "
                         f"eps {w.eps}, wd {w.weight_decay}",
@@ -653,7 +655,7 @@ def main() -> int:
             "bound": "hbm",
             "kernel": (f"adam_scaled_maxima + fold + adam_scaled_pass + scales (the whole scaled step of the main group; "
                        f"p {w.p_kind}, g {w.g_dtype}, p_out {p_out or 'none'})" if scaled else
-                       f"adam_update (p {w.p_kind}, g {w.g_dtype}, m/v f32, p_out "
+                       f"adam_update (p {w.p_kind}, g {w.g_dtype}, m/v {mv_desc}, p_out "
                        f"{p_out or 'none'}, {'AdamW' if w.mode else 'L2'}, non-capturable)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
@@ -666,9 +668,8 @@ def main() -> int:
     }
 
     # --- capturable, eager and graph -----------------------------------------
-    cap_fn = {"f32": A.adam_step_capturable, "bf16_rem": A.adam_step_remainders_capturable,
-              "bf16_scaled": A.adam_step_scaled_capturable,
-              "f16_scaled": A.adam_step_scaled_capturable}[w.p_kind]
+    cap_fn = {"bf16_rem": A.adam_step_remainders_capturable, "bf16_scaled": A.adam_step_scaled_capturable,
+              "f16_scaled": A.adam_step_scaled_capturable}.get(w.p_kind, A.adam_step_capturable)
     if not args.no_capturable and cap_fn is not None:
         d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
         d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")

@@ -25,7 +25,11 @@
  * float.  The library therefore reproduces a scalar C evaluation of these
  * expressions bit for bit.
  *
- * Two more storage schemes around the same fp32 update:
+ * The param and moment type T may be float, bf16 or fp16 (the functor takes
+ * it from the param list; apex passes its optimizer-state dtype): for a
+ * 16-bit T, p, m and v are widened to float (exactly), updated as above, and
+ * stored rounded to T (nearest even); the param-out copy is the cast of the
+ * new stored param.  Two more storage schemes around the same fp32 update:
  *   - remainders (apex _bf16_rem_to_fp32): bf16 params plus int16 low halves
  *     hold the fp32 master exactly;
  *   - scaled 16-bit state (apex distributed_fused_adam.py,
@@ -57,7 +61,7 @@
 extern "C" {
 #endif
 
-#define ADAM_ABI_VERSION 3
+#define ADAM_ABI_VERSION 4
 
 typedef enum {
     ADAM_OK = 0,
@@ -79,13 +83,14 @@ typedef enum {
  * g is only read; p_out is only written.  The layout is the apex tensor-list
  * order [p, m, v, g, p_out] (remainder mode: [p, rem, m, v, g, p_out]). */
 typedef struct {
-    void *p;          /* device: float; bf16 bits (remainder mode); bf16 or fp16
-                         (scaled state, the handle's p dtype)                     */
+    void *p;          /* device: the handle's p dtype: float, bf16 or fp16 (bf16
+                         bits in remainder mode)                                  */
     int16_t *rem;     /* device: int16 remainders (remainder mode), else NULL      */
-    void *m;          /* device: first moment: float, or p's 16-bit type (scaled)  */
-    void *v;          /* device: second moment: float, or p's 16-bit type (scaled) */
+    void *m;          /* device: first moment: float, or p's 16-bit type (16-bit
+                         or scaled state)                                         */
+    void *v;          /* device: second moment: as m                               */
     const void *g;    /* device: gradient: float, bf16 or fp16 bits                */
-    void *p_out;      /* device: bf16 or fp16 copy of the new param, or NULL       */
+    void *p_out;      /* device: float, bf16 or fp16 copy of the new param, or NULL */
     float *scales;    /* device: scaled state only: float[3] = the scales of p, m,
                          v (stored value x scale = fp32 value), read and replaced
                          by each step; NULL otherwise                             */
@@ -95,11 +100,13 @@ typedef struct {
 /* The dtypes shared by every tensor of one handle, and the work-table
  * granularity. */
 typedef struct {
-    adam_dtype p;            /* ADAM_DT_F32; ADAM_DT_BF16 with remainders;
-                                ADAM_DT_BF16 or ADAM_DT_F16 with scaled state  */
+    adam_dtype p;            /* ADAM_DT_F32, ADAM_DT_BF16 or ADAM_DT_F16 (a
+                                16-bit p means 16-bit m and v too); BF16 with
+                                remainders; BF16 or F16 with scaled state      */
     adam_dtype g;            /* ADAM_DT_F32, ADAM_DT_BF16 or ADAM_DT_F16         */
-    adam_dtype p_out;        /* ADAM_DT_NONE, ADAM_DT_BF16 or ADAM_DT_F16 (not
-                                F16 with remainders)                            */
+    adam_dtype p_out;        /* ADAM_DT_NONE, ADAM_DT_F32, ADAM_DT_BF16 or
+                                ADAM_DT_F16 (remainders: NONE or BF16; scaled
+                                state: not F32)                                 */
     int32_t with_remainders; /* 1: p is bf16 and rem holds the low fp32 halves  */
     int64_t chunk_elems;     /* elements per work-table record: 0 = automatic
                                 (the largest power of two <= 65536 that wastes
@@ -155,7 +162,8 @@ const char *adam_status_string(int status);
  * overlap (gradients may overlap other gradients; no other pair may share a
  * byte; a tensor's scales are written too); ADAM_EDTYPE for an unsupported
  * dtype set.  Supported sets (g F32|BF16|F16 in each):
- *   - fp32 master: p F32, p_out NONE|BF16|F16;
+ *   - fp32 state: p F32 (m, v float), p_out NONE|F32|BF16|F16;
+ *   - 16-bit state: p BF16|F16 (m, v the same type), p_out NONE|F32|BF16|F16;
  *   - remainders: p BF16, p_out NONE|BF16 (apex: bf16 params need fp32
  *     optimizer state for the remainder scheme; p_out is the new bf16);
  *   - scaled state: p BF16|F16 (m and v the same type), p_out NONE|BF16|F16
@@ -182,7 +190,8 @@ void adam_tl_destroy(adam_tl *tl);
 /* Copies a handle's statistics to *stats (host). ADAM_EINVAL on NULL. */
 int adam_tl_info(const adam_tl *tl, adam_tl_stats *stats);
 
-/* Non-capturable step on an fp32-param handle.
+/* Non-capturable step on a handle with fp32 or 16-bit state (no remainders,
+ * no scales).
  *   lr          host value.
  *   step_io     host int32 counter: incremented first (the first update uses
  *               t = 1), also when the handle has no elements.  ADAM_EINVAL if
@@ -197,9 +206,10 @@ int adam_tl_info(const adam_tl *tl, adam_tl_stats *stats);
 int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
               float grad_scale, const float *d_grad_scale, hipStream_t stream);
 
-/* Capturable step on an fp32-param handle: every per-step scalar lives in
- * device memory, nothing is allocated, nothing is read back, and the host
- * never waits, so the call can be recorded into a HIP graph and replayed.
+/* Capturable step on a handle with fp32 or 16-bit state: every per-step
+ * scalar lives in device memory, nothing is allocated, nothing is read back,
+ * and the host never waits, so the call can be recorded into a HIP graph and
+ * replayed.
  *   d_lr          device float.
  *   d_step        device int32 counter; advanced by one on the device after
  *                 the update, unless *d_noop == 1 (int32 wrap-around).

@@ -140,5 +140,5 @@ def desc_for(host: Sequence[HostTensor], **kw):
     elif h.scales is not None:
         p = _short(h.p) + "_scaled"
     else:
-        p = "f32"
+        p = _short(h.p)  # "f32", or 16-bit state "bf16" / "f16"
     return A.make_desc(g=_short(h.g), p=p, p_out=_short(h.p_out), **kw)

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (adam_\w+)$", out, flags=re.M))
     assert set(names) <= exported
-    assert L.adam_abi_version() == 3
+    assert L.adam_abi_version() == 4
 
 
 def test_status_strings():
@@ -170,11 +170,13 @@ def test_plan_rejects_unsupported_dtypes():
     ts = fake_tensors([64])
     desc = A.make_desc()
     # (p, g, p_out, with_remainders, scaled_state)
-    for p, g, o, r, sc in [(A.DT_BF16, A.DT_F32, A.DT_NONE, 0, 0), (A.DT_F32, A.DT_NONE, A.DT_NONE, 0, 0),
-                           (A.DT_F32, A.DT_F32, A.DT_F32, 0, 0), (A.DT_F32, A.DT_F32, A.DT_NONE, 1, 0),
+    for p, g, o, r, sc in [(A.DT_NONE, A.DT_F32, A.DT_NONE, 0, 0), (A.DT_F32, A.DT_NONE, A.DT_NONE, 0, 0),
+                           (A.DT_F32, A.DT_F32, 7, 0, 0), (A.DT_F32, A.DT_F32, A.DT_NONE, 1, 0),
                            (7, A.DT_F32, A.DT_NONE, 0, 0), (A.DT_F32, 7, A.DT_NONE, 0, 0),
                            (A.DT_BF16, A.DT_BF16, A.DT_F16, 1, 0),   # remainder p_out is bf16
+                           (A.DT_BF16, A.DT_BF16, A.DT_F32, 1, 0),
                            (A.DT_F32, A.DT_F32, A.DT_NONE, 0, 1),    # scaled state is 16-bit
+                           (A.DT_F16, A.DT_F32, A.DT_F32, 0, 1),     # scaled param-sync is 16-bit
                            (A.DT_F16, A.DT_F32, A.DT_NONE, 1, 0)]:   # remainders are bf16
         d = A.AdamTlDesc(p, g, o, r, 0, sc, 0)
         arr = A._tensor_array(ts, desc)
@@ -214,6 +216,27 @@ def test_fp16_and_scaled_state_plans():
     # 16-bit m and v: 8-byte alignment is enough for the vector path
     ts = fake_tensors([100], scaled=True, offsets={0: {"p": 8, "m": 8, "v": 8, "g": 8}})
     assert plan(ts, g="bf16", p="f16_scaled")["vector_tensors"] == 1
+
+
+def test_state16_and_fp32_param_out_plans():
+    """16-bit state (p, m, v all bf16 or fp16) and an fp32 param-out: the
+    pages' functor takes the param and moment type from the param list and
+    casts to any param-out type.  Bytes per element follow the element
+    sizes; the fp32 param-out needs 16-byte alignment for the vector path."""
+    for p in ("bf16", "f16"):
+        assert plan(fake_tensors([8]), g="bf16", p=p)["bytes_per_elem"] == 14
+        assert plan(fake_tensors([8], out=True), g="bf16", p=p, p_out="bf16")["bytes_per_elem"] == 16
+        assert plan(fake_tensors([8], out=True), g="f32", p=p, p_out="f32")["bytes_per_elem"] == 20
+        assert status_of(fake_tensors([8], rem=True), g="bf16", p=p) == A.ADAM_EINVAL  # rem without mode
+        assert status_of(fake_tensors([8], scaled=True), g="bf16", p=p) == A.ADAM_EINVAL
+        # 16-bit m and v: 8-byte alignment is enough for the vector path
+        ts = fake_tensors([100], offsets={0: {"p": 8, "m": 8, "v": 8, "g": 8}})
+        assert plan(ts, g="bf16", p=p)["vector_tensors"] == 1
+    assert plan(fake_tensors([8], out=True), p_out="f32")["bytes_per_elem"] == 32
+    ts = fake_tensors([100], out=True, offsets={0: {"p_out": 8}})  # 8 bytes off for a float stream
+    assert plan(ts, p_out="f32")["vector_tensors"] == 0
+    ts = fake_tensors([100], out=True, offsets={0: {"p_out": 2}})  # not float-aligned
+    assert status_of(ts, p_out="f32") == A.ADAM_EINVAL
 
 
 def test_plan_rejects_overlapping_buffers():

@@ -461,3 +461,89 @@ def test_scaled_capturable_graph_replay(torch, orc):
         assert_bitwise(dev.readback(), ref, ctx=f"replay lr {lr} noop {noop}")
     assert int(d_step.item()) == st[0] == 3
     tl.destroy()
+
+
+# ---------------------------------------------------------------------------
+# 16-bit state (p, m, v all bf16 or all fp16) and the fp32 param-out
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("p_kind", ["bf16", "f16"])
+@pytest.mark.parametrize("g_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("p_out", [None, "f32", "bf16", "f16"])
+def test_state16_matches_the_oracle(torch, orc, p_kind, g_dtype, p_out):
+    """Every gradient and param-out type with bf16 and fp16 state, three steps
+    (L2 for fp16 state, AdamW for bf16), bitwise: p, m, v rounded to the
+    state type, the param-out cast from the new stored param."""
+    host = host_tensors(SIZES, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out or False, seed=96,
+                        m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 0 if p_kind == "f16" else 1)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 3, grad_scale=0.5)
+    assert_bitwise(got, ref, ctx=f"{p_kind}/{g_dtype}/{p_out}")
+
+
+def test_state16_fp16_range_edges(torch, orc):
+    """fp16 state next to fp16's limits: params at and near 65504 (the update
+    can round them to infinity), subnormal second moments and first moments,
+    and gradients that make v overflow."""
+    host = host_tensors([4096, 1000, 33], g_dtype="f32", p_kind="f16", p_out="f32", seed=97,
+                        m_v_init="random")
+    t = host[0]
+    t.p[:8] = np.array([65504.0, -65504.0, 65472.0, 65000.0, 6.1e-5, 6e-8, -6e-8, 0.0], np.float16)
+    t.g[:8] = np.array([-1.0, 1.0, -1e3, 300.0, 1e-7, 1e-9, 1e-30, 0.0], np.float32)
+    t.m[8:16] = np.float16(6e-8)
+    t.v[8:16] = np.float16(6e-8)
+    host[1].g[:] = np.float32(500.0)  # v' = 0.05 * 500^2 > 65504: infinity
+    for mode in (0, 1):
+        hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+        got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
+        assert_bitwise(got, ref, ctx=f"mode {mode}")
+
+
+@pytest.mark.parametrize("p_kind,p_out", [("bf16", "bf16"), ("f16", "f32")])
+def test_state16_capturable_noop_and_graph_replay(torch, orc, p_kind, p_out):
+    """The capturable step on 16-bit state: eager calls with device lr and a
+    noop step, then the call recorded in a graph and replayed, every result
+    against the oracle."""
+    host = host_tensors([70001, 4096, 513], g_dtype="bf16", p_kind=p_kind, p_out=p_out, seed=98,
+                        m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    ref = copies(host)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    d_lr = torch.zeros(1, dtype=torch.float32, device="cuda")
+    d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ot, st = oracle_tensors(ref), [0]
+    for lr, noop in [(1e-3, 0), (2e-3, 1), (1.6e-3, 0)]:
+        d_lr.fill_(lr)
+        d_noop.fill_(noop)
+        A.adam_step_capturable(tl, hl, d_lr, d_step, None, d_noop)
+        orc.group_step(ot, hr, lr, st, 1.0, noop=noop)
+    torch.cuda.synchronize()
+    assert_bitwise(dev.readback(), ref, ctx="eager")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        A.adam_step_capturable(tl, hl, d_lr, d_step, None, d_noop)
+    torch.cuda.synchronize()
+    for lr, noop in [(5e-4, 0), (1e-3, 1), (2e-3, 0)]:
+        d_lr.fill_(lr)
+        d_noop.fill_(noop)
+        graph.replay()
+        torch.cuda.synchronize()
+        orc.group_step(ot, hr, lr, st, 1.0, noop=noop)
+        assert_bitwise(dev.readback(), ref, ctx=f"replay {lr} {noop}")
+    assert int(d_step.item()) == st[0] == 4
+    tl.destroy()
+
+
+def test_fp32_param_out_is_the_new_param(torch, orc):
+    """fp32 params with an fp32 param-out: the copy equals the new param bit
+    for bit, and both equal the oracle."""
+    host = host_tensors(SIZES, g_dtype="bf16", p_kind="f32", p_out="f32", seed=99, m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
+    assert_bitwise(got, ref)
+    for t in got:
+        assert np.array_equal(t.p_out.view(np.uint32), t.p.view(np.uint32))

@@ -253,6 +253,13 @@ def test_scaled_state_zero_shard(torch, capturable):
     tl.destroy()
 
 
+def test_state16_shard_capturable_with_noop(torch):
+    """The ZeRO shard with bf16 optimizer state (p, m, v), bf16 gradients and
+    a bf16 param-sync copy through the capturable step, noop on every 4th
+    step."""
+    run_sampled(torch, "state16_1e9", 12, capturable=True, noop_every=4, seed=11)
+
+
 def test_remainders_capturable_with_noop(torch):
     """The remainder workload through the capturable remainder step, noop on
     every 4th step."""

@@ -77,7 +77,8 @@ SWEEP_SIZES = list(range(0, 68)) + [4095, 4096, 4097, 4096 * 3 + 5, 10000, 65537
     ("bf16", "f32", True, 0), ("f32", "f32", True, 1), ("bf16", "bf16_rem", False, 1),
     ("f32", "bf16_rem", True, 0), ("bf16", "bf16_rem", True, 1), ("f16", "f32", "f16", 1),
     ("f16", "bf16_rem", True, 0), ("bf16", "f16_scaled", "f16", 1), ("f32", "f16_scaled", False, 0),
-    ("f16", "bf16_scaled", "bf16", 1)])
+    ("f16", "bf16_scaled", "bf16", 1), ("bf16", "bf16", True, 1), ("f32", "f16", "f32", 0),
+    ("f16", "f16", "bf16", 1), ("bf16", "bf16", "f16", 0), ("f32", "f32", "f32", 1), ("bf16", "f16", False, 1)])
 def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
     """Every size 0..67 plus sizes around and across work-item boundaries, with
     each buffer of each tensor at its own element offset 0..7 (so some tensors
@@ -101,7 +102,8 @@ def test_tail_and_offset_sweep(torch, orc, g_dtype, p_kind, p_out, mode):
 
 @pytest.mark.parametrize("g_dtype,p_kind,p_out,mode", [
     ("f32", "f32", False, 1), ("bf16", "f32", True, 0), ("bf16", "bf16_rem", False, 1),
-    ("f32", "bf16_rem", True, 1), ("f16", "f32", "f16", 1), ("bf16", "f16_scaled", "bf16", 0)])
+    ("f32", "bf16_rem", True, 1), ("f16", "f32", "f16", 1), ("bf16", "f16_scaled", "bf16", 0),
+    ("bf16", "bf16", True, 1), ("f16", "f16", "f32", 0), ("f32", "f32", "f32", 1)])
 def test_shared_offsets_take_the_peeled_vector_path(torch, orc, g_dtype, p_kind, p_out, mode):
     """Every stream of a tensor at the same element offset 0..7 (views at one
     offset into flat buffers): the leading elements before the first lane
@@ -140,7 +142,7 @@ def tile_elems(g_dtype="f32", p_kind="f32", p_out=False):
 
 @pytest.mark.parametrize("g_dtype,p_kind,p_out", [
     ("f32", "f32", False), ("bf16", "f32", True), ("bf16", "bf16_rem", False), ("f16", "f32", "f16"),
-    ("bf16", "f16_scaled", "f16")])
+    ("bf16", "f16_scaled", "f16"), ("bf16", "bf16", True), ("f16", "f16", "f32")])
 @pytest.mark.parametrize("layout,chunk", [("aligned", 0), ("aligned", 4096), ("shared", 0)])
 def test_every_tail_length(torch, orc, g_dtype, p_kind, p_out, layout, chunk):
     """One tensor per tail length: a full tile plus 0..tile-1 elements, so the

@@ -1,5 +1,6 @@
-"""Seeded random GPU parity cases: each case draws a dtype set (fp32 master,
-remainders, scaled state; fp32 / bf16 / fp16 gradients and param-out), tensor
+"""Seeded random GPU parity cases: each case draws a dtype set (fp32 or 16-bit
+state, remainders, scaled state; fp32 / bf16 / fp16 gradients; no, fp32,
+bf16 or fp16 param-out as the storage allows), tensor
 sizes (empty, tiny, ragged, several work items), a layout (aligned, one
 shared element offset per tensor, or independent offsets per stream),
 hyperparameters (L2 or AdamW, bias correction on or off, betas near 1 or
@@ -21,7 +22,9 @@ pytestmark = pytest.mark.gpu
 CASES = 96
 
 STORAGE = [  # (p_kind, allowed gradient types, allowed param-out)
-    ("f32", ("f32", "bf16", "f16"), (None, "bf16", "f16")),
+    ("f32", ("f32", "bf16", "f16"), (None, "bf16", "f16", "f32")),
+    ("bf16", ("f32", "bf16", "f16"), (None, "bf16", "f16", "f32")),
+    ("f16", ("f32", "bf16", "f16"), (None, "bf16", "f16", "f32")),
     ("bf16_rem", ("f32", "bf16", "f16"), (None, "bf16")),
     ("f16_scaled", ("f32", "bf16", "f16"), (None, "bf16", "f16")),
     ("bf16_scaled", ("f32", "bf16", "f16"), (None, "bf16", "f16")),
@@ -63,7 +66,7 @@ def draw_case(k):
     device_scale = bool(rng.random() < 0.5)
     chunk = int(rng.choice([0, 1024, 4096, 65536]))
     steps = int(rng.integers(1, 5))
-    capturable = p_kind in ("f32", "bf16_rem") and bool(rng.random() < 0.4)
+    capturable = bool(rng.random() < 0.4)
     noops = [int(rng.random() < 0.3) for _ in range(steps)] if capturable else [0] * steps
     return dict(p_kind=p_kind, g_dtype=g_dtype, p_out=p_out, sizes=sizes, layout=layout, mode=mode,
                 bias_correction=bias_correction, beta1=beta1, beta2=beta2, eps=eps, wd=wd, lr=lr,
@@ -101,7 +104,8 @@ def test_random_case(torch, orc, k):
         d_lr = torch.tensor([c["lr"]], dtype=torch.float32, device="cuda")
         d_step = torch.zeros(1, dtype=torch.int32, device="cuda")
         d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
-        fn = A.adam_step_remainders_capturable if c["p_kind"] == "bf16_rem" else A.adam_step_capturable
+        fn = {"bf16_rem": A.adam_step_remainders_capturable, "f16_scaled": A.adam_step_scaled_capturable,
+              "bf16_scaled": A.adam_step_scaled_capturable}.get(c["p_kind"], A.adam_step_capturable)
         for noop in c["noops"]:
             d_noop.fill_(noop)
             fn(tl, hp, d_lr, d_step, d_scale, d_noop)
@@ -109,7 +113,8 @@ def test_random_case(torch, orc, k):
         torch.cuda.synchronize()
         assert int(d_step.item()) == ref_step[0] == c["steps"] - sum(c["noops"])
     else:
-        fn = {"f32": A.adam_step, "bf16_rem": A.adam_step_remainders}.get(c["p_kind"], A.adam_step_scaled)
+        fn = {"bf16_rem": A.adam_step_remainders, "f16_scaled": A.adam_step_scaled,
+              "bf16_scaled": A.adam_step_scaled}.get(c["p_kind"], A.adam_step)
         step = A.HostStep(0)
         for _ in range(c["steps"]):
             if c["device_scale"]:

@@ -40,8 +40,9 @@ class Workload:
     name: str
     sizes: Tuple[int, ...]                 # elements per tensor (group 0)
     g_dtype: str                           # "f32", "bf16" or "f16"
-    p_kind: str                            # "f32", "bf16_rem", "bf16_scaled" or "f16_scaled"
-    p_out: object                          # False, True / "bf16", or "f16": param-out copy
+    p_kind: str                            # "f32", "bf16" / "f16" (16-bit p, m, v), "bf16_rem",
+                                           # "bf16_scaled" or "f16_scaled"
+    p_out: object                          # False, True / "bf16", "f16" or "f32": param-out copy
     lr: float
     beta1: float
     beta2: float
@@ -61,12 +62,13 @@ class Workload:
     def bytes_per_elem(self) -> int:
         """Algorithmic HBM bytes per element: every state word is read once and
         written once; the gradient is read once."""
-        scaled = self.p_kind.endswith("_scaled")
-        p = 2 if scaled else 4  # fp32 p, bf16 p + int16 rem, or a scaled 16-bit p
-        mv = 2 if scaled else 4
+        state16 = self.p_kind.endswith("_scaled") or self.p_kind in ("bf16", "f16")
+        p = 2 if state16 else 4  # fp32 p, bf16 p + int16 rem, or a 16-bit p
+        mv = 2 if state16 else 4
         g = 4 if self.g_dtype == "f32" else 2
+        out = {None: 0, "f32": 4}.get(_out_type(self.p_out), 2)
         read = p + 2 * mv + g
-        write = p + 2 * mv + (2 if self.p_out else 0)
+        write = p + 2 * mv + out
         return read + write
 
 
@@ -172,6 +174,12 @@ def workloads() -> dict:
         "scaled1e9": Workload("scaled1e9", zero_bucket_sizes(), "bf16", "f16_scaled", "bf16",
                               lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
                               weight_decay=0.1, mode=1, seed=7),
+        # the ZeRO shard with the optimizer state in bf16 (p, m, v), bf16
+        # gradients and a bf16 param-sync copy (apex's gradient and param-sync
+        # dtypes default to the state dtype): 16 B/elem
+        "state16_1e9": Workload("state16_1e9", zero_bucket_sizes(), "bf16", "bf16", "bf16",
+                                lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                                weight_decay=0.1, mode=1, seed=8),
     }
 
 
@@ -220,7 +228,7 @@ def _to_state(x: np.ndarray, state: str, role: str):
 
 
 def _out_type(p_out) -> Optional[str]:
-    """p_out option: False/None (absent), True or "bf16", or "f16"."""
+    """p_out option: False/None (absent), True or "bf16", "f16", or "f32"."""
     if p_out is None or p_out is False:
         return None
     return "bf16" if p_out is True else p_out
@@ -235,10 +243,11 @@ def host_tensors(sizes: Sequence[int], *, g_dtype: str = "f32", p_kind: str = "f
     state part-way through training); ``"large"`` draws m ~ N(0,1)*4 and
     v ~ |N(0,1)|*4 + 1.  Remainder params (p_kind "bf16_rem"): bf16 p drawn as
     the cast of N(0,1) and the int16 remainder uniform over all 65536 values,
-    so every (bf16, remainder) pair is a valid master weight.  Scaled state
+    so every (bf16, remainder) pair is a valid master weight.  16-bit state
+    (p_kind "bf16" / "f16"): p, m, v are the casts of the fp32 draws.  Scaled state
     (p_kind "bf16_scaled" / "f16_scaled"): p, m, v stored as T(x * 2^k) with
     scale 2^-k (zero moments get scale 0, as a fresh optimizer has them).
-    p_out: False, True / "bf16", or "f16"."""
+    p_out: False, True / "bf16", "f16", or "f32"."""
     rng = np.random.default_rng(seed)
     out_type = _out_type(p_out)
     out = []
@@ -261,6 +270,9 @@ def host_tensors(sizes: Sequence[int], *, g_dtype: str = "f32", p_kind: str = "f
         rem = scales = None
         if p_kind == "f32":
             p = p32
+        elif p_kind in ("bf16", "f16"):  # 16-bit state: p, m, v of one 16-bit type
+            cast = (lambda x: x.astype(np.float16)) if p_kind == "f16" else _to_bf16_bits
+            p, m, v = cast(p32), cast(m), cast(v)
         elif p_kind == "bf16_rem":
             p = _to_bf16_bits(p32)
             rem = rng.integers(-32768, 32768, size=n, dtype=np.int64).astype(np.int16)
@@ -272,7 +284,8 @@ def host_tensors(sizes: Sequence[int], *, g_dtype: str = "f32", p_kind: str = "f
             if m_v_init == "zero":
                 sm = sv = np.float32(0.0)
             scales = np.array([sp, sm, sv], np.float32)
-        po = None if out_type is None else np.zeros(n, np.float16 if out_type == "f16" else np.uint16)
+        po = None if out_type is None else np.zeros(n, {"f16": np.float16, "bf16": np.uint16,
+                                                         "f32": np.float32}[out_type])
         out.append(HostTensor(p, m, v, g, po, rem, scales))
     return out
 
@@ -305,7 +318,7 @@ def device_flat(total: int, *, g_dtype: str, p_kind: str, p_out, seed: int,
         bufs["rem"] = torch.empty(total, dtype=torch.int16, device=device)
     else:
         bufs["p"] = torch.empty(total, dtype=tdt[p_kind.split("_")[0]], device=device)
-    mv = bufs["p"].dtype if scaled else torch.float32
+    mv = bufs["p"].dtype if scaled or p_kind in ("bf16", "f16") else torch.float32
     bufs["m"] = torch.zeros(total, dtype=mv, device=device)
     bufs["v"] = torch.zeros(total, dtype=mv, device=device)
     bufs["g"] = torch.empty(total, dtype=tdt[g_dtype], device=device)
