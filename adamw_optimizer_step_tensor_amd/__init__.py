@@ -30,7 +30,10 @@ allocated and in place)::
     A.adam_clip_grad_scale(d_sumsq, d_scale, max_norm=1.0, d_noop=d_noop)
     A.adam_step_capturable(tl, hp, d_lr, d_step, d_scale, d_noop)
 
-Remainder storage uses ``make_desc(p="bf16_rem")`` with an int16 ``rem`` per
+16-bit state (p, m, v all bf16 or all fp16) uses ``make_desc(p="bf16")`` (or
+``"f16"``) with the same ``adam_step`` / ``adam_step_capturable``; any
+param-out type, fp32 included, goes with fp32 or 16-bit state.  Remainder
+storage uses ``make_desc(p="bf16_rem")`` with an int16 ``rem`` per
 tensor and ``adam_step_remainders`` (or ``..._capturable``); scaled 16-bit
 state uses ``make_desc(p="f16_scaled")`` (or ``"bf16_scaled"``) with a
 float32[3] ``scales`` per tensor and ``adam_step_scaled`` (or ``..._capturable``).
