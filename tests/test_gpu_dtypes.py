@@ -484,7 +484,8 @@ def test_state16_matches_the_oracle(torch, orc, p_kind, g_dtype, p_out):
 def test_state16_fp16_range_edges(torch, orc):
     """fp16 state next to fp16's limits: params at and near 65504 (the update
     can round them to infinity), subnormal second moments and first moments,
-    and gradients that make v overflow."""
+    gradients that make v overflow, and a NaN and an infinite gradient (the
+    non-capturable step propagates them)."""
     host = host_tensors([4096, 1000, 33], g_dtype="f32", p_kind="f16", p_out="f32", seed=97,
                         m_v_init="random")
     t = host[0]
@@ -492,7 +493,26 @@ def test_state16_fp16_range_edges(torch, orc):
     t.g[:8] = np.array([-1.0, 1.0, -1e3, 300.0, 1e-7, 1e-9, 1e-30, 0.0], np.float32)
     t.m[8:16] = np.float16(6e-8)
     t.v[8:16] = np.float16(6e-8)
+    t.g[20], t.g[21] = np.float32(np.nan), np.float32(np.inf)
     host[1].g[:] = np.float32(500.0)  # v' = 0.05 * 500^2 > 65504: infinity
+    for mode in (0, 1):
+        hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+        got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
+        assert_bitwise(got, ref, ctx=f"mode {mode}")
+
+
+def test_state16_bf16_nonfinite_and_tiny(torch, orc):
+    """bf16 state with a NaN and an infinite gradient, subnormal bf16 moments
+    and params of very different magnitudes, with an fp16 param-out (which
+    overflows for the large ones)."""
+    host = host_tensors([4096, 333], g_dtype="bf16", p_kind="bf16", p_out="f16", seed=100,
+                        m_v_init="random")
+    t = host[0]
+    t.g[5], t.g[6] = np.uint16(0x7FC0), np.uint16(0x7F80)  # NaN, +inf
+    t.m[100:110] = np.uint16(0x0001)  # smallest subnormal
+    t.v[100:110] = np.uint16(0x0001)
+    t.p[200:210] = np.array([0x7F00, 0xFF00, 0x4780, 0x0080, 0x8080, 0x3F80, 0x5000, 0x1000, 0x0001, 0x8001],
+                            np.uint16)
     for mode in (0, 1):
         hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
         got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 2)
