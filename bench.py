@@ -79,13 +79,13 @@ def measured_traffic(workload: str):
 # writable directory the rocprofv3 CSV output goes to.
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_{w} "
-             "-o run -- python3 <repo>/bench.py --workload {w} --steps 10 --warmup 2 --no-cpu",
+             "-o run -- python3 <repo>/bench.py --workload {w} > <out>/trace_{w}.log",
     "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_{w} "
              "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
     "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_{w} "
              "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
     "summary": "python bench.py --summarize-profiles --workload {w} --trace-dir <out>/trace_{w} "
-               "--fetch-dir <out>/pmc_fetch_{w} --write-dir <out>/pmc_write_{w}",
+               "--trace-log <out>/trace_{w}.log --fetch-dir <out>/pmc_fetch_{w} --write-dir <out>/pmc_write_{w}",
     "valu": "cd /tmp && rocprofv3 --pmc SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVES GRBM_GUI_ACTIVE "
             "--output-format csv -d <out>/pmc_valu_{w} -o run -- python3 <repo>/bench.py "
             "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
@@ -276,7 +276,7 @@ def _short(name: str) -> str:
     return base + (f"[{m.group(1)}]" if m else "")
 
 
-def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> None:
+def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_log: str = None) -> None:
     """Writes profiles/<kernel>_<workload>_{kernel_trace,pmc}.txt (kernel
     adam_update, or adam_scaled for scaled state) and updates
     profiles/traffic.json from rocprofv3 CSV output.
@@ -288,7 +288,11 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
     the same counter agree with the known bytes of a plain elementwise kernel
     in the same run: torch's in-place multiply that scales the gradient while
     the inputs are drawn, which reads and writes every element of an fp32
-    buffer of the workload's size once."""
+    buffer of the workload's size once.
+
+    With `trace_log` (the bench line the traced command printed), the
+    launch durations bench.py measured with HIP events in that same process
+    are set beside the trace's averages for the same dispatches."""
     import csv
 
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -333,6 +337,28 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str) -> Non
         passes = [statistics.mean(d) for (name, grid), d in per.items() if grid == big]
         lines.append(f"both passes of one step: {sum(passes):.3f} ms; algorithmic bytes per step "
                      f"{algo / 1e9:.3f} GB -> {algo / (sum(passes) * 1e-3) / 1e9:.1f} GB/s")
+    if trace_log:
+        bench_line = None
+        for line in open(trace_log):
+            if line.startswith("{"):
+                bench_line = json.loads(line)
+        assert bench_line is not None, f"no bench line in {trace_log}"
+        lines += ["", "bench.py in the same traced process (HIP events on the launch stream) vs the "
+                      "trace's average over the same main-group dispatches:"]
+        if scaled:
+            pairs = [("scaled step (both passes + fold + scales)", bench_line["roofline"]["launch_ms_mean"],
+                      sum(statistics.mean(d) for (n, g), d in per.items() if g == big))]
+        else:
+            def trace_avg(capt):
+                d = [x for (n, g), v in per.items() if g == big and n.endswith(f"{capt}>") for x in v]
+                return statistics.mean(d) if d else float("nan")
+            pairs = [("update, regular", bench_line["roofline"]["launch_ms_mean"], trace_avg("false"))]
+            if "capturable" in bench_line:
+                pairs.append(("update, capturable", bench_line["capturable"]["launch_ms_mean"], trace_avg("true")))
+        for what, ev, tr in pairs:
+            lines.append(f"  {what:42s} events {ev:9.3f} ms   trace {tr:9.3f} ms   events / trace {ev / tr:.4f}")
+        lines.append(f"  bench line of the traced run: value {bench_line['value']} {bench_line['unit']}, "
+                     f"ms/step {bench_line['ms_per_step']}, roofline.achieved {bench_line['roofline']['achieved']}")
     trace_path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_kernel_trace.txt")
     with open(trace_path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -479,6 +505,7 @@ def main() -> int:
     ap.add_argument("--summarize-profiles", action="store_true",
                     help="write profiles/ summaries from rocprofv3 CSV directories (no GPU)")
     ap.add_argument("--trace-dir")
+    ap.add_argument("--trace-log", help="stdout of the traced bench command (its bench line)")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--summarize-valu", action="store_true",
@@ -496,7 +523,8 @@ def main() -> int:
     if args.summarize_profiles:
         from workloads import workloads
 
-        summarize_profiles(workloads()[args.workload], args.trace_dir, args.fetch_dir, args.write_dir)
+        summarize_profiles(workloads()[args.workload], args.trace_dir, args.fetch_dir, args.write_dir,
+                           args.trace_log)
         return 0
     if args.summarize_valu:
         from workloads import workloads
