@@ -430,11 +430,12 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
     print("\n".join(open(trace_path).read().splitlines() + [""] + open(pmc_path).read().splitlines()))
 
 
-def cpu_baseline(w, sample_elems: int, sample_steps: int) -> dict:
+def cpu_baseline(w, sample_elems: int, sample_steps: int, target_s: float = 10.0) -> dict:
     """The oracle on whole tensors from the start of the workload's list (at
     least `sample_elems` elements, with the workload's dtypes) for
-    `sample_steps` steps, on the host's cores: one thread per core, each on
-    a contiguous slice of the concatenated sample."""
+    `sample_steps` steps (0: as many as fill about `target_s` seconds of
+    wall time, judged from the first step), on the host's cores: one thread
+    per core, each on a contiguous slice of the concatenated sample."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -469,11 +470,19 @@ def cpu_baseline(w, sample_elems: int, sample_steps: int) -> dict:
         jobs = [lambda bc1, bc2, b=b: o.update_tensor(t, hp, w.lr, bc1, bc2, w.grad_scale, b[0], b[1])
                 for b in bounds]
     del host
+    cores = min(cores, len(jobs))  # the threads that get work
     t0 = time.perf_counter()
     with ThreadPoolExecutor(cores) as ex:
-        for step in range(1, sample_steps + 1):
+        step = 0
+        while True:
+            step += 1
             bc1, bc2 = o.bias_corrections(w.beta1, w.beta2, step, 1)
             list(ex.map(lambda job: job(bc1, bc2), jobs))
+            if step == 1 and sample_steps <= 0:
+                first = time.perf_counter() - t0
+                sample_steps = max(2, min(1000, int(target_s / max(first, 1e-6))))
+            if step >= sample_steps:
+                break
     dt = time.perf_counter() - t0
     gbps = n * sample_steps * w.bytes_per_elem / dt / 1e9
     cpu_model = ""
@@ -487,7 +496,8 @@ def cpu_baseline(w, sample_elems: int, sample_steps: int) -> dict:
         pass
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"first {len(sizes)} of {len(w.sizes)} tensors ({n:,} elements, workload dtypes) x "
-                      f"{sample_steps} steps: {n * sample_steps:,} element updates in {dt:.2f} s wall",
+                      f"{sample_steps} steps: {n * sample_steps:,} element updates in {dt:.2f} s wall "
+                      f"({dt * cores:.0f} thread-seconds)",
             "elements_per_s": round(n * sample_steps / dt, 1), "cpu_model": cpu_model}
 
 
@@ -499,7 +509,8 @@ def main() -> int:
     ap.add_argument("--workload", default="bench201")
     ap.add_argument("--chunk-elems", type=int, default=0)
     ap.add_argument("--cpu-elements", type=int, default=200_000_000)
-    ap.add_argument("--cpu-steps", type=int, default=16)
+    ap.add_argument("--cpu-steps", type=int, default=0,
+                    help="oracle steps for the CPU baseline (0: about 10 s of wall time)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-capturable", action="store_true")
     ap.add_argument("--summarize-profiles", action="store_true",
