@@ -37,6 +37,13 @@ storage uses ``make_desc(p="bf16_rem")`` with an int16 ``rem`` per
 tensor and ``adam_step_remainders`` (or ``..._capturable``); scaled 16-bit
 state uses ``make_desc(p="f16_scaled")`` (or ``"bf16_scaled"``) with a
 float32[3] ``scales`` per tensor and ``adam_step_scaled`` (or ``..._capturable``).
+
+Two-buffer state (fp32, 16-bit or remainder storage): pass a second set of
+p, m, v (and rem) per tensor as ``alternates``; each step reads one set and
+writes the other, and the state lives in set ``step & 1``::
+
+    alts = [dict(p=p2, m=m2, v=v2) for p2, m2, v2 in second_set]
+    tl = A.adam_tl_build(tensors, A.make_desc(g="bf16"), alternates=alts)
 """
 from __future__ import annotations
 
@@ -80,7 +87,7 @@ class AdamTlStats(ctypes.Structure):
     _fields_ = [("tensors", c_i64), ("nonempty", c_i64), ("chunks", c_i64), ("elements", c_i64),
                 ("chunk_elems", c_i64), ("vector_tensors", c_i64), ("grid_blocks", c_i64),
                 ("tile_elems", c_i32), ("block_threads", c_i32), ("bytes_per_elem", c_i32),
-                ("device", c_i32)]
+                ("device", c_i32), ("two_buffer", c_i32), ("reserved", c_i32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -95,7 +102,7 @@ class AdamError(RuntimeError):
 _lib = None
 
 EXPORTED = ("adam_abi_version", "adam_status_string", "adam_tl_plan", "adam_tl_build",
-            "adam_tl_destroy", "adam_tl_info", "adam_step", "adam_step_capturable",
+            "adam_tl_plan_two_buffer", "adam_tl_build_two_buffer", "adam_tl_destroy", "adam_tl_info", "adam_step", "adam_step_capturable",
             "adam_step_remainders", "adam_step_remainders_capturable", "adam_step_scaled",
             "adam_step_scaled_capturable", "adam_grad_sumsq", "adam_clip_grad_scale")
 
@@ -120,6 +127,12 @@ def lib():
     L.adam_tl_build.argtypes = [ctypes.POINTER(AdamTensor), c_i64, ctypes.POINTER(AdamTlDesc), c_vp,
                                 ctypes.POINTER(c_vp)]
     L.adam_tl_build.restype = c_i32
+    L.adam_tl_plan_two_buffer.argtypes = [ctypes.POINTER(AdamTensor), ctypes.POINTER(AdamTensor), c_i64,
+                                          ctypes.POINTER(AdamTlDesc), ctypes.POINTER(AdamTlStats)]
+    L.adam_tl_plan_two_buffer.restype = c_i32
+    L.adam_tl_build_two_buffer.argtypes = [ctypes.POINTER(AdamTensor), ctypes.POINTER(AdamTensor), c_i64,
+                                           ctypes.POINTER(AdamTlDesc), c_vp, ctypes.POINTER(c_vp)]
+    L.adam_tl_build_two_buffer.restype = c_i32
     L.adam_tl_destroy.argtypes = [c_vp]
     L.adam_tl_destroy.restype = None
     L.adam_tl_info.argtypes = [c_vp, ctypes.POINTER(AdamTlStats)]
@@ -141,7 +154,7 @@ def lib():
     L.adam_grad_sumsq.restype = c_i32
     L.adam_clip_grad_scale.argtypes = [c_vp, c_vp, c_f32, c_vp, c_vp, c_vp]
     L.adam_clip_grad_scale.restype = c_i32
-    if L.adam_abi_version() != 4:
+    if L.adam_abi_version() != 5:
         raise ImportError("libadamw_mi355x.so has an unexpected ABI version")
     _lib = L
     return L
@@ -250,12 +263,30 @@ def _check(status: int, what: str):
 # The C ABI, one function each
 # ---------------------------------------------------------------------------
 
-def adam_tl_plan(tensors: Sequence, desc: AdamTlDesc) -> dict:
-    """Host-only validation and planning; returns the statistics dict."""
+def _alternate_array(alternates: Sequence, tensors: Sequence, desc: AdamTlDesc):
+    """The second buffer set of a two-buffer handle: p, m, v (and rem) per
+    tensor, numel taken from the tensor it pairs with."""
+    if len(alternates) != len(tensors):
+        raise ValueError("alternates must pair one-to-one with tensors")
+    pairs = []
+    for a, t in zip(alternates, tensors):
+        pairs.append({"p": _get(a, "p"), "m": _get(a, "m"), "v": _get(a, "v"), "rem": _get(a, "rem"),
+                      "numel": _numel(t)})
+    return _tensor_array(pairs, desc)
+
+
+def adam_tl_plan(tensors: Sequence, desc: AdamTlDesc, alternates: Optional[Sequence] = None) -> dict:
+    """Host-only validation and planning; returns the statistics dict.  With
+    ``alternates``: a two-buffer handle's plan (adam_tl_plan_two_buffer)."""
     arr = _tensor_array(tensors, desc)
     st = AdamTlStats()
-    _check(lib().adam_tl_plan(arr, len(tensors), ctypes.byref(desc), ctypes.byref(st)),
-           "adam_tl_plan")
+    if alternates is None:
+        _check(lib().adam_tl_plan(arr, len(tensors), ctypes.byref(desc), ctypes.byref(st)),
+               "adam_tl_plan")
+    else:
+        alt = _alternate_array(alternates, tensors, desc)
+        _check(lib().adam_tl_plan_two_buffer(arr, alt, len(tensors), ctypes.byref(desc), ctypes.byref(st)),
+               "adam_tl_plan_two_buffer")
     return st.as_dict()
 
 
@@ -284,16 +315,25 @@ class TensorList:
             pass
 
 
-def adam_tl_build(tensors: Sequence, desc: AdamTlDesc, stream=None) -> TensorList:
+def adam_tl_build(tensors: Sequence, desc: AdamTlDesc, stream=None,
+                  alternates: Optional[Sequence] = None) -> TensorList:
     """Builds a handle for one group (see include/adam.h).  ``tensors`` holds
     dicts or objects with p, m, v, g and optional rem / p_out / scales (torch
-    tensors or int device addresses plus ``numel``)."""
+    tensors or int device addresses plus ``numel``).  ``alternates`` (one per
+    tensor: p, m, v and rem in remainder mode) makes a two-buffer handle
+    (adam_tl_build_two_buffer): the state then lives in set ``step & 1``,
+    set 0 being ``tensors``."""
     arr = _tensor_array(tensors, desc)
     out = c_vp()
     s = _stream(stream) if len(tensors) and any(_numel(t) for t in tensors) else (stream or 0)
-    _check(lib().adam_tl_build(arr, len(tensors), ctypes.byref(desc), s, ctypes.byref(out)),
-           "adam_tl_build")
-    return TensorList(out.value, tensors, desc)
+    if alternates is None:
+        _check(lib().adam_tl_build(arr, len(tensors), ctypes.byref(desc), s, ctypes.byref(out)),
+               "adam_tl_build")
+        return TensorList(out.value, tensors, desc)
+    alt = _alternate_array(alternates, tensors, desc)
+    _check(lib().adam_tl_build_two_buffer(arr, alt, len(tensors), ctypes.byref(desc), s, ctypes.byref(out)),
+           "adam_tl_build_two_buffer")
+    return TensorList(out.value, list(tensors) + list(alternates), desc)
 
 
 class HostStep:

@@ -7,7 +7,7 @@
 // clip_grad_norm, _local_step_with_scaled_states, _apply_state_scale); the
 // header states it in full.  How it runs is this file's own design:
 //
-//  * The host turns a tensor list into a table of 64-byte work items.  Each
+//  * The host turns a tensor list into a table of 128-byte work items.  Each
 //    item is a run of at most `chunk` elements (a power of two) of one tensor
 //    with every stream pointer already advanced to the run's start.
 //  * One launch covers the whole list with one 128-thread workgroup (two
@@ -17,7 +17,7 @@
 //    MI355X: 8-element lanes (16-byte accesses of the 16-bit streams, two
 //    adjacent 16-byte accesses of the fp32 ones) run 10-25% slower on every
 //    list with a 16-bit stream.  Workgroup b reads item t >> shift of tile
-//    t = tile_of_block(b) (one 64-byte scalar load, shared through L2 by the
+//    t = tile_of_block(b) (one 128-byte scalar load, shared through L2 by the
 //    item's tiles) and updates tile t & (2^shift - 1) of it.
 //  * XCD-aware order: the hardware hands workgroups to the 8 XCDs
 //    round-robin; tile_of_block permutes each group of 8 x run workgroups so
@@ -45,6 +45,13 @@
 //    grad scale and noop flag, advances the step (unless noop == 1), and
 //    writes the resolved scalars, bias corrections included, to a 64-byte
 //    block beside the work table; every tile then reads that one block.
+//  * Two-buffer state: an item may also carry the byte offsets of a second
+//    set of p, m, v (and remainder) buffers; a step then reads one set and
+//    writes the other, chosen by the parity of the step counter (the host
+//    counter, or the device counter through the capturable prologue's
+//    block).  Measured on MI355X: writing the lines a tile has just read
+//    costs ~5% of the HBM rate (the update, and a plain 4-read / 3-write
+//    stream probe, both run ~5% faster with separate output buffers).
 //  * Scaled 16-bit state needs each buffer's largest magnitude after the
 //    update before any of it can be stored, so it takes two passes over the
 //    same tiles: the first (one wave per tile) computes the update in
@@ -119,10 +126,10 @@ constexpr int kParamRem = 1;   // bf16 params + int16 remainders, fp32 m, v
 constexpr int kParamBF16 = 2;  // bf16 p, m, v (16-bit state)
 constexpr int kParamF16 = 3;   // fp16 p, m, v (16-bit state)
 
-enum : uint32_t { kItemVector = 1u };
+enum : uint32_t { kItemVector = 1u, kItemTwoBuffer = 2u };
 
 // One run of consecutive elements of one tensor.  Pointers address the run's
-// first element; absent streams are null.
+// first element in the first buffer set; absent streams are null.
 struct alignas(64) WorkItem {
     void *p;
     void *aux;       // int16 remainders (remainder mode), or the tensor's float[3] scales (scaled state)
@@ -131,11 +138,15 @@ struct alignas(64) WorkItem {
     const void *g;
     void *p_out;
     int32_t n;       // elements in the run, 1 .. chunk
-    uint32_t flags;  // kItemVector: every stream allows 4-element accesses
+    uint32_t flags;  // kItemVector: every stream allows 4-element accesses; kItemTwoBuffer: alt is set
     int32_t head;    // elements just before the run, updated by its tile 0 (0..63)
     int32_t tensor;  // ordinal of the tensor among the non-empty ones
+    // two-buffer state: byte offsets from p, aux (remainders), m, v to the
+    // same elements of the second buffer set (multiples of 128), else 0
+    int64_t alt[4];
+    int64_t unused[4];
 };
-static_assert(sizeof(WorkItem) == 64, "work item must be one 64-byte record");
+static_assert(sizeof(WorkItem) == 128, "work item must be one 128-byte record");
 
 // Scalars of one capturable step, resolved on the device by the prologue.
 struct alignas(64) StepBlock {
@@ -143,6 +154,7 @@ struct alignas(64) StepBlock {
     float lr, scale, bc1, bc2;
     int32_t skip;       // the noop flag was 1: the update does nothing
     int32_t t;          // step used by this update
+    int32_t side;       // two-buffer state: the buffer set read ((t - 1) & 1)
 };
 
 struct StepArgs {
@@ -150,6 +162,7 @@ struct StepArgs {
     float lr, beta1, beta2, eps, weight_decay, bc1, bc2, grad_scale;
     const float *d_grad_scale;  // nullable: read on the device instead of grad_scale
     const StepBlock *block;     // capturable only
+    int32_t side;               // two-buffer state, non-capturable: the buffer set read
 };
 
 // Per-workgroup constants of the update.
@@ -457,28 +470,30 @@ __device__ __forceinline__ uint32_t out16(float x, uint32_t h)
 }
 
 // The four consecutive elements of lane group gi, updated in registers:
-// every load is issued before any arithmetic.
+// every load is issued before any arithmetic.  p, aux, m and v are read
+// through `in` and written through `out` (the same record unless the state
+// has two buffer sets); g and p_out are the same in both.
 template <class C>
-__device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Coeffs &c)
+__device__ __forceinline__ void update_group(const WorkItem &in, const WorkItem &out, int gi, const Coeffs &c)
 {
     float p[kLane], m[kLane], v[kLane], g[kLane];
     uint32_t hp[kLane], hm[kLane], hv[kLane];
     if constexpr (C::st != kNone) {
-        load_u16x4(w.m, gi, hm);
-        load_u16x4(w.v, gi, hv);
+        load_u16x4(in.m, gi, hm);
+        load_u16x4(in.v, gi, hv);
     } else {
-        load_f32x4(w.m, gi, m);
-        load_f32x4(w.v, gi, v);
+        load_f32x4(in.m, gi, m);
+        load_f32x4(in.v, gi, v);
     }
-    load_grad4<C::gt>(w.g, gi, g);
+    load_grad4<C::gt>(in.g, gi, g);
     if constexpr (C::pk == kParamRem) {
         uint32_t r[kLane];
-        load_u16x4(w.p, gi, hp);
-        load_u16x4(w.aux, gi, r);
+        load_u16x4(in.p, gi, hp);
+        load_u16x4(in.aux, gi, r);
 #pragma unroll
         for (int k = 0; k < kLane; ++k) p[k] = master_from(hp[k], r[k]);
     } else if constexpr (C::st != kNone) {
-        load_u16x4(w.p, gi, hp);
+        load_u16x4(in.p, gi, hp);
 #pragma unroll
         for (int k = 0; k < kLane; ++k) {
             p[k] = widen16<C::st>(hp[k]);
@@ -486,7 +501,7 @@ __device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Co
             v[k] = widen16<C::st>(hv[k]);
         }
     } else {
-        load_f32x4(w.p, gi, p);
+        load_f32x4(in.p, gi, p);
     }
 #pragma unroll
     for (int k = 0; k < kLane; ++k) p[k] = update_element<C::mode>(p[k], g[k], m[k], v[k], c);
@@ -498,22 +513,22 @@ __device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Co
             hv[k] = narrow16<C::st>(v[k]);
             hp[k] = narrow16<C::st>(p[k]);
         }
-        store_u16x4(w.m, gi, hm);
-        store_u16x4(w.v, gi, hv);
-        store_u16x4(w.p, gi, hp);
+        store_u16x4(out.m, gi, hm);
+        store_u16x4(out.v, gi, hv);
+        store_u16x4(out.p, gi, hp);
     } else {
-        store_f32x4(w.m, gi, m);
-        store_f32x4(w.v, gi, v);
+        store_f32x4(out.m, gi, m);
+        store_f32x4(out.v, gi, v);
     }
     if constexpr (C::pk == kParamRem) {
         uint32_t r[kLane];
 #pragma unroll
         for (int k = 0; k < kLane; ++k) master_to(p[k], hp[k], r[k]);
-        store_u16x4(w.p, gi, hp);
-        store_u16x4(w.aux, gi, r);
-        if constexpr (C::ot != kNone) store_u16x4(w.p_out, gi, hp);
+        store_u16x4(out.p, gi, hp);
+        store_u16x4(out.aux, gi, r);
+        if constexpr (C::ot != kNone) store_u16x4(out.p_out, gi, hp);
     } else {
-        if constexpr (C::pk == kParamF32) store_f32x4(w.p, gi, p);
+        if constexpr (C::pk == kParamF32) store_f32x4(out.p, gi, p);
         if constexpr (C::ot == kF32) {
             float o[kLane];
 #pragma unroll
@@ -523,56 +538,57 @@ __device__ __forceinline__ void update_group(const WorkItem &w, int gi, const Co
                 else
                     o[k] = widen16<C::st>(hp[k]);
             }
-            store_f32x4(w.p_out, gi, o);
+            store_f32x4(out.p_out, gi, o);
         } else if constexpr (C::ot != kNone) {
             uint32_t o[kLane];
 #pragma unroll
             for (int k = 0; k < kLane; ++k) o[k] = out16<C::ot, C::st>(p[k], hp[k]);
-            store_u16x4(w.p_out, gi, o);
+            store_u16x4(out.p_out, gi, o);
         }
     }
 }
 
-// One element at index i of an item, with plain (narrow) accesses.
+// One element at index i of an item, with plain (narrow) accesses; `in`
+// and `out` as for update_group.
 template <class C>
-__device__ __forceinline__ void update_single(const WorkItem &w, int i, const Coeffs &c)
+__device__ __forceinline__ void update_single(const WorkItem &in, const WorkItem &out, int i, const Coeffs &c)
 {
-    const float g = load_grad1<C::gt>(w.g, i);
+    const float g = load_grad1<C::gt>(in.g, i);
     if constexpr (C::pk == kParamRem) {
-        float m = load_one<float>(w.m, i);
-        float v = load_one<float>(w.v, i);
-        const float p = master_from(load_one<uint16_t>(w.p, i), load_one<uint16_t>(w.aux, i));
+        float m = load_one<float>(in.m, i);
+        float v = load_one<float>(in.v, i);
+        const float p = master_from(load_one<uint16_t>(in.p, i), load_one<uint16_t>(in.aux, i));
         const float pn = update_element<C::mode>(p, g, m, v, c);
         uint32_t h, r;
         master_to(pn, h, r);
-        store_one<uint16_t>(w.p, i, uint16_t(h));
-        store_one<uint16_t>(w.aux, i, uint16_t(r));
-        if constexpr (C::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(h));
-        store_one<float>(w.m, i, m);
-        store_one<float>(w.v, i, v);
+        store_one<uint16_t>(out.p, i, uint16_t(h));
+        store_one<uint16_t>(out.aux, i, uint16_t(r));
+        if constexpr (C::ot != kNone) store_one<uint16_t>(out.p_out, i, uint16_t(h));
+        store_one<float>(out.m, i, m);
+        store_one<float>(out.v, i, v);
     } else if constexpr (C::st != kNone) {
-        float m = widen16<C::st>(load_one<uint16_t>(w.m, i));
-        float v = widen16<C::st>(load_one<uint16_t>(w.v, i));
-        const float pn = update_element<C::mode>(widen16<C::st>(load_one<uint16_t>(w.p, i)), g, m, v, c);
+        float m = widen16<C::st>(load_one<uint16_t>(in.m, i));
+        float v = widen16<C::st>(load_one<uint16_t>(in.v, i));
+        const float pn = update_element<C::mode>(widen16<C::st>(load_one<uint16_t>(in.p, i)), g, m, v, c);
         const uint32_t h = narrow16<C::st>(pn);
-        store_one<uint16_t>(w.m, i, uint16_t(narrow16<C::st>(m)));
-        store_one<uint16_t>(w.v, i, uint16_t(narrow16<C::st>(v)));
-        store_one<uint16_t>(w.p, i, uint16_t(h));
+        store_one<uint16_t>(out.m, i, uint16_t(narrow16<C::st>(m)));
+        store_one<uint16_t>(out.v, i, uint16_t(narrow16<C::st>(v)));
+        store_one<uint16_t>(out.p, i, uint16_t(h));
         if constexpr (C::ot == kF32)
-            store_one<float>(w.p_out, i, widen16<C::st>(h));
+            store_one<float>(out.p_out, i, widen16<C::st>(h));
         else if constexpr (C::ot != kNone)
-            store_one<uint16_t>(w.p_out, i, uint16_t(out16<C::ot, C::st>(pn, h)));
+            store_one<uint16_t>(out.p_out, i, uint16_t(out16<C::ot, C::st>(pn, h)));
     } else {
-        float m = load_one<float>(w.m, i);
-        float v = load_one<float>(w.v, i);
-        const float pn = update_element<C::mode>(load_one<float>(w.p, i), g, m, v, c);
-        store_one<float>(w.p, i, pn);
+        float m = load_one<float>(in.m, i);
+        float v = load_one<float>(in.v, i);
+        const float pn = update_element<C::mode>(load_one<float>(in.p, i), g, m, v, c);
+        store_one<float>(out.p, i, pn);
         if constexpr (C::ot == kF32)
-            store_one<float>(w.p_out, i, pn);
+            store_one<float>(out.p_out, i, pn);
         else if constexpr (C::ot != kNone)
-            store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<C::ot>(pn)));
-        store_one<float>(w.m, i, m);
-        store_one<float>(w.v, i, v);
+            store_one<uint16_t>(out.p_out, i, uint16_t(narrow16<C::ot>(pn)));
+        store_one<float>(out.m, i, m);
+        store_one<float>(out.v, i, v);
     }
 }
 
@@ -645,6 +661,7 @@ __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict
     if (start >= w.n) return;  // past the end of a tensor's last item
 
     Coeffs c = host_coeffs(a);
+    int32_t side = a.side;
     if constexpr (C::capturable) {
         const StepBlock s = *a.block;
         if (s.skip) return;
@@ -654,18 +671,38 @@ __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict
         c.rbc2 = s.rbc2;
         c.bc1 = s.bc1;
         c.bc2 = s.bc2;
+        side = s.side;
+    }
+    // two-buffer state: read the set `side`, write the other one
+    WorkItem in = w, out = w;
+    if (w.flags & kItemTwoBuffer) {
+        void *p1 = static_cast<char *>(w.p) + w.alt[0];
+        void *aux1 = w.aux != nullptr ? static_cast<char *>(w.aux) + w.alt[1] : nullptr;
+        void *m1 = static_cast<char *>(w.m) + w.alt[2];
+        void *v1 = static_cast<char *>(w.v) + w.alt[3];
+        if (side) {
+            in.p = p1;
+            in.aux = aux1;
+            in.m = m1;
+            in.v = v1;
+        } else {
+            out.p = p1;
+            out.aux = aux1;
+            out.m = m1;
+            out.v = v1;
+        }
     }
 
     const int n = min(kTile, w.n - start);
     const int tid = threadIdx.x;
     if (w.flags & kItemVector) {
-        if (start == 0 && tid < w.head) update_single<C>(w, tid - w.head, c);
+        if (start == 0 && tid < w.head) update_single<C>(in, out, tid - w.head, c);
         const int groups = n / kLane;
-        if (tid < groups) update_group<C>(w, start / kLane + tid, c);
+        if (tid < groups) update_group<C>(in, out, start / kLane + tid, c);
         // the 0..3 elements after the last whole group of a ragged tile
-        if (tid < n - groups * kLane) update_single<C>(w, start + groups * kLane + tid, c);
+        if (tid < n - groups * kLane) update_single<C>(in, out, start + groups * kLane + tid, c);
     } else {
-        for (int i = tid; i < n; i += kBlock) update_single<C>(w, start + i, c);
+        for (int i = tid; i < n; i += kBlock) update_single<C>(in, out, start + i, c);
     }
 }
 
@@ -684,6 +721,7 @@ __global__ void adam_capture_prologue(StepBlock *block, const float *d_lr, int32
     StepBlock s;
     s.skip = skip ? 1 : 0;
     s.t = t;
+    s.side = int32_t((uint32_t(t) - 1u) & 1u);
     s.lr = *d_lr;
     s.scale = d_grad_scale != nullptr ? *d_grad_scale : 1.0f;
     step_corrections(beta1, beta2, t, bias_correction, s.bc1, s.bc2, s.rbc1, s.rbc2);
@@ -1271,14 +1309,17 @@ int64_t auto_chunk(const std::vector<int64_t> &sizes, int64_t tile)
     return tile;
 }
 
-int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc, Plan &plan,
-              bool keep_items)
+// `alts` (nullable): the second buffer set of a two-buffer state, one entry
+// per tensor with only p, m, v (and rem) set.
+int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count, const adam_tl_desc *desc,
+              Plan &plan, bool keep_items)
 {
     if (desc == nullptr || count < 0 || (count > 0 && tensors == nullptr)) return ADAM_EINVAL;
     if (desc->reserved1 != 0) return ADAM_EINVAL;
     if (desc->with_remainders != 0 && desc->with_remainders != 1) return ADAM_EINVAL;
     if (desc->scaled_state != 0 && desc->scaled_state != 1) return ADAM_EINVAL;
     if (desc->with_remainders == 1 && desc->scaled_state == 1) return ADAM_EINVAL;
+    if (alts != nullptr && desc->scaled_state == 1) return ADAM_EINVAL;  // scaled state stays in place
     if (!valid_dtype_set(*desc)) return ADAM_EDTYPE;
     if (desc->chunk_elems != 0 &&
         (!is_pow2(desc->chunk_elems) || desc->chunk_elems < kMinChunk || desc->chunk_elems > kMaxChunk))
@@ -1300,14 +1341,16 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
     st.block_threads = kBlock;
     st.tile_elems = int32_t(tile);
     st.device = -1;
+    st.two_buffer = alts != nullptr ? 1 : 0;
 
     std::vector<Span> spans;
     std::vector<int64_t> sizes;  // elements covered by records (a vector body excludes its head)
     std::vector<int32_t> heads;  // head elements of a vector tensor, -1 for the element path
-    spans.reserve(size_t(count) * 7);
+    spans.reserve(size_t(count) * (alts != nullptr ? 11 : 7));
     for (int64_t k = 0; k < count; ++k) {
         const adam_tensor &t = tensors[k];
         if (t.numel < 0 || t.numel > kMaxNumel) return ADAM_EINVAL;
+        if (alts != nullptr && alts[k].numel != t.numel) return ADAM_EINVAL;
         if (t.numel == 0) continue;
         if (t.p == nullptr || t.m == nullptr || t.v == nullptr || t.g == nullptr) return ADAM_EINVAL;
         if ((t.rem != nullptr) != rem || (t.p_out != nullptr) != out || (t.scales != nullptr) != scaled)
@@ -1320,6 +1363,23 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
         if (rem) spans.push_back({uintptr_t(t.rem), uintptr_t(t.rem) + n * 2, false});
         if (out) spans.push_back({uintptr_t(t.p_out), uintptr_t(t.p_out) + n * out_size, false});
         if (scaled) spans.push_back({uintptr_t(t.scales), uintptr_t(t.scales) + 3 * sizeof(float), false});
+        if (alts != nullptr) {
+            // the second set: p, m, v (and rem), each a multiple of 128 bytes
+            // away from the first, so both sets share every alignment
+            const adam_tensor &a = alts[k];
+            if (a.p == nullptr || a.m == nullptr || a.v == nullptr || (a.rem != nullptr) != rem ||
+                a.g != nullptr || a.p_out != nullptr || a.scales != nullptr)
+                return ADAM_EINVAL;
+            auto apart = [](const void *x, const void *y) {
+                return (intptr_t(x) - intptr_t(y)) % 128 == 0;
+            };
+            if (!apart(a.p, t.p) || !apart(a.m, t.m) || !apart(a.v, t.v) || (rem && !apart(a.rem, t.rem)))
+                return ADAM_EINVAL;
+            spans.push_back({uintptr_t(a.p), uintptr_t(a.p) + n * p_size, false});
+            spans.push_back({uintptr_t(a.m), uintptr_t(a.m) + n * mv_size, false});
+            spans.push_back({uintptr_t(a.v), uintptr_t(a.v) + n * mv_size, false});
+            if (rem) spans.push_back({uintptr_t(a.rem), uintptr_t(a.rem) + n * 2, false});
+        }
         // every stream must be naturally aligned for its element type
         if (uintptr_t(t.p) % p_size || uintptr_t(t.m) % mv_size || uintptr_t(t.v) % mv_size ||
             uintptr_t(t.g) % g_size || (rem && uintptr_t(t.rem) % 2) ||
@@ -1390,6 +1450,14 @@ int make_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *des
             w.flags = head >= 0 ? kItemVector : 0u;
             w.head = off == 0 && head > 0 ? head : 0;
             w.tensor = ordinal;
+            if (alts != nullptr) {
+                const adam_tensor &a = alts[k];
+                w.flags |= kItemTwoBuffer;
+                w.alt[0] = intptr_t(a.p) - intptr_t(t.p);
+                w.alt[1] = rem ? intptr_t(a.rem) - intptr_t(t.rem) : 0;
+                w.alt[2] = intptr_t(a.m) - intptr_t(t.m);
+                w.alt[3] = intptr_t(a.v) - intptr_t(t.v);
+            }
             plan.items.push_back(w);
         }
     }
@@ -1521,6 +1589,7 @@ int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
     a.weight_decay = hp->weight_decay;
     a.grad_scale = grad_scale;
     a.d_grad_scale = d_grad_scale;
+    a.side = int32_t(uint32_t(before) & 1u);  // two-buffer state: the set the step reads
     step_corrections(hp->beta1, hp->beta2, t, hp->bias_correction, a.bc1, a.bc2, a.rbc1, a.rbc2);
     DeviceGuard guard(tl->stats.device);
     int rc = ADAM_EHIP;
@@ -1574,14 +1643,18 @@ const char *adam_status_string(int status)
     }
 }
 
-int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
-                 adam_tl_stats *stats)
+}  // extern "C"
+
+namespace {
+
+int plan_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count, const adam_tl_desc *desc,
+            adam_tl_stats *stats)
 {
     if (stats == nullptr) return ADAM_EINVAL;
     Plan plan;
     int rc;
     try {
-        rc = make_plan(tensors, count, desc, plan, false);
+        rc = make_plan(tensors, alts, count, desc, plan, false);
     } catch (const std::bad_alloc &) {
         return ADAM_ENOMEM;
     }
@@ -1589,15 +1662,15 @@ int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *
     return rc;
 }
 
-int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
-                  hipStream_t stream, adam_tl **out)
+int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count, const adam_tl_desc *desc,
+             hipStream_t stream, adam_tl **out)
 {
     if (out == nullptr) return ADAM_EINVAL;
     *out = nullptr;
     Plan plan;
     int rc;
     try {
-        rc = make_plan(tensors, count, desc, plan, true);
+        rc = make_plan(tensors, alts, count, desc, plan, true);
     } catch (const std::bad_alloc &) {
         return ADAM_ENOMEM;
     }
@@ -1684,6 +1757,41 @@ int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc 
     }
     *out = tl;
     return ADAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
+                 adam_tl_stats *stats)
+{
+    return plan_tl(tensors, nullptr, count, desc, stats);
+}
+
+int adam_tl_plan_two_buffer(const adam_tensor *tensors, const adam_tensor *alternates, int64_t count,
+                            const adam_tl_desc *desc, adam_tl_stats *stats)
+{
+    if (count > 0 && alternates == nullptr) return ADAM_EINVAL;
+    static const adam_tensor kNone[1] = {};  // an empty list: nothing to read
+    return plan_tl(tensors, alternates != nullptr ? alternates : kNone, count, desc, stats);
+}
+
+int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
+                  hipStream_t stream, adam_tl **out)
+{
+    return build_tl(tensors, nullptr, count, desc, stream, out);
+}
+
+int adam_tl_build_two_buffer(const adam_tensor *tensors, const adam_tensor *alternates, int64_t count,
+                             const adam_tl_desc *desc, hipStream_t stream, adam_tl **out)
+{
+    if (count > 0 && alternates == nullptr) {
+        if (out != nullptr) *out = nullptr;
+        return ADAM_EINVAL;
+    }
+    static const adam_tensor kNone[1] = {};  // an empty list: nothing to read
+    return build_tl(tensors, alternates != nullptr ? alternates : kNone, count, desc, stream, out);
 }
 
 void adam_tl_destroy(adam_tl *tl)

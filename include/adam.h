@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define ADAM_ABI_VERSION 4
+#define ADAM_ABI_VERSION 5
 
 typedef enum {
     ADAM_OK = 0,
@@ -143,6 +143,8 @@ typedef struct {
                                 state maxima pass runs one 64-lane wave per tile) */
     int32_t bytes_per_elem;  /* algorithmic HBM bytes per element (read + write)  */
     int32_t device;          /* HIP device of the handle (-1 from adam_tl_plan)   */
+    int32_t two_buffer;      /* 1: built by adam_tl_build_two_buffer               */
+    int32_t reserved;        /* 0                                                 */
 } adam_tl_stats;
 
 typedef struct adam_tl adam_tl; /* opaque handle: device work table */
@@ -172,7 +174,7 @@ int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *
                  adam_tl_stats *stats);
 
 /* Builds a handle for one group: validates as adam_tl_plan, then copies the
- * work table (one 64-byte record per chunk, plus a 64-byte scalar block used
+ * work table (one 128-byte record per chunk, plus a 64-byte scalar block used
  * by the capturable steps, partial-sum scratch for adam_grad_sumsq, and for
  * scaled state 12 bytes of maxima per 512-element tile and 24 bytes of maxima
  * and reciprocal scales per tensor) to the current device,
@@ -183,6 +185,38 @@ int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *
  * holds no device memory.  Errors: as adam_tl_plan; ADAM_ENOMEM; ADAM_EHIP. */
 int adam_tl_build(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
                   hipStream_t stream, adam_tl **out);
+
+/* Two-buffer state.  The apex patch "Enhance Distributed Fused Adam
+ * (#1794)" (DistAdamCapturableFunctor::operator()) reads and writes p, m and
+ * v in place; the same values can go to a second set of buffers instead.  In
+ * place, every written line is one the step has just read, and on MI355X
+ * that read-modify-write of the same lines costs about 5% of the HBM rate.
+ * Where p, m, v are the optimizer's own state (the fp32 master shards of
+ * apex distributed_fused_adam.py, whose model sees only the param-sync copy
+ * p_out), they may live in two buffer sets and alternate:
+ *   - `alternates` (host array of `count`, parallel to `tensors`) gives each
+ *     tensor's second set: p, m, v (and rem in remainder mode) with the same
+ *     numel; g, p_out and scales must be NULL (they are not alternated).
+ *     Each second-set pointer must lie a multiple of 128 bytes away from its
+ *     first-set pointer, and no buffer of either set may overlap another.
+ *   - The state lives in set (t & 1), t the group's step counter (host
+ *     step_io, or the device d_step of the capturable calls): set 0 before
+ *     the first step.  A step with counter t reads set ((t - 1) & 1) and
+ *     writes set (t & 1); it leaves the set it read unchanged (it then holds
+ *     the state before the step).  A noop step moves neither the counter
+ *     nor the state.  Because the capturable calls take the set from the
+ *     device counter, a recorded graph replays correctly.
+ *   - The caller must not change the counter other than through the step
+ *     calls, or must move the state to set (t & 1) itself.
+ * Storage schemes: fp32 state, 16-bit state and remainders (the scaled
+ * state's two passes stay in place: ADAM_EINVAL).  Everything else is as
+ * adam_tl_plan / adam_tl_build; the step, norm and clip calls are the same
+ * for both kinds of handle.  ADAM_EINVAL also for NULL `alternates` with
+ * count > 0 or an entry that breaks the rules above. */
+int adam_tl_plan_two_buffer(const adam_tensor *tensors, const adam_tensor *alternates, int64_t count,
+                            const adam_tl_desc *desc, adam_tl_stats *stats);
+int adam_tl_build_two_buffer(const adam_tensor *tensors, const adam_tensor *alternates, int64_t count,
+                             const adam_tl_desc *desc, hipStream_t stream, adam_tl **out);
 
 /* Frees a handle (NULL is allowed).  Work enqueued with it must be finished. */
 void adam_tl_destroy(adam_tl *tl);

@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (adam_\w+)$", out, flags=re.M))
     assert set(names) <= exported
-    assert L.adam_abi_version() == 4
+    assert L.adam_abi_version() == 5
 
 
 def test_status_strings():
@@ -255,6 +255,69 @@ def test_plan_rejects_overlapping_buffers():
     ts = fake_tensors([1000], out=True)
     ts[0]["p_out"] = ts[0]["p"]                # p_out aliasing p
     assert status_of(ts, p_out="bf16") == A.ADAM_EINVAL
+
+
+def alt_tensors(ts, *, rem=False, shift=0):
+    """A second buffer set for fake_tensors: p, m, v (and rem) at slots 7..,
+    far from every first-set buffer."""
+    return [dict(p=fake(i, 7, shift) + 1 * STRIDE // 4, m=fake(i, 7, shift) + 2 * STRIDE // 4,
+                 v=fake(i, 7, shift) + 3 * STRIDE // 4, rem=fake(i, 7, shift) if rem else None)
+            for i, _ in enumerate(ts)]
+
+
+def two_buffer_status(ts, alts, **kw):
+    try:
+        A.adam_tl_plan(ts, A.make_desc(**kw), alternates=alts)
+        return 0
+    except A.AdamError as e:
+        return e.status
+
+
+def test_two_buffer_plan_matches_the_in_place_plan():
+    for kw, rem in (({}, False), ({"g": "bf16", "p_out": "bf16"}, False), ({"p": "bf16"}, False),
+                    ({"p": "bf16_rem", "g": "bf16"}, True)):
+        ts = fake_tensors([4096, 1000, 7, 0, 70001], rem=rem, out="p_out" in kw)
+        one = A.adam_tl_plan(ts, A.make_desc(**kw))
+        two = A.adam_tl_plan(ts, A.make_desc(**kw), alternates=alt_tensors(ts, rem=rem))
+        assert one["two_buffer"] == 0 and two["two_buffer"] == 1
+        assert {k: v for k, v in one.items() if k != "two_buffer"} == \
+               {k: v for k, v in two.items() if k != "two_buffer"}, kw
+    empty = A.adam_tl_plan([], A.make_desc(), alternates=[])
+    assert empty["two_buffer"] == 1 and empty["chunks"] == 0
+
+
+def test_two_buffer_plan_rejects_bad_second_sets():
+    ts = fake_tensors([4096, 1000])
+    ok = alt_tensors(ts)
+    assert two_buffer_status(ts, ok) == 0
+    bad = [dict(ok[0]), ok[1]]
+    bad[0]["p"] += 64                       # not a multiple of 128 bytes away
+    assert two_buffer_status(ts, bad) == A.ADAM_EINVAL
+    bad = [dict(ok[0], m=None), ok[1]]      # a missing stream
+    assert two_buffer_status(ts, bad) == A.ADAM_EINVAL
+    bad = [dict(ok[0], v=ts[0]["v"] + 128), ok[1]]  # overlaps the first set
+    assert two_buffer_status(ts, bad) == A.ADAM_EINVAL
+    bad = [ok[0], dict(ok[1], p=ok[0]["p"])]  # two tensors share a second-set buffer
+    assert two_buffer_status(ts, bad) == A.ADAM_EINVAL
+    bad = [dict(ok[0], rem=fake(0, 7)), ok[1]]  # rem outside remainder mode
+    assert two_buffer_status(ts, bad) == A.ADAM_EINVAL
+    tr = fake_tensors([4096], rem=True)
+    assert two_buffer_status(tr, alt_tensors(tr), p="bf16_rem") == A.ADAM_EINVAL  # rem missing
+    assert two_buffer_status(tr, alt_tensors(tr, rem=True), p="bf16_rem") == 0
+    tsc = fake_tensors([4096], scaled=True)
+    assert two_buffer_status(tsc, alt_tensors(tsc), p="f16_scaled") == A.ADAM_EINVAL  # scaled stays in place
+    # g, p_out and scales are never alternated
+    L = A.lib()
+    desc = A.make_desc()
+    arr = A._tensor_array(ts, desc)
+    alt = A._alternate_array(ok, ts, desc)
+    alt[0].g = ts[0]["g"]
+    st = A.AdamTlStats()
+    assert L.adam_tl_plan_two_buffer(arr, alt, 2, desc, st) == A.ADAM_EINVAL
+    alt = A._alternate_array(ok, ts, desc)
+    alt[1].numel = 999                      # numel must match the tensor it pairs with
+    assert L.adam_tl_plan_two_buffer(arr, alt, 2, desc, st) == A.ADAM_EINVAL
+    assert L.adam_tl_plan_two_buffer(arr, None, 2, desc, st) == A.ADAM_EINVAL
 
 
 def test_empty_handle_advances_host_counter_without_a_gpu():

@@ -8,7 +8,10 @@ not, eps, weight decay, lr, grad scale on the host or the device), a chunk
 size and a number of steps, then runs the library (capturable where the
 storage allows it and the case says so, with the noop flag raised on random
 steps) and the oracle from the same inputs and compares every output bit
-for bit (NaN as NaN) and the step counter."""
+for bit (NaN as NaN) and the step counter.  A third of the cases whose
+storage allows it (drawn from a separate seed, so the other draws stay
+fixed) give the state a second buffer set; the result is then read from set
+(steps taken & 1)."""
 import os
 
 import numpy as np
@@ -71,10 +74,11 @@ def draw_case(k):
     steps = int(rng.integers(1, 5))
     capturable = bool(rng.random() < 0.4)
     noops = [int(rng.random() < 0.3) for _ in range(steps)] if capturable else [0] * steps
+    two_buffer = not p_kind.endswith("_scaled") and np.random.default_rng(500000 + k).random() < 1 / 3
     return dict(p_kind=p_kind, g_dtype=g_dtype, p_out=p_out, sizes=sizes, layout=layout, mode=mode,
                 bias_correction=bias_correction, beta1=beta1, beta2=beta2, eps=eps, wd=wd, lr=lr,
                 grad_scale=grad_scale, device_scale=device_scale, chunk=chunk, steps=steps,
-                capturable=capturable, noops=noops, seed=2000 + k, rng=rng)
+                capturable=capturable, noops=noops, seed=2000 + k, rng=rng, two_buffer=two_buffer)
 
 
 @pytest.mark.parametrize("k", range(CASES))
@@ -97,7 +101,20 @@ def test_random_case(torch, orc, k):
         offsets = [{r: int(rng.integers(0, 9)) for r in roles} for _ in c["sizes"]]
     ref = copies(host)
     dev = DeviceSet(host, offsets)
-    tl = A.adam_tl_build(dev.tensors, desc_for(host, chunk_elems=c["chunk"]))
+    alt = None
+    if c["two_buffer"]:
+        second = copies(host)  # the second set starts as values no step produces
+        for h in second:
+            for r in ("p", "m", "v", "rem"):
+                a = getattr(h, r)
+                if a is not None and a.size:
+                    a.view(np.uint8)[...] = 0x7B
+        alt = DeviceSet(second, offsets)
+        alts = [{r: (d.get(r) if h.p.size else None) for r in ("p", "m", "v", "rem")}
+                for d, h in zip(alt.tensors, host)]
+        tl = A.adam_tl_build(dev.tensors, desc_for(host, chunk_elems=c["chunk"]), alternates=alts)
+    else:
+        tl = A.adam_tl_build(dev.tensors, desc_for(host, chunk_elems=c["chunk"]))
     hp = A.AdamHParams(c["beta1"], c["beta2"], c["eps"], c["wd"], c["mode"], c["bias_correction"])
     hr = oracle.HParams(c["beta1"], c["beta2"], c["eps"], c["wd"], c["mode"], c["bias_correction"])
     d_scale = torch.tensor([c["grad_scale"]], dtype=torch.float32, device="cuda")
@@ -128,6 +145,10 @@ def test_random_case(torch, orc, k):
         torch.cuda.synchronize()
         assert step.value == ref_step[0] == c["steps"]
     got = dev.readback()
+    if alt is not None and ref_step[0] & 1:  # the state is in the second set
+        second = alt.readback()
+        for gt, sd in zip(got, second):
+            gt.p, gt.m, gt.v, gt.rem = sd.p, sd.m, sd.v, sd.rem
     tl.destroy()
     ctx = {k2: v for k2, v in c.items() if k2 != "sizes"} | {"sizes": c["sizes"]}
     assert_bitwise(got, ref, ctx=str(ctx))
