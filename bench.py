@@ -17,7 +17,10 @@ counting algorithmic bytes (every state word read and written once, the
 gradient read once: 28 B/element here).  The same K steps are also timed for
 the capturable call (device lr/step/grad scale/noop) and for a HIP-graph
 replay of the capturable call; per-launch kernel durations come from HIP
-events recorded on the launch stream around each launch.
+events recorded on the launch stream around each launch.  Where a second
+set of p, m, v fits in HBM, the same K steps are timed once more on a
+two-buffer handle (``two_buffer_state``: each step reads one buffer set and
+writes the other); ``value`` and ``roofline`` stay the in-place step.
 
 The CPU baseline is the oracle (plain scalar C) on a bounded sample of the
 same workload, run on the host's cores (one thread per core, each on a
@@ -81,26 +84,30 @@ PROFILE_COMMANDS = {
     "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_{w} "
              "-o run -- python3 <repo>/bench.py --workload {w} > <out>/trace_{w}.log",
     "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_{w} "
-             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable "
+             "> <out>/pmc_fetch_{w}.log",
     "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_{w} "
-             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable "
+             "> <out>/pmc_write_{w}.log",
     "summary": "python bench.py --summarize-profiles --workload {w} --trace-dir <out>/trace_{w} "
-               "--trace-log <out>/trace_{w}.log --fetch-dir <out>/pmc_fetch_{w} --write-dir <out>/pmc_write_{w}",
+               "--trace-log <out>/trace_{w}.log --fetch-dir <out>/pmc_fetch_{w} --write-dir <out>/pmc_write_{w} "
+               "--fetch-log <out>/pmc_fetch_{w}.log --write-log <out>/pmc_write_{w}.log",
     "valu": "cd /tmp && rocprofv3 --pmc SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVES GRBM_GUI_ACTIVE "
             "--output-format csv -d <out>/pmc_valu_{w} -o run -- python3 <repo>/bench.py "
-            "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+            "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
     "valu_summary": "python bench.py --summarize-valu --workload {w} --valu-dir <out>/pmc_valu_{w}",
     "occupancy": "cd /tmp && rocprofv3 --pmc MeanOccupancyPerCU OccupancyPercent --output-format csv "
                  "-d <out>/pmc_occ_{w} -o run -- python3 <repo>/bench.py --workload {w} "
-                 "--steps 3 --warmup 1 --no-cpu --no-capturable",
+                 "--steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
     "occupancy_summary": "python bench.py --summarize-occupancy --workload {w} --occupancy-dir <out>/pmc_occ_{w}",
     "dram_req": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_WRREQ_sum "
                 "TCC_EA0_WRREQ_64B_sum --output-format csv -d <out>/pmc_dreq_{w} -o run -- "
-                "python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+                "python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable "
+                "--no-two-buffer",
     "dram_stall": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_WRREQ_LEVEL_sum "
                   "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum GRBM_GUI_ACTIVE "
                   "--output-format csv -d <out>/pmc_dstall_{w} -o run -- python3 <repo>/bench.py "
-                  "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable",
+                  "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
     "dram_summary": "python bench.py --summarize-dram --workload {w} --dram-req-dir <out>/pmc_dreq_{w} "
                     "--dram-stall-dir <out>/pmc_dstall_{w}",
 }
@@ -276,7 +283,29 @@ def _short(name: str) -> str:
     return base + (f"[{m.group(1)}]" if m else "")
 
 
-def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_log: str = None) -> None:
+def _bench_line(path):
+    """The last bench line (JSON) a profiled bench command printed, or None."""
+    if not path:
+        return None
+    line = None
+    for text in open(path):
+        if text.startswith("{"):
+            line = json.loads(text)
+    return line
+
+
+def _two_buffer_launches(line) -> int:
+    """Launches of the main group's two-buffer step in a bench run (its last
+    non-capturable update launches), 0 when it did not run."""
+    tb = (line or {}).get("two_buffer_state")
+    return line["warmup"] + line["steps"] if isinstance(tb, dict) and "ms_per_step" in tb else 0
+
+
+TWO_BUFFER_TAG = " [two-buffer]"
+
+
+def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_log: str = None,
+                       fetch_log: str = None, write_log: str = None) -> None:
     """Writes profiles/<kernel>_<workload>_{kernel_trace,pmc}.txt (kernel
     adam_update, or adam_scaled for scaled state) and updates
     profiles/traffic.json from rocprofv3 CSV output.
@@ -292,7 +321,12 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
 
     With `trace_log` (the bench line the traced command printed), the
     launch durations bench.py measured with HIP events in that same process
-    are set beside the trace's averages for the same dispatches."""
+    are set beside the trace's averages for the same dispatches.  When a
+    run also timed the two-buffer step (the bench line says so), its update
+    launches are that run's last non-capturable ones of the main group; they
+    are reported apart from the in-place ones (`fetch_log` and `write_log`
+    are the counter runs' bench lines).  The bench line's roofline and
+    profiles/traffic.json describe the in-place kernel."""
     import csv
 
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -320,8 +354,16 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
         name = _short(r["Kernel_Name"])
         if main_kernel(name):
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
-            per.setdefault((name, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])), []).append(dur)
+            per.setdefault((name, int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])), []).append(
+                (int(r["Start_Timestamp"]), dur))
     big = max(g for _, g in per)
+    bench_line = _bench_line(trace_log)
+    n_tb = 0 if scaled else _two_buffer_launches(bench_line)
+    for (name, grid) in list(per):
+        if n_tb and grid == big and name.endswith("false>"):
+            d = sorted(per.pop((name, grid)))
+            per[(name, grid)], per[(name + TWO_BUFFER_TAG, grid)] = d[:-n_tb], d[-n_tb:]
+    per = {k: [dur for _, dur in v] for k, v in per.items()}
     lines += ["", ("scaled-state passes" if scaled else "update kernel") +
               " per dispatch (main group = the largest grid):",
               f"{'kernel':46s} {'workgroups':>13s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} "
@@ -338,10 +380,6 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
         lines.append(f"both passes of one step: {sum(passes):.3f} ms; algorithmic bytes per step "
                      f"{algo / 1e9:.3f} GB -> {algo / (sum(passes) * 1e-3) / 1e9:.1f} GB/s")
     if trace_log:
-        bench_line = None
-        for line in open(trace_log):
-            if line.startswith("{"):
-                bench_line = json.loads(line)
         assert bench_line is not None, f"no bench line in {trace_log}"
         lines += ["", "bench.py in the same traced process (HIP events on the launch stream) vs the "
                       "trace's average over the same main-group dispatches:"]
@@ -355,6 +393,10 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
             pairs = [("update, regular", bench_line["roofline"]["launch_ms_mean"], trace_avg("false"))]
             if "capturable" in bench_line:
                 pairs.append(("update, capturable", bench_line["capturable"]["launch_ms_mean"], trace_avg("true")))
+            if n_tb:
+                d = [x for (nm, g), v in per.items() if g == big and nm.endswith(TWO_BUFFER_TAG) for x in v]
+                pairs.append(("update, two-buffer state", bench_line["two_buffer_state"]["launch_ms_mean"],
+                              statistics.mean(d)))
         for what, ev, tr in pairs:
             lines.append(f"  {what:42s} events {ev:9.3f} ms   trace {tr:9.3f} ms   events / trace {ev / tr:.4f}")
         lines.append(f"  bench line of the traced run: value {bench_line['value']} {bench_line['unit']}, "
@@ -364,16 +406,27 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
         f.write("\n".join(lines) + "\n")
 
     # counters
-    def per_kernel(path):
+    def per_kernel(path, log):
+        """Counter value per dispatch, by kernel, in dispatch order; the main
+        group's last two-buffer launches (if the run made them) apart."""
+        rows = list(csv.DictReader(open(os.path.join(path, "run_counter_collection.csv"))))
+        if rows and "Dispatch_Id" in rows[0]:
+            rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         agg = {}
-        for r in csv.DictReader(open(os.path.join(path, "run_counter_collection.csv"))):
+        for r in rows:
             name = _short(r["Kernel_Name"])
             if main_kernel(name) and int(r["Grid_Size"]) // int(r["Workgroup_Size"]) != big:
                 name += " (small group)"
             agg.setdefault(name, []).append(float(r["Counter_Value"]))
+        n = 0 if scaled else _two_buffer_launches(_bench_line(log))
+        if n:
+            main = [k for k in agg if main_kernel(k) and not k.endswith("(small group)")]
+            assert len(main) == 1, main
+            vals = agg.pop(main[0])
+            agg[main[0]], agg[main[0] + TWO_BUFFER_TAG] = vals[:-n], vals[-n:]
         return agg
 
-    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    fetch, write = per_kernel(fetch_dir, fetch_log), per_kernel(write_dir, write_log)
     cal = [k for k in fetch if "AUnaryFunctor" in k]
     assert cal, "calibration kernel (elementwise multiply) not found"
     # fp32 temporaries of all elements, read once and written once: the
@@ -384,8 +437,13 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
     known_kib = draws * w.numel * 4 / 1024
     f_factor = known_kib / sum(fetch[cal[0]])
     w_factor = known_kib / sum(write[cal[0]])
-    upd = [k for k in fetch if main_kernel(k) and not k.endswith("(small group)")]
+    upd = [k for k in fetch if main_kernel(k) and not k.endswith("(small group)") and
+           not k.endswith(TWO_BUFFER_TAG)]
     assert len(upd) == (2 if scaled else 1), upd
+    tb_key = [k for k in fetch if k.endswith(TWO_BUFFER_TAG)]
+    tb_traffic = None
+    if tb_key and tb_key[0] in write:
+        tb_traffic = (statistics.mean(fetch[tb_key[0]]) * f_factor + statistics.mean(write[tb_key[0]]) * w_factor) * 1024
     fetch_kib = sum(statistics.mean(fetch[k]) for k in upd)
     write_kib = sum(statistics.mean(write[k]) for k in upd)
     k = " + ".join(upd)
@@ -407,8 +465,11 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
               f"read {fetch_kib * f_factor * 1024 / 1e9:.3f} GB, "
               f"write {write_kib * w_factor * 1024 / 1e9:.3f} GB, total {traffic / 1e9:.3f} GB",
               f"algorithmic bytes per launch: {algo / 1e9:.3f} GB ({n0:,} elements x {w.bytes_per_elem} B); "
-              f"measured / algorithmic = {traffic / algo:.4f}",
-              f"kernel source sha256[:16] = {source_hash()}"]
+              f"measured / algorithmic = {traffic / algo:.4f}"]
+    if tb_traffic is not None:
+        lines.append(f"two-buffer state (the runs' last {len(fetch[tb_key[0]])} update launches): "
+                     f"{tb_traffic / 1e9:.3f} GB per launch; measured / algorithmic = {tb_traffic / algo:.4f}")
+    lines.append(f"kernel source sha256[:16] = {source_hash()}")
     if scaled:
         lines.append("scaled state reads p, m, v and g twice (the maxima pass, then the store pass "
                      "recomputes the update): the second read is counted whether the Infinity Cache "
@@ -425,6 +486,8 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
                       "ratio": round(traffic / algo, 5), "fetch_factor": round(f_factor, 5),
                       "write_factor": round(w_factor, 5), "kernel": k,
                       "source_sha256_16": source_hash()}
+    if tb_traffic is not None:
+        allrec[w.name]["two_buffer_bytes_per_launch"] = round(tb_traffic)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(allrec, f, indent=1, sort_keys=True)
     print("\n".join(open(trace_path).read().splitlines() + [""] + open(pmc_path).read().splitlines()))
@@ -516,10 +579,14 @@ def main() -> int:
                     help="oracle steps for the CPU baseline (0: about 10 s of wall time)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-capturable", action="store_true")
+    ap.add_argument("--no-two-buffer", action="store_true",
+                    help="skip the two-buffer-state measurement")
     ap.add_argument("--summarize-profiles", action="store_true",
                     help="write profiles/ summaries from rocprofv3 CSV directories (no GPU)")
     ap.add_argument("--trace-dir")
     ap.add_argument("--trace-log", help="stdout of the traced bench command (its bench line)")
+    ap.add_argument("--fetch-log", help="stdout of the FETCH_SIZE run (its bench line)")
+    ap.add_argument("--write-log", help="stdout of the WRITE_SIZE run (its bench line)")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--summarize-valu", action="store_true",
@@ -538,7 +605,7 @@ def main() -> int:
         from workloads import workloads
 
         summarize_profiles(workloads()[args.workload], args.trace_dir, args.fetch_dir, args.write_dir,
-                           args.trace_log)
+                           args.trace_log, args.fetch_log, args.write_log)
         return 0
     if args.summarize_valu:
         from workloads import workloads
@@ -792,6 +859,56 @@ def main() -> int:
             "grad_sumsq_launch_ms": round(sumsq_ms, 4),
             "grad_sumsq_gbps": round(g_bytes / (sumsq_ms * 1e-3) / 1e9, 1),
         }
+
+    # --- two-buffer state: the same step reading one buffer set of p, m, v
+    # (and remainders) and writing a second one (adam_tl_build_two_buffer) ---
+    if not scaled and not args.no_two_buffer:
+        keys = [k for k in ("p", "rem", "m", "v") if k in bufs]
+        extra = sum(bufs[k].numel() * bufs[k].element_size() for k in keys)
+        free, _ = torch.cuda.mem_get_info()
+        if extra * 1.02 + (2 << 30) > free:
+            result["two_buffer_state"] = {
+                "skipped": f"a second set of p, m, v ({extra / 1e9:.1f} GB) does not fit beside the first "
+                           f"({free / 1e9:.1f} GB free)"}
+        else:
+            alt_bufs = {k: torch.empty_like(bufs[k]) for k in keys}
+            tb_handles = []
+            off = 0
+            for (sizes, wd), (_, hp, n, _, _) in zip(groups, handles):
+                views = {k: split_views(v[off:off + n], sizes) for k, v in bufs.items()}
+                aviews = {k: split_views(v[off:off + n], sizes) for k, v in alt_bufs.items()}
+                tensors = [{k: views[k][i] for k in views} for i in range(len(sizes))]
+                alts = [{k: aviews[k][i] for k in aviews} for i in range(len(sizes))]
+                desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out, chunk_elems=args.chunk_elems)
+                tb_handles.append((A.adam_tl_build(tensors, desc, alternates=alts), hp, A.HostStep(0)))
+                off += n
+
+            def one_step_tb(ev=None):
+                for i, (tl, hp, host_step) in enumerate(tb_handles):
+                    launch_timed(ev if i == 0 else None,
+                                 lambda: step_fn(tl, hp, w.lr, host_step, 1.0, d_scale, stream))
+
+            for _ in range(args.warmup):
+                one_step_tb()
+            tb_wall, tb_per = timed(one_step_tb, args.steps)
+            tb_launch = statistics.mean(tb_per)
+            tb_achieved = launch_bytes / (tb_launch * 1e-3) / 1e9
+            log(f"two-buffer state: {tb_wall:.3f} ms/step wall, {bytes_step / (tb_wall * 1e-3) / 1e9:.1f} GB/s")
+            result["two_buffer_state"] = {
+                "what": "the same non-capturable step with p, m, v (and remainders) read from one buffer set "
+                        "and written to a second (adam_tl_build_two_buffer); same algorithmic bytes",
+                "ms_per_step": round(tb_wall, 4),
+                "value": round(bytes_step / (tb_wall * 1e-3) / 1e9, 2),
+                "pct_of_hbm_peak": round(100 * bytes_step / (tb_wall * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                "launch_ms_mean": round(tb_launch, 4),
+                "achieved": round(tb_achieved, 2),
+                "frac": round(tb_achieved / HBM_PEAK_GBPS, 4),
+                "vs_in_place": round(tb_wall / wall_ms, 4),
+                "extra_device_bytes": extra,
+            }
+            for h in tb_handles:
+                h[0].destroy()
+            del alt_bufs
 
     for h in handles:
         h[0].destroy()

@@ -127,3 +127,56 @@ def test_profile_summary_from_synthetic_counters(tmp_path, monkeypatch):
     rec = json.loads((tmp_path / "profiles" / "traffic.json").read_text())["tiny"]
     assert rec["bytes_per_launch"] == n * 28 and rec["ratio"] == 1.0
     assert rec["source_sha256_16"] == bench.source_hash()
+
+
+def test_profile_summary_splits_the_two_buffer_launches(tmp_path, monkeypatch):
+    """A run that also timed the two-buffer step ends with its launches (the
+    bench line gives their number, warmup + steps): the summary reports them
+    apart, with their own event / trace comparison and traffic."""
+    w = workloads()["tiny"]
+    n = sum(w.sizes)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "profiles" / "traffic.json"))
+    (tmp_path / "profiles").mkdir()
+    upd = "void (anonymous namespace)::adam_update<(anonymous namespace)::Config<1, 0, 0, 1, {}> >(...)"
+    cal = "void at::native::vectorized_elementwise_kernel<4, at::native::AUnaryFunctor<float, float, float, X>>(...)"
+    blocks = 10
+    _write_csv(tmp_path / "trace" / "run_kernel_stats.csv",
+               [dict(Name=upd.format("false"), Calls=7, AverageNs=900, MinNs=800, MaxNs=1000)])
+    # 4 in-place launches of 1000 ns, 2 capturable ones, then 3 two-buffer launches of 800 ns
+    trace = [dict(Kernel_Name=upd.format("false"), Start_Timestamp=10_000 * i, End_Timestamp=10_000 * i + 1000,
+                  Grid_Size_X=blocks * 128, Workgroup_Size_X=128) for i in range(4)]
+    trace += [dict(Kernel_Name=upd.format("true"), Start_Timestamp=50_000 + 10_000 * i,
+                   End_Timestamp=50_000 + 10_000 * i + 1100, Grid_Size_X=blocks * 128, Workgroup_Size_X=128)
+              for i in range(2)]
+    trace += [dict(Kernel_Name=upd.format("false"), Start_Timestamp=90_000 + 10_000 * i,
+                   End_Timestamp=90_000 + 10_000 * i + 800, Grid_Size_X=blocks * 128, Workgroup_Size_X=128)
+              for i in range(3)]
+    _write_csv(tmp_path / "trace" / "run_kernel_trace.csv", trace[::-1])  # any row order
+    line = {"value": 1.0, "unit": "GB/s", "ms_per_step": 0.002, "warmup": 1, "steps": 2,
+            "roofline": {"launch_ms_mean": 0.001, "achieved": 1.0}, "capturable": {"launch_ms_mean": 0.0011},
+            "two_buffer_state": {"ms_per_step": 0.0009, "launch_ms_mean": 0.0008}}
+    for name in ("trace", "fetch", "write"):
+        (tmp_path / f"{name}.log").write_text(json.dumps(line) + "\n")
+    known_kib = n * 4 / 1024
+    read_kib, write_kib = n * 16 / 1024, n * 12 / 1024
+    for which, upd_val, tb_val, cal_val in (("fetch", read_kib / 2, read_kib * 0.55, known_kib / 2),
+                                            ("write", write_kib, write_kib, known_kib)):
+        rows = [dict(Dispatch_Id=1, Kernel_Name=cal, Grid_Size=4096, Workgroup_Size=256, Counter_Value=cal_val)]
+        rows += [dict(Dispatch_Id=2 + i, Kernel_Name=upd.format("false"), Grid_Size=blocks * 128,
+                      Workgroup_Size=128, Counter_Value=upd_val) for i in range(4)]
+        rows += [dict(Dispatch_Id=6 + i, Kernel_Name=upd.format("false"), Grid_Size=blocks * 128,
+                      Workgroup_Size=128, Counter_Value=tb_val) for i in range(3)]
+        _write_csv(tmp_path / which / "run_counter_collection.csv", rows[::-1])
+    bench.summarize_profiles(w, str(tmp_path / "trace"), str(tmp_path / "fetch"), str(tmp_path / "write"),
+                             str(tmp_path / "trace.log"), str(tmp_path / "fetch.log"), str(tmp_path / "write.log"))
+    trace_txt = (tmp_path / "profiles" / "adam_update_tiny_kernel_trace.txt").read_text()
+    assert "update, two-buffer state" in trace_txt
+    assert trace_txt.count("events / trace 1.0000") == 3
+    assert "false> [two-buffer]" in trace_txt
+    pmc_txt = (tmp_path / "profiles" / "adam_update_tiny_pmc.txt").read_text()
+    assert "measured / algorithmic = 1.0000" in pmc_txt
+    assert "two-buffer state (the runs' last 3 update launches)" in pmc_txt
+    rec = json.loads((tmp_path / "profiles" / "traffic.json").read_text())["tiny"]
+    assert rec["ratio"] == 1.0
+    assert rec["two_buffer_bytes_per_launch"] == round((read_kib * 0.55 * 2 + write_kib) * 1024)
