@@ -3,10 +3,12 @@
  * copies them to the device, runs `steps` calls of adam_step on a stream of
  * its own, and writes the updated p, m, v and the host step counter back.
  *
- *   gpu_step IN OUT
+ *   gpu_step IN OUT [two-buffer]
  *   IN : int64 n; float lr, beta1, beta2, eps, wd, grad_scale;
  *        int32 mode, bias_correction, steps; float32 p[n], m[n], v[n], g[n]
  *   OUT: float32 p[n], m[n], v[n]; int32 step
+ * With "two-buffer" the handle is built by adam_tl_build_two_buffer with a
+ * second set of p, m, v, and the state is read back from set (step & 1).
  * Exit status 0 on success; a failing call prints its status and exits 1. */
 #include <stdio.h>
 #include <stdlib.h>
@@ -41,15 +43,18 @@ int main(int argc, char **argv)
     int32_t hi[3];
     float *h[4];
     float *d[4];
+    float *d2[3] = {NULL, NULL, NULL};
+    int two = 0;
     int i, k;
     int32_t step = 0;
-    adam_tensor t;
+    adam_tensor t, t2;
     adam_tl_desc desc = {ADAM_DT_F32, ADAM_DT_F32, ADAM_DT_NONE, 0, 0, 0, 0};
     adam_hparams hp;
     adam_tl *tl = NULL;
     hipStream_t stream;
 
-    if (argc != 3) return 2;
+    if (argc == 4 && argv[3][0] == 't') two = 1;
+    else if (argc != 3) return 2;
     in = fopen(argv[1], "rb");
     if (in == NULL || !read_all(in, &n, sizeof n) || !read_all(in, hf, sizeof hf) || !read_all(in, hi, sizeof hi))
         return 2;
@@ -79,7 +84,17 @@ int main(int argc, char **argv)
     hp.weight_decay = hf[4];
     hp.mode = hi[0];
     hp.bias_correction = hi[1];
-    CHECK_ADAM(adam_tl_build(&t, 1, &desc, stream, &tl));
+    if (two) {
+        for (i = 0; i < 3; ++i) CHECK_HIP(hipMalloc((void **)&d2[i], (size_t)n * sizeof(float)));
+        t2 = t;
+        t2.p = d2[0];
+        t2.m = d2[1];
+        t2.v = d2[2];
+        t2.g = NULL;
+        CHECK_ADAM(adam_tl_build_two_buffer(&t, &t2, 1, &desc, stream, &tl));
+    } else {
+        CHECK_ADAM(adam_tl_build(&t, 1, &desc, stream, &tl));
+    }
     for (k = 0; k < hi[2]; ++k) CHECK_ADAM(adam_step(tl, &hp, hf[0], &step, hf[5], NULL, stream));
     CHECK_HIP(hipStreamSynchronize(stream));
     adam_tl_destroy(tl);
@@ -87,7 +102,8 @@ int main(int argc, char **argv)
     out = fopen(argv[2], "wb");
     if (out == NULL) return 2;
     for (i = 0; i < 3; ++i) {
-        CHECK_HIP(hipMemcpy(h[i], d[i], (size_t)n * sizeof(float), hipMemcpyDeviceToHost));
+        const float *src = two && (step & 1) ? d2[i] : d[i];
+        CHECK_HIP(hipMemcpy(h[i], src, (size_t)n * sizeof(float), hipMemcpyDeviceToHost));
         if (fwrite(h[i], sizeof(float), (size_t)n, out) != (size_t)n) return 2;
     }
     if (fwrite(&step, sizeof step, 1, out) != 1) return 2;
@@ -96,6 +112,8 @@ int main(int argc, char **argv)
         CHECK_HIP(hipFree(d[i]));
         free(h[i]);
     }
+    for (i = 0; i < 3; ++i)
+        if (d2[i] != NULL) CHECK_HIP(hipFree(d2[i]));
     CHECK_HIP(hipStreamDestroy(stream));
     return 0;
 }

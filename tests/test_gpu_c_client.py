@@ -2,7 +2,8 @@
 __graft_entry__.build() from tests/c_abi/gpu_step.c) is a C99 program that
 uses only the HIP runtime and the C ABI -- no Python, no torch -- to copy
 one fp32 tensor to the device, run several adam_step calls on a stream of
-its own and copy the result back.  Its output must equal the oracle's, bit
+its own and copy the result back (also with the state in two buffer sets,
+read back from set (step & 1)).  Its output must equal the oracle's, bit
 for bit, and its host counter the number of steps."""
 import os
 import struct
@@ -20,8 +21,9 @@ pytestmark = pytest.mark.gpu
 EXE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "gpu_step")
 
 
-@pytest.mark.parametrize("mode,bias_correction,grad_scale", [(1, 1, 1.0), (0, 1, 0.5), (1, 0, 2.0)])
-def test_c_client_matches_the_oracle(tmp_path, mode, bias_correction, grad_scale):
+@pytest.mark.parametrize("mode,bias_correction,grad_scale,two", [(1, 1, 1.0, False), (0, 1, 0.5, False),
+                                                                (1, 0, 2.0, False), (1, 1, 1.0, True)])
+def test_c_client_matches_the_oracle(tmp_path, mode, bias_correction, grad_scale, two):
     if not torch_mod().cuda.is_available():
         pytest.skip("no GPU")
     assert os.path.exists(EXE), "tests/c_abi/gpu_step is not built (run __graft_entry__.build())"
@@ -34,7 +36,8 @@ def test_c_client_matches_the_oracle(tmp_path, mode, bias_correction, grad_scale
         for a in (h.p, h.m, h.v, h.g):
             f.write(np.ascontiguousarray(a, np.float32).tobytes())
     print(f"c client: n={n} steps={steps} mode={mode} bias_correction={bias_correction}", flush=True)
-    run = subprocess.run([EXE, str(src), str(dst)], capture_output=True, text=True, timeout=120)
+    run = subprocess.run([EXE, str(src), str(dst)] + (["two-buffer"] if two else []), capture_output=True,
+                         text=True, timeout=120)
     assert run.returncode == 0, run.stderr
     raw = np.fromfile(dst, np.uint8)
     got = raw[:3 * 4 * n].view(np.float32).reshape(3, n)
