@@ -65,9 +65,11 @@ def source_hash() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none for this workload or the kernel source changed since."""
+def measured_traffic(workload: str, key: str = "bytes_per_launch"):
+    """HBM bytes per launch from the committed counter summary (`key`:
+    "bytes_per_launch" for the in-place update, "two_buffer_bytes_per_launch"
+    for the two-buffer one), or None when there is none for this workload or
+    the kernel source changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(workload)
@@ -75,7 +77,7 @@ def measured_traffic(workload: str):
         return None
     if not rec or rec.get("source_sha256_16") != source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(key)
 
 
 # The commands behind profiles/: <repo> is the repository root, <out> any
@@ -904,6 +906,7 @@ def main() -> int:
                 "achieved": round(tb_achieved, 2),
                 "frac": round(tb_achieved / HBM_PEAK_GBPS, 4),
                 "vs_in_place": round(tb_wall / wall_ms, 4),
+                "traffic": measured_traffic(w.name, "two_buffer_bytes_per_launch"),
                 "extra_device_bytes": extra,
             }
             for h in tb_handles:

@@ -180,3 +180,15 @@ def test_profile_summary_splits_the_two_buffer_launches(tmp_path, monkeypatch):
     rec = json.loads((tmp_path / "profiles" / "traffic.json").read_text())["tiny"]
     assert rec["ratio"] == 1.0
     assert rec["two_buffer_bytes_per_launch"] == round((read_kib * 0.55 * 2 + write_kib) * 1024)
+
+
+def test_measured_traffic_of_the_two_buffer_step(tmp_path, monkeypatch):
+    rec = {"w": {"bytes_per_launch": 123, "two_buffer_bytes_per_launch": 125,
+                 "source_sha256_16": "0123456789abcdef"}}
+    path = tmp_path / "traffic.json"
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    monkeypatch.setattr(bench, "source_hash", lambda: "0123456789abcdef")
+    assert bench.measured_traffic("w", "two_buffer_bytes_per_launch") == 125
+    monkeypatch.setattr(bench, "source_hash", lambda: "fedcba9876543210")
+    assert bench.measured_traffic("w", "two_buffer_bytes_per_launch") is None
