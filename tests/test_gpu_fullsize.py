@@ -83,7 +83,11 @@ def compare(got, ref, roles):
 
 
 def run_sampled(torch, wname, steps, *, capturable=False, noop_every=0, seed=0,
-                whole_limit=4_000_000):
+                whole_limit=4_000_000, two_buffer=False):
+    """With `two_buffer`, each group's handle also gets a second set of p, m,
+    v (and rem), filled with 0x7B bytes; at the end the sampled state must
+    be the oracle's in set (steps taken & 1) and its state one step earlier
+    in the other set."""
     w = workloads()[wname]
     rng = np.random.default_rng(seed)
     groups = [(w.sizes, w.weight_decay)] + list(w.extra_groups)
@@ -93,6 +97,12 @@ def run_sampled(torch, wname, steps, *, capturable=False, noop_every=0, seed=0,
     rem = w.p_kind == "bf16_rem"
     roles = [r for r in ("p", "rem", "m", "v", "g") if r in bufs]
     out_roles = ["p", "m", "v"] + (["rem"] if rem else []) + (["p_out"] if w.p_out else [])
+    state_roles = [r for r in ("p", "rem", "m", "v") if r in bufs]
+    alt = {}
+    if two_buffer:
+        for r in state_roles:
+            alt[r] = torch.empty_like(bufs[r])
+            alt[r].view(torch.uint8).fill_(0x7B)
     handles, samples = [], []
     off = 0
     for sizes, wd in groups:
@@ -100,8 +110,9 @@ def run_sampled(torch, wname, steps, *, capturable=False, noop_every=0, seed=0,
         pos = sample_positions(sizes, rng, whole_limit) + off
         pos_dev = torch.from_numpy(pos).to("cuda")
         host = {r: gather(torch, bufs[r], pos_dev) for r in roles}
+        alts = group_tensors(alt, sizes, off) if two_buffer else None
         tl = A.adam_tl_build(group_tensors(bufs, sizes, off),
-                             A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=out_type(w)))
+                             A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=out_type(w)), alternates=alts)
         hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
         hr = oracle.HParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
         handles.append(dict(tl=tl, hp=hp, hr=hr, step=A.HostStep(0),
@@ -139,12 +150,20 @@ def run_sampled(torch, wname, steps, *, capturable=False, noop_every=0, seed=0,
             bufs["g"][inf_pos] = saved
             d_noop.fill_(0)
         for h, smp in zip(handles, samples):
+            if two_buffer and not skip:
+                smp["prev"] = {r: getattr(smp["ref"], r).copy() for r in state_roles}
             o.group_step([smp["ref"]], h["hr"], w.lr, h["ref_step"], w.grad_scale,
                          noop=(1 if skip else 0) if capturable else None)
     torch.cuda.synchronize()
     for h, smp in zip(handles, samples):
-        got = {r: gather(torch, bufs[r], smp["pos_dev"]) for r in out_roles}
+        cur = alt if two_buffer and h["ref_step"][0] & 1 else bufs
+        got = {r: gather(torch, cur[r] if r in state_roles else bufs[r], smp["pos_dev"]) for r in out_roles}
         compare(got, smp["ref"], out_roles)
+        if two_buffer:
+            other = bufs if cur is alt else alt
+            before = oracle.OracleTensor(**{r: smp["prev"].get(r) for r in ("p", "m", "v", "rem")},
+                                         g=None, p_out=None)
+            compare({r: gather(torch, other[r], smp["pos_dev"]) for r in state_roles}, before, state_roles)
         want_steps = steps - (steps // noop_every if noop_every else 0)
         assert h["ref_step"][0] == want_steps
         if capturable:
@@ -264,6 +283,23 @@ def test_remainders_capturable_with_noop(torch):
     """The remainder workload through the capturable remainder step, noop on
     every 4th step."""
     run_sampled(torch, "rem5e8", 12, capturable=True, noop_every=4, seed=10, whole_limit=1_000_000)
+
+
+def test_bench201_two_buffer_state_ten_steps(torch):
+    """The benchmark's list with a second buffer set (its two-buffer
+    measurement): ten host steps, then the state in set 0 and the state one
+    step earlier in set 1."""
+    run_sampled(torch, "bench201", 10, seed=12, two_buffer=True)
+
+
+def test_zero_shard_two_buffer_capturable_with_noop(torch):
+    """The ZeRO shard with a second buffer set through the capturable step,
+    noop on every 4th step: the side follows the device counter."""
+    run_sampled(torch, "zero1e9", 11, capturable=True, noop_every=4, seed=13, two_buffer=True)
+
+
+def test_remainders_two_buffer_state(torch):
+    run_sampled(torch, "rem5e8", 7, seed=14, whole_limit=1_000_000, two_buffer=True)
 
 
 def test_single_tensor_beyond_2_pow_31_elements(torch):
