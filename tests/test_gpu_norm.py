@@ -170,22 +170,36 @@ def test_clip_argument_errors(torch):
     assert L.adam_grad_sumsq(None, d.data_ptr(), 0, None) == A.ADAM_EINVAL
 
 
-@pytest.mark.parametrize("g_dtype,p_kind,p_out", [("bf16", "f32", "bf16"), ("bf16", "bf16_rem", "bf16"),
-                                                 ("f16", "f32", "f16"), ("bf16", "f16_scaled", "f16")])
-def test_whole_capturable_step_in_one_graph(torch, orc, g_dtype, p_kind, p_out):
+@pytest.mark.parametrize("g_dtype,p_kind,p_out,two_buffer",
+                         [("bf16", "f32", "bf16", False), ("bf16", "bf16_rem", "bf16", False),
+                          ("f16", "f32", "f16", False), ("bf16", "f16_scaled", "f16", False),
+                          ("bf16", "f32", "bf16", True), ("bf16", "bf16_rem", "bf16", True)])
+def test_whole_capturable_step_in_one_graph(torch, orc, g_dtype, p_kind, p_out, two_buffer):
     """Two groups (decay and no decay): per step the gradient sum of squares
     of both groups, the clip / found-inf step, then the capturable update of
-    each group (fp32 master, bf16 + remainders, or scaled fp16 state), all
-    recorded in one HIP graph and replayed; an infinite gradient on the third
-    replay skips that step.  Each replay equals the oracle fed the same sum
-    of squares."""
+    each group (fp32 master, bf16 + remainders, or scaled fp16 state; also
+    with the state in two buffer sets), all recorded in one HIP graph and
+    replayed; an infinite gradient on the third replay skips that step.
+    Each replay equals the oracle fed the same sum of squares; with two
+    buffer sets the four steps taken leave the state in the first set."""
     h1 = host_tensors([40000, 4096, 333], g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=56)
     h2 = host_tensors([4096] * 3, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=57)
     cap = {"bf16_rem": A.adam_step_remainders_capturable,
            "f16_scaled": A.adam_step_scaled_capturable}.get(p_kind, A.adam_step_capturable)
     d1, d2 = DeviceSet(h1), DeviceSet(h2)
-    t1 = A.adam_tl_build(d1.tensors, desc_for(h1))
-    t2 = A.adam_tl_build(d2.tensors, desc_for(h2))
+    if two_buffer:
+        keep = []
+
+        def second(dev):
+            alts = [{r: torch.full_like(t[r], 7) for r in ("p", "m", "v", "rem") if r in t} for t in dev.tensors]
+            keep.append(alts)
+            return alts
+
+        t1 = A.adam_tl_build(d1.tensors, desc_for(h1), alternates=second(d1))
+        t2 = A.adam_tl_build(d2.tensors, desc_for(h2), alternates=second(d2))
+    else:
+        t1 = A.adam_tl_build(d1.tensors, desc_for(h1))
+        t2 = A.adam_tl_build(d2.tensors, desc_for(h2))
     hp1, hr1 = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
     hp2, hr2 = hp_pair(0.9, 0.95, 1e-8, 0.0, 1)
     d_lr = torch.tensor([1.6e-3], dtype=torch.float32, device="cuda")
