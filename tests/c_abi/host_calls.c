@@ -1,6 +1,6 @@
 /* A C99 client of the library: includes adam.h as a C translation unit and
- * makes the calls that need no GPU (plan, a handle over an empty list, the
- * host step counter of that handle, status strings).  Exit status 0 when
+ * makes the calls that need no GPU (plan, two-buffer plan, a handle over an
+ * empty list, the host step counter of that handle, status strings).  Exit status 0 when
  * every call behaves as the header states, else the number of the first
  * failed check. */
 #include <stdio.h>
@@ -10,7 +10,7 @@
 
 int main(void)
 {
-    adam_tensor t[2];
+    adam_tensor t[2], a[2];
     adam_tl_desc d;
     adam_tl_stats st;
     adam_tl *tl = NULL;
@@ -45,6 +45,28 @@ int main(void)
     adam_tl_destroy(tl);
     adam_tl_destroy(NULL);
     if (strcmp(adam_status_string(ADAM_EDTYPE), adam_status_string(ADAM_OK)) == 0) return 11;
+
+    /* two-buffer state: a second set of p, m, v, 128-byte multiples away */
+    memset(a, 0, sizeof a);
+    a[0].p = (void *)0x500000;
+    a[0].m = (void *)0x600000;
+    a[0].v = (void *)0x700000;
+    a[0].numel = 4096;
+    if (adam_tl_plan_two_buffer(t, a, 2, &d, &st) != ADAM_OK || st.two_buffer != 1 || st.chunks == 0) return 12;
+    if (adam_tl_plan(t, 2, &d, &st) != ADAM_OK || st.two_buffer != 0) return 13;
+    a[0].m = (void *)0x600040; /* 64 bytes off: the sets would not share alignment */
+    if (adam_tl_plan_two_buffer(t, a, 2, &d, &st) != ADAM_EINVAL) return 14;
+    a[0].m = (void *)0x600000;
+    a[0].g = (const void *)0x800000; /* the gradient has one buffer */
+    if (adam_tl_plan_two_buffer(t, a, 2, &d, &st) != ADAM_EINVAL) return 15;
+    a[0].g = NULL;
+    if (adam_tl_plan_two_buffer(t, NULL, 2, &d, &st) != ADAM_EINVAL) return 16;
+    if (adam_tl_build_two_buffer(t, a, 0, &d, 0, &tl) != ADAM_OK || tl == NULL) return 17;
+    step = 0;
+    if (adam_step(tl, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_EINVAL) return 18; /* hp.mode is still 2 */
+    hp.mode = 1;
+    if (adam_step(tl, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_OK || step != 1) return 19;
+    adam_tl_destroy(tl);
     puts("ok");
     return 0;
 }
