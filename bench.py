@@ -112,6 +112,10 @@ PROFILE_COMMANDS = {
                   "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
     "dram_summary": "python bench.py --summarize-dram --workload {w} --dram-req-dir <out>/pmc_dreq_{w} "
                     "--dram-stall-dir <out>/pmc_dstall_{w}",
+    "memunit": "cd /tmp && rocprofv3 --pmc TA_TA_BUSY_sum GRBM_GUI_ACTIVE MemUnitStalled --output-format csv "
+               "-d <out>/pmc_mem_{w} -o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 "
+               "--no-cpu --no-capturable --no-two-buffer",
+    "memunit_summary": "python bench.py --summarize-memunit --workload {w} --memunit-dir <out>/pmc_mem_{w}",
 }
 
 # the kernels that stream the elements: the update, and the scaled-state
@@ -201,6 +205,51 @@ def summarize_occupancy(w, occ_dir: str) -> None:
     lines += ["", "waves/CU: mean resident waves per compute unit over the kernel (4 SIMDs, at most",
               "8 waves each); VGPRs as rocprofv3 reports them for the code object."]
     path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_occupancy.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+XCDS = 8            # GRBM_GUI_ACTIVE adds up the busy cycles of every XCD
+CUS = 256           # one texture-address unit per compute unit
+
+
+def summarize_memunit(w, mem_dir: str) -> None:
+    """Writes profiles/<kernel>_<workload>_memunit.txt: how busy the vector
+    memory path of the main group's kernels is, from one rocprofv3 --pmc
+    pass: TA_TA_BUSY_sum (busy cycles of the 256 texture-address units, the
+    first stage of every vector memory instruction) over GRBM_GUI_ACTIVE
+    (GPU busy cycles summed over the 8 XCDs) and rocprofv3's derived
+    MemUnitStalled (% of time the memory unit is stalled).  The clock implied
+    by GRBM_GUI_ACTIVE / 8 over the dispatch's duration checks that
+    normalisation."""
+    import csv
+
+    cmds = {k: v.format(w=w.name) for k, v in PROFILE_COMMANDS.items()}
+    n0 = sum(w.sizes)
+    prefix = "adam_scaled" if w.p_kind.endswith("_scaled") else "adam_update"
+    vals, grids, times = {}, {}, {}
+    for r in csv.DictReader(open(os.path.join(mem_dir, "run_counter_collection.csv"))):
+        key = (_short(r["Kernel_Name"]), r["Dispatch_Id"])
+        vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
+        times[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
+    per = {}
+    for key, c in vals.items():
+        if grids[key] == big and key[0].startswith(MAIN_KERNELS):
+            per.setdefault(key[0], []).append((c, times[key]))
+    lines = [f"rocprofv3 memory-unit counters: workload {w.name}, main group ({n0:,} elements, {big:,} workgroups)",
+             f"command: {cmds['memunit']}", f"summary: {cmds['memunit_summary']}", "",
+             f"{'kernel':40s} {'n':>3s} {'TA busy %':>10s} {'MemUnitStalled %':>17s} {'implied GHz':>12s}"]
+    for name, cs in sorted(per.items()):
+        busy = statistics.mean(c["TA_TA_BUSY_sum"] / (CUS * c["GRBM_GUI_ACTIVE"] / XCDS) for c, _ in cs)
+        stall = statistics.mean(c["MemUnitStalled"] for c, _ in cs)
+        ghz = statistics.mean(c["GRBM_GUI_ACTIVE"] / XCDS / t / 1e9 for c, t in cs if t > 0)
+        lines.append(f"{name:40s} {len(cs):3d} {100 * busy:10.1f} {stall:17.2f} {ghz:12.2f}")
+    lines += ["", "TA busy: TA_TA_BUSY_sum / (256 units x GRBM_GUI_ACTIVE / 8 XCDs): the share of cycles",
+              "the address units are working; MemUnitStalled: rocprofv3's derived stall percentage."]
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{w.name}_memunit.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -599,6 +648,9 @@ def main() -> int:
     ap.add_argument("--occupancy-dir")
     ap.add_argument("--summarize-dram", action="store_true",
                     help="write profiles/ memory-request summary from two rocprofv3 counter directories (no GPU)")
+    ap.add_argument("--summarize-memunit", action="store_true",
+                    help="write profiles/ memory-unit summary from a rocprofv3 counter directory (no GPU)")
+    ap.add_argument("--memunit-dir")
     ap.add_argument("--dram-req-dir")
     ap.add_argument("--dram-stall-dir")
     args = ap.parse_args()
@@ -618,6 +670,11 @@ def main() -> int:
         from workloads import workloads
 
         summarize_occupancy(workloads()[args.workload], args.occupancy_dir)
+        return 0
+    if args.summarize_memunit:
+        from workloads import workloads
+
+        summarize_memunit(workloads()[args.workload], args.memunit_dir)
         return 0
     if args.summarize_dram:
         from workloads import workloads
