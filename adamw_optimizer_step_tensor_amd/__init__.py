@@ -87,7 +87,7 @@ class AdamTlStats(ctypes.Structure):
     _fields_ = [("tensors", c_i64), ("nonempty", c_i64), ("chunks", c_i64), ("elements", c_i64),
                 ("chunk_elems", c_i64), ("vector_tensors", c_i64), ("grid_blocks", c_i64),
                 ("tile_elems", c_i32), ("block_threads", c_i32), ("bytes_per_elem", c_i32),
-                ("device", c_i32), ("two_buffer", c_i32), ("reserved", c_i32)]
+                ("device", c_i32), ("two_buffer", c_i32), ("pieces", c_i32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}

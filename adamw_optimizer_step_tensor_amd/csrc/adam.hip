@@ -109,6 +109,14 @@ constexpr int64_t kMaxHead = 63;            // a 2-byte stream reaches a 128-byt
 constexpr int kRunElems = ADAM_RUN_ELEMS;   // elements each XCD updates before the next XCD's run
 constexpr uint32_t kRun = uint32_t(kRunElems / kTile);
 constexpr uint32_t kNormRun = ADAM_NORM_RUN_ELEMS / kTile;  // tiles per reduction workgroup
+// Scaled state: a list of at least kPipelineMinTiles tiles (4M elements) in
+// two or more tensors runs its step in up to kMaxPieces pieces of
+// consecutive tensors, pipelined so that one piece's store pass (bound by
+// HBM) runs beside the next piece's maxima pass (bound by the VALU).
+// Measured on MI355X on the 1e9-element fp16-state shard: 4.29 ms in one
+// piece, 4.12 ms in two, 4.02-4.06 ms in four.
+constexpr int kMaxPieces = 4;
+constexpr uint32_t kPipelineMinTiles = (1u << 22) / kTile;
 static_assert(kBlock > kMaxHead, "tile 0 updates the head with one element per lane");
 static_assert(kBlock % 64 == 0, "whole waves");
 static_assert(kMinChunk % kTile == 0 && kRunElems % kTile == 0 && ADAM_NORM_RUN_ELEMS % kTile == 0,
@@ -938,13 +946,13 @@ constexpr int kMaxBlock = 64;
 
 template <class S>
 __global__ __launch_bounds__(kMaxBlock) void adam_scaled_maxima(const WorkItem *__restrict__ items,
-                                                                 uint32_t shift, StepArgs a,
+                                                                 uint32_t shift, uint32_t tile0, StepArgs a,
                                                                  uint32_t *__restrict__ maxima)
 {
     static_assert(kTile == 2 * kLane * kMaxBlock, "two lane groups per lane");
     Coeffs c;
     if (!step_coeffs(a, c)) return;  // a noop step changes nothing (the fold skips too)
-    const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
+    const uint32_t b = tile0 + tile_of_block<kRun>(blockIdx.x, gridDim.x);
     const WorkItem w = items[b >> shift];
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
     const int tid = threadIdx.x;
@@ -971,10 +979,10 @@ __global__ __launch_bounds__(kMaxBlock) void adam_scaled_maxima(const WorkItem *
 // update): reads the reciprocal scales of its tensor from folded[6k + 3 ..].
 template <class S>
 __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__restrict__ items,
-                                                            uint32_t shift, StepArgs a,
+                                                            uint32_t shift, uint32_t tile0, StepArgs a,
                                                             uint32_t *__restrict__ folded)
 {
-    const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
+    const uint32_t b = tile0 + tile_of_block<kRun>(blockIdx.x, gridDim.x);
     const WorkItem w = items[b >> shift];
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
     const int tid = threadIdx.x;
@@ -1007,11 +1015,11 @@ constexpr int kFoldMaxBlock = 256;
 template <int ST>
 __global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t *__restrict__ tile_maxima,
                                                                   const uint32_t *__restrict__ tiles,
-                                                                  uint32_t *__restrict__ folded,
+                                                                  uint32_t *__restrict__ folded, uint32_t k0,
                                                                   const StepBlock *__restrict__ block)
 {
     if (block != nullptr && block->skip) return;
-    const uint32_t k = blockIdx.x;
+    const uint32_t k = k0 + blockIdx.x;
     const uint32_t lo = tiles[2 * k], hi = tiles[2 * k + 1];
     uint32_t x[3] = {0u, 0u, 0u};
     for (uint32_t t = lo + threadIdx.x; t < hi; t += kFoldMaxBlock)
@@ -1035,12 +1043,12 @@ __global__ __launch_bounds__(kFoldMaxBlock) void adam_scaled_fold(const uint32_t
 // One lane per tensor: the new scales, amax / limit (none for a noop step).
 template <int ST>
 __global__ void adam_scaled_finish(float *const *__restrict__ scale_ptrs,
-                                   const uint32_t *__restrict__ folded, uint32_t tensors,
+                                   const uint32_t *__restrict__ folded, uint32_t k0, uint32_t k1,
                                    const StepBlock *__restrict__ block)
 {
     if (block != nullptr && block->skip) return;
-    const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= tensors) return;
+    const uint32_t k = k0 + blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= k1) return;
     float *s = scale_ptrs[k];
 #pragma unroll
     for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(folded[6 * size_t(k) + j]) / scaled_limit<ST>();
@@ -1188,7 +1196,7 @@ __global__ void clip_grad_scale_kernel(const double *d_sumsq, float *d_grad_scal
 // ---------------------------------------------------------------------------
 
 typedef void (*UpdateFn)(const WorkItem *, uint32_t, StepArgs);
-typedef void (*ScaledFn)(const WorkItem *, uint32_t, StepArgs, uint32_t *);
+typedef void (*ScaledFn)(const WorkItem *, uint32_t, uint32_t, StepArgs, uint32_t *);
 
 constexpr int kGradTypes[3] = {kF32, kBF16, kF16};
 constexpr int kOutTypes[3] = {kNone, kBF16, kF16};              // scaled state
@@ -1342,6 +1350,7 @@ int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count
     st.tile_elems = int32_t(tile);
     st.device = -1;
     st.two_buffer = alts != nullptr ? 1 : 0;
+    st.pieces = 1;
 
     std::vector<Span> spans;
     std::vector<int64_t> sizes;  // elements covered by records (a vector body excludes its head)
@@ -1418,6 +1427,8 @@ int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count
     if ((st.chunks << shift) >= kMaxGrid) return ADAM_EINVAL;
     st.chunk_elems = chunk;
     st.grid_blocks = st.chunks << shift;
+    if (scaled && st.nonempty >= 2 && st.grid_blocks >= int64_t(kPipelineMinTiles))
+        st.pieces = int32_t(std::min<int64_t>(kMaxPieces, st.nonempty));
     plan.stats = st;
     plan.shift = shift;
     if (!keep_items) return ADAM_OK;
@@ -1489,6 +1500,7 @@ bool valid_hparams(const adam_hparams *hp)
            (hp->bias_correction == 0 || hp->bias_correction == 1);
 }
 
+
 // What kind of storage a handle updates; each step entry point takes one.
 enum class Kind { Plain, Remainders, Scaled };
 
@@ -1511,6 +1523,13 @@ struct adam_tl {
     uint32_t *d_folded;    // scaled state: three magnitude maxima, then three reciprocal scales, per non-empty tensor
     uint32_t n_tensors;    // non-empty tensors
     int lds_per_cu;        // local data share bytes per compute unit of the device (0: unknown)
+    // scaled state: the step's pieces (consecutive tensors), pipelined over
+    // the caller's stream and `aux` when there are two or more
+    int n_pieces;
+    uint32_t piece_tile[kMaxPieces + 1];    // first tile of each piece, then the grid
+    uint32_t piece_tensor[kMaxPieces + 1];  // first tensor of each piece, then n_tensors
+    hipStream_t aux;                        // null unless n_pieces >= 2
+    hipEvent_t ev[kMaxPieces + 2];          // fork, after each piece's maxima and fold, join
 };
 
 namespace {
@@ -1554,21 +1573,42 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
 {
     const int base = type_pos(kGradTypes, 3, tl->g) +
                      3 * (type_pos(kOutTypes, 3, tl->out) + 3 * (type_pos(kStateTypes, 2, tl->p) + 2 * mode));
-    const dim3 grid(uint32_t(tl->stats.grid_blocks));
-    hipLaunchKernelGGL(ScaledKernels::fns[base], grid, dim3(kMaxBlock), 0, stream, tl->d_items, tl->shift,
-                       args, tl->d_tile_max);
-    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     auto fold = tl->p == kBF16 ? adam_scaled_fold<kBF16> : adam_scaled_fold<kF16>;
-    hipLaunchKernelGGL(fold, dim3(tl->n_tensors), dim3(kFoldMaxBlock), 0, stream,
-                       tl->d_tile_max, tl->d_tiles, tl->d_folded, args.block);
-    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
-    hipLaunchKernelGGL(ScaledKernels::fns[base + 36], grid, dim3(kBlock), 0, stream, tl->d_items, tl->shift,
-                       args, tl->d_folded);
-    if (hipGetLastError() != hipSuccess) return ADAM_EHIP;
     auto finish = tl->p == kBF16 ? adam_scaled_finish<kBF16> : adam_scaled_finish<kF16>;
-    hipLaunchKernelGGL(finish, dim3((tl->n_tensors + 255) / 256), dim3(256), 0, stream,
-                       tl->d_scale_ptrs, tl->d_folded, tl->n_tensors, args.block);
-    return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
+    // piece i: its tiles' maxima, then its tensors' fold ...
+    auto maxima = [&](int i, hipStream_t s) {
+        const uint32_t t0 = tl->piece_tile[i], k0 = tl->piece_tensor[i];
+        hipLaunchKernelGGL(ScaledKernels::fns[base], dim3(tl->piece_tile[i + 1] - t0), dim3(kMaxBlock), 0, s,
+                           tl->d_items, tl->shift, t0, args, tl->d_tile_max);
+        hipLaunchKernelGGL(fold, dim3(tl->piece_tensor[i + 1] - k0), dim3(kFoldMaxBlock), 0, s,
+                           tl->d_tile_max, tl->d_tiles, tl->d_folded, k0, args.block);
+        return hipGetLastError() == hipSuccess;
+    };
+    // ... and its store pass, then its tensors' new scales
+    auto store = [&](int i, hipStream_t s) {
+        const uint32_t t0 = tl->piece_tile[i], k0 = tl->piece_tensor[i], k1 = tl->piece_tensor[i + 1];
+        hipLaunchKernelGGL(ScaledKernels::fns[base + 36], dim3(tl->piece_tile[i + 1] - t0), dim3(kBlock), 0, s,
+                           tl->d_items, tl->shift, t0, args, tl->d_folded);
+        hipLaunchKernelGGL(finish, dim3((k1 - k0 + 255) / 256), dim3(256), 0, s, tl->d_scale_ptrs, tl->d_folded,
+                           k0, k1, args.block);
+        return hipGetLastError() == hipSuccess;
+    };
+    if (tl->n_pieces <= 1) return maxima(0, stream) && store(0, stream) ? ADAM_OK : ADAM_EHIP;
+    // Pieces alternate between the caller's stream and aux; piece i starts
+    // once piece i-1's maxima and fold are done, so its maxima pass runs
+    // beside piece i-1's store pass.  Events fork aux from the caller's
+    // stream and join it back (the same pattern holds under graph capture).
+    if (hipEventRecord(tl->ev[0], stream) != hipSuccess || hipStreamWaitEvent(tl->aux, tl->ev[0], 0) != hipSuccess)
+        return ADAM_EHIP;
+    for (int i = 0; i < tl->n_pieces; ++i) {
+        hipStream_t s = i % 2 == 0 ? stream : tl->aux;
+        if (i > 0 && hipStreamWaitEvent(s, tl->ev[i], 0) != hipSuccess) return ADAM_EHIP;
+        if (!maxima(i, s) || hipEventRecord(tl->ev[i + 1], s) != hipSuccess || !store(i, s)) return ADAM_EHIP;
+    }
+    const int j = tl->n_pieces + 1;
+    if (hipEventRecord(tl->ev[j], tl->aux) != hipSuccess || hipStreamWaitEvent(stream, tl->ev[j], 0) != hipSuccess)
+        return ADAM_EHIP;
+    return ADAM_OK;
 }
 
 int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
@@ -1647,6 +1687,52 @@ const char *adam_status_string(int status)
 
 namespace {
 
+// Destroys the pipelining stream and events of a handle (if any).
+void release_pieces(adam_tl *tl)
+{
+    for (hipEvent_t &e : tl->ev) {
+        if (e != nullptr) (void)hipEventDestroy(e);
+        e = nullptr;
+    }
+    if (tl->aux != nullptr) (void)hipStreamDestroy(tl->aux);
+    tl->aux = nullptr;
+    tl->n_pieces = 1;
+}
+
+// Splits a large scaled-state list into pieces of consecutive tensors of
+// about equal tiles and creates the second stream and the events that
+// pipeline them.  Anything that cannot be created leaves one piece (the
+// same results, one sequence of launches).
+void plan_pieces(adam_tl *tl, const std::vector<uint32_t> &tile_ranges)
+{
+    const uint32_t tiles = uint32_t(tl->stats.grid_blocks);
+    const int n = int(std::min<uint32_t>(kMaxPieces, tl->n_tensors));
+    if (n < 2 || tiles < kPipelineMinTiles) return;
+    uint32_t k = 0;
+    for (int i = 1; i < n; ++i) {
+        const uint64_t target = uint64_t(tiles) * uint64_t(i) / uint64_t(n);
+        k = std::max(k, tl->piece_tensor[i - 1] + 1);
+        while (k + uint32_t(n - i) < tl->n_tensors && tile_ranges[2 * k] < target) ++k;
+        tl->piece_tensor[i] = k;
+        tl->piece_tile[i] = tile_ranges[2 * k];
+    }
+    tl->piece_tensor[n] = tl->n_tensors;
+    tl->piece_tile[n] = tiles;
+    bool ok = hipStreamCreateWithFlags(&tl->aux, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; ok && i < n + 2; ++i)
+        ok = hipEventCreateWithFlags(&tl->ev[i], hipEventDisableTiming) == hipSuccess;
+    if (ok) {
+        tl->n_pieces = n;
+        tl->stats.pieces = n;
+        return;
+    }
+    (void)hipGetLastError();
+    release_pieces(tl);
+    tl->stats.pieces = 1;
+    tl->piece_tile[1] = tiles;
+    tl->piece_tensor[1] = tl->n_tensors;
+}
+
 int plan_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count, const adam_tl_desc *desc,
             adam_tl_stats *stats)
 {
@@ -1696,6 +1782,13 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     tl->d_folded = nullptr;
     tl->n_tensors = uint32_t(plan.stats.nonempty);
     tl->lds_per_cu = 0;
+    tl->n_pieces = 1;
+    tl->piece_tile[0] = 0;
+    tl->piece_tile[1] = uint32_t(plan.stats.grid_blocks);
+    tl->piece_tensor[0] = 0;
+    tl->piece_tensor[1] = tl->n_tensors;
+    tl->aux = nullptr;
+    for (hipEvent_t &e : tl->ev) e = nullptr;
     if (plan.items.empty()) {  // nothing to launch: no device state at all
         *out = tl;
         return ADAM_OK;
@@ -1755,6 +1848,7 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
         delete tl;
         return ADAM_EHIP;
     }
+    if (scaled) plan_pieces(tl, plan.tile_ranges);
     *out = tl;
     return ADAM_OK;
 }
@@ -1799,6 +1893,7 @@ void adam_tl_destroy(adam_tl *tl)
     if (tl == nullptr) return;
     if (tl->d_items != nullptr) {
         DeviceGuard guard(tl->stats.device);
+        release_pieces(tl);
         (void)hipFree(tl->d_items);
     }
     delete tl;

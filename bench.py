@@ -121,9 +121,34 @@ PROFILE_COMMANDS = {
 # the kernels that stream the elements: the update, and the scaled-state
 # maxima and store passes
 MAIN_KERNELS = ("adam_update", "adam_scaled_maxima", "adam_scaled_pass")
+# the kernels of one scaled-state step, once per piece
+SCALED_STEP_KERNELS = ("adam_scaled_maxima", "adam_scaled_fold", "adam_scaled_pass", "adam_scaled_finish")
 
 CU_NUM = 256
 XCD_NUM = 8
+
+
+def _plan_pieces(w) -> int:
+    """Pieces a scaled-state step of the workload's first group runs in, from
+    a host-only plan of its tensor list (addresses are never dereferenced)."""
+    import adamw_optimizer_step_tensor_amd as A
+
+    base, stride = 1 << 44, 1 << 38
+    tensors = [dict(p=base + (8 * i) * stride, m=base + (8 * i + 1) * stride, v=base + (8 * i + 2) * stride,
+                    g=base + (8 * i + 3) * stride, scales=base + (8 * i + 4) * stride,
+                    p_out=base + (8 * i + 5) * stride if w.p_out else None, numel=n)
+               for i, n in enumerate(w.sizes)]
+    p_out = ("bf16" if w.p_out is True else w.p_out) or None
+    return A.adam_tl_plan(tensors, A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out))["pieces"]
+
+
+def _main_dispatches(names_grids, scaled):
+    """The (kernel, dispatch) keys of the step's main kernels: for scaled
+    state every piece's (each has its own grid), else the largest grid."""
+    if scaled:
+        return {k for k in names_grids if k[0].startswith(MAIN_KERNELS)}
+    big = max(g for (n, _), g in names_grids.items() if n.startswith(MAIN_KERNELS))
+    return {k for k, g in names_grids.items() if g == big and k[0].startswith(MAIN_KERNELS)}
 
 
 def summarize_valu(w, valu_dir: str) -> None:
@@ -146,16 +171,18 @@ def summarize_valu(w, valu_dir: str) -> None:
         key = (name, r["Dispatch_Id"])
         vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
         grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
-    big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
+    main = _main_dispatches(grids, scaled)
     per = {}
     for key, c in vals.items():
-        if grids[key] == big and key[0].startswith(MAIN_KERNELS):
+        if key in main:
             per.setdefault(key[0], []).append(c)
-    lines = [f"rocprofv3 VALU counters: workload {w.name}, main group ({n0:,} elements)",
+    pieces = _plan_pieces(w) if scaled else 1
+    lines = [f"rocprofv3 VALU counters: workload {w.name}, main group ({n0:,} elements"
+             + (f", {pieces} piece(s) per step)" if scaled else ")"),
              f"command: {cmds['valu']}", f"summary: {cmds['valu_summary']}", "",
              f"{'kernel':40s} {'n':>3s} {'VALU insts/elem':>16s} {'VALU busy %':>12s} {'waves':>12s}"]
     for name, cs in sorted(per.items()):
-        insts = statistics.mean(c["SQ_INSTS_VALU"] for c in cs)
+        insts = sum(c["SQ_INSTS_VALU"] for c in cs) / (len(cs) / pieces)  # per step
         active = statistics.mean(c["SQ_ACTIVE_INST_VALU"] for c in cs)
         gui = statistics.mean(c["GRBM_GUI_ACTIVE"] for c in cs) / XCD_NUM  # per-XCD cycles
         waves = statistics.mean(c["SQ_WAVES"] for c in cs)
@@ -189,12 +216,15 @@ def summarize_occupancy(w, occ_dir: str) -> None:
         vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
         grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
         regs[name] = (int(r["Workgroup_Size"]), int(r["VGPR_Count"]), int(r["SGPR_Count"]), int(r["LDS_Block_Size"]))
-    big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
+    scaled = w.p_kind.endswith("_scaled")
+    main = _main_dispatches(grids, scaled)
+    big = max(grids[k] for k in main)
     per = {}
     for key, c in vals.items():
-        if grids[key] == big and key[0].startswith(MAIN_KERNELS):
+        if key in main:
             per.setdefault(key[0], []).append(c)
-    lines = [f"rocprofv3 occupancy: workload {w.name}, main group ({n0:,} elements, {big:,} workgroups)",
+    lines = [f"rocprofv3 occupancy: workload {w.name}, main group ({n0:,} elements, "
+             + ("every piece of the step)" if scaled else f"{big:,} workgroups)"),
              f"command: {cmds['occupancy']}", f"summary: {cmds['occupancy_summary']}", "",
              f"{'kernel':40s} {'n':>3s} {'waves/CU':>9s} {'% of 32':>8s} {'wg size':>8s} {'VGPRs':>6s} {'SGPRs':>6s} {'LDS':>6s}"]
     for name, cs in sorted(per.items()):
@@ -234,12 +264,15 @@ def summarize_memunit(w, mem_dir: str) -> None:
         vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
         grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
         times[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
-    big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
+    scaled = w.p_kind.endswith("_scaled")
+    main = _main_dispatches(grids, scaled)
+    big = max(grids[k] for k in main)
     per = {}
     for key, c in vals.items():
-        if grids[key] == big and key[0].startswith(MAIN_KERNELS):
+        if key in main:
             per.setdefault(key[0], []).append((c, times[key]))
-    lines = [f"rocprofv3 memory-unit counters: workload {w.name}, main group ({n0:,} elements, {big:,} workgroups)",
+    lines = [f"rocprofv3 memory-unit counters: workload {w.name}, main group ({n0:,} elements, "
+             + ("every piece of the step)" if scaled else f"{big:,} workgroups)"),
              f"command: {cmds['memunit']}", f"summary: {cmds['memunit_summary']}", "",
              f"{'kernel':40s} {'n':>3s} {'TA busy %':>10s} {'MemUnitStalled %':>17s} {'implied GHz':>12s}"]
     for name, cs in sorted(per.items()):
@@ -415,8 +448,21 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
             d = sorted(per.pop((name, grid)))
             per[(name, grid)], per[(name + TWO_BUFFER_TAG, grid)] = d[:-n_tb], d[-n_tb:]
     per = {k: [dur for _, dur in v] for k, v in per.items()}
+    pieces = int(((bench_line or {}).get("config") or {}).get("pieces", 1))
+    spans = []
+    if scaled:
+        # a scaled step is 4 kernels per piece, the pieces pipelined over two
+        # streams; its time is its first dispatch's start to its last's end
+        disp = []
+        for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
+            if _short(r["Kernel_Name"]).startswith(SCALED_STEP_KERNELS):
+                disp.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+        disp.sort()
+        k = 4 * pieces
+        spans = [(max(e for _, e in disp[i:i + k]) - disp[i][0]) / 1e6 for i in range(0, len(disp) - k + 1, k)]
     lines += ["", ("scaled-state passes" if scaled else "update kernel") +
-              " per dispatch (main group = the largest grid):",
+              (f" per dispatch ({pieces} piece(s) per step, each its own grid):" if scaled else
+               " per dispatch (main group = the largest grid):"),
               f"{'kernel':46s} {'workgroups':>13s} {'calls':>5s} {'avg ms':>9s} {'min ms':>9s} "
               f"{'max ms':>9s} {'GB/s(avg)':>10s}"]
     for (name, grid), durs in sorted(per.items()):
@@ -424,19 +470,24 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
         gbps = f"{algo / (avg * 1e-3) / 1e9:10.1f}" if grid == big and not scaled else ""
         lines.append(f"{name:46s} {grid:13d} {len(durs):5d} {avg:9.3f} {min(durs):9.3f} "
                      f"{max(durs):9.3f} {gbps}")
-    if scaled:
-        # both passes of the main group make one step (the fold and scales
-        # kernels are a few microseconds)
-        passes = [statistics.mean(d) for (name, grid), d in per.items() if grid == big]
-        lines.append(f"both passes of one step: {sum(passes):.3f} ms; algorithmic bytes per step "
-                     f"{algo / 1e9:.3f} GB -> {algo / (sum(passes) * 1e-3) / 1e9:.1f} GB/s")
+    if scaled and spans:
+        # kernel time per step: every piece's maxima and store pass
+        kern = sum(sum(d) for d in per.values()) / len(spans)
+        step = statistics.mean(spans)
+        lines.append(f"one step: {step:.3f} ms from its first dispatch to its last (mean of {len(spans)} steps), "
+                     f"{kern:.3f} ms of maxima and store pass time summed over its pieces; algorithmic bytes "
+                     f"per step {algo / 1e9:.3f} GB -> {algo / (step * 1e-3) / 1e9:.1f} GB/s")
     if trace_log:
         assert bench_line is not None, f"no bench line in {trace_log}"
         lines += ["", "bench.py in the same traced process (HIP events on the launch stream) vs the "
                       "trace's average over the same main-group dispatches:"]
         if scaled:
-            pairs = [("scaled step (both passes + fold + scales)", bench_line["roofline"]["launch_ms_mean"],
-                      sum(statistics.mean(d) for (n, g), d in per.items() if g == big))]
+            nw = bench_line["warmup"] + bench_line["steps"]
+            pairs = [("scaled step, regular (all pieces)", bench_line["roofline"]["launch_ms_mean"],
+                      statistics.mean(spans[:nw]))]
+            if "capturable" in bench_line and len(spans) >= 2 * nw:
+                pairs.append(("scaled step, capturable", bench_line["capturable"]["launch_ms_mean"],
+                              statistics.mean(spans[nw:2 * nw])))
         else:
             def trace_avg(capt):
                 d = [x for (n, g), v in per.items() if g == big and n.endswith(f"{capt}>") for x in v]
@@ -466,7 +517,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
         agg = {}
         for r in rows:
             name = _short(r["Kernel_Name"])
-            if main_kernel(name) and int(r["Grid_Size"]) // int(r["Workgroup_Size"]) != big:
+            if not scaled and main_kernel(name) and int(r["Grid_Size"]) // int(r["Workgroup_Size"]) != big:
                 name += " (small group)"
             agg.setdefault(name, []).append(float(r["Counter_Value"]))
         n = 0 if scaled else _two_buffer_launches(_bench_line(log))
@@ -495,8 +546,15 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
     tb_traffic = None
     if tb_key and tb_key[0] in write:
         tb_traffic = (statistics.mean(fetch[tb_key[0]]) * f_factor + statistics.mean(write[tb_key[0]]) * w_factor) * 1024
-    fetch_kib = sum(statistics.mean(fetch[k]) for k in upd)
-    write_kib = sum(statistics.mean(write[k]) for k in upd)
+    if scaled:
+        # every piece's dispatches of both passes, per step
+        line_f = _bench_line(fetch_log)
+        steps_run = line_f["warmup"] + line_f["steps"] if line_f else len(fetch[upd[0]])
+        fetch_kib = sum(sum(fetch[k]) for k in upd) / steps_run
+        write_kib = sum(sum(write[k]) for k in upd) / steps_run
+    else:
+        fetch_kib = sum(statistics.mean(fetch[k]) for k in upd)
+        write_kib = sum(statistics.mean(write[k]) for k in upd)
     k = " + ".join(upd)
     traffic = (fetch_kib * f_factor + write_kib * w_factor) * 1024
     lines = [f"rocprofv3 counters: workload {w.name}, kernel {k} (main group, {n0:,} elements)",
@@ -816,6 +874,7 @@ def main() -> int:
             "grid_blocks": info["grid_blocks"],
             "block_threads": info["block_threads"],
             "tile_elems": info["tile_elems"],
+            "pieces": info["pieces"],
         },
         "elements_per_s": round(total / (wall_ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),

@@ -144,7 +144,11 @@ typedef struct {
     int32_t bytes_per_elem;  /* algorithmic HBM bytes per element (read + write)  */
     int32_t device;          /* HIP device of the handle (-1 from adam_tl_plan)   */
     int32_t two_buffer;      /* 1: built by adam_tl_build_two_buffer               */
-    int32_t reserved;        /* 0                                                 */
+    int32_t pieces;          /* scaled state: pieces of consecutive tensors the
+                                step is pipelined in over the caller's stream
+                                and a second stream of the handle (lists of at
+                                least 4M elements in two or more tensors: up to
+                                4); 1 otherwise                                   */
 } adam_tl_stats;
 
 typedef struct adam_tl adam_tl; /* opaque handle: device work table */
