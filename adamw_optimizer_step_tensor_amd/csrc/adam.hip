@@ -114,8 +114,9 @@ constexpr uint32_t kNormRun = ADAM_NORM_RUN_ELEMS / kTile;  // tiles per reducti
 // consecutive tensors, pipelined so that one piece's store pass (bound by
 // HBM) runs beside the next piece's maxima pass (bound by the VALU).
 // Measured on MI355X on the 1e9-element fp16-state shard: 4.29 ms in one
-// piece, 4.12 ms in two, 4.02-4.06 ms in four.
-constexpr int kMaxPieces = 4;
+// piece, 4.12 ms in two, 4.02-4.06 ms in four; in one later process at most
+// 2, 4, 6 and 8 pieces gave 4.40, 4.32, 4.29 and 4.25 ms.
+constexpr int kMaxPieces = 8;
 constexpr uint32_t kPipelineMinTiles = (1u << 22) / kTile;
 static_assert(kBlock > kMaxHead, "tile 0 updates the head with one element per lane");
 static_assert(kBlock % 64 == 0, "whole waves");

@@ -148,7 +148,7 @@ typedef struct {
                                 step is pipelined in over the caller's stream
                                 and a second stream of the handle (lists of at
                                 least 4M elements in two or more tensors: up to
-                                4); 1 otherwise                                   */
+                                8); 1 otherwise                                   */
 } adam_tl_stats;
 
 typedef struct adam_tl adam_tl; /* opaque handle: device work table */
