@@ -73,3 +73,30 @@ def test_pipelined_scaled_steps_match_the_oracle(torch, p_kind, g_dtype, p_out):
         assert_bitwise(dev.readback(), ref, ctx=f"graph replay lr {lr}")
     del graph
     tl.destroy()
+
+
+@pytest.mark.parametrize("sizes", [
+    [(1 << 22) + 4097, 1],                       # two tensors, one of them a single element
+    [1] * 9 + [(1 << 22) + 3],                   # many tiny tensors, then one that holds the tiles
+    [700001, 3, 1 << 20, 5, 1 << 21, 77, 900000, 65536, 1 << 20, 9],  # ten uneven tensors
+])
+def test_pieces_cover_every_tensor_once(torch, sizes):
+    """However the list is cut into pieces (each at least one tensor, about
+    equal tiles), every tensor's values, scales and param-sync copy equal
+    the oracle's after two steps."""
+    host = host_tensors(sizes, g_dtype="bf16", p_kind="f16_scaled", p_out="bf16", seed=len(sizes),
+                        m_v_init="random")
+    assert sum(sizes) >= 1 << 22
+    ref = copies(host)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    assert tl.info()["pieces"] == min(8, len(sizes))
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    orc = oracle.default()
+    ot, st, step = oracle_tensors(ref), [0], A.HostStep(0)
+    for _ in range(2):
+        A.adam_step_scaled(tl, hl, 1.6e-3, step)
+        orc.group_step(ot, hr, 1.6e-3, st, 1.0)
+    torch.cuda.synchronize()
+    assert_bitwise(dev.readback(), ref, ctx=f"{len(sizes)} tensors")
+    tl.destroy()
