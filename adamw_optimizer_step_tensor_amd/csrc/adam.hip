@@ -63,6 +63,10 @@
 //    stores it with those; a one-lane-per-tensor kernel then writes the
 //    scales.  (Folding with one atomic maximum per workgroup instead was
 //    measured 8x slower: a tensor's ~1000 workgroups contend for one word.)
+//    A large list's step runs in up to 8 pieces of consecutive tensors,
+//    alternating between the caller's stream and a second stream of the
+//    handle, each piece's maxima pass (VALU-bound) beside the previous
+//    piece's store pass (HBM-bound); events fork and join the streams.
 //  * Arithmetic follows the header's expressions operation for operation in
 //    binary32 (the library is built with -ffp-contract=off; division and
 //    square root are correctly rounded -- the compiler's sequences, or for
