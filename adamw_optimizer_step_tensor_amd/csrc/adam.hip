@@ -63,7 +63,7 @@
 //    stores it with those; a one-lane-per-tensor kernel then writes the
 //    scales.  (Folding with one atomic maximum per workgroup instead was
 //    measured 8x slower: a tensor's ~1000 workgroups contend for one word.)
-//    A large list's step runs in up to 8 pieces of consecutive tensors,
+//    A large list's step runs in up to 16 pieces of consecutive tensors,
 //    alternating between the caller's stream and a second stream of the
 //    handle, each piece's maxima pass (VALU-bound) beside the previous
 //    piece's store pass (HBM-bound); events fork and join the streams.
@@ -115,13 +115,23 @@ constexpr uint32_t kRun = uint32_t(kRunElems / kTile);
 constexpr uint32_t kNormRun = ADAM_NORM_RUN_ELEMS / kTile;  // tiles per reduction workgroup
 // Scaled state: a list of at least kPipelineMinTiles tiles (4M elements) in
 // two or more tensors runs its step in up to kMaxPieces pieces of
-// consecutive tensors, pipelined so that one piece's store pass (bound by
-// HBM) runs beside the next piece's maxima pass (bound by the VALU).
-// Measured on MI355X on the 1e9-element fp16-state shard: 4.29 ms in one
-// piece, 4.12 ms in two, 4.02-4.06 ms in four; in one later process at most
-// 2, 4, 6 and 8 pieces gave 4.40, 4.32, 4.29 and 4.25 ms.
-constexpr int kMaxPieces = 8;
+// consecutive tensors, each piece at least kMinPieceTiles tiles (512K
+// elements), pipelined so that one piece's store pass (bound by HBM) runs
+// beside the next piece's maxima pass (bound by the VALU).  Measured on
+// MI355X on the 1e9-element fp16-state shard: 4.29 ms in one piece, 4.12 ms
+// in two, 4.02-4.06 ms in four; in one later process at most 2, 4, 6 and 8
+// pieces gave 4.40, 4.32, 4.29 and 4.25 ms; in a third, 8, 16, 24 and 32
+// pieces gave 4.12-4.15, 4.08-4.10, 4.13-4.17 and 4.23-4.24 ms.
+constexpr int kMaxPieces = 16;
 constexpr uint32_t kPipelineMinTiles = (1u << 22) / kTile;
+constexpr uint32_t kMinPieceTiles = (1u << 19) / kTile;
+
+// Pieces of a scaled step over `tensors` nonempty tensors and `tiles` tiles.
+int piece_count(int64_t tensors, int64_t tiles)
+{
+    if (tensors < 2 || tiles < int64_t(kPipelineMinTiles)) return 1;
+    return int(std::min<int64_t>(std::min<int64_t>(kMaxPieces, tensors), tiles / kMinPieceTiles));
+}
 static_assert(kBlock > kMaxHead, "tile 0 updates the head with one element per lane");
 static_assert(kBlock % 64 == 0, "whole waves");
 static_assert(kMinChunk % kTile == 0 && kRunElems % kTile == 0 && ADAM_NORM_RUN_ELEMS % kTile == 0,
@@ -1432,8 +1442,7 @@ int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count
     if ((st.chunks << shift) >= kMaxGrid) return ADAM_EINVAL;
     st.chunk_elems = chunk;
     st.grid_blocks = st.chunks << shift;
-    if (scaled && st.nonempty >= 2 && st.grid_blocks >= int64_t(kPipelineMinTiles))
-        st.pieces = int32_t(std::min<int64_t>(kMaxPieces, st.nonempty));
+    if (scaled) st.pieces = int32_t(piece_count(st.nonempty, st.grid_blocks));
     plan.stats = st;
     plan.shift = shift;
     if (!keep_items) return ADAM_OK;
@@ -1711,8 +1720,8 @@ void release_pieces(adam_tl *tl)
 void plan_pieces(adam_tl *tl, const std::vector<uint32_t> &tile_ranges)
 {
     const uint32_t tiles = uint32_t(tl->stats.grid_blocks);
-    const int n = int(std::min<uint32_t>(kMaxPieces, tl->n_tensors));
-    if (n < 2 || tiles < kPipelineMinTiles) return;
+    const int n = piece_count(tl->n_tensors, tiles);
+    if (n < 2) return;
     uint32_t k = 0;
     for (int i = 1; i < n; ++i) {
         const uint64_t target = uint64_t(tiles) * uint64_t(i) / uint64_t(n);

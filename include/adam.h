@@ -146,10 +146,12 @@ typedef struct {
     int32_t two_buffer;      /* 1: built by adam_tl_build_two_buffer               */
     int32_t pieces;          /* scaled state: pieces of consecutive tensors the
                                 step is pipelined in over the caller's stream
-                                and a second stream of the handle: up to 8 for
-                                a list of two or more tensors whose work table
-                                holds at least 8192 tiles (grid_blocks, about
-                                4M elements); 1 otherwise                         */
+                                and a second stream of the handle, for a list
+                                of two or more tensors whose work table holds
+                                at least 8192 tiles (grid_blocks, about 4M
+                                elements): the least of 16, the tensors and
+                                grid_blocks / 1024 (a piece holds at least
+                                1024 tiles, 512K elements); 1 otherwise          */
 } adam_tl_stats;
 
 typedef struct adam_tl adam_tl; /* opaque handle: device work table */

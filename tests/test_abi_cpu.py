@@ -407,10 +407,13 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 def test_scaled_plans_report_their_pieces():
     """A scaled-state list of at least 8192 tiles (4M elements, tensor ends
     rounded up to whole records) in two or more tensors is pipelined in
-    min(8, tensors) pieces; anything else runs in one."""
+    min(16, tensors, tiles / 1024) pieces; anything else runs in one."""
     big = [1 << 21, 1 << 21]
     assert plan(fake_tensors(big, scaled=True), p="f16_scaled")["pieces"] == 2
-    assert plan(fake_tensors([1 << 20] * 12, scaled=True), p="bf16_scaled")["pieces"] == 8
+    assert plan(fake_tensors([1 << 20] * 12, scaled=True), p="bf16_scaled")["pieces"] == 12
+    assert plan(fake_tensors([1 << 20] * 20, scaled=True), p="f16_scaled")["pieces"] == 16  # 40960 tiles
+    assert plan(fake_tensors([1 << 18] * 20, scaled=True), p="f16_scaled")["pieces"] == 10  # 10240 tiles
+    assert plan(fake_tensors([1 << 19] * 8 + [1], scaled=True), p="f16_scaled")["pieces"] == 8  # 8193 tiles
     assert plan(fake_tensors([1 << 21, 1], scaled=True), p="f16_scaled")["pieces"] == 1  # 4224 tiles
     assert plan(fake_tensors([1 << 23], scaled=True), p="f16_scaled")["pieces"] == 1  # one tensor
     assert plan(fake_tensors(big), p="f32")["pieces"] == 1  # not scaled

@@ -75,12 +75,13 @@ def test_pipelined_scaled_steps_match_the_oracle(torch, p_kind, g_dtype, p_out):
     tl.destroy()
 
 
-@pytest.mark.parametrize("sizes", [
-    [(1 << 22) + 4097, 1],                       # two tensors, one of them a single element
-    [1] * 9 + [(1 << 22) + 3],                   # many tiny tensors, then one that holds the tiles
-    [700001, 3, 1 << 20, 5, 1 << 21, 77, 900000, 65536, 1 << 20, 9],  # ten uneven tensors
+@pytest.mark.parametrize("sizes,pieces", [
+    ([(1 << 22) + 4097, 1], 2),                  # two tensors, one of them a single element
+    ([1] * 9 + [(1 << 22) + 3], 8),              # many tiny tensors, then one that holds the tiles
+    ([700001, 3, 1 << 20, 5, 1 << 21, 77, 900000, 65536, 1 << 20, 9], 10),  # ten uneven tensors
+    ([(1 << 19) + 977 * i for i in range(20)], 16),  # twenty tensors: the most pieces
 ])
-def test_pieces_cover_every_tensor_once(torch, sizes):
+def test_pieces_cover_every_tensor_once(torch, sizes, pieces):
     """However the list is cut into pieces (each at least one tensor, about
     equal tiles), every tensor's values, scales and param-sync copy equal
     the oracle's after two steps."""
@@ -90,7 +91,7 @@ def test_pieces_cover_every_tensor_once(torch, sizes):
     ref = copies(host)
     dev = DeviceSet(host)
     tl = A.adam_tl_build(dev.tensors, desc_for(host))
-    assert tl.info()["pieces"] == min(8, len(sizes))
+    assert tl.info()["pieces"] == pieces
     hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
     orc = oracle.default()
     ot, st, step = oracle_tensors(ref), [0], A.HostStep(0)
