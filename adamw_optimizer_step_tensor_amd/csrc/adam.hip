@@ -108,7 +108,14 @@ constexpr int64_t kMinChunk = 1024;
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
 constexpr int64_t kAutoChunkMax = 65536;
 constexpr int64_t kMaxNumel = int64_t(1) << 56;
-constexpr int64_t kMaxGrid = int64_t(1) << 31;
+constexpr int64_t kMaxGrid = int64_t(1) << 31;  // tiles of one list (32-bit tile indices)
+// Tiles of one dispatch.  A dispatch packet counts its grid in work-items
+// with 32 bits, so a dispatch of 128-thread workgroups holds fewer than 2^25
+// of them (64-thread ones fewer than 2^26); larger lists are launched as
+// several dispatches, each over consecutive tiles.  A multiple of the XCD
+// group (8 XCDs x kRun tiles) keeps every dispatch but the last in the
+// XCD-ordered tile map.
+constexpr int64_t kDispatchTiles = (int64_t(1) << 25) - 512;
 constexpr int64_t kMaxHead = 63;            // a 2-byte stream reaches a 128-byte boundary within 63 elements
 constexpr int kRunElems = ADAM_RUN_ELEMS;   // elements each XCD updates before the next XCD's run
 constexpr uint32_t kRun = uint32_t(kRunElems / kTile);
@@ -134,6 +141,8 @@ int piece_count(int64_t tensors, int64_t tiles)
 }
 static_assert(kBlock > kMaxHead, "tile 0 updates the head with one element per lane");
 static_assert(kBlock % 64 == 0, "whole waves");
+static_assert(kDispatchTiles % (8 * kRun) == 0 && kDispatchTiles * kBlock <= int64_t(UINT32_MAX),
+              "a dispatch keeps whole XCD groups and a 32-bit work-item count");
 static_assert(kMinChunk % kTile == 0 && kRunElems % kTile == 0 && ADAM_NORM_RUN_ELEMS % kTile == 0,
               "records and runs hold whole tiles");
 
@@ -672,13 +681,13 @@ __device__ __forceinline__ bool step_coeffs(const StepArgs &a, Coeffs &c)
     return true;
 }
 
-// The update: workgroup b handles tile t = tile_of_block(b): tile
-// (t & mask) of work item (t >> shift).
+// The update: workgroup b of a dispatch that starts at tile `tile0` handles
+// tile t = tile0 + tile_of_block(b): tile (t & mask) of work item (t >> shift).
 template <class C>
 __global__ __launch_bounds__(kBlock) void adam_update(const WorkItem *__restrict__ items,
-                                                       uint32_t shift, StepArgs a)
+                                                       uint32_t shift, uint32_t tile0, StepArgs a)
 {
-    const uint32_t b = tile_of_block<kRun>(blockIdx.x, gridDim.x);
+    const uint32_t b = tile0 + tile_of_block<kRun>(blockIdx.x, gridDim.x);
     const WorkItem w = items[b >> shift];
     const int start = int(b & ((1u << shift) - 1u)) * kTile;
     if (start >= w.n) return;  // past the end of a tensor's last item
@@ -894,9 +903,12 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x)
 // max|p~| - 2.5 E has an exact magnitude below that one's; so the exact
 // maximum is the maximum over the elements at or above the cut, each
 // recomputed exactly.  The bound assumes finite values clear of overflow and
-// a normal (or zero) v_hat: a wave with a subnormal v_hat, or |q~|, |u~|, |t~|
-// or |p~| not below 2^126 (NaN included), recomputes all its elements, as
-// does every wave when `approx` is off (eps < 0 or >= 2^125, |lr| >= 2^126).
+// a normal (or zero) v_hat: a wave with a subnormal v_hat of either sign (the
+// hardware root flushes it to a signed zero, where the exact root of a
+// negative one is NaN), or |q~|, |u~|, |t~| or |p~| not below 2^126 (NaN
+// included; a negative normal v_hat gives NaN in both chains), recomputes
+// all its elements, as does every wave when `approx` is off (eps < 0 or
+// >= 2^125, |lr| >= 2^126).
 template <class S, int G>
 __device__ __forceinline__ void scaled_group_max(const WorkItem &w, int gi0, int groups, const Coeffs &c,
                                                  const float *sc, bool approx, uint32_t *mx)
@@ -924,7 +936,7 @@ __device__ __forceinline__ void scaled_group_max(const WorkItem &w, int gi0, int
             moments<S::mode, true>(p[j][k], g[k], m, v, c, m_hat[j][k], v_hat[j][k]);
             mx[1] = max(mx[1], abs_bits(m));
             mx[2] = max(mx[2], abs_bits(v));
-            ok = ok && !__builtin_isfpclass(v_hat[j][k], __FPCLASS_POSSUBNORMAL);
+            ok = ok && !__builtin_isfpclass(v_hat[j][k], __FPCLASS_POSSUBNORMAL | __FPCLASS_NEGSUBNORMAL);
             const float q = m_hat[j][k] * __builtin_amdgcn_rcpf(__builtin_amdgcn_sqrtf(v_hat[j][k]) + c.eps);
             float u = q;
             if constexpr (S::mode == 1) u = q + c.wd * p[j][k];
@@ -1210,7 +1222,7 @@ __global__ void clip_grad_scale_kernel(const double *d_sumsq, float *d_grad_scal
 // Host side: kernel tables
 // ---------------------------------------------------------------------------
 
-typedef void (*UpdateFn)(const WorkItem *, uint32_t, StepArgs);
+typedef void (*UpdateFn)(const WorkItem *, uint32_t, uint32_t, StepArgs);
 typedef void (*ScaledFn)(const WorkItem *, uint32_t, uint32_t, StepArgs, uint32_t *);
 
 constexpr int kGradTypes[3] = {kF32, kBF16, kF16};
@@ -1281,9 +1293,51 @@ struct Plan {
     adam_tl_stats stats;
     uint32_t shift;
     std::vector<WorkItem> items;
-    std::vector<float *> scale_ptrs;  // scaled state: per non-empty tensor
-    std::vector<uint32_t> tile_ranges;  // scaled state: [first, end) tiles per non-empty tensor
+    std::vector<float *> scale_ptrs;    // scaled state: per non-empty tensor
+    std::vector<uint32_t> tile_ranges;  // [first, end) tiles per non-empty tensor
+    uint32_t piece_tile[kMaxPieces + 1];    // scaled state: first tile of each piece, then the grid
+    uint32_t piece_tensor[kMaxPieces + 1];  // scaled state: first tensor of each piece, then the tensors
 };
+
+// Dispatches that cover `tiles` tiles at most `per` at a time.
+int32_t dispatch_count(uint32_t tiles, int32_t per)
+{
+    return int32_t((int64_t(tiles) + per - 1) / per);
+}
+
+// Splits a scaled-state list into pieces of consecutive tensors (see
+// kMaxPieces): about equal tiles each, cut only at tensor boundaries, every
+// piece at least kMinPieceTiles.  `ranges` holds each non-empty tensor's
+// [first, end) tiles; fills tile[0..n] and tensor[0..n] (piece i is tiles
+// [tile[i], tile[i+1]) and tensors [tensor[i], tensor[i+1])) and n.
+void plan_pieces(const std::vector<uint32_t> &ranges, uint32_t tiles, uint32_t *tile, uint32_t *tensor, int32_t &n)
+{
+    const uint32_t count = uint32_t(ranges.size() / 2);
+    const int want = piece_count(count, tiles);
+    n = 0;
+    tile[0] = 0;
+    tensor[0] = 0;
+    if (want >= 2) {
+        // greedy: close a piece once it reaches its share of the tiles
+        // still to cut, if what is left after it is a piece too
+        uint32_t k = 0;
+        while (n < want - 1) {
+            const uint32_t first = tile[n];
+            const uint64_t share = (uint64_t(tiles) - first) / uint64_t(want - n);
+            while (k < count && ranges[2 * k + 1] - first < share) ++k;
+            if (k >= count) break;
+            const uint32_t end = ranges[2 * k + 1];  // the piece ends with tensor k
+            if (end - first < kMinPieceTiles || tiles - end < kMinPieceTiles) break;
+            ++k;
+            ++n;
+            tile[n] = end;
+            tensor[n] = k;
+        }
+    }
+    ++n;  // the last piece takes the rest
+    tile[n] = tiles;
+    tensor[n] = count;
+}
 
 bool valid_dtype_set(const adam_tl_desc &d)
 {
@@ -1338,7 +1392,7 @@ int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count
               Plan &plan, bool keep_items)
 {
     if (desc == nullptr || count < 0 || (count > 0 && tensors == nullptr)) return ADAM_EINVAL;
-    if (desc->reserved1 != 0) return ADAM_EINVAL;
+    if (desc->dispatch_tiles < 0) return ADAM_EINVAL;
     if (desc->with_remainders != 0 && desc->with_remainders != 1) return ADAM_EINVAL;
     if (desc->scaled_state != 0 && desc->scaled_state != 1) return ADAM_EINVAL;
     if (desc->with_remainders == 1 && desc->scaled_state == 1) return ADAM_EINVAL;
@@ -1442,9 +1496,31 @@ int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count
     if ((st.chunks << shift) >= kMaxGrid) return ADAM_EINVAL;
     st.chunk_elems = chunk;
     st.grid_blocks = st.chunks << shift;
-    if (scaled) st.pieces = int32_t(piece_count(st.nonempty, st.grid_blocks));
-    plan.stats = st;
+    st.dispatch_tiles = int32_t(desc->dispatch_tiles == 0 ? kDispatchTiles
+                                                          : std::min<int64_t>(desc->dispatch_tiles, kDispatchTiles));
     plan.shift = shift;
+    // each non-empty tensor's tiles [first, end): records are per tensor
+    std::vector<uint32_t> &ranges = plan.tile_ranges;
+    ranges.reserve(2 * sizes.size());
+    int64_t records = 0;
+    for (int64_t n : sizes) {
+        ranges.push_back(uint32_t(records << shift));
+        records += (n + chunk - 1) / chunk;
+        ranges.push_back(uint32_t(records << shift));
+    }
+    st.pieces = 1;
+    if (scaled) {
+        plan_pieces(ranges, uint32_t(st.grid_blocks), plan.piece_tile, plan.piece_tensor, st.pieces);
+        for (int i = 0; i < st.pieces; ++i)
+            st.dispatches += dispatch_count(plan.piece_tile[i + 1] - plan.piece_tile[i], st.dispatch_tiles);
+    } else {
+        plan.piece_tile[0] = 0;
+        plan.piece_tile[1] = uint32_t(st.grid_blocks);
+        plan.piece_tensor[0] = 0;
+        plan.piece_tensor[1] = uint32_t(sizes.size());
+        st.dispatches = dispatch_count(uint32_t(st.grid_blocks), st.dispatch_tiles);
+    }
+    plan.stats = st;
     if (!keep_items) return ADAM_OK;
 
     plan.items.reserve(size_t(st.chunks));
@@ -1456,12 +1532,7 @@ int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count
         const int32_t head = heads[j];
         const int64_t body = sizes[j++];
         const int64_t first = head > 0 ? head : 0;  // element index where records start
-        if (scaled) {
-            const int64_t records = (body + chunk - 1) / chunk;
-            plan.scale_ptrs.push_back(t.scales);
-            plan.tile_ranges.push_back(uint32_t(int64_t(plan.items.size()) << shift));
-            plan.tile_ranges.push_back(uint32_t((int64_t(plan.items.size()) + records) << shift));
-        }
+        if (scaled) plan.scale_ptrs.push_back(t.scales);
         for (int64_t off = 0; off < body; off += chunk) {
             const int64_t e = first + off;
             WorkItem w = {};
@@ -1568,7 +1639,35 @@ size_t update_lds_reserve(const adam_tl *tl)
     return size_t(tl->lds_per_cu / kResidentFp32Moments) / 512 * 512;
 }
 
-int launch_update(const adam_tl *tl, int mode, bool capturable, const StepArgs &args, hipStream_t stream)
+// Counts the launches a step has enqueued, so that a failure can tell
+// whether anything of the step reached the stream.
+struct Launches {
+    int enqueued = 0;
+    bool ok(hipError_t e)
+    {
+        if (e != hipSuccess) return false;
+        ++enqueued;
+        return true;
+    }
+};
+
+// Enqueues kernel `fn` over tiles [t0, t1) as dispatches of at most
+// `per` tiles, each told its first tile.
+template <class Fn, class... Args>
+bool launch_tiles(Launches &log, Fn fn, uint32_t t0, uint32_t t1, int32_t per, int threads, size_t lds,
+                  hipStream_t stream, const WorkItem *items, uint32_t shift, Args... args)
+{
+    for (uint32_t first = t0; first < t1;) {
+        const uint32_t n = uint32_t(std::min<int64_t>(per, int64_t(t1) - first));
+        hipLaunchKernelGGL(fn, dim3(n), dim3(threads), lds, stream, items, shift, first, args...);
+        if (!log.ok(hipGetLastError())) return false;
+        first += n;
+    }
+    return true;
+}
+
+int launch_update(const adam_tl *tl, int mode, bool capturable, const StepArgs &args, hipStream_t stream,
+                  Launches &log)
 {
     const int pk = tl->kind == Kind::Remainders ? kParamRem
                    : tl->p == kBF16             ? kParamBF16
@@ -1578,34 +1677,38 @@ int launch_update(const adam_tl *tl, int mode, bool capturable, const StepArgs &
                     3 * (pk + 4 * (type_pos(kUpdateOutTypes, 4, tl->out) + 4 * (mode + 2 * int(capturable))));
     const UpdateFn fn = UpdateKernels::fns[idx];
     if (fn == nullptr) return ADAM_EDTYPE;
-    hipLaunchKernelGGL(fn, dim3(uint32_t(tl->stats.grid_blocks)), dim3(kBlock), update_lds_reserve(tl), stream,
-                       tl->d_items, tl->shift, args);
-    return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
+    return launch_tiles(log, fn, 0u, uint32_t(tl->stats.grid_blocks), tl->stats.dispatch_tiles, kBlock,
+                        update_lds_reserve(tl), stream, tl->d_items, tl->shift, args)
+               ? ADAM_OK
+               : ADAM_EHIP;
 }
 
-int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t stream)
+int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t stream, Launches &log)
 {
     const int base = type_pos(kGradTypes, 3, tl->g) +
                      3 * (type_pos(kOutTypes, 3, tl->out) + 3 * (type_pos(kStateTypes, 2, tl->p) + 2 * mode));
     auto fold = tl->p == kBF16 ? adam_scaled_fold<kBF16> : adam_scaled_fold<kF16>;
     auto finish = tl->p == kBF16 ? adam_scaled_finish<kBF16> : adam_scaled_finish<kF16>;
+    const int32_t per = tl->stats.dispatch_tiles;
     // piece i: its tiles' maxima, then its tensors' fold ...
     auto maxima = [&](int i, hipStream_t s) {
-        const uint32_t t0 = tl->piece_tile[i], k0 = tl->piece_tensor[i];
-        hipLaunchKernelGGL(ScaledKernels::fns[base], dim3(tl->piece_tile[i + 1] - t0), dim3(kMaxBlock), 0, s,
-                           tl->d_items, tl->shift, t0, args, tl->d_tile_max);
+        const uint32_t k0 = tl->piece_tensor[i];
+        if (!launch_tiles(log, ScaledKernels::fns[base], tl->piece_tile[i], tl->piece_tile[i + 1], per, kMaxBlock,
+                          0, s, tl->d_items, tl->shift, args, tl->d_tile_max))
+            return false;
         hipLaunchKernelGGL(fold, dim3(tl->piece_tensor[i + 1] - k0), dim3(kFoldMaxBlock), 0, s,
                            tl->d_tile_max, tl->d_tiles, tl->d_folded, k0, args.block);
-        return hipGetLastError() == hipSuccess;
+        return log.ok(hipGetLastError());
     };
     // ... and its store pass, then its tensors' new scales
     auto store = [&](int i, hipStream_t s) {
-        const uint32_t t0 = tl->piece_tile[i], k0 = tl->piece_tensor[i], k1 = tl->piece_tensor[i + 1];
-        hipLaunchKernelGGL(ScaledKernels::fns[base + 36], dim3(tl->piece_tile[i + 1] - t0), dim3(kBlock), 0, s,
-                           tl->d_items, tl->shift, t0, args, tl->d_folded);
+        const uint32_t k0 = tl->piece_tensor[i], k1 = tl->piece_tensor[i + 1];
+        if (!launch_tiles(log, ScaledKernels::fns[base + 36], tl->piece_tile[i], tl->piece_tile[i + 1], per, kBlock,
+                          0, s, tl->d_items, tl->shift, args, tl->d_folded))
+            return false;
         hipLaunchKernelGGL(finish, dim3((k1 - k0 + 255) / 256), dim3(256), 0, s, tl->d_scale_ptrs, tl->d_folded,
                            k0, k1, args.block);
-        return hipGetLastError() == hipSuccess;
+        return log.ok(hipGetLastError());
     };
     if (tl->n_pieces <= 1) return maxima(0, stream) && store(0, stream) ? ADAM_OK : ADAM_EHIP;
     // Pieces alternate between the caller's stream and aux; piece i starts
@@ -1647,10 +1750,13 @@ int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
     step_corrections(hp->beta1, hp->beta2, t, hp->bias_correction, a.bc1, a.bc2, a.rbc1, a.rbc2);
     DeviceGuard guard(tl->stats.device);
     int rc = ADAM_EHIP;
+    Launches log;
     if (guard.status == hipSuccess)
-        rc = want == Kind::Scaled ? launch_scaled(tl, hp->mode, a, stream)
-                                  : launch_update(tl, hp->mode, false, a, stream);
-    if (rc != ADAM_OK) *step_io = before;
+        rc = want == Kind::Scaled ? launch_scaled(tl, hp->mode, a, stream, log)
+                                  : launch_update(tl, hp->mode, false, a, stream, log);
+    // a failure before anything was enqueued leaves the counter; once part
+    // of the step is on the stream the counter stays with the step
+    if (rc != ADAM_OK && log.enqueued == 0) *step_io = before;
     return rc;
 }
 
@@ -1673,8 +1779,9 @@ int capturable_step(const adam_tl *tl, const adam_hparams *hp, const float *d_lr
     a.eps = hp->eps;
     a.weight_decay = hp->weight_decay;
     a.block = tl->d_block;
-    return want == Kind::Scaled ? launch_scaled(tl, hp->mode, a, stream)
-                                : launch_update(tl, hp->mode, true, a, stream);
+    Launches log;
+    return want == Kind::Scaled ? launch_scaled(tl, hp->mode, a, stream, log)
+                                : launch_update(tl, hp->mode, true, a, stream, log);
 }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1713,36 +1820,21 @@ void release_pieces(adam_tl *tl)
     tl->n_pieces = 1;
 }
 
-// Splits a large scaled-state list into pieces of consecutive tensors of
-// about equal tiles and creates the second stream and the events that
-// pipeline them.  Anything that cannot be created leaves one piece (the
-// same results, one sequence of launches).
-void plan_pieces(adam_tl *tl, const std::vector<uint32_t> &tile_ranges)
+// Creates the second stream and the events that pipeline a scaled-state
+// list planned in two or more pieces.  Anything that cannot be created
+// leaves one piece (the same results, one sequence of launches).
+void start_pieces(adam_tl *tl)
 {
-    const uint32_t tiles = uint32_t(tl->stats.grid_blocks);
-    const int n = piece_count(tl->n_tensors, tiles);
-    if (n < 2) return;
-    uint32_t k = 0;
-    for (int i = 1; i < n; ++i) {
-        const uint64_t target = uint64_t(tiles) * uint64_t(i) / uint64_t(n);
-        k = std::max(k, tl->piece_tensor[i - 1] + 1);
-        while (k + uint32_t(n - i) < tl->n_tensors && tile_ranges[2 * k] < target) ++k;
-        tl->piece_tensor[i] = k;
-        tl->piece_tile[i] = tile_ranges[2 * k];
-    }
-    tl->piece_tensor[n] = tl->n_tensors;
-    tl->piece_tile[n] = tiles;
+    if (tl->n_pieces < 2) return;
     bool ok = hipStreamCreateWithFlags(&tl->aux, hipStreamNonBlocking) == hipSuccess;
-    for (int i = 0; ok && i < n + 2; ++i)
+    for (int i = 0; ok && i < tl->n_pieces + 2; ++i)
         ok = hipEventCreateWithFlags(&tl->ev[i], hipEventDisableTiming) == hipSuccess;
-    if (ok) {
-        tl->n_pieces = n;
-        tl->stats.pieces = n;
-        return;
-    }
+    if (ok) return;
     (void)hipGetLastError();
     release_pieces(tl);
+    const uint32_t tiles = uint32_t(tl->stats.grid_blocks);
     tl->stats.pieces = 1;
+    tl->stats.dispatches = dispatch_count(tiles, tl->stats.dispatch_tiles);
     tl->piece_tile[1] = tiles;
     tl->piece_tensor[1] = tl->n_tensors;
 }
@@ -1796,11 +1888,9 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     tl->d_folded = nullptr;
     tl->n_tensors = uint32_t(plan.stats.nonempty);
     tl->lds_per_cu = 0;
-    tl->n_pieces = 1;
-    tl->piece_tile[0] = 0;
-    tl->piece_tile[1] = uint32_t(plan.stats.grid_blocks);
-    tl->piece_tensor[0] = 0;
-    tl->piece_tensor[1] = tl->n_tensors;
+    tl->n_pieces = plan.stats.pieces;
+    std::copy(plan.piece_tile, plan.piece_tile + tl->n_pieces + 1, tl->piece_tile);
+    std::copy(plan.piece_tensor, plan.piece_tensor + tl->n_pieces + 1, tl->piece_tensor);
     tl->aux = nullptr;
     for (hipEvent_t &e : tl->ev) e = nullptr;
     if (plan.items.empty()) {  // nothing to launch: no device state at all
@@ -1828,7 +1918,7 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     const size_t partials_off = block_off + sizeof(StepBlock);
     const size_t ptrs_off = align_up(partials_off + tl->n_partials * sizeof(double), 8);
     const size_t tiles_off = ptrs_off + plan.scale_ptrs.size() * sizeof(float *);
-    const size_t tile_max_off = tiles_off + plan.tile_ranges.size() * sizeof(uint32_t);
+    const size_t tile_max_off = tiles_off + (scaled ? plan.tile_ranges.size() * sizeof(uint32_t) : 0);
     const size_t folded_off =
         tile_max_off + (scaled ? 3 * sizeof(uint32_t) * size_t(tl->stats.grid_blocks) : 0);
     const size_t total = folded_off + (scaled ? 6 * sizeof(uint32_t) * tl->n_tensors : 0);
@@ -1862,7 +1952,7 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
         delete tl;
         return ADAM_EHIP;
     }
-    if (scaled) plan_pieces(tl, plan.tile_ranges);
+    if (scaled) start_pieces(tl);
     *out = tl;
     return ADAM_OK;
 }

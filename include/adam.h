@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define ADAM_ABI_VERSION 5
+#define ADAM_ABI_VERSION 6
 
 typedef enum {
     ADAM_OK = 0,
@@ -115,7 +115,13 @@ typedef struct {
                                 do not depend on it.                           */
     int32_t scaled_state;    /* 1: p, m, v are p's 16-bit type with per-tensor
                                 scales (adam_tensor.scales); 0: no             */
-    int32_t reserved1;       /* must be 0                                       */
+    int32_t dispatch_tiles;  /* tiles (512 elements each) per kernel dispatch of
+                                the streaming passes: 0 = the most one dispatch
+                                can carry (2^25 - 512: a dispatch counts its
+                                work-items in 32 bits); else a positive limit,
+                                capped at that.  Longer lists are launched as
+                                several dispatches over consecutive tiles.
+                                Results do not depend on it.                   */
 } adam_tl_desc;
 
 /* Per-group hyperparameters (apex defaults: betas (0.9, 0.999), eps 1e-8,
@@ -137,7 +143,8 @@ typedef struct {
     int64_t elements;        /* sum of numel                                      */
     int64_t chunk_elems;     /* elements per record                               */
     int64_t vector_tensors;  /* tensors whose buffers all allow 4-element vectors */
-    int64_t grid_blocks;     /* workgroups per launch of the update kernel        */
+    int64_t grid_blocks;     /* tiles: workgroups of the update kernel per step,
+                                over all its dispatches                          */
     int32_t tile_elems;      /* elements per workgroup (one tile)                 */
     int32_t block_threads;   /* threads per workgroup of the update (the scaled-
                                 state maxima pass runs one 64-lane wave per tile) */
@@ -146,12 +153,17 @@ typedef struct {
     int32_t two_buffer;      /* 1: built by adam_tl_build_two_buffer               */
     int32_t pieces;          /* scaled state: pieces of consecutive tensors the
                                 step is pipelined in over the caller's stream
-                                and a second stream of the handle, for a list
-                                of two or more tensors whose work table holds
-                                at least 8192 tiles (grid_blocks, about 4M
-                                elements): the least of 16, the tensors and
-                                grid_blocks / 1024 (a piece holds at least
-                                1024 tiles, 512K elements); 1 otherwise          */
+                                and a second stream of the handle (see
+                                adam_step_scaled): for a list of two or more
+                                tensors whose work table holds at least 8192
+                                tiles (about 4M elements), up to 16 pieces of
+                                about equal tiles, cut at tensor boundaries,
+                                each of at least 1024 tiles (512K elements);
+                                1 otherwise                                     */
+    int32_t dispatch_tiles;  /* tiles per kernel dispatch (adam_tl_desc)         */
+    int32_t dispatches;      /* dispatches of the update kernel per step (scaled
+                                state: of each of its two passes, summed over
+                                the pieces)                                     */
 } adam_tl_stats;
 
 typedef struct adam_tl adam_tl; /* opaque handle: device work table */
@@ -166,7 +178,7 @@ const char *adam_status_string(int status);
  * HIP call, no device allocation); fills *stats (device = -1).
  * Errors: ADAM_EINVAL for a NULL desc/stats, count < 0, NULL `tensors` with
  * count > 0, numel < 0, a NULL required pointer in a non-empty tensor, a
- * pointer given where the dtype says none, a bad chunk_elems, reserved1 != 0,
+ * pointer given where the dtype says none, a bad chunk_elems, dispatch_tiles < 0,
  * with_remainders or scaled_state not 0/1 or both 1, or two buffers that
  * overlap (gradients may overlap other gradients; no other pair may share a
  * byte; a tensor's scales are written too); ADAM_EDTYPE for an unsupported

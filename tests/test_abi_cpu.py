@@ -31,7 +31,7 @@ def test_library_loads_and_exports_every_declared_symbol():
                          text=True, check=True).stdout
     exported = set(re.findall(r" T (adam_\w+)$", out, flags=re.M))
     assert set(names) <= exported
-    assert L.adam_abi_version() == 5
+    assert L.adam_abi_version() == 6
 
 
 def test_status_strings():
@@ -183,7 +183,7 @@ def test_plan_rejects_unsupported_dtypes():
         st = A.AdamTlStats()
         assert A.lib().adam_tl_plan(arr, 1, ctypes.byref(d), ctypes.byref(st)) == A.ADAM_EDTYPE, (p, g, o, r, sc)
     st = A.AdamTlStats()
-    for r, sc, r1 in ((2, 0, 0), (0, 2, 0), (1, 1, 0), (0, 0, 1)):  # flags 0/1, not both; reserved 0
+    for r, sc, r1 in ((2, 0, 0), (0, 2, 0), (1, 1, 0), (0, 0, -1)):  # flags 0/1, not both; dispatch tiles >= 0
         d = A.AdamTlDesc(A.DT_BF16, A.DT_F32, A.DT_NONE, r, 0, sc, r1)
         assert A.lib().adam_tl_plan(A._tensor_array(ts, desc), 1, ctypes.byref(d),
                                     ctypes.byref(st)) == A.ADAM_EINVAL, (r, sc, r1)
@@ -406,14 +406,48 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 def test_scaled_plans_report_their_pieces():
     """A scaled-state list of at least 8192 tiles (4M elements, tensor ends
-    rounded up to whole records) in two or more tensors is pipelined in
-    min(16, tensors, tiles / 1024) pieces; anything else runs in one."""
+    rounded up to whole records) in two or more tensors is pipelined in up to
+    min(16, tensors, tiles / 1024) pieces of about equal tiles, cut at tensor
+    boundaries, none below 1024 tiles; anything else runs in one."""
     big = [1 << 21, 1 << 21]
     assert plan(fake_tensors(big, scaled=True), p="f16_scaled")["pieces"] == 2
     assert plan(fake_tensors([1 << 20] * 12, scaled=True), p="bf16_scaled")["pieces"] == 12
     assert plan(fake_tensors([1 << 20] * 20, scaled=True), p="f16_scaled")["pieces"] == 16  # 40960 tiles
     assert plan(fake_tensors([1 << 18] * 20, scaled=True), p="f16_scaled")["pieces"] == 10  # 10240 tiles
-    assert plan(fake_tensors([1 << 19] * 8 + [1], scaled=True), p="f16_scaled")["pieces"] == 8  # 8193 tiles
+    assert plan(fake_tensors([1 << 19] * 16, scaled=True), p="f16_scaled")["pieces"] == 16  # 16384 tiles
+    # 8256 tiles (the one-element tensor takes a whole 64-tile record): the
+    # first share (1032 tiles) needs two tensors, and the last piece keeps
+    # the one-element tensor instead of running it alone
+    assert plan(fake_tensors([1 << 19] * 8 + [1], scaled=True), p="f16_scaled")["pieces"] == 7
+    # a piece never holds only small tensors: nine one-element tensors and a
+    # 4M one (8264 tiles) run in one piece, which is all of the big tensor
+    assert plan(fake_tensors([1] * 9 + [1 << 22], scaled=True), p="f16_scaled")["pieces"] == 1
+    # 7 x 1024 tiles then 16384: two pieces of three tensors, then the rest
+    assert plan(fake_tensors([1 << 19] * 7 + [1 << 23], scaled=True), p="f16_scaled")["pieces"] == 3
     assert plan(fake_tensors([1 << 21, 1], scaled=True), p="f16_scaled")["pieces"] == 1  # 4224 tiles
     assert plan(fake_tensors([1 << 23], scaled=True), p="f16_scaled")["pieces"] == 1  # one tensor
     assert plan(fake_tensors(big), p="f32")["pieces"] == 1  # not scaled
+
+
+def test_lists_beyond_one_dispatch_are_split():
+    """A dispatch counts its work-items in 32 bits, so one dispatch of the
+    128-thread update (or of a scaled-state pass) carries at most 2^25 - 512
+    tiles (a whole number of XCD groups).  Plans at that limit and one record
+    (128 tiles) past it, on fake addresses 4 TiB apart: the tiles are all
+    planned, and launched as one, two or three dispatches."""
+    limit = (1 << 25) - 512
+    assert limit * 128 < 1 << 32 and (limit + 512) * 128 == 1 << 32
+    base, stride = 1 << 44, 1 << 42
+    for tiles, want in ((limit, 1), (limit + 128, 2), (1 << 25, 2), (2 * limit, 2), (2 * limit + 128, 3)):
+        n = tiles * 512
+        for scaled in (False, True):
+            t = dict(p=base, m=base + stride, v=base + 2 * stride, g=base + 3 * stride, numel=n,
+                     scales=base + 4 * stride if scaled else None)
+            st = plan([t], p="f16_scaled" if scaled else "f32", chunk_elems=65536)
+            assert st["grid_blocks"] == tiles and st["elements"] == n
+            assert (st["dispatch_tiles"], st["dispatches"]) == (limit, want), (tiles, scaled)
+    # a requested limit above what a dispatch carries is capped; any positive one is kept
+    t = dict(p=base, m=base + stride, v=base + 2 * stride, g=base + 3 * stride, numel=4096 * 512)
+    assert plan([t], dispatch_tiles=1 << 30)["dispatch_tiles"] == limit
+    st = plan([t], dispatch_tiles=1000)
+    assert (st["dispatch_tiles"], st["dispatches"]) == (1000, 5)

@@ -364,6 +364,27 @@ def test_scaled_maxima_subnormal_second_moment(torch, orc, mode):
     assert_bitwise(got, ref, ctx=f"mode {mode}")
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_scaled_maxima_negative_subnormal_second_moment(torch, orc, mode):
+    """One element of a tensor whose other second moments are normal holds a
+    negative stored v that unscales to a subnormal, with zero param, first
+    moment and gradient: its v_hat is a negative subnormal, whose exact root
+    is NaN (so the tensor's new param scale is NaN) while the hardware root
+    flushes it to -0 and the approximate param is 0, far below the cut.  The
+    wave must be recomputed exactly."""
+    host = _f16_scaled([70001, 4096], 88, g_dtype="f32")
+    t = host[1]
+    t.scales[2] = np.float32(1e-33)
+    t.v[:] = (np.abs(np.random.default_rng(89).standard_normal(t.v.size)) * 1000 + 1).astype(np.float16)
+    t.v[77] = np.uint16(0x8001).view(np.float16)  # the smallest negative fp16 subnormal
+    t.p[77] = t.m[77] = 0
+    t.g[77] = 0
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    got, ref = run_steps(orc, host, hl, hr, 1.6e-3, 1)
+    assert np.isnan(ref[1].scales[0])
+    assert_bitwise(got, ref, ctx=f"mode {mode}")
+
+
 @pytest.mark.parametrize("p_kind", ["f16_scaled", "bf16_scaled"])
 def test_scaled_maxima_wide_magnitudes(torch, orc, p_kind):
     """Stored params drawn over every finite 16-bit pattern (fp16 subnormals to

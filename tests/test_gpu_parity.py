@@ -175,6 +175,45 @@ def test_results_do_not_depend_on_chunk(torch, orc):
         assert_bitwise(r, results[0])
 
 
+@pytest.mark.parametrize("g_dtype,p_kind,p_out,mode,dispatch_tiles", [
+    ("f32", "f32", False, 1, 1), ("bf16", "f32", True, 0, 3), ("bf16", "bf16_rem", True, 1, 7),
+    ("f16", "bf16", "f32", 1, 64), ("bf16", "f16_scaled", "bf16", 1, 5), ("f32", "f32", "f32", 0, 513)])
+def test_split_dispatches_match_the_oracle(torch, orc, g_dtype, p_kind, p_out, mode, dispatch_tiles):
+    """A list launched as many dispatches of at most `dispatch_tiles` tiles
+    (the way lists beyond one dispatch's 32-bit work-item count run): host
+    steps, then capturable steps, bitwise against the oracle."""
+    sizes = SWEEP_SIZES
+    host = host_tensors(sizes, g_dtype=g_dtype, p_kind=p_kind, p_out=p_out, seed=43, m_v_init="random")
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, mode)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host, chunk_elems=4096, dispatch_tiles=dispatch_tiles))
+    info = tl.info()
+    assert info["dispatch_tiles"] == dispatch_tiles
+    assert info["dispatches"] == -(-info["grid_blocks"] // dispatch_tiles) > 1
+    scaled = host[0].scales is not None
+    host_fn = (A.adam_step_scaled if scaled else A.adam_step_remainders if host[0].rem is not None
+               else A.adam_step)
+    cap_fn = (A.adam_step_scaled_capturable if scaled else A.adam_step_remainders_capturable
+              if host[0].rem is not None else A.adam_step_capturable)
+    ref = copies(host)
+    ot, st, step = oracle_tensors(ref), [0], A.HostStep(0)
+    for _ in range(2):
+        host_fn(tl, hl, 1.6e-3, step, 0.5)
+        orc.group_step(ot, hr, 1.6e-3, st, 0.5)
+    torch.cuda.synchronize()
+    assert_bitwise(dev.readback(), ref, ctx=f"host steps, {info['dispatches']} dispatches")
+    d_lr = torch.tensor([1.6e-3], dtype=torch.float32, device="cuda")
+    d_step = torch.tensor([st[0]], dtype=torch.int32, device="cuda")
+    d_s = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        cap_fn(tl, hl, d_lr, d_step, d_s, None)
+        orc.group_step(ot, hr, 1.6e-3, st, 0.5)
+    torch.cuda.synchronize()
+    assert int(d_step.item()) == st[0] == 4
+    assert_bitwise(dev.readback(), ref, ctx=f"capturable steps, {info['dispatches']} dispatches")
+    tl.destroy()
+
+
 def test_device_grad_scale_equals_host_grad_scale(torch, orc):
     host = host_tensors([5000, 333], seed=22)
     hl, hr = hp_pair(0.9, 0.999, 1e-8, 0.01, 0)

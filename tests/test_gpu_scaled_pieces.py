@@ -75,23 +75,27 @@ def test_pipelined_scaled_steps_match_the_oracle(torch, p_kind, g_dtype, p_out):
     tl.destroy()
 
 
-@pytest.mark.parametrize("sizes,pieces", [
-    ([(1 << 22) + 4097, 1], 2),                  # two tensors, one of them a single element
-    ([1] * 9 + [(1 << 22) + 3], 8),              # many tiny tensors, then one that holds the tiles
-    ([700001, 3, 1 << 20, 5, 1 << 21, 77, 900000, 65536, 1 << 20, 9], 10),  # ten uneven tensors
-    ([(1 << 19) + 977 * i for i in range(20)], 16),  # twenty tensors: the most pieces
+@pytest.mark.parametrize("sizes,pieces,dispatch_tiles,dispatches", [
+    # two tensors, one of them a single element: one piece (the element
+    # alone would be a piece of 32 tiles)
+    ([(1 << 22) + 4097, 1], 1, 0, 1),
+    ([1] * 9 + [(1 << 22) + 3], 1, 0, 1),        # many tiny tensors, then one that holds the tiles
+    ([700001, 3, 1 << 20, 5, 1 << 21, 77, 900000, 65536, 1 << 20, 9], 5, 0, 5),  # ten uneven tensors
+    ([(1 << 19) + 977 * i for i in range(20)], 15, 0, 15),  # twenty tensors: fifteen pieces
+    # the same list with each pass launched in dispatches of at most 333 tiles
+    ([700001, 3, 1 << 20, 5, 1 << 21, 77, 900000, 65536, 1 << 20, 9], 5, 333, 38),
 ])
-def test_pieces_cover_every_tensor_once(torch, sizes, pieces):
+def test_pieces_cover_every_tensor_once(torch, sizes, pieces, dispatch_tiles, dispatches):
     """However the list is cut into pieces (each at least one tensor, about
-    equal tiles), every tensor's values, scales and param-sync copy equal
-    the oracle's after two steps."""
+    equal tiles) and each piece's passes into dispatches, every tensor's
+    values, scales and param-sync copy equal the oracle's after two steps."""
     host = host_tensors(sizes, g_dtype="bf16", p_kind="f16_scaled", p_out="bf16", seed=len(sizes),
                         m_v_init="random")
     assert sum(sizes) >= 1 << 22
     ref = copies(host)
     dev = DeviceSet(host)
-    tl = A.adam_tl_build(dev.tensors, desc_for(host))
-    assert tl.info()["pieces"] == pieces
+    tl = A.adam_tl_build(dev.tensors, desc_for(host, dispatch_tiles=dispatch_tiles))
+    assert (tl.info()["pieces"], tl.info()["dispatches"]) == (pieces, dispatches)
     hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
     orc = oracle.default()
     ot, st, step = oracle_tensors(ref), [0], A.HostStep(0)

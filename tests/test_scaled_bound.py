@@ -33,8 +33,9 @@ def _chains(p, mh, vh, lr, wd, eps, mode, ks, kr):
         u = f(q + f(wd * p)) if mode == 1 else q
         pe = f(p - f(lr * u))
         sa = _nudge(np.sqrt(vh), ks)
-        # the hardware flushes subnormal inputs: sqrt to 0, rcp to +inf
-        sa = np.where((vh > 0) & (vh < f(2.0 ** -126)), f(0.0), sa)
+        # the hardware flushes subnormal inputs of either sign: sqrt to a
+        # zero of the input's sign, rcp to +inf
+        sa = np.where((vh != 0) & (np.abs(vh) < f(2.0 ** -126)), np.copysign(f(0.0), vh), sa)
         da = f(sa + eps)
         ra = np.where(da < f(2.0 ** -126), f(np.inf), _nudge(f(f(1.0) / da), kr))
         qa = f(mh * ra)
@@ -89,7 +90,7 @@ def _bound(qa, ta, pa, lr):
 def _valid(eps, lr, vh, qa, ua, ta, pa):
     """The kernel's conditions for using the bound (else: every element exact)."""
     return (eps >= 0 and eps < 2.0 ** 125 and abs(lr) < 2.0 ** 126
-            and not np.any((vh > 0) & (vh < f(2.0 ** -126)))
+            and not np.any((vh != 0) & (np.abs(vh) < f(2.0 ** -126)))
             and _abs_bits(pa).max() < 0x7E800000
             and np.nanmax(np.abs(qa)) < 2.0 ** 126 and np.nanmax(np.abs(ua)) < 2.0 ** 126
             and np.nanmax(np.abs(ta)) < 2.0 ** 126)
@@ -145,3 +146,26 @@ def test_subnormal_second_moment_takes_the_exact_path():
     pe, qa, ua, ta, pa = _chains(p, mh, vh, f(1.6e-3), f(0.1), f(1e-8), 1, np.zeros(N, int), np.zeros(N, int))
     assert not _valid(f(1e-8), f(1.6e-3), vh, qa, ua, ta, pa)
     assert _valid(f(1e-8), f(1.6e-3), np.where(vh < 1e-38, f(0.0), vh), qa, ua, ta, pa)
+
+
+def test_negative_second_moment_takes_the_exact_path():
+    """A negative v_hat (a negative stored v or scale): the exact root is NaN.
+    The hardware root of a negative subnormal is the flushed -0, so the
+    approximate param comes out finite where the exact one is NaN; of a
+    negative normal it is NaN, as the exact one.  Both put the wave outside
+    the bound's assumptions, so every element is recomputed exactly and the
+    NaN reaches the maximum."""
+    rng = np.random.default_rng(11)
+    p = f(rng.standard_normal(N)); mh = f(rng.standard_normal(N) * 1e-3)
+    vh = f(np.abs(rng.standard_normal(N)) * 1e-6)
+    for bad in (f(-1e-40), f(-2.0 ** -149), f(-1e-6), f(-3.0)):
+        v = vh.copy()
+        v[33] = bad
+        pe, qa, ua, ta, pa = _chains(p, mh, v, f(1.6e-3), f(0.1), f(1e-8), 1, np.zeros(N, int),
+                                     np.zeros(N, int))
+        assert np.isnan(pe[33])
+        if bad > f(-2.0 ** -126):
+            assert np.isfinite(pa[33])  # the hazard: the approximate chain misses the NaN
+        else:
+            assert np.isnan(pa[33])
+        assert not _valid(f(1e-8), f(1.6e-3), v, qa, ua, ta, pa)
