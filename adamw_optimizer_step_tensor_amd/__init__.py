@@ -54,7 +54,7 @@ from typing import Iterable, Optional, Sequence
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_PKG, "libadamw_mi355x.so")
 
-ADAM_OK, ADAM_EINVAL, ADAM_EDTYPE, ADAM_ENOMEM, ADAM_EHIP = 0, -1, -2, -3, -4
+ADAM_OK, ADAM_EINVAL, ADAM_EDTYPE, ADAM_ENOMEM, ADAM_EHIP, ADAM_ETOOBIG = 0, -1, -2, -3, -4, -5
 DT_NONE, DT_F32, DT_BF16, DT_F16 = 0, 1, 2, 3
 
 c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
@@ -105,7 +105,7 @@ _lib = None
 EXPORTED = ("adam_abi_version", "adam_status_string", "adam_tl_plan", "adam_tl_build",
             "adam_tl_plan_two_buffer", "adam_tl_build_two_buffer", "adam_tl_destroy", "adam_tl_info", "adam_step", "adam_step_capturable",
             "adam_step_remainders", "adam_step_remainders_capturable", "adam_step_scaled",
-            "adam_step_scaled_capturable", "adam_grad_sumsq", "adam_clip_grad_scale")
+            "adam_step_scaled_capturable", "adam_grad_sumsq", "adam_clip_grad_scale", "adam_step_noalloc")
 
 
 def lib():
@@ -155,6 +155,9 @@ def lib():
     L.adam_grad_sumsq.restype = c_i32
     L.adam_clip_grad_scale.argtypes = [c_vp, c_vp, c_f32, c_vp, c_vp, c_vp]
     L.adam_clip_grad_scale.restype = c_i32
+    L.adam_step_noalloc.argtypes = [ctypes.POINTER(AdamTensor), c_i64, ctypes.POINTER(AdamTlDesc),
+                                    ctypes.POINTER(AdamHParams), c_f32, ctypes.POINTER(c_i32), c_f32, c_vp, c_vp]
+    L.adam_step_noalloc.restype = c_i32
     if L.adam_abi_version() != 6:
         raise ImportError("libadamw_mi355x.so has an unexpected ABI version")
     _lib = L
@@ -424,3 +427,15 @@ def adam_clip_grad_scale(d_sumsq, d_grad_scale=None, max_norm: float = 0.0, d_no
                                       _addr(d_norm), _addr(d_noop), _stream(stream)),
            "adam_clip_grad_scale")
 
+
+
+def adam_step_noalloc(tensors: Sequence, desc: AdamTlDesc, hp: AdamHParams, lr: float, step: HostStep,
+                      grad_scale: float = 1.0, d_grad_scale=None, stream=None) -> None:
+    """adam_step without a handle, for callers that cannot allocate device
+    memory: the work table goes to the library's static device array (see
+    include/adam.h; calls on one device must not overlap)."""
+    arr = _tensor_array(tensors, desc)
+    s = _stream(stream) if any(_numel(t) for t in tensors) else (0 if stream is None else _stream(stream))
+    _check(lib().adam_step_noalloc(arr, len(tensors), ctypes.byref(desc), ctypes.byref(hp), float(lr),
+                                   ctypes.byref(step._c), float(grad_scale), _addr(d_grad_scale), s),
+           "adam_step_noalloc")

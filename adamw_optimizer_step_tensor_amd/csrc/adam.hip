@@ -80,6 +80,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -1728,16 +1729,10 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
     return ADAM_OK;
 }
 
-int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
-              const float *d_grad_scale, hipStream_t stream, Kind want)
+// The arguments of a non-capturable step whose counter was `before`.
+StepArgs host_args(const adam_hparams *hp, float lr, int32_t before, float grad_scale, const float *d_grad_scale)
 {
-    if (tl == nullptr || step_io == nullptr || !valid_hparams(hp)) return ADAM_EINVAL;
-    if (tl->kind != want) return ADAM_EINVAL;
-    const int32_t before = *step_io;
-    if (before < 0 || before == INT32_MAX) return ADAM_EINVAL;
     const int32_t t = before + 1;
-    *step_io = t;  // the counter advances even for a list with no elements
-    if (tl->stats.chunks == 0) return ADAM_OK;
     StepArgs a = {};
     a.lr = lr;
     a.beta1 = hp->beta1;
@@ -1748,6 +1743,19 @@ int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
     a.d_grad_scale = d_grad_scale;
     a.side = int32_t(uint32_t(before) & 1u);  // two-buffer state: the set the step reads
     step_corrections(hp->beta1, hp->beta2, t, hp->bias_correction, a.bc1, a.bc2, a.rbc1, a.rbc2);
+    return a;
+}
+
+int host_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
+              const float *d_grad_scale, hipStream_t stream, Kind want)
+{
+    if (tl == nullptr || step_io == nullptr || !valid_hparams(hp)) return ADAM_EINVAL;
+    if (tl->kind != want) return ADAM_EINVAL;
+    const int32_t before = *step_io;
+    if (before < 0 || before == INT32_MAX) return ADAM_EINVAL;
+    *step_io = before + 1;  // the counter advances even for a list with no elements
+    if (tl->stats.chunks == 0) return ADAM_OK;
+    const StepArgs a = host_args(hp, lr, before, grad_scale, d_grad_scale);
     DeviceGuard guard(tl->stats.device);
     int rc = ADAM_EHIP;
     Launches log;
@@ -1800,6 +1808,7 @@ const char *adam_status_string(int status)
     case ADAM_EDTYPE: return "unsupported dtype combination";
     case ADAM_ENOMEM: return "out of memory";
     case ADAM_EHIP: return "HIP runtime or launch failure";
+    case ADAM_ETOOBIG: return "list needs more work-table records than the static scratch holds (65536)";
     default: return "unknown status";
     }
 }
@@ -2077,4 +2086,125 @@ int adam_clip_grad_scale(const double *d_sumsq, float *d_grad_scale, float max_n
     return hipGetLastError() == hipSuccess ? ADAM_OK : ADAM_EHIP;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The step without a handle, for callers that cannot allocate device memory:
+// its work table goes to a static device array instead of a handle's
+// allocation.  Every call on a device shares that device's copy of the
+// array, so calls that overlap on one device race.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kScratchItems = 65536;  // work-table records: 8 MiB
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) WorkItem scratch[kScratchItems];
+
+struct ScratchOfDevice {
+    WorkItem *table = nullptr;  // the device's copy of `scratch`
+    int lds_per_cu = 0;
+};
+std::mutex scratch_mutex;
+ScratchOfDevice scratch_of_device[kMaxDevices];
+
+// The device address of `scratch` on `device` (current), looked up once per
+// device; the array's host-side name is not a device address.
+int scratch_table(int device, ScratchOfDevice &out)
+{
+    if (device < 0 || device >= kMaxDevices) return ADAM_EHIP;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    ScratchOfDevice &d = scratch_of_device[device];
+    if (d.table == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return ADAM_EHIP;
+        }
+        if (hipDeviceGetAttribute(&d.lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device) !=
+            hipSuccess) {
+            (void)hipGetLastError();
+            d.lds_per_cu = 0;
+        }
+        d.table = static_cast<WorkItem *>(ptr);
+    }
+    out = d;
+    return ADAM_OK;
+}
+
+// Plans a list for the static table: with an automatic chunk, the chunk is
+// doubled until the table fits, while that still merges records (a tensor
+// takes at least one record; coarser records also round tensor ends up to
+// more tiles).
+int plan_for_scratch(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc, Plan &plan)
+{
+    int rc = make_plan(tensors, nullptr, count, desc, plan, true);
+    adam_tl_desc d = *desc;
+    while (rc == ADAM_OK && int64_t(plan.items.size()) > kScratchItems) {
+        if (desc->chunk_elems != 0 || plan.stats.chunks == plan.stats.nonempty ||
+            plan.stats.chunk_elems >= kMaxChunk)
+            return ADAM_ETOOBIG;
+        d.chunk_elems = std::max(kMinChunk, plan.stats.chunk_elems * 2);
+        plan = Plan();
+        rc = make_plan(tensors, nullptr, count, &d, plan, true);
+        if (rc != ADAM_OK) return ADAM_ETOOBIG;  // the list planned, but not at a coarser chunk
+    }
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int adam_step_noalloc(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
+                      const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
+                      const float *d_grad_scale, hipStream_t stream)
+{
+    if (desc == nullptr || step_io == nullptr || !valid_hparams(hp)) return ADAM_EINVAL;
+    if (desc->with_remainders != 0 || desc->scaled_state != 0) return ADAM_EINVAL;  // adam_step's storage
+    const int32_t before = *step_io;
+    if (before < 0 || before == INT32_MAX) return ADAM_EINVAL;
+    Plan plan;
+    int rc;
+    try {
+        rc = plan_for_scratch(tensors, count, desc, plan);
+    } catch (const std::bad_alloc &) {
+        return ADAM_ENOMEM;
+    }
+    if (rc != ADAM_OK) return rc;
+    if (plan.items.empty()) {
+        *step_io = before + 1;  // the counter advances even for a list with no elements
+        return ADAM_OK;
+    }
+    int device = 0;
+    ScratchOfDevice sd;
+    if (hipGetDevice(&device) != hipSuccess) return ADAM_EHIP;
+    rc = scratch_table(device, sd);
+    if (rc != ADAM_OK) return rc;
+    // the table is enqueued behind earlier work on `stream` (which may still
+    // read the previous table) and the host waits for the copy, so the
+    // planned records can be released on return
+    if (hipMemcpyAsync(sd.table, plan.items.data(), plan.items.size() * sizeof(WorkItem), hipMemcpyHostToDevice,
+                       stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return ADAM_EHIP;
+    }
+    adam_tl tl{};
+    tl.stats = plan.stats;
+    tl.stats.device = device;
+    tl.shift = plan.shift;
+    tl.kind = Kind::Plain;
+    tl.g = desc->g;
+    tl.p = desc->p;
+    tl.out = desc->p_out;
+    tl.d_items = sd.table;
+    tl.lds_per_cu = sd.lds_per_cu;
+    tl.n_pieces = 1;
+    *step_io = before + 1;
+    Launches log;
+    rc = launch_update(&tl, hp->mode, false, host_args(hp, lr, before, grad_scale, d_grad_scale), stream, log);
+    if (rc != ADAM_OK && log.enqueued == 0) *step_io = before;
+    return rc;
+}
 }  // extern "C"

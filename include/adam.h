@@ -68,7 +68,9 @@ typedef enum {
     ADAM_EINVAL = -1, /* bad argument (null pointer, size, flag value, overlap) */
     ADAM_EDTYPE = -2, /* dtype combination the library does not implement     */
     ADAM_ENOMEM = -3, /* device or host allocation failed                     */
-    ADAM_EHIP = -4    /* a HIP runtime call or kernel launch failed           */
+    ADAM_EHIP = -4,   /* a HIP runtime call or kernel launch failed           */
+    ADAM_ETOOBIG = -5 /* adam_step_noalloc: the list needs more work-table
+                         records than its static scratch holds (65536)       */
 } adam_status;
 
 typedef enum {
@@ -339,6 +341,32 @@ int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_
 int adam_step_scaled_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
                                 int32_t *d_step, const float *d_grad_scale, const int32_t *d_noop,
                                 hipStream_t stream);
+
+/* For callers that cannot allocate device memory (harnesses that forbid
+ * hipMalloc, loops that must not allocate): adam_step without a handle.  The
+ * call validates and plans `tensors` (host array of `count`) as
+ * adam_tl_build does, copies the work table into a static device array of
+ * the library (65,536 records of 128 bytes, 8 MiB, held on every device the
+ * library runs on until the process ends) with an asynchronous copy on
+ * `stream`, waits on the host for that copy (and so for the work enqueued
+ * on `stream` before it), and enqueues the update.  It calls no device
+ * allocation routine.
+ *   - Storage: fp32 or 16-bit state (desc as for adam_tl_build; remainders
+ *     and scaled state: ADAM_EINVAL).  With chunk_elems 0 the chunk is the
+ *     automatic one, doubled until the table fits; a list that needs more
+ *     than 65,536 records at the largest chunk (2^30 elements), or at the
+ *     chunk the caller fixed, is refused with ADAM_ETOOBIG before anything
+ *     runs (in practice: more than 65,536 non-empty tensors).
+ *   - lr, step_io, grad_scale, d_grad_scale, errors and the counter rules:
+ *     as adam_step.  The results equal adam_step's on a handle of the same
+ *     list, bit for bit.
+ *   - Every call on one device shares that device's array, which keeps the
+ *     last call's table: calls that overlap on one device (two streams, two
+ *     host threads) race; order them.  The call is not capturable (the host
+ *     waits for the copy). */
+int adam_step_noalloc(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
+                      const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
+                      const float *d_grad_scale, hipStream_t stream);
 
 /* Sum of squares of every gradient element of a handle: the local part of
  * the global gradient norm that apex's distributed_fused_adam.py computes in

@@ -1,6 +1,7 @@
 /* A C99 client of the library: includes adam.h as a C translation unit and
  * makes the calls that need no GPU (plan, two-buffer plan, a handle over an
- * empty list, the host step counter of that handle, status strings).  Exit status 0 when
+ * empty list, the host step counter of that handle, the handle-free step
+ * on an empty list, status strings).  Exit status 0 when
  * every call behaves as the header states, else the number of the first
  * failed check. */
 #include <stdio.h>
@@ -67,6 +68,15 @@ int main(void)
     hp.mode = 1;
     if (adam_step(tl, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_OK || step != 1) return 19;
     adam_tl_destroy(tl);
+
+    /* the step without a handle: an empty list advances the counter without
+     * touching a device; a refused list leaves it */
+    step = 0;
+    if (adam_step_noalloc(t, 0, &d, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_OK || step != 1) return 20;
+    d.with_remainders = 1;
+    if (adam_step_noalloc(t, 1, &d, &hp, 1e-3f, &step, 1.0f, NULL, 0) != ADAM_EINVAL || step != 1) return 21;
+    d.with_remainders = 0;
+    if (adam_status_string(ADAM_ETOOBIG) == adam_status_string(-99)) return 22;
     puts("ok");
     return 0;
 }
