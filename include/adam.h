@@ -170,14 +170,26 @@ typedef struct {
 
 typedef struct adam_tl adam_tl; /* opaque handle: device work table */
 
-/* ABI version of the loaded library (ADAM_ABI_VERSION). */
+/* ABI version of the loaded library (ADAM_ABI_VERSION).  This library's own
+ * (the pages' interface is a Python extension module). */
 int adam_abi_version(void);
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL).  This library's own: the
+ * pages' launcher reports errors through TORCH_CHECK and C10_CUDA_CHECK
+ * (apex patch "Enhance Distributed Fused Adam (#1794)",
+ * multi_tensor_fused_adam_capturable_cuda); here every call returns a code. */
 const char *adam_status_string(int status);
 
 /* Validates a tensor list and computes its work table on the host only (no
- * HIP call, no device allocation); fills *stats (device = -1).
+ * HIP call, no device allocation); fills *stats (device = -1).  The list is
+ * the one the pages hand to multi_tensor_applier (apex
+ * distributed_fused_adam.py, _local_step: list(zip(*group_buffers)) of
+ * [param, exp_avg, exp_avg_sq, grad, param-sync] per bucket); the dtype sets
+ * are those of the DISPATCH_FLOAT_HALF_AND_BFLOAT over T, GRAD_T and
+ * PARAM_OUT_T in the patch's multi_tensor_fused_adam_capturable_cuda, plus
+ * the remainder and scaled-state schemes of distributed_fused_adam.py
+ * (_check_params_shard_dtypes, _local_step_with_param_remainders,
+ * _local_step_with_scaled_states).
  * Errors: ADAM_EINVAL for a NULL desc/stats, count < 0, NULL `tensors` with
  * count > 0, numel < 0, a NULL required pointer in a non-empty tensor, a
  * pointer given where the dtype says none, a bad chunk_elems, dispatch_tiles < 0,
@@ -194,8 +206,15 @@ const char *adam_status_string(int status);
 int adam_tl_plan(const adam_tensor *tensors, int64_t count, const adam_tl_desc *desc,
                  adam_tl_stats *stats);
 
-/* Builds a handle for one group: validates as adam_tl_plan, then copies the
- * work table (one 128-byte record per chunk, plus a 64-byte scalar block used
+/* Builds a handle for one group.  The pages rebuild a chunk table at every
+ * launch: multi_tensor_apply<5> in the patch's
+ * multi_tensor_fused_adam_capturable_cuda fills TensorListMetadata, and the
+ * functor's operator() finds its (tensor, chunk) through
+ * tl.block_to_tensor[blockIdx.x] and tl.block_to_chunk[blockIdx.x] (apex
+ * patch "Enhance Distributed Fused Adam (#1794)",
+ * DistAdamCapturableFunctor::operator()).  This library computes the
+ * equivalent table once per list, for the life of the handle: validates as
+ * adam_tl_plan, then copies the work table (one 128-byte record per chunk, plus a 64-byte scalar block used
  * by the capturable steps, partial-sum scratch for adam_grad_sumsq, and for
  * scaled state 12 bytes of maxima per 512-element tile and 24 bytes of maxima
  * and reciprocal scales per tensor) to the current device,
@@ -239,14 +258,20 @@ int adam_tl_plan_two_buffer(const adam_tensor *tensors, const adam_tensor *alter
 int adam_tl_build_two_buffer(const adam_tensor *tensors, const adam_tensor *alternates, int64_t count,
                              const adam_tl_desc *desc, hipStream_t stream, adam_tl **out);
 
-/* Frees a handle (NULL is allowed).  Work enqueued with it must be finished. */
+/* Frees a handle (NULL is allowed).  Work enqueued with it must be finished.
+ * This library's own (the handle has no counterpart on the pages). */
 void adam_tl_destroy(adam_tl *tl);
 
-/* Copies a handle's statistics to *stats (host). ADAM_EINVAL on NULL. */
+/* Copies a handle's statistics to *stats (host). ADAM_EINVAL on NULL.  This
+ * library's own. */
 int adam_tl_info(const adam_tl *tl, adam_tl_stats *stats);
 
 /* Non-capturable step on a handle with fp32 or 16-bit state (no remainders,
- * no scales).
+ * no scales): apex distributed_fused_adam.py, _local_step with capturable
+ * off (multi_tensor_fused_adam, the DistAdamFunctor whose name the patch's
+ * hunk header shows; its body is not on the pages, and the update is read as
+ * DistAdamCapturableFunctor::local_step with host scalars), after step()
+ * advances the counter (self.state["step"] += 1).
  *   lr          host value.
  *   step_io     host int32 counter: incremented first (the first update uses
  *               t = 1), also when the handle has no elements.  ADAM_EINVAL if
@@ -255,14 +280,21 @@ int adam_tl_info(const adam_tl *tl, adam_tl_stats *stats);
  *               NULL; d_grad_scale (device float, nullable) is read on the
  *               device instead (apex passes its grad scale as a device
  *               tensor).
- * On ADAM_EHIP from the launch the counter is restored.  Errors: ADAM_EINVAL
+ * On ADAM_EHIP the counter is restored if nothing of the step had been
+ * enqueued; if a later launch of the step failed, the counter keeps the new
+ * value and the buffers may hold a partly applied step.  Errors: ADAM_EINVAL
  * (NULL tl/hp/step_io, mode not 0/1, bias_correction not 0/1, a remainder
  * or scaled-state handle). */
 int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
               float grad_scale, const float *d_grad_scale, hipStream_t stream);
 
-/* Capturable step on a handle with fp32 or 16-bit state: every per-step
- * scalar lives in device memory, nothing is allocated, nothing is read back,
+/* Capturable step on a handle with fp32 or 16-bit state: apex patch
+ * "Enhance Distributed Fused Adam (#1794)", DistAdamCapturableFunctor::
+ * operator() (returns when *noop_gmem == 1; reads *lr, *step and
+ * *grad_scale_ptr on the device) and distributed_fused_adam.py step() with
+ * capturable on (the counter advances by (_dummy_overflow_buf != 1); the
+ * functor sees the advanced counter).  Every per-step scalar lives in device
+ * memory, nothing is allocated, nothing is read back,
  * and the host never waits, so the call can be recorded into a HIP graph and
  * replayed.
  *   d_lr          device float.
@@ -277,13 +309,18 @@ int adam_step(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step
  * the handle's scalar block; capturable steps of one handle must therefore
  * be ordered (one stream, or synchronised streams).
  * Errors: ADAM_EINVAL (NULL tl/hp/d_lr/d_step, bad mode/flag, a remainder
- * or scaled-state handle); ADAM_EHIP. */
+ * or scaled-state handle); ADAM_EHIP (if the prologue was enqueued before a
+ * launch failed, the device counter advances and the buffers may hold a
+ * partly applied step). */
 int adam_step_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
                          int32_t *d_step, const float *d_grad_scale, const int32_t *d_noop,
                          hipStream_t stream);
 
 /* Non-capturable step on a remainder handle (bf16 params + int16
- * remainders, fp32 m and v).  Each element's fp32 master is rebuilt from its
+ * remainders, fp32 m and v): apex distributed_fused_adam.py,
+ * _local_step_with_param_remainders (multi_tensor_fused_adam_with_param_
+ * remainders, whose functor the patch names but does not show) and
+ * _bf16_rem_to_fp32.  Each element's fp32 master is rebuilt from its
  * bf16 bits and remainder as apex's _bf16_rem_to_fp32 defines, updated as
  * above, and stored back in the same encoding (remainder = low 16 bits of the
  * fp32 word; bf16 = high 16 bits, plus one when that remainder is negative
@@ -296,10 +333,11 @@ int adam_step_remainders(const adam_tl *tl, const adam_hparams *hp, float lr,
 
 /* Capturable step on a remainder handle: the arithmetic and encoding of
  * adam_step_remainders with the device scalars, noop flag and counter rules
- * of adam_step_capturable (apex refuses remainders with its capturable
- * option; nothing in the update needs host scalars, so this library offers
- * both).  Errors as adam_step_capturable; ADAM_EINVAL for a handle that is
- * not in remainder mode. */
+ * of adam_step_capturable.  An extension of this library: apex
+ * distributed_fused_adam.py's constructor refuses store_param_remainders
+ * with capturable ("doesn't support CUDA graph yet"); nothing in the update
+ * needs host scalars, so both are offered.  Errors as adam_step_capturable;
+ * ADAM_EINVAL for a handle that is not in remainder mode. */
 int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, const float *d_lr,
                                     int32_t *d_step, const float *d_grad_scale,
                                     const int32_t *d_noop, hipStream_t stream);
@@ -321,11 +359,22 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
  * Note: with bf16 state a tensor whose largest magnitude is below about 0.5
  * gets a subnormal scale whose reciprocal overflows, so its values store as
  * +-inf (0 becomes NaN) -- the pages' formula does this; fp16 state does not.
- * Empty tensors keep their scales.  The call enqueues four kernels (a pass
- * that computes each tile's maxima of the updated buffers, a fold of those
- * maxima per tensor, a pass that recomputes the update and stores it, a
- * per-tensor kernel that writes the new scales); steps of one handle must be
- * ordered.
+ * Empty tensors keep their scales.  Per piece of the list (adam_tl_stats.
+ * pieces) the call enqueues four kernels: a pass that computes each tile's
+ * maxima of the updated buffers, a fold of those maxima per tensor, a pass
+ * that recomputes the update and stores it, a per-tensor kernel that writes
+ * the new scales (each pass as adam_tl_stats.dispatch_tiles allows).  With
+ * two or more pieces they alternate between `stream` and a second stream the
+ * handle owns, so that one piece's store pass runs beside the next piece's
+ * maxima pass: the call records an event on `stream` that the second stream
+ * waits for, events between the pieces, and a last event on the second
+ * stream that `stream` waits for, so all of the step is ordered after the
+ * work enqueued on `stream` before the call and before the work enqueued
+ * on it after.  Under stream capture the same calls record that fork and
+ * join into the graph.  The events and the second stream belong to the
+ * handle (the call uses them through the const handle): steps of one handle
+ * must be ordered (one stream, or synchronised streams), and one handle
+ * must not be captured into two graphs that run at the same time.
  * Arguments and errors as adam_step; ADAM_EINVAL for a handle without
  * scaled state. */
 int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
@@ -368,7 +417,9 @@ int adam_step_noalloc(const adam_tensor *tensors, int64_t count, const adam_tl_d
                       const adam_hparams *hp, float lr, int32_t *step_io, float grad_scale,
                       const float *d_grad_scale, hipStream_t stream);
 
-/* Sum of squares of every gradient element of a handle: the local part of
+/* Sum of squares of every gradient element of a handle (apex
+ * distributed_fused_adam.py, grad_norm: multi_tensor_l2norm over the grad
+ * shards, then the square summed and all-reduced): the local part of
  * the global gradient norm that apex's distributed_fused_adam.py computes in
  * grad_norm (per-bucket L2 norms of the gradient shards, squared and summed,
  * then all-reduced across ranks).  Each square of a float, bf16 or fp16 gradient is
