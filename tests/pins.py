@@ -802,20 +802,33 @@ def _from_numpy_state(a: np.ndarray, state_dtype):
 
 
 def torch_apply_state_scale(x32: np.ndarray, state_dtype):
-    """The pages' _apply_state_scale followed by the copy into the state
-    dtype, as the torch op sequence they print (CPU, float32)."""
-    import torch
+    """The per-tensor scaling that apex distributed_fused_adam.py defines in
+    DistributedFusedAdam._apply_state_scale, and the copy into the state
+    dtype T that follows it, restated from its mathematics in numpy float32
+    (every operation one IEEE rounding):
+        amax = max |X|                  (NaN if any element is NaN)
+        L    = largest finite T / 2     (exact in float32 for bf16 and fp16)
+        S    = amax / L
+        r    = 1 / S if S > 0 else 0
+        x    = T(X * r)                 (round to nearest even)
+    The casts to T are library conversions: numpy's float16 cast, torch's
+    CPU bfloat16 cast.  Returns (stored x as numpy bits, S)."""
+    x = np.ascontiguousarray(x32, np.float32)
+    fp16 = np.dtype(state_dtype) == np.float16
+    big = np.float32(np.finfo(np.float16).max) if fp16 else np.float32(2.0 - 2.0 ** -7) * np.float32(2.0 ** 127)
+    limit = big / np.float32(2.0)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        amax = np.max(np.abs(x))
+        scale = np.float32(amax / limit)
+        rscale = np.float32(np.float32(1.0) / scale) if scale > 0 else np.float32(0.0)
+        y = (x * rscale).astype(np.float32)
+        if fp16:
+            stored = y.astype(np.float16)
+        else:
+            import torch
 
-    t = torch.from_numpy(np.ascontiguousarray(x32, np.float32).copy())
-    dt = _torch_state_dtype(state_dtype)
-    max_scaled = torch.full([1], torch.finfo(dt).max / 2, dtype=torch.float32)
-    min_val, max_val = torch.aminmax(t)
-    absmax = torch.maximum(-min_val, max_val).to(torch.float32)
-    scale = torch.empty([1], dtype=torch.float32)
-    torch.div(absmax, max_scaled, out=scale)
-    rscale = torch.where(scale > 0, scale.reciprocal(), 0.0)
-    t.mul_(rscale)
-    return _to_numpy_state(t.to(dt), state_dtype), np.float32(scale.item())
+            stored = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+    return stored, np.float32(scale)
 
 
 def torch_unscale(a: np.ndarray, scale, state_dtype) -> np.ndarray:
