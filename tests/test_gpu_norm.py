@@ -21,6 +21,32 @@ pytestmark = pytest.mark.gpu
 SUMSQ_RTOL = 1e-12
 
 
+def assert_clip_from_exact_sum(orc, exact, gpu, scale0, max_norm, got_norm, got_scale, got_noop):
+    """The norm, new grad scale and found-inf flag the oracle computes from
+    its own exact sum of squares equal the GPU's (which started from the
+    GPU's sum).  The two sums differ by at most SUMSQ_RTOL (relative), so
+    their float norms can differ only when the norm of the exact sum lies
+    within that window of a float rounding boundary (the square root halves
+    the relative difference); then the two float norms must be neighbours
+    with that boundary between them."""
+    import math
+
+    norm, new_s, found = orc.clip_grad_scale(exact, scale0, max_norm)
+    same = lambda a, b: a == b or (np.isnan(a) and np.isnan(b))
+    if not (math.isfinite(exact) and math.isfinite(gpu)):
+        assert same(np.float32(gpu), np.float32(exact))  # both inf, or both NaN
+    raw_exact = np.float32(math.sqrt(exact)) if exact == exact else np.float32(np.nan)
+    raw_gpu = np.float32(math.sqrt(gpu)) if gpu == gpu else np.float32(np.nan)
+    if same(raw_exact, raw_gpu):
+        assert same(np.float32(got_norm), norm), (got_norm, norm)
+        assert np.float32(got_scale) == new_s, (got_scale, new_s)
+        assert got_noop == found
+    else:
+        assert np.nextafter(raw_exact, raw_gpu) == raw_gpu, (raw_exact, raw_gpu)
+        boundary = (float(raw_exact) + float(raw_gpu)) / 2
+        assert abs(math.sqrt(exact) - boundary) <= SUMSQ_RTOL * boundary
+
+
 @pytest.fixture(scope="module")
 def torch():
     t = torch_mod()
@@ -152,6 +178,10 @@ def test_clip_grad_scale_equals_the_oracle_bitwise(torch, orc, case):
     assert (got_norm == norm) or (np.isnan(got_norm) and np.isnan(norm))
     assert np.float32(d_scale.item()) == new_s
     assert int(d_noop.item()) == found == (1 if case in ("inf", "nan") else 0)
+    # the same from the oracle's own exact sum of the gradients
+    exact = orc.grad_sumsq([h.g for h in host])
+    assert_clip_from_exact_sum(orc, exact, float(d_sumsq.item()), np.float32(scale0), max_norm,
+                               got_norm, d_scale.item(), int(d_noop.item()))
     if case == "clip":
         assert new_s < np.float32(scale0)
     if case in ("no_clip", "max_norm_zero", "inf", "nan"):
@@ -245,6 +275,9 @@ def test_whole_capturable_step_in_one_graph(torch, orc, g_dtype, p_kind, p_out, 
         norm, new_s, found = orc.clip_grad_scale(sumsq, 1.0, max_norm)
         assert np.float32(d_norm.item()) == norm or (np.isnan(norm) and np.isnan(d_norm.item()))
         assert np.float32(d_scale.item()) == new_s
+        # the same from the oracle's own exact sum
+        assert_clip_from_exact_sum(orc, want, sumsq, 1.0, max_norm, d_norm.item(), d_scale.item(),
+                                   int(d_noop.item()))
         orc.group_step(r1, hr1, 1.6e-3, st1, float(new_s), noop=found)
         orc.group_step(r2, hr2, 1.6e-3, st2, float(new_s), noop=found)
     assert int(s1.item()) == st1[0] == 4 and int(s2.item()) == st2[0] == 4
