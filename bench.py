@@ -1,6 +1,6 @@
 """Benchmark of the fused multi-tensor AdamW step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bench201]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload bench201] [--no-extra]
 
 Default workload: 201 fp32 tensors of 320*65536 = 20,971,520 elements
 (4,215,275,520 elements; p, g, m, v fp32), AdamW, lr 1.6e-3, betas
@@ -22,9 +22,20 @@ set of p, m, v fits in HBM, the same K steps are timed once more on a
 two-buffer handle (``two_buffer_state``: each step reads one buffer set and
 writes the other); ``value`` and ``roofline`` stay the in-place step.
 
+In the same process, three interleaved rounds of K update steps and K
+launches of an in-place streaming probe over the same buffers (the same
+streams read and written once each, in the update's tile map, with no
+arithmetic: ``tests/hw/stream_probe.hip``) give the ceiling this machine's HBM
+reaches for the workload's own stream mix (``ceiling``).  With the default
+workload the other configurations follow, one at a time, each with its
+ceiling, its 85%-of-8-TB/s target and a short oracle sample
+(``workloads``): the 30B-class shard (non-capturable, two groups), the ZeRO
+shard (capturable), the remainder list, 16-bit state and scaled 16-bit
+state.
+
 The CPU baseline is the oracle (plain scalar C) on a bounded sample of the
-same workload, run on the host's cores (one thread per core, each on a
-contiguous slice).
+same workload, run on every core of the process's affinity mask (one thread
+per core, each on a contiguous slice).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -84,36 +95,36 @@ def measured_traffic(workload: str, key: str = "bytes_per_launch"):
 # writable directory the rocprofv3 CSV output goes to.
 PROFILE_COMMANDS = {
     "trace": "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace_{w} "
-             "-o run -- python3 <repo>/bench.py --workload {w} > <out>/trace_{w}.log",
+             "-o run -- python3 <repo>/bench.py --workload {w} --no-extra --no-ceiling > <out>/trace_{w}.log",
     "fetch": "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/pmc_fetch_{w} "
-             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable "
+             "-o run -- python3 <repo>/bench.py --workload {w} --no-extra --no-ceiling --steps 3 --warmup 1 --no-cpu --no-capturable "
              "> <out>/pmc_fetch_{w}.log",
     "write": "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/pmc_write_{w} "
-             "-o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable "
+             "-o run -- python3 <repo>/bench.py --workload {w} --no-extra --no-ceiling --steps 3 --warmup 1 --no-cpu --no-capturable "
              "> <out>/pmc_write_{w}.log",
     "summary": "python bench.py --summarize-profiles --workload {w} --trace-dir <out>/trace_{w} "
                "--trace-log <out>/trace_{w}.log --fetch-dir <out>/pmc_fetch_{w} --write-dir <out>/pmc_write_{w} "
                "--fetch-log <out>/pmc_fetch_{w}.log --write-log <out>/pmc_write_{w}.log",
     "valu": "cd /tmp && rocprofv3 --pmc SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_WAVES GRBM_GUI_ACTIVE "
             "--output-format csv -d <out>/pmc_valu_{w} -o run -- python3 <repo>/bench.py "
-            "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
+            "--workload {w} --no-extra --no-ceiling --steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
     "valu_summary": "python bench.py --summarize-valu --workload {w} --valu-dir <out>/pmc_valu_{w}",
     "occupancy": "cd /tmp && rocprofv3 --pmc MeanOccupancyPerCU OccupancyPercent --output-format csv "
-                 "-d <out>/pmc_occ_{w} -o run -- python3 <repo>/bench.py --workload {w} "
+                 "-d <out>/pmc_occ_{w} -o run -- python3 <repo>/bench.py --workload {w} --no-extra --no-ceiling "
                  "--steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
     "occupancy_summary": "python bench.py --summarize-occupancy --workload {w} --occupancy-dir <out>/pmc_occ_{w}",
     "dram_req": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_WRREQ_sum "
                 "TCC_EA0_WRREQ_64B_sum --output-format csv -d <out>/pmc_dreq_{w} -o run -- "
-                "python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable "
+                "python3 <repo>/bench.py --workload {w} --no-extra --no-ceiling --steps 3 --warmup 1 --no-cpu --no-capturable "
                 "--no-two-buffer",
     "dram_stall": "cd /tmp && rocprofv3 --pmc TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_WRREQ_LEVEL_sum "
                   "TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum GRBM_GUI_ACTIVE "
                   "--output-format csv -d <out>/pmc_dstall_{w} -o run -- python3 <repo>/bench.py "
-                  "--workload {w} --steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
+                  "--workload {w} --no-extra --no-ceiling --steps 3 --warmup 1 --no-cpu --no-capturable --no-two-buffer",
     "dram_summary": "python bench.py --summarize-dram --workload {w} --dram-req-dir <out>/pmc_dreq_{w} "
                     "--dram-stall-dir <out>/pmc_dstall_{w}",
     "memunit": "cd /tmp && rocprofv3 --pmc TA_TA_BUSY_sum GRBM_GUI_ACTIVE MemUnitStalled --output-format csv "
-               "-d <out>/pmc_mem_{w} -o run -- python3 <repo>/bench.py --workload {w} --steps 3 --warmup 1 "
+               "-d <out>/pmc_mem_{w} -o run -- python3 <repo>/bench.py --workload {w} --no-extra --no-ceiling --steps 3 --warmup 1 "
                "--no-cpu --no-capturable --no-two-buffer",
     "memunit_summary": "python bench.py --summarize-memunit --workload {w} --memunit-dir <out>/pmc_mem_{w}",
 }
@@ -616,7 +627,7 @@ def cpu_baseline(w, sample_elems: int, sample_steps: int, target_s: float = 10.0
     from workloads import host_tensors
 
     o = oracle.default()
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    cores = max(1, len(os.sched_getaffinity(0)))  # every core the process may run on
     if w.p_kind.endswith("_scaled"):
         sample_elems //= 8  # the scaled-state oracle is ~8x slower per element
     sizes = []
@@ -660,20 +671,282 @@ def cpu_baseline(w, sample_elems: int, sample_steps: int, target_s: float = 10.0
                 break
     dt = time.perf_counter() - t0
     gbps = n * sample_steps * w.bytes_per_elem / dt / 1e9
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu_model = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": f"first {len(sizes)} of {len(w.sizes)} tensors ({n:,} elements, workload dtypes) x "
                       f"{sample_steps} steps: {n * sample_steps:,} element updates in {dt:.2f} s wall "
                       f"({dt * cores:.0f} thread-seconds)",
-            "elements_per_s": round(n * sample_steps / dt, 1), "cpu_model": cpu_model}
+            "elements_per_s": round(n * sample_steps / dt, 1), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: model name, family, model and
+    stepping of the first processor, and whether it runs under a hypervisor."""
+    info = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if not line.strip():
+                    break  # the first processor's block
+                key, _, val = line.partition(":")
+                info.setdefault(key.strip(), val.strip())
+    except OSError:
+        return ""
+    text = info.get("model name", "")
+    ids = [f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info]
+    extra = ids + (["virtualised (hypervisor flag)"] if "hypervisor" in info.get("flags", "").split() else [])
+    return f"{text} ({', '.join(extra)})" if extra else text
+
+
+def build_run(w, args, A, torch):
+    """Draws a workload's inputs on the GPU and builds one handle per group
+    (views into flat buffers); returns the buffers, handles and step
+    helpers."""
+    from types import SimpleNamespace
+
+    from workloads import device_flat, scaled_p_scale, split_views
+
+    groups = [(w.sizes, w.weight_decay)] + list(w.extra_groups)
+    total = w.numel
+    t0 = time.perf_counter()
+    bufs = device_flat(total, g_dtype=w.g_dtype, p_kind=w.p_kind, p_out=w.p_out, seed=w.seed,
+                       g_multiplier=w.grad_multiplier)
+    torch.cuda.synchronize()
+    log(f"{w.name}: inputs drawn on the GPU in {time.perf_counter() - t0:.1f} s")
+
+    # one handle per group, views into the flat buffers
+    scaled = w.p_kind.endswith("_scaled")
+    mv_desc = "scaled 16-bit" if scaled else w.p_kind if w.p_kind in ("bf16", "f16") else "f32"
+    p_out = ("bf16" if w.p_out is True else w.p_out) or None
+    handles = []
+    scale_bufs = []
+    off = 0
+    for sizes, wd in groups:
+        n = sum(sizes)
+        views = {k: split_views(v[off:off + n], sizes) for k, v in bufs.items()}
+        tensors = [{k: views[k][i] for k in views} for i in range(len(sizes))]
+        if scaled:
+            # per-tensor scales of p, m, v: the drawn p's power-of-two scale;
+            # zero moments carry scale 0 (a fresh optimizer)
+            sc = torch.zeros((len(sizes), 3), dtype=torch.float32, device="cuda")
+            sc[:, 0] = scaled_p_scale(w.p_kind)
+            scale_bufs.append(sc)
+            for i, t in enumerate(tensors):
+                t["scales"] = sc[i]
+        desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out, chunk_elems=args.chunk_elems)
+        tl = A.adam_tl_build(tensors, desc)
+        hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
+        # each group keeps its own counter, host and device
+        handles.append((tl, hp, n, A.HostStep(0), torch.zeros(1, dtype=torch.int32, device="cuda")))
+        off += n
+    info = handles[0][0].info()
+    log(f"{w.name}: work table: {info['chunks']} records of {info['chunk_elems']} elements; "
+        f"{info['grid_blocks']} workgroups of {info['block_threads']} threads, "
+        f"{info['tile_elems']} elements each, {info['dispatches']} dispatch(es)")
+
+    step_fn = {"bf16_rem": A.adam_step_remainders, "bf16_scaled": A.adam_step_scaled,
+               "f16_scaled": A.adam_step_scaled}.get(w.p_kind, A.adam_step)
+    cap_fn = {"bf16_rem": A.adam_step_remainders_capturable, "bf16_scaled": A.adam_step_scaled_capturable,
+              "f16_scaled": A.adam_step_scaled_capturable}.get(w.p_kind, A.adam_step_capturable)
+    stream = torch.cuda.current_stream()
+    d_scale = torch.tensor([w.grad_scale], dtype=torch.float32, device="cuda")
+    d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
+    d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def launch_timed(ev, launch):
+        """Runs launch(); when ev is a list, brackets it with HIP events on the
+        launch stream and appends the pair."""
+        if ev is None:
+            launch()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+        ev.append((e0, e1))
+
+    def one_step_noncap(ev=None):
+        """One step: every group once; events bracket the first (largest)
+        group's launch."""
+        for i, (tl, hp, _, host_step, _) in enumerate(handles):
+            launch_timed(ev if i == 0 else None,
+                         lambda: step_fn(tl, hp, w.lr, host_step, 1.0, d_scale, stream))
+
+    def one_step_cap(ev=None, s=stream):
+        """One capturable step of every group (device lr, counter, grad scale
+        and noop flag); events bracket the first group's call."""
+        for i, (tl, hp, _, _, d_step) in enumerate(handles):
+            launch_timed(ev if i == 0 else None,
+                         lambda: cap_fn(tl, hp, d_lr, d_step, d_scale, d_noop, s))
+
+    def timed(step_once, k, events=True):
+        """Runs k steps between two synchronisations; returns (wall ms per
+        step, per-launch event ms of the first group's launches)."""
+        ev = [] if events else None
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(k):
+            step_once(ev)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t_start) * 1e3 / k
+        per = [a.elapsed_time(b) for a, b in (ev or [])]
+        return wall, per
+
+    def destroy():
+        for h in handles:
+            h[0].destroy()
+
+    return SimpleNamespace(w=w, groups=groups, total=total, bufs=bufs, handles=handles, scale_bufs=scale_bufs,
+                           info=info, scaled=scaled, mv_desc=mv_desc, p_out=p_out, step_fn=step_fn, cap_fn=cap_fn,
+                           stream=stream, d_scale=d_scale, d_lr=d_lr, d_noop=d_noop, launch_timed=launch_timed,
+                           one_step_noncap=one_step_noncap, one_step_cap=one_step_cap, timed=timed, destroy=destroy)
+
+
+# ---------------------------------------------------------------------------
+# The streaming ceiling of a workload's own stream mix, in the same process
+# ---------------------------------------------------------------------------
+
+PROBE_LIBRARY = os.path.join(ROOT, "tests", "hw", "libstream_probe.so")
+# The update launches fp32-moment lists with at most this many workgroups per
+# compute unit (the library's occupancy limit); the probe copies it.
+FP32_MOMENT_WG_PER_CU = 7
+
+
+def probe_library():
+    """The in-place streaming probe (tests/hw/stream_probe.hip), or None if it
+    has not been built."""
+    import ctypes
+
+    if not os.path.exists(PROBE_LIBRARY):
+        return None
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    vp = ctypes.c_void_p
+    lib.stream_probe_mix_run.restype = ctypes.c_int
+    lib.stream_probe_mix_run.argtypes = [ctypes.c_int] * 5 + [vp] * 6 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                                        vp, ctypes.POINTER(ctypes.c_float)]
+    return lib
+
+
+def probe_mix(w):
+    """(p, m/v, g, p_out bytes per element, remainders) of a workload's streams,
+    and the probe's resident-workgroup limit (the update's)."""
+    state16 = w.p_kind in ("bf16", "f16") or w.p_kind.endswith("_scaled")
+    rem = w.p_kind == "bf16_rem"
+    pb = 2 if state16 or rem else 4
+    mb = 2 if state16 else 4
+    gb = 4 if w.g_dtype == "f32" else 2
+    out = ("bf16" if w.p_out is True else w.p_out) or None
+    ob = {None: 0, "f32": 4}.get(out, 2)
+    limit = FP32_MOMENT_WG_PER_CU if mb == 4 else 0
+    return (pb, mb, gb, ob, 1 if rem else 0), limit
+
+
+def probe_ms(lib, r, launches: int) -> float:
+    """Mean launch time of the in-place probe over the workload's own flat
+    buffers (p, m, v and remainders read and written back unchanged, g read,
+    p_out written), `launches` launches on the run's stream."""
+    import ctypes
+
+    mix, limit = probe_mix(r.w)
+    b = r.bufs
+    ptr = lambda k: ctypes.c_void_p(b[k].data_ptr()) if k in b else None
+    ms = ctypes.c_float(0.0)
+    rc = lib.stream_probe_mix_run(*mix, ptr("p"), ptr("rem"), ptr("m"), ptr("v"), ptr("g"), ptr("p_out"),
+                                  r.total - r.total % 4, limit, launches, ctypes.c_void_p(r.stream.cuda_stream),
+                                  ctypes.byref(ms))
+    if rc != 0:
+        raise RuntimeError(f"stream_probe_mix_run failed: {rc}")
+    return ms.value
+
+
+def interleaved_rounds(r, lib, step_once, k: int, rounds: int) -> dict:
+    """`rounds` rounds of: k steps of the update (wall time per step between
+    two synchronisations, and HIP-event time of the first group's launch),
+    then k launches of the probe of the same stream mix over the same
+    buffers; medians over the rounds."""
+    upd, upd_launch, probe = [], [], []
+    for _ in range(rounds):
+        wall, per = r.timed(step_once, k)
+        upd.append(wall)
+        upd_launch.append(statistics.mean(per))
+        probe_ms(lib, r, 1)  # the probe's first launch in a round is not timed
+        probe.append(probe_ms(lib, r, k))
+    bytes_step = r.total * r.w.bytes_per_elem
+    u, ul, c = statistics.median(upd), statistics.median(upd_launch), statistics.median(probe)
+    (pb, mb, gb, ob, rem), limit = probe_mix(r.w)
+    return {
+        "what": f"in-place probe of the same streams (p {pb} B, m/v {mb} B, g {gb} B, p_out {ob} B, "
+                f"remainders {'2 B' if rem else 'none'} per element; read and written once, no arithmetic; "
+                f"the update's tile map{', ' + str(limit) + ' workgroups per CU' if limit else ''}), "
+                f"interleaved with the update, medians of {rounds} rounds of {k}",
+        "gbps": round(bytes_step / (c * 1e-3) / 1e9, 1),
+        "frac": round(bytes_step / (c * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "probe_ms": round(c, 4),
+        "update_ms_per_step": round(u, 4),
+        "update_launch_ms": round(ul, 4),
+        "update_gbps": round(bytes_step / (u * 1e-3) / 1e9, 1),
+        "update_over_ceiling": round(c / u, 4),
+        "rounds_update_ms": [round(x, 4) for x in upd],
+        "rounds_probe_ms": [round(x, 4) for x in probe],
+    }
+
+
+# The configurations timed beside the main workload, each with the step call
+# its configuration names ("capturable": device scalars, noop flag 0).
+EXTRA_WORKLOADS = ("shard30b", "zero1e9", "rem5e8", "state16_1e9", "scaled1e9")
+CAPTURABLE_WORKLOADS = ("zero1e9",)
+TARGET_FRAC = 0.85
+
+
+def measure_extra(name, args, A, torch, lib) -> dict:
+    """Draws one more workload, times its step (and the probe of its stream
+    mix) in interleaved rounds, and times the oracle on a short sample."""
+    from workloads import workloads
+
+    w = workloads()[name]
+    r = build_run(w, args, A, torch)
+    capt = name in CAPTURABLE_WORKLOADS
+    step_once = r.one_step_cap if capt else r.one_step_noncap
+    for _ in range(args.warmup):
+        step_once()
+    torch.cuda.synchronize()
+    bytes_step = r.total * w.bytes_per_elem
+    out = {"config": f"{len(w.sizes) + sum(len(s) for s, _ in w.extra_groups)} tensors, {r.total:,} elements, "
+                     f"p {w.p_kind}, g {w.g_dtype}, m/v {r.mv_desc}, p_out {r.p_out or 'none'}, "
+                     f"{w.bytes_per_elem} B/elem",
+           "call": (r.cap_fn if capt else r.step_fn).__name__,
+           "pieces": r.info["pieces"], "dispatches": r.info["dispatches"]}
+    if lib is not None:
+        rounds = interleaved_rounds(r, lib, step_once, args.steps, args.rounds)
+        ms = rounds["update_ms_per_step"]
+        out["ceiling"] = {k: rounds[k] for k in ("what", "gbps", "frac", "probe_ms", "update_over_ceiling",
+                                                 "rounds_update_ms", "rounds_probe_ms")}
+        launch = rounds["update_launch_ms"]
+    else:
+        ms, per = r.timed(step_once, args.steps)
+        launch = statistics.mean(per)
+        out["ceiling"] = None
+    gbps = bytes_step / (ms * 1e-3) / 1e9
+    target_ms = bytes_step / (TARGET_FRAC * HBM_PEAK_GBPS * 1e9) * 1e3
+    out.update({
+        "ms_per_step": round(ms, 4),
+        "gbps": round(gbps, 1),
+        "frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "elements_per_s": round(r.total / (ms * 1e-3), 1),
+        "first_group_launch_ms": round(launch, 4),
+        "target_ms_at_85pct": round(target_ms, 3),
+        "meets_target": ms <= target_ms,
+        "traffic": measured_traffic(name),
+    })
+    log(f"{name}: {ms:.3f} ms/step, {gbps:.0f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}%), ceiling "
+        f"{(out['ceiling'] or {}).get('gbps')} GB/s")
+    r.destroy()
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_elements // 4, 0, target_s=args.extra_cpu_seconds)
+    return out
 
 
 def main() -> int:
@@ -690,6 +963,16 @@ def main() -> int:
     ap.add_argument("--no-capturable", action="store_true")
     ap.add_argument("--no-two-buffer", action="store_true",
                     help="skip the two-buffer-state measurement")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the in-place streaming probe of the same stream mix")
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="interleaved rounds of update and probe for the ceilings")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time the main workload only (no per-configuration map)")
+    ap.add_argument("--extra", default=",".join(EXTRA_WORKLOADS),
+                    help="configurations timed after the default workload (comma separated)")
+    ap.add_argument("--extra-cpu-seconds", type=float, default=2.0,
+                    help="wall seconds of oracle time per extra configuration")
     ap.add_argument("--summarize-profiles", action="store_true",
                     help="write profiles/ summaries from rocprofv3 CSV directories (no GPU)")
     ap.add_argument("--trace-dir")
@@ -748,7 +1031,7 @@ def main() -> int:
     import torch
 
     import adamw_optimizer_step_tensor_amd as A
-    from workloads import device_flat, scaled_p_scale, split_views, workloads
+    from workloads import split_views, workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -760,79 +1043,11 @@ def main() -> int:
     log(f"workload {w.name}: {total:,} elements in {sum(len(s) for s, _ in groups)} tensors, "
         f"{w.bytes_per_elem} B/elem, {total * w.bytes_per_elem / 1e9:.2f} GB per step")
 
-    t0 = time.perf_counter()
-    bufs = device_flat(total, g_dtype=w.g_dtype, p_kind=w.p_kind, p_out=w.p_out, seed=w.seed,
-                       g_multiplier=w.grad_multiplier)
-    torch.cuda.synchronize()
-    log(f"inputs drawn on the GPU in {time.perf_counter() - t0:.1f} s")
-
-    # one handle per group, views into the flat buffers
-    scaled = w.p_kind.endswith("_scaled")
-    mv_desc = "scaled 16-bit" if scaled else w.p_kind if w.p_kind in ("bf16", "f16") else "f32"
-    p_out = ("bf16" if w.p_out is True else w.p_out) or None
-    handles = []
-    scale_bufs = []
-    off = 0
-    for sizes, wd in groups:
-        n = sum(sizes)
-        views = {k: split_views(v[off:off + n], sizes) for k, v in bufs.items()}
-        tensors = [{k: views[k][i] for k in views} for i in range(len(sizes))]
-        if scaled:
-            # per-tensor scales of p, m, v: the drawn p's power-of-two scale;
-            # zero moments carry scale 0 (a fresh optimizer)
-            sc = torch.zeros((len(sizes), 3), dtype=torch.float32, device="cuda")
-            sc[:, 0] = scaled_p_scale(w.p_kind)
-            scale_bufs.append(sc)
-            for i, t in enumerate(tensors):
-                t["scales"] = sc[i]
-        desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out, chunk_elems=args.chunk_elems)
-        tl = A.adam_tl_build(tensors, desc)
-        hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
-        # each group keeps its own counter, host and device
-        handles.append((tl, hp, n, A.HostStep(0), torch.zeros(1, dtype=torch.int32, device="cuda")))
-        off += n
-    info = handles[0][0].info()
-    log(f"work table: {info['chunks']} records of {info['chunk_elems']} elements; "
-        f"{info['grid_blocks']} workgroups of {info['block_threads']} threads, "
-        f"{info['tile_elems']} elements each")
-
-    step_fn = {"bf16_rem": A.adam_step_remainders, "bf16_scaled": A.adam_step_scaled,
-               "f16_scaled": A.adam_step_scaled}.get(w.p_kind, A.adam_step)
-    stream = torch.cuda.current_stream()
-    d_scale = torch.tensor([w.grad_scale], dtype=torch.float32, device="cuda")
-
-    def launch_timed(ev, launch):
-        """Runs launch(); when ev is a list, brackets it with HIP events on the
-        launch stream and appends the pair."""
-        if ev is None:
-            launch()
-            return
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        launch()
-        e1.record(stream)
-        ev.append((e0, e1))
-
-    def one_step_noncap(ev=None):
-        """One step: every group once; events bracket the first (largest)
-        group's launch."""
-        for i, (tl, hp, _, host_step, _) in enumerate(handles):
-            launch_timed(ev if i == 0 else None,
-                         lambda: step_fn(tl, hp, w.lr, host_step, 1.0, d_scale, stream))
-
-    def timed(step_once, k, events=True):
-        """Runs k steps between two synchronisations; returns (wall ms per
-        step, per-launch event ms of the first group's launches)."""
-        ev = [] if events else None
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for _ in range(k):
-            step_once(ev)
-        torch.cuda.synchronize()
-        wall = (time.perf_counter() - t_start) * 1e3 / k
-        per = [a.elapsed_time(b) for a, b in (ev or [])]
-        return wall, per
+    r = build_run(w, args, A, torch)
+    bufs, handles, scale_bufs, info = r.bufs, r.handles, r.scale_bufs, r.info
+    scaled, mv_desc, p_out = r.scaled, r.mv_desc, r.p_out
+    step_fn, stream, d_scale = r.step_fn, r.stream, r.d_scale
+    launch_timed, one_step_noncap, timed = r.launch_timed, r.one_step_noncap, r.timed
 
     # --- non-capturable -----------------------------------------------------
     for _ in range(args.warmup):
@@ -894,18 +1109,20 @@ def main() -> int:
         },
     }
 
+    # --- the streaming ceiling of the same stream mix, interleaved -----------
+    probe = None if args.no_ceiling else probe_library()
+    if args.no_ceiling:
+        result["ceiling"] = None
+    elif probe is None:
+        result["ceiling"] = {"skipped": f"{PROBE_LIBRARY} is not built"}
+    else:
+        result["ceiling"] = interleaved_rounds(r, probe, one_step_noncap, args.steps, args.rounds)
+        log(f"ceiling: probe {result['ceiling']['gbps']} GB/s, update {result['ceiling']['update_gbps']} GB/s "
+            f"(update / ceiling {result['ceiling']['update_over_ceiling']})")
+
     # --- capturable, eager and graph -----------------------------------------
-    cap_fn = {"bf16_rem": A.adam_step_remainders_capturable, "bf16_scaled": A.adam_step_scaled_capturable,
-              "f16_scaled": A.adam_step_scaled_capturable}.get(w.p_kind, A.adam_step_capturable)
+    cap_fn, d_lr, d_noop, one_step_cap = r.cap_fn, r.d_lr, r.d_noop, r.one_step_cap
     if not args.no_capturable and cap_fn is not None:
-        d_lr = torch.tensor([w.lr], dtype=torch.float32, device="cuda")
-        d_noop = torch.zeros(1, dtype=torch.int32, device="cuda")
-
-        def one_step_cap(ev=None, s=stream):
-            for i, (tl, hp, _, _, d_step) in enumerate(handles):
-                launch_timed(ev if i == 0 else None,
-                             lambda: cap_fn(tl, hp, d_lr, d_step, d_scale, d_noop, s))
-
         for _ in range(args.warmup):
             one_step_cap()
         cap_wall, cap_per = timed(one_step_cap, args.steps)
@@ -1029,10 +1246,22 @@ def main() -> int:
                 h[0].destroy()
             del alt_bufs
 
-    for h in handles:
-        h[0].destroy()
-    del bufs, scale_bufs
+    r.destroy()
+    del bufs, scale_bufs, r
     torch.cuda.empty_cache()
+
+    # --- the other configurations, each with its own ceiling -----------------
+    extra = [] if args.no_extra or args.workload != "bench201" else \
+        [x for x in args.extra.split(",") if x and x != w.name]
+    if extra:
+        if probe is None and not args.no_ceiling:
+            probe = probe_library()
+        result["workloads"] = {}
+        for name in extra:
+            result["workloads"][name] = measure_extra(name, args, A, torch, None if args.no_ceiling else probe)
+            print(f"[bench] {name}: " + json.dumps({k: v for k, v in result['workloads'][name].items()
+                                                    if k not in ('cpu_baseline', 'ceiling')}),
+                  file=sys.stderr, flush=True)
 
     if not args.no_cpu:
         log("cpu baseline (oracle) ...")
