@@ -69,7 +69,8 @@ class AdamTensor(ctypes.Structure):
 class AdamTlDesc(ctypes.Structure):
     """adam_tl_desc"""
     _fields_ = [("p", c_i32), ("g", c_i32), ("p_out", c_i32), ("with_remainders", c_i32),
-                ("chunk_elems", c_i64), ("scaled_state", c_i32), ("dispatch_tiles", c_i32)]
+                ("chunk_elems", c_i64), ("scaled_state", c_i32), ("dispatch_tiles", c_i32),
+                ("scaled_passes", c_i32), ("scaled_wait_us", c_i32)]
 
 
 class AdamHParams(ctypes.Structure):
@@ -88,7 +89,7 @@ class AdamTlStats(ctypes.Structure):
                 ("chunk_elems", c_i64), ("vector_tensors", c_i64), ("grid_blocks", c_i64),
                 ("tile_elems", c_i32), ("block_threads", c_i32), ("bytes_per_elem", c_i32),
                 ("device", c_i32), ("two_buffer", c_i32), ("pieces", c_i32),
-                ("dispatch_tiles", c_i32), ("dispatches", c_i32)]
+                ("dispatch_tiles", c_i32), ("dispatches", c_i32), ("scaled_passes", c_i32)]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -235,18 +236,22 @@ def _tensor_array(tensors: Sequence, desc: AdamTlDesc):
     return arr
 
 
-def make_desc(*, g="f32", p="f32", p_out=None, chunk_elems=0, dispatch_tiles=0) -> AdamTlDesc:
+def make_desc(*, g="f32", p="f32", p_out=None, chunk_elems=0, dispatch_tiles=0, scaled_passes=0,
+              scaled_wait_us=0) -> AdamTlDesc:
     """Descriptor from short names: g in {"f32", "bf16", "f16"}; p in {"f32",
     "bf16", "f16" (16-bit p, m, v), "bf16_rem" (bf16 + int16 remainders, fp32
     m, v), "bf16_scaled", "f16_scaled" (scaled 16-bit p, m, v)}; p_out in
     {None, "f32", "bf16", "f16"}; dispatch_tiles: tiles per kernel dispatch
-    (0: the most one dispatch carries)."""
+    (0: the most one dispatch carries); scaled_passes (scaled state): 0
+    automatic, 1 one pass, 2 two passes; scaled_wait_us: the one-pass wait
+    (0: default, -1: none)."""
     gd = {"f32": DT_F32, "bf16": DT_BF16, "f16": DT_F16}[g]
     pd, rem, scaled = {"f32": (DT_F32, 0, 0), "bf16": (DT_BF16, 0, 0), "f16": (DT_F16, 0, 0),
                        "bf16_rem": (DT_BF16, 1, 0),
                        "bf16_scaled": (DT_BF16, 0, 1), "f16_scaled": (DT_F16, 0, 1)}[p]
     od = {None: DT_NONE, "f32": DT_F32, "bf16": DT_BF16, "f16": DT_F16}[p_out]
-    return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), scaled, int(dispatch_tiles))
+    return AdamTlDesc(pd, gd, od, rem, int(chunk_elems), scaled, int(dispatch_tiles), int(scaled_passes),
+                      int(scaled_wait_us))
 
 
 def _stream(stream) -> Optional[int]:

@@ -123,7 +123,21 @@ typedef struct {
                                 work-items in 32 bits); else a positive limit,
                                 capped at that.  Longer lists are launched as
                                 several dispatches over consecutive tiles.
+                                One-pass scaled state runs one persistent
+                                dispatch; a nonzero value caps its workgroups
+                                at dispatch_tiles / 8.  Results do not depend
+                                on it.                                         */
+    int32_t scaled_passes;   /* scaled state: 0 or 2 = two passes, 1 = one pass
+                                (see adam_step_scaled; ADAM_EINVAL if the list
+                                does not allow it); must be 0 otherwise.
                                 Results do not depend on it.                   */
+    int32_t scaled_wait_us;  /* one-pass scaled state: how long a workgroup
+                                waits for the rest of its tensor before it
+                                leaves its stores to the follow-up pass:
+                                0 = 200 us, > 0 = that many us, -1 = no wait
+                                (every tile but each tensor's last is stored
+                                by the follow-up pass).  Results do not
+                                depend on it.                                  */
 } adam_tl_desc;
 
 /* Per-group hyperparameters (apex defaults: betas (0.9, 0.999), eps 1e-8,
@@ -165,7 +179,8 @@ typedef struct {
     int32_t dispatch_tiles;  /* tiles per kernel dispatch (adam_tl_desc)         */
     int32_t dispatches;      /* dispatches of the update kernel per step (scaled
                                 state: of each of its two passes, summed over
-                                the pieces)                                     */
+                                the pieces; one pass: of the one-pass kernel)  */
+    int32_t scaled_passes;   /* scaled state: 1 (one pass) or 2; 0 otherwise    */
 } adam_tl_stats;
 
 typedef struct adam_tl adam_tl; /* opaque handle: device work table */
@@ -375,6 +390,17 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
  * handle (the call uses them through the const handle): steps of one handle
  * must be ordered (one stream, or synchronised streams), and one handle
  * must not be captured into two graphs that run at the same time.
+ * One pass (adam_tl_desc.scaled_passes = 1): a persistent kernel whose
+ * workgroups each update a 4096-element tile exactly, publish its maxima,
+ * and store it once the last workgroup of its tensor has published the
+ * tensor's scales (each input is read once, where two passes read it
+ * twice); a follow-up kernel stores any tile whose bounded wait ran out
+ * (adam_tl_desc.scaled_wait_us), and a per-tensor kernel writes the new
+ * scales.  Same results bit for bit.  It needs every tensor within 2M
+ * elements and 4-element accesses, and a device that keeps the kernel's
+ * grid resident; on MI355X it measured slower than two passes (its
+ * per-tile exchange between workgroups goes through device-coherent
+ * memory), so two passes are the default.
  * Arguments and errors as adam_step; ADAM_EINVAL for a handle without
  * scaled state. */
 int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,

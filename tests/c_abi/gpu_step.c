@@ -48,7 +48,7 @@ int main(int argc, char **argv)
     int i, k;
     int32_t step = 0;
     adam_tensor t, t2;
-    adam_tl_desc desc = {ADAM_DT_F32, ADAM_DT_F32, ADAM_DT_NONE, 0, 0, 0, 0};
+    adam_tl_desc desc = {ADAM_DT_F32, ADAM_DT_F32, ADAM_DT_NONE, 0, 0, 0, 0, 0, 0};
     adam_hparams hp;
     adam_tl *tl = NULL;
     hipStream_t stream;

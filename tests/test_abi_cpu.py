@@ -405,27 +405,27 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 
 def test_scaled_plans_report_their_pieces():
-    """A scaled-state list of at least 8192 tiles (4M elements, tensor ends
+    """Two-pass scaled state: a list of at least 8192 tiles (4M elements, tensor ends
     rounded up to whole records) in two or more tensors is pipelined in up to
     min(16, tensors, tiles / 1024) pieces of about equal tiles, cut at tensor
     boundaries, none below 1024 tiles; anything else runs in one."""
     big = [1 << 21, 1 << 21]
-    assert plan(fake_tensors(big, scaled=True), p="f16_scaled")["pieces"] == 2
-    assert plan(fake_tensors([1 << 20] * 12, scaled=True), p="bf16_scaled")["pieces"] == 12
-    assert plan(fake_tensors([1 << 20] * 20, scaled=True), p="f16_scaled")["pieces"] == 16  # 40960 tiles
-    assert plan(fake_tensors([1 << 18] * 20, scaled=True), p="f16_scaled")["pieces"] == 10  # 10240 tiles
-    assert plan(fake_tensors([1 << 19] * 16, scaled=True), p="f16_scaled")["pieces"] == 16  # 16384 tiles
+    assert plan(fake_tensors(big, scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 2
+    assert plan(fake_tensors([1 << 20] * 12, scaled=True), p="bf16_scaled", scaled_passes=2)["pieces"] == 12
+    assert plan(fake_tensors([1 << 20] * 20, scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 16  # 40960 tiles
+    assert plan(fake_tensors([1 << 18] * 20, scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 10  # 10240 tiles
+    assert plan(fake_tensors([1 << 19] * 16, scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 16  # 16384 tiles
     # 8256 tiles (the one-element tensor takes a whole 64-tile record): the
     # first share (1032 tiles) needs two tensors, and the last piece keeps
     # the one-element tensor instead of running it alone
-    assert plan(fake_tensors([1 << 19] * 8 + [1], scaled=True), p="f16_scaled")["pieces"] == 7
+    assert plan(fake_tensors([1 << 19] * 8 + [1], scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 7
     # a piece never holds only small tensors: nine one-element tensors and a
     # 4M one (8264 tiles) run in one piece, which is all of the big tensor
-    assert plan(fake_tensors([1] * 9 + [1 << 22], scaled=True), p="f16_scaled")["pieces"] == 1
+    assert plan(fake_tensors([1] * 9 + [1 << 22], scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 1
     # 7 x 1024 tiles then 16384: two pieces of three tensors, then the rest
-    assert plan(fake_tensors([1 << 19] * 7 + [1 << 23], scaled=True), p="f16_scaled")["pieces"] == 3
-    assert plan(fake_tensors([1 << 21, 1], scaled=True), p="f16_scaled")["pieces"] == 1  # 4224 tiles
-    assert plan(fake_tensors([1 << 23], scaled=True), p="f16_scaled")["pieces"] == 1  # one tensor
+    assert plan(fake_tensors([1 << 19] * 7 + [1 << 23], scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 3
+    assert plan(fake_tensors([1 << 21, 1], scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 1  # 4224 tiles
+    assert plan(fake_tensors([1 << 23], scaled=True), p="f16_scaled", scaled_passes=2)["pieces"] == 1  # one tensor
     assert plan(fake_tensors(big), p="f32")["pieces"] == 1  # not scaled
 
 
@@ -451,3 +451,33 @@ def test_lists_beyond_one_dispatch_are_split():
     assert plan([t], dispatch_tiles=1 << 30)["dispatch_tiles"] == limit
     st = plan([t], dispatch_tiles=1000)
     assert (st["dispatch_tiles"], st["dispatches"]) == (1000, 5)
+
+
+def test_scaled_plans_choose_one_or_two_passes():
+    """Scaled state runs in two passes unless one is asked for; one pass
+    needs every tensor within 512 one-pass tiles of 4096 elements (2M
+    elements), taking 4-element accesses, and records of whole one-pass
+    tiles (the automatic chunk is at least 4096 then).  One pass has no
+    pieces and one persistent dispatch."""
+    small = fake_tensors([1 << 20, 700001, 3, 1 << 21], scaled=True)
+    st = plan(small, p="f16_scaled")
+    assert st["scaled_passes"] == 2
+    assert plan(small, p="f16_scaled", scaled_passes=2)["scaled_passes"] == 2
+    st = plan(small, p="f16_scaled", scaled_passes=1)
+    assert (st["scaled_passes"], st["pieces"], st["dispatches"]) == (1, 1, 1) and st["chunk_elems"] % 4096 == 0
+    assert plan(small, p="f16_scaled", scaled_passes=1, dispatch_tiles=64)["dispatches"] == 1
+    # a tensor beyond 2M elements, records finer than a one-pass tile, or a
+    # tensor on the element path (buffers not alignable at one element)
+    big = fake_tensors([1 << 20, (1 << 21) + 1], scaled=True)
+    odd = fake_tensors([1 << 20, 4097], scaled=True, offsets={1: {"m": 2}})
+    assert status_of(big, p="bf16_scaled", scaled_passes=1) == A.ADAM_EINVAL
+    assert status_of(small, p="f16_scaled", chunk_elems=2048, scaled_passes=1) == A.ADAM_EINVAL
+    assert status_of(odd, p="f16_scaled", scaled_passes=1) == A.ADAM_EINVAL
+    assert plan(odd, p="f16_scaled")["scaled_passes"] == 2
+    # the fields belong to scaled state and take these values only
+    assert status_of(fake_tensors([8]), scaled_passes=1) == A.ADAM_EINVAL
+    assert status_of(fake_tensors([8]), scaled_wait_us=5) == A.ADAM_EINVAL
+    assert status_of(small, p="f16_scaled", scaled_passes=3) == A.ADAM_EINVAL
+    assert status_of(small, p="f16_scaled", scaled_wait_us=-2) == A.ADAM_EINVAL
+    assert plan(small, p="f16_scaled", scaled_passes=1, scaled_wait_us=-1)["scaled_passes"] == 1
+    assert plan(fake_tensors([8]))["scaled_passes"] == 0

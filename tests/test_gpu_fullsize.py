@@ -215,10 +215,10 @@ def test_zero_shard_fp16_capturable_with_noop(torch):
     run_sampled(torch, "zero1e9_f16", 10, capturable=True, noop_every=5, seed=8)
 
 
-@pytest.mark.parametrize("capturable", [False, True])
-def test_scaled_state_zero_shard(torch, capturable):
+@pytest.mark.parametrize("capturable,passes", [(False, 1), (True, 1), (False, 2), (True, 2)])
+def test_scaled_state_zero_shard(torch, capturable, passes):
     """1e9 elements of scaled fp16 p, m, v in 2048 buckets, bf16 gradients,
-    bf16 param-sync copy, five steps from a fresh state (capturable: six
+    bf16 param-sync copy, in one pass and in two, five steps from a fresh state (capturable: six
     calls from device scalars, the fourth a noop).  The new scales of a
     tensor depend on all of it, so the samples are whole tensors (first,
     middle, last and five random buckets): their initial state goes to the
@@ -244,7 +244,8 @@ def test_scaled_state_zero_shard(torch, capturable):
         refs.append(oracle.OracleTensor(host["p"], host["m"], host["v"], host["g"],
                                         np.zeros(hi - lo, np.uint16), None,
                                         dev_to_np(scales[k]).astype(np.float32)))
-    tl = A.adam_tl_build(tensors, A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=out_type(w)))
+    tl = A.adam_tl_build(tensors, A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=out_type(w), scaled_passes=passes))
+    assert tl.info()["scaled_passes"] == passes
     hp = A.AdamHParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
     hr = oracle.HParams(w.beta1, w.beta2, w.eps, w.weight_decay, w.mode, 1)
     step, ref_step = A.HostStep(0), [0]

@@ -275,9 +275,11 @@ def test_whole_capturable_step_in_one_graph(torch, orc, g_dtype, p_kind, p_out, 
         norm, new_s, found = orc.clip_grad_scale(sumsq, 1.0, max_norm)
         assert np.float32(d_norm.item()) == norm or (np.isnan(norm) and np.isnan(d_norm.item()))
         assert np.float32(d_scale.item()) == new_s
-        # the same from the oracle's own exact sum
-        assert_clip_from_exact_sum(orc, want, sumsq, 1.0, max_norm, d_norm.item(), d_scale.item(),
-                                   int(d_noop.item()))
+        # the same from the oracle's own exact sum (on the replay with the
+        # injected inf, the oracle's copy of the gradients does not hold it)
+        if k != 2:
+            assert_clip_from_exact_sum(orc, want, sumsq, 1.0, max_norm, d_norm.item(), d_scale.item(),
+                                       int(d_noop.item()))
         orc.group_step(r1, hr1, 1.6e-3, st1, float(new_s), noop=found)
         orc.group_step(r2, hr2, 1.6e-3, st2, float(new_s), noop=found)
     assert int(s1.item()) == st1[0] == 4 and int(s2.item()) == st2[0] == 4

@@ -1,6 +1,6 @@
-"""Scaled state on a list large enough (>= 4M elements in two or more
-tensors) that the step runs in pieces of consecutive tensors pipelined over
-two streams: the results must still equal the oracle's bit for bit (values,
+"""Two-pass scaled state on a list large enough (>= 4M elements in two or
+more tensors) that the step runs in pieces of consecutive tensors pipelined
+over two streams: the results must still equal the oracle's bit for bit (values,
 scales and the param-sync copy), through the host step, the capturable step
 with a noop step, and a HIP graph of one capturable step replayed."""
 import numpy as np
@@ -33,7 +33,8 @@ def test_pipelined_scaled_steps_match_the_oracle(torch, p_kind, g_dtype, p_out):
     assert sum(SIZES) >= 1 << 22
     ref = copies(host)
     dev = DeviceSet(host)
-    tl = A.adam_tl_build(dev.tensors, desc_for(host))
+    tl = A.adam_tl_build(dev.tensors, desc_for(host, scaled_passes=2))
+    assert tl.info()["scaled_passes"] == 2 and tl.info()["pieces"] > 1
     hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
     orc = oracle.default()
     ot, st = oracle_tensors(ref), [0]
@@ -94,7 +95,7 @@ def test_pieces_cover_every_tensor_once(torch, sizes, pieces, dispatch_tiles, di
     assert sum(sizes) >= 1 << 22
     ref = copies(host)
     dev = DeviceSet(host)
-    tl = A.adam_tl_build(dev.tensors, desc_for(host, dispatch_tiles=dispatch_tiles))
+    tl = A.adam_tl_build(dev.tensors, desc_for(host, dispatch_tiles=dispatch_tiles, scaled_passes=2))
     assert (tl.info()["pieces"], tl.info()["dispatches"]) == (pieces, dispatches)
     hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
     orc = oracle.default()
