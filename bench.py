@@ -131,9 +131,16 @@ PROFILE_COMMANDS = {
 
 # the kernels that stream the elements: the update, and the scaled-state
 # maxima and store passes
-MAIN_KERNELS = ("adam_update", "adam_scaled_maxima", "adam_scaled_pass")
-# the kernels of one scaled-state step, once per piece
+MAIN_KERNELS = ("adam_update", "adam_scaled_maxima", "adam_scaled_pass", "adam_scaled_one")
+# the kernels of one scaled-state step, once per piece (one pass: the
+# persistent kernel, its follow-up pass and the per-tensor scales)
 SCALED_STEP_KERNELS = ("adam_scaled_maxima", "adam_scaled_fold", "adam_scaled_pass", "adam_scaled_finish")
+ONE_PASS_STEP_KERNELS = ("adam_scaled_one",)  # adam_scaled_one, _one_redo, _one_finish
+
+
+def is_main(name: str) -> bool:
+    """A kernel that streams the elements (not the per-tensor scales one)."""
+    return name.startswith(MAIN_KERNELS) and not name.startswith("adam_scaled_one_finish")
 
 CU_NUM = 256
 XCD_NUM = 8
@@ -150,16 +157,17 @@ def _plan_pieces(w) -> int:
                     p_out=base + (8 * i + 5) * stride if w.p_out else None, numel=n)
                for i, n in enumerate(w.sizes)]
     p_out = ("bf16" if w.p_out is True else w.p_out) or None
-    return A.adam_tl_plan(tensors, A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out))["pieces"]
+    return A.adam_tl_plan(tensors, A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out,
+                                               scaled_passes=w.scaled_passes))["pieces"]
 
 
 def _main_dispatches(names_grids, scaled):
     """The (kernel, dispatch) keys of the step's main kernels: for scaled
     state every piece's (each has its own grid), else the largest grid."""
     if scaled:
-        return {k for k in names_grids if k[0].startswith(MAIN_KERNELS)}
-    big = max(g for (n, _), g in names_grids.items() if n.startswith(MAIN_KERNELS))
-    return {k for k, g in names_grids.items() if g == big and k[0].startswith(MAIN_KERNELS)}
+        return {k for k in names_grids if is_main(k[0])}
+    big = max(g for (n, _), g in names_grids.items() if is_main(n))
+    return {k for k, g in names_grids.items() if g == big and is_main(k[0])}
 
 
 def summarize_valu(w, valu_dir: str) -> None:
@@ -322,10 +330,10 @@ def summarize_dram(w, req_dir: str, stall_dir: str) -> None:
             key = (_short(r["Kernel_Name"]), r["Dispatch_Id"])
             vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
             grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
-        big = max(g for (n, _), g in grids.items() if n.startswith(MAIN_KERNELS))
+        big = max(g for (n, _), g in grids.items() if is_main(n))
         per = {}
         for key, c in vals.items():
-            if grids[key] == big and key[0].startswith(MAIN_KERNELS):
+            if grids[key] == big and is_main(key[0]):
                 per.setdefault(key[0], []).append(c)
         return per
 
@@ -369,7 +377,8 @@ def _short(name: str) -> str:
 
     n = name.replace("(anonymous namespace)::", "")
     for kernel, cfg_name in (("adam_update", "Config<"), ("adam_scaled_maxima", "ScaledConfig<"),
-                             ("adam_scaled_pass", "ScaledConfig<")):
+                             ("adam_scaled_pass", "ScaledConfig<"), ("adam_scaled_one_redo", "ScaledConfig<"),
+                             ("adam_scaled_one", "ScaledConfig<")):
         if kernel in n and cfg_name in n:
             i = n.index(cfg_name) + len(cfg_name)
             return f"{kernel}<{n[i:n.index('>', i)]}>"
@@ -432,7 +441,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
     prefix = "adam_scaled" if scaled else "adam_update"
 
     def main_kernel(name):
-        return name.startswith(MAIN_KERNELS)
+        return is_main(name)
 
     # kernel trace: all kernels (stats), then the update kernel per dispatch
     rows = list(csv.DictReader(open(os.path.join(trace_dir, "run_kernel_stats.csv"))))
@@ -465,11 +474,12 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
         # a scaled step is 4 kernels per piece, the pieces pipelined over two
         # streams; its time is its first dispatch's start to its last's end
         disp = []
+        step_kernels = ONE_PASS_STEP_KERNELS if w.scaled_passes == 1 else SCALED_STEP_KERNELS
         for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv"))):
-            if _short(r["Kernel_Name"]).startswith(SCALED_STEP_KERNELS):
+            if _short(r["Kernel_Name"]).startswith(step_kernels):
                 disp.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
         disp.sort()
-        k = 4 * pieces
+        k = 3 if w.scaled_passes == 1 else 4 * pieces
         spans = [(max(e for _, e in disp[i:i + k]) - disp[i][0]) / 1e6 for i in range(0, len(disp) - k + 1, k)]
     lines += ["", ("scaled-state passes" if scaled else "update kernel") +
               (f" per dispatch ({pieces} piece(s) per step, each its own grid):" if scaled else
@@ -581,7 +591,7 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
               f"  (scaling the drawn fp32 temporaries: the gradient's, and the param's for scaled fp16 state);",
               f"  counters summed over its dispatches give",
               f"  FETCH factor {f_factor:.4f}, WRITE factor {w_factor:.4f}",
-              f"{'both passes per step' if scaled else 'update kernel per launch'}: "
+              f"{('one-pass kernels per step' if w.scaled_passes == 1 else 'both passes per step') if scaled else 'update kernel per launch'}: "
               f"read {fetch_kib * f_factor * 1024 / 1e9:.3f} GB, "
               f"write {write_kib * w_factor * 1024 / 1e9:.3f} GB, total {traffic / 1e9:.3f} GB",
               f"algorithmic bytes per launch: {algo / 1e9:.3f} GB ({n0:,} elements x {w.bytes_per_elem} B); "
@@ -590,7 +600,10 @@ def summarize_profiles(w, trace_dir: str, fetch_dir: str, write_dir: str, trace_
         lines.append(f"two-buffer state (the runs' last {len(fetch[tb_key[0]])} update launches): "
                      f"{tb_traffic / 1e9:.3f} GB per launch; measured / algorithmic = {tb_traffic / algo:.4f}")
     lines.append(f"kernel source sha256[:16] = {source_hash()}")
-    if scaled:
+    if scaled and w.scaled_passes == 1:
+        lines.append("one pass: each of p, m, v and g is read once (a tile is stored from registers "
+                     "and local memory once its tensor's scales are published)")
+    elif scaled:
         lines.append("scaled state reads p, m, v and g twice (the maxima pass, then the store pass "
                      "recomputes the update): the second read is counted whether the Infinity Cache "
                      "or HBM serves it")
@@ -733,7 +746,8 @@ def build_run(w, args, A, torch):
             scale_bufs.append(sc)
             for i, t in enumerate(tensors):
                 t["scales"] = sc[i]
-        desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out, chunk_elems=args.chunk_elems)
+        desc = A.make_desc(g=w.g_dtype, p=w.p_kind, p_out=p_out, chunk_elems=args.chunk_elems,
+                           scaled_passes=w.scaled_passes)
         tl = A.adam_tl_build(tensors, desc)
         hp = A.AdamHParams(w.beta1, w.beta2, w.eps, wd, w.mode, 1)
         # each group keeps its own counter, host and device
@@ -894,7 +908,7 @@ def interleaved_rounds(r, lib, step_once, k: int, rounds: int) -> dict:
 
 # The configurations timed beside the main workload, each with the step call
 # its configuration names ("capturable": device scalars, noop flag 0).
-EXTRA_WORKLOADS = ("shard30b", "zero1e9", "rem5e8", "state16_1e9", "scaled1e9")
+EXTRA_WORKLOADS = ("shard30b", "zero1e9", "rem5e8", "state16_1e9", "scaled1e9", "scaled1e9_one")
 CAPTURABLE_WORKLOADS = ("zero1e9",)
 TARGET_FRAC = 0.85
 
@@ -1082,7 +1096,9 @@ def main() -> int:
                         f"{'AdamW' if w.mode else 'L2'}, lr {w.lr}, betas ({w.beta1}, {w.beta2}), "
                         f"eps {w.eps}, wd {w.weight_decay}",
             "path": f"{step_fn.__name__} (non-capturable), "
-                    + ("four launches per group per step (maxima pass, per-tensor fold, store pass, scales)"
+                    + (("one pass: a persistent kernel, a follow-up pass and the per-tensor scales"
+                        if w.scaled_passes == 1 else
+                        "four launches per piece (maxima pass, per-tensor fold, store pass, scales)")
                        if scaled else "one launch per group per step"),
             "bytes_per_elem": w.bytes_per_elem,
             "chunk_elems": info["chunk_elems"],
@@ -1095,7 +1111,9 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": (f"adam_scaled_maxima + fold + adam_scaled_pass + scales (the whole scaled step of the main group; "
+            "kernel": (f"adam_scaled_one + follow-up + scales (the whole one-pass scaled step; p {w.p_kind}, "
+                       f"g {w.g_dtype}, p_out {p_out or 'none'})" if scaled and w.scaled_passes == 1 else
+                       f"adam_scaled_maxima + fold + adam_scaled_pass + scales (the whole scaled step of the main group; "
                        f"p {w.p_kind}, g {w.g_dtype}, p_out {p_out or 'none'})" if scaled else
                        f"adam_update (p {w.p_kind}, g {w.g_dtype}, m/v {mv_desc}, p_out "
                        f"{p_out or 'none'}, {'AdamW' if w.mode else 'L2'}, non-capturable)"),

@@ -53,6 +53,7 @@ class Workload:
     grad_multiplier: float = 1.0           # loss scale folded into the grads
     seed: int = 0
     extra_groups: Tuple[Tuple[Tuple[int, ...], float], ...] = ()  # (sizes, wd)
+    scaled_passes: int = 0                 # scaled state: 1 = one pass, else two
 
     @property
     def numel(self) -> int:
@@ -174,6 +175,10 @@ def workloads() -> dict:
         "scaled1e9": Workload("scaled1e9", zero_bucket_sizes(), "bf16", "f16_scaled", "bf16",
                               lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
                               weight_decay=0.1, mode=1, seed=7),
+        # the same, stepped in one pass (each input read once)
+        "scaled1e9_one": Workload("scaled1e9_one", zero_bucket_sizes(), "bf16", "f16_scaled", "bf16",
+                                  lr=1.6e-3, beta1=0.9, beta2=0.95, eps=1e-8,
+                                  weight_decay=0.1, mode=1, seed=7, scaled_passes=1),
         # the ZeRO shard with the optimizer state in bf16 (p, m, v), bf16
         # gradients and a bf16 param-sync copy (apex's gradient and param-sync
         # dtypes default to the state dtype): 16 B/elem
