@@ -414,6 +414,20 @@ __device__ __forceinline__ T load_one(const void *base, int idx)
     return ((const ADAM_GLOBAL T *)(base))[idx];
 }
 
+// A scaled tensor's three scales (p, m, v), the same for every lane and
+// never written while a kernel that reads them runs: scalar loads through
+// the constant address space.  They count apart from the vector loads, so
+// waiting for them never waits for a vector load in flight (as a flat load,
+// counted by both counters, or a vector load issued after others would).
+#define ADAM_CONSTANT __attribute__((address_space(4)))
+__device__ __forceinline__ void load_scales(const void *aux, float *sc)
+{
+    const ADAM_CONSTANT float *s = (const ADAM_CONSTANT float *)aux;
+    sc[0] = s[0];
+    sc[1] = s[1];
+    sc[2] = s[2];
+}
+
 template <class T>
 __device__ __forceinline__ void store_one(void *base, int idx, T val)
 {
@@ -987,8 +1001,8 @@ __global__ __launch_bounds__(kMaxBlock) void adam_scaled_maxima(const WorkItem *
     const int tid = threadIdx.x;
     uint32_t mx[3] = {0u, 0u, 0u};
     if (start < w.n) {  // uniform across the wave
-        const float *scales = static_cast<const float *>(w.aux);
-        const float sc[3] = {scales[0], scales[1], scales[2]};
+        float sc[3];
+        load_scales(w.aux, sc);
         const int n = min(kTile, w.n - start);
         if (w.flags & kItemVector) {
             if (start == 0 && tid < w.head) scaled_single<S>(w, tid - w.head, c, sc, nullptr, mx);
@@ -1019,8 +1033,8 @@ __global__ __launch_bounds__(kBlock) void adam_scaled_pass(const WorkItem *__res
     Coeffs c;
     if (!step_coeffs(a, c)) return;
 
-    const float *scales = static_cast<const float *>(w.aux);
-    const float sc[3] = {scales[0], scales[1], scales[2]};
+    float sc[3];
+    load_scales(w.aux, sc);
     const uint32_t *f = folded + 6 * size_t(w.tensor) + 3;
     const float r[3] = {__uint_as_float(f[0]), __uint_as_float(f[1]), __uint_as_float(f[2])};
 
@@ -1085,34 +1099,36 @@ __global__ void adam_scaled_finish(float *const *__restrict__ scale_ptrs,
 
 // ---------------------------------------------------------------------------
 // Scaled state in one pass.  A workgroup (four waves) updates a 4096-element
-// tile exactly, writes its param-sync copy, publishes the tile's three
-// magnitude maxima and counts itself in as arrived for the tile's tensor;
-// the workgroup that arrives last for a tensor folds that tensor's tile
-// maxima, derives the reciprocal scales and publishes them; the tile is
-// stored once its tensor's scales are out.  The inputs are read once and the
-// update is computed once (the two-pass step reads them twice and computes
-// the update twice).  A tile whose bounded wait runs out is left to a
-// follow-up pass, which recomputes it from its untouched inputs; a kernel of
-// one lane per tensor then writes the new scales and clears the counts.
+// tile exactly into registers, publishes the tile's three magnitude maxima
+// and counts itself in as arrived for the tile's tensor; the workgroup that
+// arrives last for a tensor folds that tensor's tile maxima, derives the
+// reciprocal scales and publishes them; the tile (state and param-sync
+// copy) is stored once its tensor's scales are out.  The inputs are read
+// once and the update is computed once (the two-pass step reads them twice
+// and computes the update twice).  A tile whose bounded wait runs out is
+// left to a follow-up pass, which recomputes it from its untouched inputs; a
+// kernel of one lane per tensor then writes the new scales and clears the
+// counts and the published scales.
 //
 // Everything shared between workgroups (tile maxima, counts, reciprocal
-// scales, flags, the follow-up list) is read and written with relaxed
-// device-scope atomic operations, which go to the device-coherent level of
-// the memory hierarchy; a wait for the completion of a workgroup's stores
-// orders them before its count, and a waiter reads the scales only after it
-// has seen the flag that was stored after them.  No release or acquire fence
-// of device scope (which would write back or invalidate whole L2 caches) is
-// needed.
+// scales, the follow-up list) is read and written with relaxed device-scope
+// atomic operations, which go to the device-coherent level of the memory
+// hierarchy; a wait for the completion of a workgroup's stores orders them
+// before its count.  A reciprocal scale is published as one 64-bit word, a
+// tag bit above the float's bits, so a waiter that sees the tag has the
+// value from the same store: no separate flag, and one round trip reads all
+// three.  No release or acquire fence of device scope (which would write
+// back or invalidate whole L2 caches) is needed.
 //
-// Measured on MI355X (1e9 elements in 2048 tensors): 4.66 ms per step
-// against 4.01 for the two pipelined passes, and 3.28 for a copy of the
-// one-pass kernel without the exchange (inexact): each tile's arrival, fold
-// and wait are several dependent trips to device-coherent memory, some
-// microseconds each under full streaming load, which one workgroup's next
-// tile cannot cover at the three waves per SIMD its registers allow.  So
-// two passes are the default; one pass, which moves a third fewer bytes (16
-// per element instead of 24 with fp16 state and bf16 gradients), is there
-// for callers who want that.
+// Measured on MI355X (1e9 elements in 2048 tensors): 3.80 ms per step
+// against 3.97 for the two pipelined passes in the same process.  What it
+// took: each tile's exchange costs two round trips to device-coherent
+// memory (the wait for the maxima's stores, the count), the previous
+// tile's scales riding along with the first; and the waits the compiler
+// places on the vector memory counter, which drains in issue order, let
+// the next tile's loads and the previous tile's stores stay in flight
+// while a tile is computed (a first version waited for everything once per
+// tile and took 4.66 ms).
 // ---------------------------------------------------------------------------
 constexpr int kOneBlock = 256;                            // four waves
 constexpr int kOneGroups = 4;                             // lane groups per lane
@@ -1126,13 +1142,16 @@ struct OneArgs {
     const uint32_t *tiles;     // per tensor: [first, end) update tiles
     const uint32_t *arrivals;  // per tensor: its non-empty one-pass tiles
     uint32_t *count;           // per tensor: workgroups arrived in this step (0 between steps)
-    uint32_t *flag;            // per tensor: 1 once its reciprocal scales are published (0 between steps)
+    uint64_t *ready;           // per tensor: its three reciprocal scales, kPublished | bits once published
+                               // (0 between steps)
     uint32_t *tile_max;        // per one-pass tile: three magnitude maxima
     uint32_t *folded;          // per tensor: three magnitude maxima, three reciprocal scales (float bits)
     uint32_t *redo;            // [0]: tiles left to the follow-up pass, then their indices
     uint64_t wait_ticks;       // a workgroup's wait, in ticks of the device's real-time clock; 0: none
-    uint32_t wait_polls;       // and at most this many polls of the flag (each takes longer than 0.25 us)
+    uint32_t wait_polls;       // and at most this many polls of the scales (each takes longer than 0.25 us)
 };
+
+constexpr uint64_t kPublished = uint64_t(1) << 32;  // the tag of a published reciprocal scale
 
 __device__ __forceinline__ uint32_t shared_load(const uint32_t *p)
 {
@@ -1144,8 +1163,18 @@ __device__ __forceinline__ void shared_store(uint32_t *p, uint32_t x)
     __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ uint64_t shared_load64(const uint64_t *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void shared_store64(uint64_t *p, uint64_t x)
+{
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One element at index i of a record: the exact update of its unscaled
-// value, the param-sync copy stored; P, M, V the new fp32 values.
+// value; P, M, V the new fp32 values.
 template <class S>
 __device__ __forceinline__ void one_element(const WorkItem &w, int i, const Coeffs &c, const float *sc, float &P,
                                             float &M, float &V)
@@ -1155,15 +1184,17 @@ __device__ __forceinline__ void one_element(const WorkItem &w, int i, const Coef
     M = widen16<S::st>(load_one<uint16_t>(w.m, i)) * sc[1];
     V = widen16<S::st>(load_one<uint16_t>(w.v, i)) * sc[2];
     P = update_element<S::mode, true>(P, g, M, V, c);
-    if constexpr (S::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<S::ot>(P)));
 }
 
+// Stores it: the scaled state with the reciprocal scales r, the param-sync
+// copy of P.
 template <class S>
 __device__ __forceinline__ void one_store_element(const WorkItem &w, int i, const float *r, float P, float M, float V)
 {
     store_one<uint16_t>(w.p, i, uint16_t(narrow16<S::st>(P * r[0])));
     store_one<uint16_t>(w.m, i, uint16_t(narrow16<S::st>(M * r[1])));
     store_one<uint16_t>(w.v, i, uint16_t(narrow16<S::st>(V * r[2])));
+    if constexpr (S::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<S::ot>(P)));
 }
 
 // The lane's elements of a one-pass tile (start, n elements of record w).
@@ -1175,8 +1206,8 @@ struct OneSlots {
     float P[kOneSlots + 2], M[kOneSlots + 2], V[kOneSlots + 2];
 };
 
-// Computes the lane's elements (and stores their param-sync copy); folds
-// their magnitudes into mx when it is not null.
+// Computes the lane's elements; folds their magnitudes into mx when it is
+// not null.
 template <class S>
 __device__ __forceinline__ void one_compute(const WorkItem &w, int start, int n, const Coeffs &c, const float *sc,
                                             OneSlots &x, uint32_t *mx)
@@ -1217,12 +1248,6 @@ __device__ __forceinline__ void one_compute(const WorkItem &w, int start, int n,
                     P = update_element<S::mode, true>(P, g[j][e], M, V, c);
                     fold(P, M, V);
                 }
-                if constexpr (S::ot != kNone) {
-                    uint32_t o[kLane];
-#pragma unroll
-                    for (int e = 0; e < kLane; ++e) o[e] = narrow16<S::ot>(x.P[j * kLane + e]);
-                    store_u16x4(w.p_out, start / kLane + lg, o);
-                }
             }
         }
         if (tid < n - groups * kLane) {
@@ -1244,7 +1269,8 @@ __device__ __forceinline__ void one_compute(const WorkItem &w, int start, int n,
     }
 }
 
-// Stores the lane's elements with the reciprocal scales r.
+// Stores the lane's elements with the reciprocal scales r, and their
+// param-sync copy.
 template <class S>
 __device__ __forceinline__ void one_store(const WorkItem &w, int start, int n, const float *r, const OneSlots &x)
 {
@@ -1266,6 +1292,12 @@ __device__ __forceinline__ void one_store(const WorkItem &w, int start, int n, c
                 store_u16x4(w.p, gi, hp);
                 store_u16x4(w.m, gi, hm);
                 store_u16x4(w.v, gi, hv);
+                if constexpr (S::ot != kNone) {
+                    uint32_t o[kLane];
+#pragma unroll
+                    for (int e = 0; e < kLane; ++e) o[e] = narrow16<S::ot>(x.P[j * kLane + e]);
+                    store_u16x4(w.p_out, gi, o);
+                }
             }
         }
         if (tid < n - groups * kLane)
@@ -1307,25 +1339,50 @@ struct OneRaw {
     typename std::conditional<GT == kF32, f32x4, u32x2>::type g[kOneGroups];
 };
 
-template <int GT>
-__device__ __forceinline__ void one_load_raw(const WorkItem &w, int start, int n, OneRaw<GT> &raw)
+// Whether a one-pass tile is whole: 4096 elements in lane groups, no head.
+__device__ __forceinline__ bool one_whole(const WorkItem &w, int start, int n)
 {
-    const int groups = n / kLane;
+    return n == kOneTile && (start != 0 || w.head == 0);
+}
+
+// Issues the loads of `groups` lane groups of a tile (0 for no tile): always
+// 16 per lane, lanes past the tile's groups reading `spare` (any 16 readable
+// bytes).  The vector memory counter is waited on in issue order, so a fixed
+// count lets the compiler wait for exactly one tile's loads while the next
+// tile's loads and the previous tile's stores stay in flight.
+template <int GT>
+__device__ __forceinline__ void one_load_raw(const WorkItem &w, int start, int groups, const void *spare,
+                                             OneRaw<GT> &raw)
+{
+    using G = std::remove_reference_t<decltype(raw.g[0])>;
+    const int tid = threadIdx.x;
+    const int g0 = start / kLane;
+    if (groups == kOneGroups * kOneBlock) {
 #pragma unroll
-    for (int j = 0; j < kOneGroups; ++j) {
-        const int lg = j * kOneBlock + int(threadIdx.x);
-        if (lg < groups) {
-            const int gi = start / kLane + lg;
+        for (int j = 0; j < kOneGroups; ++j) {
+            const int gi = g0 + j * kOneBlock + tid;
             raw.p[j] = load_stream<u32x2>(w.p, gi);
             raw.m[j] = load_stream<u32x2>(w.m, gi);
             raw.v[j] = load_stream<u32x2>(w.v, gi);
-            raw.g[j] = load_stream<std::remove_reference_t<decltype(raw.g[0])>>(w.g, gi);
+            raw.g[j] = load_stream<G>(w.g, gi);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kOneGroups; ++j) {
+            const int lg = j * kOneBlock + tid;
+            const bool in = lg < groups;
+            const int gi = in ? g0 + lg : 0;
+            raw.p[j] = load_stream<u32x2>(in ? w.p : spare, gi);
+            raw.m[j] = load_stream<u32x2>(in ? w.m : spare, gi);
+            raw.v[j] = load_stream<u32x2>(in ? w.v : spare, gi);
+            raw.g[j] = load_stream<G>(in ? w.g : spare, gi);
         }
     }
 }
 
-// one_compute for a 4-element tile whose lane groups are already loaded.
-template <class S>
+// one_compute for a 4-element tile whose lane groups are already loaded;
+// WHOLE: a whole tile (no condition, no element path, no memory access).
+template <class S, bool WHOLE>
 __device__ __forceinline__ void one_compute_raw(const WorkItem &w, int start, int n, const Coeffs &c, const float *sc,
                                                 const OneRaw<S::gt> &raw, OneSlots &x, uint32_t *mx)
 {
@@ -1338,7 +1395,7 @@ __device__ __forceinline__ void one_compute_raw(const WorkItem &w, int start, in
     };
 #pragma unroll
     for (int j = 0; j < kOneGroups; ++j) {
-        if (j * kOneBlock + tid < groups) {
+        if (WHOLE || j * kOneBlock + tid < groups) {
             const uint32_t hp[kLane] = {raw.p[j].x & 0xFFFFu, raw.p[j].x >> 16, raw.p[j].y & 0xFFFFu, raw.p[j].y >> 16};
             const uint32_t hm[kLane] = {raw.m[j].x & 0xFFFFu, raw.m[j].x >> 16, raw.m[j].y & 0xFFFFu, raw.m[j].y >> 16};
             const uint32_t hv[kLane] = {raw.v[j].x & 0xFFFFu, raw.v[j].x >> 16, raw.v[j].y & 0xFFFFu, raw.v[j].y >> 16};
@@ -1363,39 +1420,37 @@ __device__ __forceinline__ void one_compute_raw(const WorkItem &w, int start, in
                 P = update_element<S::mode, true>(P, g[e], M, V, c);
                 fold(P, M, V);
             }
-            if constexpr (S::ot != kNone) {
-                uint32_t o[kLane];
-#pragma unroll
-                for (int e = 0; e < kLane; ++e) o[e] = narrow16<S::ot>(x.P[j * kLane + e]);
-                store_u16x4(w.p_out, start / kLane + j * kOneBlock + tid, o);
-            }
         }
     }
-    if (tid < n - groups * kLane) {
-        one_element<S>(w, start + groups * kLane + tid, c, sc, x.P[kOneSlots], x.M[kOneSlots], x.V[kOneSlots]);
-        fold(x.P[kOneSlots], x.M[kOneSlots], x.V[kOneSlots]);
-    }
-    if (start == 0 && tid < w.head) {
-        one_element<S>(w, tid - w.head, c, sc, x.P[kOneSlots + 1], x.M[kOneSlots + 1], x.V[kOneSlots + 1]);
-        fold(x.P[kOneSlots + 1], x.M[kOneSlots + 1], x.V[kOneSlots + 1]);
+    if constexpr (!WHOLE) {
+        if (tid < n - groups * kLane) {
+            one_element<S>(w, start + groups * kLane + tid, c, sc, x.P[kOneSlots], x.M[kOneSlots], x.V[kOneSlots]);
+            fold(x.P[kOneSlots], x.M[kOneSlots], x.V[kOneSlots]);
+        }
+        if (start == 0 && tid < w.head) {
+            one_element<S>(w, tid - w.head, c, sc, x.P[kOneSlots + 1], x.M[kOneSlots + 1], x.V[kOneSlots + 1]);
+            fold(x.P[kOneSlots + 1], x.M[kOneSlots + 1], x.V[kOneSlots + 1]);
+        }
     }
 }
 
 // The one-pass step, persistent: workgroup j takes the tiles at positions
 // j, j + G, j + 2G, ... (G = the grid; position -> tile in the update's XCD
-// order), in that order.  For each tile it loads the next tile's lane groups
-// first, computes the tile into registers (storing its param-sync copy),
-// arrives for the tile's tensor (folding and publishing the tensor's scales
-// if it is the last), then waits for the previous tile's tensor and stores
-// the previous tile from local memory, where it then puts this tile.  The
-// wait for a tensor thus overlaps the next tile's loads and arithmetic.  A
-// workgroup waits for the tensor of its previous tile only after arriving
-// for its current one, so no wait depends on a tile of the same workgroup
-// unless a tensor spans more than 2G positions; the handle keeps tensors
-// below that, and the bounded wait covers the rest.  Every tensor of a
-// one-pass list takes 4-element accesses: a list with a tensor on the
-// element path (buffers that cannot all be aligned at one element) takes
-// two passes, which keeps this kernel at three waves per SIMD.
+// order), in that order.  For each tile it issues the next tile's loads,
+// computes the tile into registers, arrives for the tile's tensor (folding
+// and publishing the tensor's scales if it is the last), then stores the
+// previous tile from local memory once its tensor's scales are out, and
+// puts this tile there.  The wait for a tensor thus has the next tile's
+// loads and arithmetic to cover it, and its scales are read in the same
+// round trip as the arrival.  Publishing never waits for anything but
+// stores already issued, and a workgroup waits for the tensor of its
+// previous tile only after arriving for its current one, so no wait depends
+// on a tile of the same workgroup unless a tensor spans more than 2G
+// positions; the handle keeps tensors below that, and the bounded wait
+// covers the rest.  Every tensor of a one-pass list takes 4-element
+// accesses: a list with a tensor on the element path (buffers that cannot
+// all be aligned at one element) takes two passes, which keeps this kernel
+// at three waves per SIMD.
 template <class S>
 __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__restrict__ items, uint32_t shift,
                                                               uint32_t total, StepArgs a, OneArgs f)
@@ -1404,39 +1459,53 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
     if (!step_coeffs(a, c)) return;  // a noop step changes nothing
     __shared__ float keep[3][kOneSlots][kOneBlock];  // the previous tile's new p, m, v (4-element slots)
     __shared__ uint32_t last, ready;
+    __shared__ uint64_t qs[3];  // what lane 0 of wave 0 read of the previous tile's tensor's scales
     __shared__ float rs[3];
     const int tid = threadIdx.x;
     const uint32_t mask = (1u << shift) - 1u;
     auto tile_at = [&](uint32_t pos) { return tile_of_block<kOneRun>(pos, total); };
+    auto published = [](const uint64_t *q) { return (q[0] & q[1] & q[2] & kPublished) != 0u; };
 
     uint32_t pos = blockIdx.x;
-    OneRaw<S::gt> raw;
+    OneRaw<S::gt> raw[2];  // the current and the next tile's lane groups, alternating
     {
         const uint32_t t = tile_at(pos);
         const WorkItem w = items[t >> shift];
         const int start = int(t & mask) * kOneTile;
-        if (start < w.n) one_load_raw<S::gt>(w, start, min(kOneTile, w.n - start), raw);
+        one_load_raw<S::gt>(w, start, start < w.n ? min(kOneTile, w.n - start) / kLane : 0, items, raw[0]);
+        __builtin_amdgcn_s_waitcnt(0);  // enter the loop with nothing in flight
     }
-    bool have_prev = false;
+    bool have_prev = false, whole_prev = false;
     uint32_t t_prev = 0;
     float sp[2] = {0.0f, 0.0f}, sm[2] = {0.0f, 0.0f}, sv[2] = {0.0f, 0.0f};  // the previous tile's tail and head
 
-    // waits for the previous tile's tensor and stores that tile (all lanes)
-    auto finish_prev = [&]() {
-        const WorkItem w = items[t_prev >> shift];
-        const uint32_t k = uint32_t(w.tensor);
+    // lane 0 of wave 0: the previous tile's tensor's published words
+    auto look = [&](uint64_t *q) {
+        const uint64_t *rk = f.ready + 3 * size_t(items[t_prev >> shift].tensor);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) q[j] = shared_load64(rk + j);
+    };
+
+    // waits (lane 0 of wave 0) until the previous tile's tensor's scales are
+    // out, qs being what it last read of them, else leaves the tile to the
+    // follow-up pass; whether they are out, for every lane
+    auto wait_prev = [&]() {
         if (tid == 0) {
-            uint32_t seen = 0u;
-            if (f.wait_ticks != 0) {
+            uint64_t q[3] = {qs[0], qs[1], qs[2]};
+            bool seen = f.wait_ticks != 0 && published(q);
+            if (f.wait_ticks != 0 && !seen) {
                 const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-                for (uint32_t polls = 0; (seen = shared_load(f.flag + k)) == 0u && polls < f.wait_polls &&
+                for (uint32_t polls = 0; !seen && polls < f.wait_polls &&
                                          __builtin_amdgcn_s_memrealtime() - t0 < f.wait_ticks;
-                     ++polls)
+                     ++polls) {
                     __builtin_amdgcn_s_sleep(16);
+                    look(q);
+                    seen = published(q);
+                }
             }
             if (seen) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) rs[j] = __uint_as_float(shared_load(f.folded + 6 * size_t(k) + 3 + j));
+                for (int j = 0; j < 3; ++j) rs[j] = __uint_as_float(uint32_t(q[j]));
             } else {
                 // leave the tile to the follow-up pass (its inputs are untouched)
                 const uint32_t slot = __hip_atomic_fetch_add(f.redo, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1445,96 +1514,151 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
             ready = seen ? 1u : 0u;
         }
         __syncthreads();
-        if (!ready) return;
-        // the slots stream from local memory, a lane group at a time
-        const int start = int(t_prev & mask) * kOneTile;
-        const int n = min(kOneTile, w.n - start);
-        const float r[3] = {rs[0], rs[1], rs[2]};
-        {
-            const int groups = n / kLane;
+        return ready != 0u;
+    };
+
+    // stores the previous tile from local memory: its lane groups (all of
+    // them for a whole tile) ...
+    auto store_groups = [&](const WorkItem &w, int start, int groups, bool whole, const float *r) {
 #pragma unroll
-            for (int j = 0; j < kOneGroups; ++j) {
-                const int lg = j * kOneBlock + tid;
-                if (lg < groups) {
-                    uint32_t hp[kLane], hm[kLane], hv[kLane];
+        for (int j = 0; j < kOneGroups; ++j) {
+            const int lg = j * kOneBlock + tid;
+            if (whole || lg < groups) {
+                uint32_t hp[kLane], hm[kLane], hv[kLane];
+                float P[kLane];
 #pragma unroll
-                    for (int e = 0; e < kLane; ++e) {
-                        hp[e] = narrow16<S::st>(keep[0][j * kLane + e][tid] * r[0]);
-                        hm[e] = narrow16<S::st>(keep[1][j * kLane + e][tid] * r[1]);
-                        hv[e] = narrow16<S::st>(keep[2][j * kLane + e][tid] * r[2]);
-                    }
-                    const int gi = start / kLane + lg;
-                    store_u16x4(w.p, gi, hp);
-                    store_u16x4(w.m, gi, hm);
-                    store_u16x4(w.v, gi, hv);
+                for (int e = 0; e < kLane; ++e) {
+                    P[e] = keep[0][j * kLane + e][tid];
+                    hp[e] = narrow16<S::st>(P[e] * r[0]);
+                    hm[e] = narrow16<S::st>(keep[1][j * kLane + e][tid] * r[1]);
+                    hv[e] = narrow16<S::st>(keep[2][j * kLane + e][tid] * r[2]);
+                }
+                const int gi = start / kLane + lg;
+                store_u16x4(w.p, gi, hp);
+                store_u16x4(w.m, gi, hm);
+                store_u16x4(w.v, gi, hv);
+                if constexpr (S::ot != kNone) {
+                    uint32_t o[kLane];
+#pragma unroll
+                    for (int e = 0; e < kLane; ++e) o[e] = narrow16<S::ot>(P[e]);
+                    store_u16x4(w.p_out, gi, o);
                 }
             }
+        }
+    };
+
+    // ... and, for a tile that is not whole, its element path
+    auto store_prev = [&](bool whole) {
+        const WorkItem w = items[t_prev >> shift];
+        const int start = int(t_prev & mask) * kOneTile;
+        const int n = min(kOneTile, w.n - start);
+        const int groups = n / kLane;
+        const float r[3] = {rs[0], rs[1], rs[2]};
+        if (whole) {
+            store_groups(w, start, groups, true, r);
+        } else {
+            store_groups(w, start, groups, false, r);
             if (tid < n - groups * kLane) one_store_element<S>(w, start + groups * kLane + tid, r, sp[0], sm[0], sv[0]);
             if (start == 0 && tid < w.head) one_store_element<S>(w, tid - w.head, r, sp[1], sm[1], sv[1]);
         }
     };
 
-    // counts this workgroup in for tile t of tensor k with maxima mx (lane 0
-    // of wave 0); the tensor's last workgroup folds its maxima and publishes
-    // the reciprocal scales (all lanes)
-    auto arrive = [&](uint32_t t, uint32_t k, uint32_t *mx) {
-        if (tid == 0) {
-            // publish the tile's maxima, wait until they are stored, arrive
+    // the last workgroup of tensor k: fold the maxima of its non-empty
+    // one-pass tiles, publish the reciprocal scales (all lanes)
+    auto fold = [&](uint32_t k) {
+        const uint32_t lo = f.tiles[2 * k] / kOneSub, hi = f.tiles[2 * k + 1] / kOneSub;
+        uint32_t m[3] = {0u, 0u, 0u};
+        for (uint32_t u = lo + tid; u < hi; u += kOneBlock) {
+            const bool live_u = int(u & mask) * kOneTile < items[u >> shift].n;
+            uint32_t x[3];
 #pragma unroll
-            for (int j = 0; j < 3; ++j) shared_store(f.tile_max + 3 * size_t(t) + j, mx[j]);
-            __builtin_amdgcn_s_waitcnt(0);
-            const uint32_t before = __hip_atomic_fetch_add(f.count + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = before + 1u == f.arrivals[k] ? 1u : 0u;
-        }
-        __syncthreads();
-        if (last) {
-            // every tile of the tensor has published: fold the maxima of its
-            // non-empty one-pass tiles, publish the reciprocal scales
-            const uint32_t lo = f.tiles[2 * k] / kOneSub, hi = f.tiles[2 * k + 1] / kOneSub;
-            uint32_t m[3] = {0u, 0u, 0u};
-            for (uint32_t u = lo + tid; u < hi; u += kOneBlock) {
-                if (int(u & mask) * kOneTile >= items[u >> shift].n) continue;
+            for (int j = 0; j < 3; ++j) x[j] = shared_load(f.tile_max + 3 * size_t(u) + j);
+            if (live_u) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) m[j] = max(m[j], shared_load(f.tile_max + 3 * size_t(u) + j));
+                for (int j = 0; j < 3; ++j) m[j] = max(m[j], x[j]);
             }
-            one_block_max(m);
-            if (tid == 0) {
+        }
+        one_block_max(m);
+        if (tid == 0) {
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    shared_store(f.folded + 6 * size_t(k) + j, m[j]);
-                    shared_store(f.folded + 6 * size_t(k) + 3 + j, __float_as_uint(rscale_of<S::st>(m[j])));
-                }
-                __builtin_amdgcn_s_waitcnt(0);
-                shared_store(f.flag + k, 1u);
+            for (int j = 0; j < 3; ++j) {
+                const uint32_t rbits = __float_as_uint(rscale_of<S::st>(m[j]));
+                shared_store(f.folded + 6 * size_t(k) + j, m[j]);
+                shared_store(f.folded + 6 * size_t(k) + 3 + j, rbits);
+                shared_store64(f.ready + 3 * size_t(k) + j, kPublished | rbits);
             }
         }
     };
 
-    for (; pos < total; pos += gridDim.x) {
+    // one tile: the next one's loads into nxt, this one computed from cur
+    auto body = [&](const OneRaw<S::gt> &cur, OneRaw<S::gt> &nxt) {
         const uint32_t t = tile_at(pos);
         const WorkItem w = items[t >> shift];
         const int start = int(t & mask) * kOneTile;
         const bool live = start < w.n;
         const int n = live ? min(kOneTile, w.n - start) : 0;
-        // the next tile's lane groups, in flight while this one is computed
-        OneRaw<S::gt> next;
-        if (pos + gridDim.x < total) {
-            const uint32_t t2 = tile_at(pos + gridDim.x);
+        {
+            // the next tile's lane groups, in flight while this one is computed
+            const bool more = pos + gridDim.x < total;
+            const uint32_t t2 = more ? tile_at(pos + gridDim.x) : t;
             const WorkItem w2 = items[t2 >> shift];
             const int start2 = int(t2 & mask) * kOneTile;
-            if (start2 < w2.n) one_load_raw<S::gt>(w2, start2, min(kOneTile, w2.n - start2), next);
+            const int groups2 = more && start2 < w2.n ? min(kOneTile, w2.n - start2) / kLane : 0;
+            one_load_raw<S::gt>(w2, start2, groups2, items, nxt);
         }
+        // Waits for vector memory are counted in issue order: every path
+        // but a whole tile's (computed from registers, then its previous
+        // tile stored whole) ends with nothing in flight, so that the waits
+        // the compiler places count exactly one whole tile's stores and the
+        // next tile's loads behind the loads this tile waits for.
         const uint32_t k = uint32_t(w.tensor);
-        const float *scales = static_cast<const float *>(w.aux);  // every tensor takes 4-element accesses
+        const bool whole = live && one_whole(w, start, n);
         OneSlots x;
-        if (live) {
-            const float sc[3] = {scales[0], scales[1], scales[2]};
-            uint32_t mx[3] = {0u, 0u, 0u};
-            one_compute_raw<S>(w, start, n, c, sc, raw, x, mx);
-            one_block_max(mx);
-            arrive(t, k, mx);
+        uint32_t mx[3] = {0u, 0u, 0u};
+        if (whole) {
+            float sc[3];
+            load_scales(w.aux, sc);  // every tensor of a one-pass list takes 4-element accesses
+            one_compute_raw<S, true>(w, start, n, c, sc, cur, x, mx);
+        } else {
+            if (live) {
+                float sc[3];
+                load_scales(w.aux, sc);
+                one_compute_raw<S, false>(w, start, n, c, sc, cur, x, mx);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
         }
-        if (have_prev) finish_prev();
+        if (live) one_block_max(mx);
+        if (tid == 0) {
+            // read the previous tile's scales, publish this tile's maxima,
+            // wait until both are done, arrive
+            uint64_t q[3] = {0u, 0u, 0u};
+            if (have_prev) look(q);
+            if (live) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) shared_store(f.tile_max + 3 * size_t(t) + j, mx[j]);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            if (live) {
+                const uint32_t before =
+                    __hip_atomic_fetch_add(f.count + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = before + 1u == f.arrivals[k] ? 1u : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j) qs[j] = q[j];
+        }
+        __syncthreads();
+        if (live && last) fold(k);
+        // the previous tile
+        if (have_prev && wait_prev()) {
+            if (whole_prev) {
+                store_prev(true);
+            } else {
+                store_prev(false);
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+        }
         __syncthreads();  // the previous tile's slots are read
         if (live) {
 #pragma unroll
@@ -1552,9 +1676,26 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
             t_prev = t;
         }
         have_prev = live;
-        raw = next;
+        whole_prev = whole;
+        pos += gridDim.x;
+    };
+
+    // two tiles per turn, so that the two buffers swap roles without copies
+    while (pos < total) {
+        body(raw[0], raw[1]);
+        if (pos >= total) break;
+        body(raw[1], raw[0]);
     }
-    if (have_prev) finish_prev();
+    if (have_prev) {
+        if (tid == 0) {
+            uint64_t q[3];
+            look(q);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) qs[j] = q[j];
+        }
+        __syncthreads();
+        if (wait_prev()) store_prev(whole_prev);
+    }
 }
 
 // The follow-up pass: recomputes and stores the one-pass tiles whose wait
@@ -1571,8 +1712,8 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one_redo(const WorkItem
         const WorkItem w = items[b >> shift];
         const int start = int(b & ((1u << shift) - 1u)) * kOneTile;
         const int n = min(kOneTile, w.n - start);
-        const float *scales = static_cast<const float *>(w.aux);
-        const float sc[3] = {scales[0], scales[1], scales[2]};
+        float sc[3];
+        load_scales(w.aux, sc);
         const uint32_t *rk = f.folded + 6 * size_t(w.tensor) + 3;
         const float r[3] = {__uint_as_float(shared_load(rk)), __uint_as_float(shared_load(rk + 1)),
                             __uint_as_float(shared_load(rk + 2))};
@@ -1583,7 +1724,8 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one_redo(const WorkItem
 }
 
 // One lane per tensor: the new scales (amax / limit), and the counts and
-// flags cleared for the next step; lane 0 clears the follow-up list.
+// published scales cleared for the next step; lane 0 clears the follow-up
+// list.
 template <int ST>
 __global__ void adam_scaled_one_finish(float *const *__restrict__ scale_ptrs, OneArgs f, uint32_t tensors,
                                        const StepBlock *__restrict__ block)
@@ -1596,7 +1738,8 @@ __global__ void adam_scaled_one_finish(float *const *__restrict__ scale_ptrs, On
 #pragma unroll
     for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(shared_load(f.folded + 6 * size_t(k) + j)) / scaled_limit<ST>();
     shared_store(f.count + k, 0u);
-    shared_store(f.flag + k, 0u);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) shared_store64(f.ready + 3 * size_t(k) + j, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -2183,10 +2326,11 @@ struct adam_tl {
     uint32_t *d_tiles;     // scaled state: [first, end) tile range per non-empty tensor
     uint32_t *d_tile_max;  // scaled state: three magnitude maxima per tile
     uint32_t *d_folded;    // scaled state: three magnitude maxima, then three reciprocal scales, per non-empty tensor
-    // one-pass scaled state (one_pass): per tensor its non-empty one-pass
-    // tiles, arrival count and published flag; the follow-up list
+    // one-pass scaled state (one_pass): per tensor its published reciprocal
+    // scales, arrival count and non-empty one-pass tiles; the follow-up list
     bool one_pass;
-    uint32_t *d_arrivals, *d_count, *d_flag, *d_redo;
+    uint64_t *d_ready;
+    uint32_t *d_count, *d_redo, *d_arrivals;
     uint64_t wait_ticks;
     uint32_t wait_polls;
     uint32_t one_grid;     // workgroups of the persistent one-pass kernel
@@ -2277,7 +2421,7 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
     if (tl->one_pass) {
         // the one-pass kernel, its follow-up pass, the new scales
         const int idx = base;  // the one-pass tables use the scaled passes' order
-        const OneArgs f = {tl->d_tiles,   tl->d_arrivals, tl->d_count,      tl->d_flag,      tl->d_tile_max,
+        const OneArgs f = {tl->d_tiles,   tl->d_arrivals, tl->d_count,      tl->d_ready,     tl->d_tile_max,
                            tl->d_folded,  tl->d_redo,     tl->wait_ticks,   tl->wait_polls};
         const uint32_t shift = tl->shift - 3;  // one-pass tiles per record: 2^shift
         const uint32_t tiles = uint32_t(tl->stats.grid_blocks) / kOneSub;
@@ -2551,7 +2695,8 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     tl->d_tile_max = nullptr;
     tl->d_folded = nullptr;
     tl->one_pass = plan.stats.scaled_passes == 1;
-    tl->d_arrivals = tl->d_count = tl->d_flag = tl->d_redo = nullptr;
+    tl->d_ready = nullptr;
+    tl->d_arrivals = tl->d_count = tl->d_redo = nullptr;
     tl->wait_ticks = 0;
     tl->wait_polls = 0;
     tl->one_grid = 0;
@@ -2603,7 +2748,8 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     }
     // layout: [work table][scalar block][partial sums][scale pointers]
     //         [tile ranges][per-tile maxima][per-tensor maxima]
-    //         [one pass: arrivals, counts, flags per tensor; follow-up list]
+    //         [one pass: published reciprocal scales (three 64-bit words)
+    //          and counts per tensor; follow-up list; arrivals per tensor]
     const bool scaled = tl->kind == Kind::Scaled;
     const size_t table_bytes = plan.items.size() * sizeof(WorkItem);
     const size_t block_off = table_bytes;
@@ -2613,9 +2759,11 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     const size_t tile_max_off = tiles_off + (scaled ? plan.tile_ranges.size() * sizeof(uint32_t) : 0);
     const size_t folded_off =
         tile_max_off + (scaled ? 3 * sizeof(uint32_t) * size_t(tl->stats.grid_blocks) : 0);
-    const size_t one_off = folded_off + (scaled ? 6 * sizeof(uint32_t) * tl->n_tensors : 0);
+    const size_t one_off = align_up(folded_off + (scaled ? 6 * sizeof(uint32_t) * tl->n_tensors : 0), 8);
     const size_t one_tiles = size_t(tl->stats.grid_blocks / kOneSub);
-    const size_t total = one_off + (tl->one_pass ? sizeof(uint32_t) * (3 * size_t(tl->n_tensors) + 1 + one_tiles) : 0);
+    // the part that starts at zero: published scales, counts, follow-up list
+    const size_t one_zero = 3 * sizeof(uint64_t) * tl->n_tensors + sizeof(uint32_t) * (tl->n_tensors + 1 + one_tiles);
+    const size_t total = one_off + (tl->one_pass ? one_zero + sizeof(uint32_t) * tl->n_tensors : 0);
     void *mem = nullptr;
     if (hipMalloc(&mem, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -2633,10 +2781,10 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
         tl->d_folded = reinterpret_cast<uint32_t *>(base + folded_off);
     }
     if (tl->one_pass) {
-        tl->d_arrivals = reinterpret_cast<uint32_t *>(base + one_off);
-        tl->d_count = tl->d_arrivals + tl->n_tensors;
-        tl->d_flag = tl->d_count + tl->n_tensors;
-        tl->d_redo = tl->d_flag + tl->n_tensors;
+        tl->d_ready = reinterpret_cast<uint64_t *>(base + one_off);
+        tl->d_count = reinterpret_cast<uint32_t *>(tl->d_ready + 3 * size_t(tl->n_tensors));
+        tl->d_redo = tl->d_count + tl->n_tensors;
+        tl->d_arrivals = tl->d_redo + 1 + one_tiles;
     }
     bool ok = hipMemcpyAsync(tl->d_items, plan.items.data(), table_bytes, hipMemcpyHostToDevice,
                              stream) == hipSuccess;
@@ -2647,11 +2795,10 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
              hipMemcpyAsync(tl->d_tiles, plan.tile_ranges.data(),
                             plan.tile_ranges.size() * sizeof(uint32_t), hipMemcpyHostToDevice,
                             stream) == hipSuccess;
-    if (ok && tl->one_pass)  // counts, flags and the follow-up list start at zero
+    if (ok && tl->one_pass)
         ok = hipMemcpyAsync(tl->d_arrivals, plan.arrivals.data(), plan.arrivals.size() * sizeof(uint32_t),
                             hipMemcpyHostToDevice, stream) == hipSuccess &&
-             hipMemsetAsync(tl->d_count, 0, sizeof(uint32_t) * (2 * size_t(tl->n_tensors) + 1 + one_tiles),
-                            stream) == hipSuccess;
+             hipMemsetAsync(tl->d_ready, 0, one_zero, stream) == hipSuccess;
     if (!ok || hipStreamSynchronize(stream) != hipSuccess) {
         (void)hipFree(mem);
         delete tl;
