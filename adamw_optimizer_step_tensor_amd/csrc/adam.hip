@@ -1135,8 +1135,10 @@ constexpr int kOneGroups = 4;                             // lane groups per lan
 constexpr int kOneSlots = kOneGroups * kLane;             // elements per lane (16)
 constexpr int kOneTile = kOneBlock * kOneSlots;           // 4096 elements
 constexpr uint32_t kOneSub = uint32_t(kOneTile / kTile);  // update tiles per one-pass tile (8)
+constexpr uint32_t kOneSubLog = kOneSub == 8 ? 3 : kOneSub == 4 ? 2 : kOneSub == 2 ? 1 : 0;
 constexpr uint32_t kOneRun = uint32_t(kRunElems / kOneTile);
-static_assert(kOneBlock > kMaxHead && kRunElems % kOneTile == 0, "one-pass tile shape");
+static_assert(kOneBlock > kMaxHead && kRunElems % kOneTile == 0 && (1u << kOneSubLog) == kOneSub,
+              "one-pass tile shape");
 
 struct OneArgs {
     const uint32_t *tiles;     // per tensor: [first, end) update tiles
@@ -1347,9 +1349,7 @@ __device__ __forceinline__ bool one_whole(const WorkItem &w, int start, int n)
 
 // Issues the loads of `groups` lane groups of a tile (0 for no tile): always
 // 16 per lane, lanes past the tile's groups reading `spare` (any 16 readable
-// bytes).  The vector memory counter is waited on in issue order, so a fixed
-// count lets the compiler wait for exactly one tile's loads while the next
-// tile's loads and the previous tile's stores stay in flight.
+// bytes), so that every path leaves the same loads in flight.
 template <int GT>
 __device__ __forceinline__ void one_load_raw(const WorkItem &w, int start, int groups, const void *spare,
                                              OneRaw<GT> &raw)
@@ -1517,9 +1517,14 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
         return ready != 0u;
     };
 
-    // stores the previous tile from local memory: its lane groups (all of
-    // them for a whole tile) ...
-    auto store_groups = [&](const WorkItem &w, int start, int groups, bool whole, const float *r) {
+    // Stores the previous tile from local memory once its scales are out:
+    // its lane groups (all of them for a whole tile) ...
+    auto store_prev = [&](bool whole) {
+        const WorkItem w = items[t_prev >> shift];
+        const int start = int(t_prev & mask) * kOneTile;
+        const int n = min(kOneTile, w.n - start);
+        const int groups = n / kLane;
+        const float r[3] = {rs[0], rs[1], rs[2]};
 #pragma unroll
         for (int j = 0; j < kOneGroups; ++j) {
             const int lg = j * kOneBlock + tid;
@@ -1545,19 +1550,8 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
                 }
             }
         }
-    };
-
-    // ... and, for a tile that is not whole, its element path
-    auto store_prev = [&](bool whole) {
-        const WorkItem w = items[t_prev >> shift];
-        const int start = int(t_prev & mask) * kOneTile;
-        const int n = min(kOneTile, w.n - start);
-        const int groups = n / kLane;
-        const float r[3] = {rs[0], rs[1], rs[2]};
-        if (whole) {
-            store_groups(w, start, groups, true, r);
-        } else {
-            store_groups(w, start, groups, false, r);
+        // ... and, for a tile that is not whole, its element path
+        if (!whole) {
             if (tid < n - groups * kLane) one_store_element<S>(w, start + groups * kLane + tid, r, sp[0], sm[0], sv[0]);
             if (start == 0 && tid < w.head) one_store_element<S>(w, tid - w.head, r, sp[1], sm[1], sv[1]);
         }
@@ -1606,11 +1600,6 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
             const int groups2 = more && start2 < w2.n ? min(kOneTile, w2.n - start2) / kLane : 0;
             one_load_raw<S::gt>(w2, start2, groups2, items, nxt);
         }
-        // Waits for vector memory are counted in issue order: every path
-        // but a whole tile's (computed from registers, then its previous
-        // tile stored whole) ends with nothing in flight, so that the waits
-        // the compiler places count exactly one whole tile's stores and the
-        // next tile's loads behind the loads this tile waits for.
         const uint32_t k = uint32_t(w.tensor);
         const bool whole = live && one_whole(w, start, n);
         OneSlots x;
@@ -1619,15 +1608,19 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
             float sc[3];
             load_scales(w.aux, sc);  // every tensor of a one-pass list takes 4-element accesses
             one_compute_raw<S, true>(w, start, n, c, sc, cur, x, mx);
-        } else {
-            if (live) {
-                float sc[3];
-                load_scales(w.aux, sc);
-                one_compute_raw<S, false>(w, start, n, c, sc, cur, x, mx);
-            }
-            __builtin_amdgcn_s_waitcnt(0);
+        } else if (live) {
+            float sc[3];
+            load_scales(w.aux, sc);
+            one_compute_raw<S, false>(w, start, n, c, sc, cur, x, mx);
         }
         if (live) one_block_max(mx);
+        // Waits for vector memory count in issue order, and the compiler
+        // places them from what any path may leave in flight.  A drain here,
+        // after the tile's arithmetic (and the barrier of its maxima, which
+        // keeps it there), costs little: the next tile's loads and the
+        // previous tile's stores have had that long.  It leaves the next
+        // tile's arithmetic with no wait on its loads, complete by then.
+        __builtin_amdgcn_s_waitcnt(0);
         if (tid == 0) {
             // read the previous tile's scales, publish this tile's maxima,
             // wait until both are done, arrive
@@ -1649,16 +1642,7 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
         __syncthreads();
         if (live && last) fold(k);
         // the previous tile
-        if (have_prev && wait_prev()) {
-            if (whole_prev) {
-                store_prev(true);
-            } else {
-                store_prev(false);
-                __builtin_amdgcn_s_waitcnt(0);
-            }
-        } else {
-            __builtin_amdgcn_s_waitcnt(0);
-        }
+        if (have_prev && wait_prev()) store_prev(whole_prev);
         __syncthreads();  // the previous tile's slots are read
         if (live) {
 #pragma unroll
@@ -1995,7 +1979,7 @@ uint32_t one_position(uint32_t u, uint32_t total)
 // A one-pass list's largest tensor, in one-pass tiles (2M elements): half of
 // what MI355X keeps resident of the one-pass kernel (1280 workgroups at 5
 // per compute unit); the handle checks the device's own figure.
-constexpr int64_t kOneMaxTensorTiles = 512;
+constexpr int64_t kOneMaxTensorTiles = (int64_t(1) << 21) / kOneTile;  // tensors of at most 2M elements
 constexpr uint32_t kOneRedoBlocks = 1024;  // workgroups of the follow-up pass
 constexpr int kOneWaitUs = 200;            // default wait of a one-pass workgroup
 
@@ -2423,7 +2407,7 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
         const int idx = base;  // the one-pass tables use the scaled passes' order
         const OneArgs f = {tl->d_tiles,   tl->d_arrivals, tl->d_count,      tl->d_ready,     tl->d_tile_max,
                            tl->d_folded,  tl->d_redo,     tl->wait_ticks,   tl->wait_polls};
-        const uint32_t shift = tl->shift - 3;  // one-pass tiles per record: 2^shift
+        const uint32_t shift = tl->shift - kOneSubLog;  // one-pass tiles per record: 2^shift
         const uint32_t tiles = uint32_t(tl->stats.grid_blocks) / kOneSub;
         hipLaunchKernelGGL(OneKernels::fns[idx], dim3(tl->one_grid), dim3(kOneBlock), 0, stream, tl->d_items, shift,
                            tiles, args, f);
@@ -2634,7 +2618,7 @@ int one_pass_fits(adam_tl *tl, int device, const Plan &plan, const adam_tl_desc 
     // no workgroup may hold three tiles of one tensor: every tensor's tiles
     // must lie within 2 * grid - 1 consecutive positions
     bool fits = grid > 0;
-    const uint32_t shift = tl->shift - 3;
+    const uint32_t shift = tl->shift - kOneSubLog;
     for (size_t k = 0; fits && k < plan.arrivals.size(); ++k) {
         const uint32_t lo = plan.tile_ranges[2 * k] / kOneSub, hi = plan.tile_ranges[2 * k + 1] / kOneSub;
         uint32_t first = UINT32_MAX, end = 0;
