@@ -8,6 +8,9 @@ Flags that define the arithmetic:
   no fast-math        division and square root stay correctly rounded and
                       fp32 denormals are kept.
 Packed fp32 instructions are disabled (-packed-fp32-ops).
+The atomic optimizer is off: every atomic operation here is issued by one
+lane, and the optimizer's rewrite uses its result at once, which would wait
+for it where the one-pass kernel lets it complete under other work.
 """
 import os
 import subprocess
@@ -29,6 +32,7 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

@@ -1120,15 +1120,20 @@ __global__ void adam_scaled_finish(float *const *__restrict__ scale_ptrs,
 // three.  No release or acquire fence of device scope (which would write
 // back or invalidate whole L2 caches) is needed.
 //
-// Measured on MI355X (1e9 elements in 2048 tensors): 3.80 ms per step
-// against 3.97 for the two pipelined passes in the same process.  What it
-// took: each tile's exchange costs two round trips to device-coherent
-// memory (the wait for the maxima's stores, the count), the previous
-// tile's scales riding along with the first; and the waits the compiler
-// places on the vector memory counter, which drains in issue order, let
-// the next tile's loads and the previous tile's stores stay in flight
-// while a tile is computed (a first version waited for everything once per
-// tile and took 4.66 ms).
+// Measured on MI355X (1e9 elements in 2048 tensors): 3.65 ms per step
+// against 3.97 for the two pipelined passes in the same process (a copy
+// without the exchange, inexact, takes 3.29).  What it took: the tiles of
+// one round of the grid cover a few tensors, and device-scope atomic
+// operations on one address are performed one at a time, so each tensor's
+// count is spread over kOneSpread addresses; each tile's exchange costs
+// two round trips to device-coherent memory (the wait for the maxima's
+// stores, with the previous tile's scales riding along, and the count),
+// the second completing under the previous tile's stores; barriers order
+// the local data share only; and the waits the compiler places on the
+// vector memory counter, which drains in issue order, let the next tile's
+// loads and the previous tile's stores stay in flight while a tile is
+// computed (a first version waited for everything once per tile, with one
+// counter per tensor, and took 4.66 ms).
 // ---------------------------------------------------------------------------
 constexpr int kOneBlock = 256;                            // four waves
 constexpr int kOneGroups = 4;                             // lane groups per lane
@@ -1142,8 +1147,9 @@ static_assert(kOneBlock > kMaxHead && kRunElems % kOneTile == 0 && (1u << kOneSu
 
 struct OneArgs {
     const uint32_t *tiles;     // per tensor: [first, end) update tiles
-    const uint32_t *arrivals;  // per tensor: its non-empty one-pass tiles
-    uint32_t *count;           // per tensor: workgroups arrived in this step (0 between steps)
+    const uint32_t *arrivals;  // per tensor: its non-empty spread counters, then kOneSpread rows (one per
+                               // spread s) of its non-empty tiles at positions = s mod kOneSpread
+    uint32_t *count;           // the same layout: arrivals in this step (0 between steps)
     uint64_t *ready;           // per tensor: its three reciprocal scales, kPublished | bits once published
                                // (0 between steps)
     uint32_t *tile_max;        // per one-pass tile: three magnitude maxima
@@ -1151,7 +1157,16 @@ struct OneArgs {
     uint32_t *redo;            // [0]: tiles left to the follow-up pass, then their indices
     uint64_t wait_ticks;       // a workgroup's wait, in ticks of the device's real-time clock; 0: none
     uint32_t wait_polls;       // and at most this many polls of the scales (each takes longer than 0.25 us)
+    uint32_t tensors;          // non-empty tensors (the row length of arrivals and count)
 };
+
+// A tensor's arrivals are counted in kOneSpread counters, by the tile's
+// position modulo kOneSpread; the last arrival at each of those counts
+// itself in at the tensor's own counter, whose last arrival folds.  The
+// tiles of one round of the grid cover a few tensors, and device-scope
+// atomic operations on one address are performed one at a time: spread
+// over several addresses they wait on each other far less.
+constexpr uint32_t kOneSpread = 8;
 
 constexpr uint64_t kPublished = uint64_t(1) << 32;  // the tag of a published reciprocal scale
 
@@ -1313,6 +1328,27 @@ __device__ __forceinline__ void one_store(const WorkItem &w, int start, int n, c
     }
 }
 
+// Waits until at most N vector memory operations of the wave are in flight
+// (they complete in issue order): expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vector_memory()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// A workgroup barrier that orders the local data share only.  The one-pass
+// kernel shares nothing else between the waves of a workgroup (its global
+// accesses are ordered by explicit waits), and a barrier with a fence over
+// all memory would wait for every load and store in flight, such as the
+// next tile's loads and the count's round trip.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The largest of three values per lane over the workgroup, in lane 0 of
 // wave 0 (every lane must call it).
 __device__ __forceinline__ void one_block_max(uint32_t *mx)
@@ -1324,7 +1360,7 @@ __device__ __forceinline__ void one_block_max(uint32_t *mx)
         wave_maxima[1][threadIdx.x / 64] = x1;
         wave_maxima[2][threadIdx.x / 64] = x2;
     }
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0)
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -1513,18 +1549,18 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
             }
             ready = seen ? 1u : 0u;
         }
-        __syncthreads();
+        lds_barrier();
         return ready != 0u;
     };
 
     // Stores the previous tile from local memory once its scales are out:
     // its lane groups (all of them for a whole tile) ...
-    auto store_prev = [&](bool whole) {
+    auto store_prev = [&](auto whole_tag, const float *r) {
+        constexpr bool whole = decltype(whole_tag)::value;
         const WorkItem w = items[t_prev >> shift];
         const int start = int(t_prev & mask) * kOneTile;
         const int n = min(kOneTile, w.n - start);
         const int groups = n / kLane;
-        const float r[3] = {rs[0], rs[1], rs[2]};
 #pragma unroll
         for (int j = 0; j < kOneGroups; ++j) {
             const int lg = j * kOneBlock + tid;
@@ -1582,6 +1618,7 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
                 shared_store64(f.ready + 3 * size_t(k) + j, kPublished | rbits);
             }
         }
+        lds_barrier();  // the block maxima are read before any wave writes them again
     };
 
     // one tile: the next one's loads into nxt, this one computed from cur
@@ -1616,34 +1653,77 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
         if (live) one_block_max(mx);
         // Waits for vector memory count in issue order, and the compiler
         // places them from what any path may leave in flight.  A drain here,
-        // after the tile's arithmetic (and the barrier of its maxima, which
-        // keeps it there), costs little: the next tile's loads and the
-        // previous tile's stores have had that long.  It leaves the next
-        // tile's arithmetic with no wait on its loads, complete by then.
+        // after the tile's arithmetic (the scheduling barrier keeps it
+        // there), costs little: the next tile's loads and the previous
+        // tile's stores have had that long.  It leaves the next tile's
+        // arithmetic with no wait on its loads, complete by then.
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(0);
+        // lane 0 of wave 0: read the previous tile's scales, publish this
+        // tile's maxima, wait until both are done, then count this tile in
+        // (the count's round trip runs while the previous tile is stored)
+        const size_t sub = size_t(1 + pos % kOneSpread) * f.tensors + k;
+        uint32_t before = 0u;
         if (tid == 0) {
-            // read the previous tile's scales, publish this tile's maxima,
-            // wait until both are done, arrive
-            uint64_t q[3] = {0u, 0u, 0u};
-            if (have_prev) look(q);
-            if (live) {
+            // (both unconditional: a branch here lets the compiler split the
+            // block and leave the reads unwaited on some path; without a
+            // previous tile the words read are ignored, and an empty tile's
+            // maxima, all 0, are never folded)
+            uint64_t q[3];
+            look(q);
 #pragma unroll
-                for (int j = 0; j < 3; ++j) shared_store(f.tile_max + 3 * size_t(t) + j, mx[j]);
-            }
+            for (int j = 0; j < 3; ++j) shared_store(f.tile_max + 3 * size_t(t) + j, mx[j]);
             __builtin_amdgcn_s_waitcnt(0);
-            if (live) {
-                const uint32_t before =
-                    __hip_atomic_fetch_add(f.count + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                last = before + 1u == f.arrivals[k] ? 1u : 0u;
-            }
 #pragma unroll
             for (int j = 0; j < 3; ++j) qs[j] = q[j];
+            if (live) before = __hip_atomic_fetch_add(f.count + sub, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();
+        lds_barrier();
+        // the previous tile, if its scales are out already
+        const uint64_t q[3] = {qs[0], qs[1], qs[2]};
+        const bool early = have_prev && f.wait_ticks != 0 && published(q);
+        // The count's round trip (lane 0 of wave 0) then completes under the
+        // previous tile's stores: issued after it, a whole tile's kPrevStores
+        // stores may stay in flight while the wait retires the count.
+        constexpr int kPrevStores = kOneGroups * (S::ot != kNone ? 4 : 3);
+        if (early) {
+            const float r[3] = {__uint_as_float(uint32_t(q[0])), __uint_as_float(uint32_t(q[1])),
+                                __uint_as_float(uint32_t(q[2]))};
+            if (whole_prev) {
+                store_prev(std::true_type(), r);
+                wait_vector_memory<kPrevStores>();
+            } else {
+                store_prev(std::false_type(), r);
+                wait_vector_memory<0>();
+            }
+        } else {
+            wait_vector_memory<0>();
+        }
+        // this tile's count (its tensor's last tile folds: publishing never
+        // waits for anything but the stores and counts already issued)
+        if (tid == 0 && live) {
+            // the count's value is first used here, after the stores above
+            // (the compiler would otherwise use it, and wait for it, at once)
+            asm volatile("" : "+v"(before)::"memory");
+            const ADAM_CONSTANT uint32_t *arrivals = (const ADAM_CONSTANT uint32_t *)f.arrivals;
+            uint32_t is_last = 0u;
+            if (before + 1u == arrivals[sub]) {
+                const uint32_t before_k =
+                    __hip_atomic_fetch_add(f.count + k, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                is_last = before_k + 1u == arrivals[k] ? 1u : 0u;
+            }
+            last = is_last;
+        }
+        lds_barrier();
         if (live && last) fold(k);
-        // the previous tile
-        if (have_prev && wait_prev()) store_prev(whole_prev);
-        __syncthreads();  // the previous tile's slots are read
+        // the previous tile, if its scales were not out: wait for them
+        if (have_prev && !early && wait_prev()) {
+            if (whole_prev)
+                store_prev(std::true_type(), rs);
+            else
+                store_prev(std::false_type(), rs);
+        }
+        // each lane's own columns of keep: no lane reads another's
         if (live) {
 #pragma unroll
             for (int j = 0; j < kOneSlots; ++j) {
@@ -1677,8 +1757,13 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
 #pragma unroll
             for (int j = 0; j < 3; ++j) qs[j] = q[j];
         }
-        __syncthreads();
-        if (wait_prev()) store_prev(whole_prev);
+        lds_barrier();
+        if (wait_prev()) {
+            if (whole_prev)
+                store_prev(std::true_type(), rs);
+            else
+                store_prev(std::false_type(), rs);
+        }
     }
 }
 
@@ -1721,7 +1806,8 @@ __global__ void adam_scaled_one_finish(float *const *__restrict__ scale_ptrs, On
     float *s = scale_ptrs[k];
 #pragma unroll
     for (int j = 0; j < 3; ++j) s[j] = __uint_as_float(shared_load(f.folded + 6 * size_t(k) + j)) / scaled_limit<ST>();
-    shared_store(f.count + k, 0u);
+#pragma unroll
+    for (uint32_t row = 0; row <= kOneSpread; ++row) shared_store(f.count + size_t(row) * tensors + k, 0u);
 #pragma unroll
     for (int j = 0; j < 3; ++j) shared_store64(f.ready + 3 * size_t(k) + j, 0u);
 }
@@ -2406,7 +2492,8 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
         // the one-pass kernel, its follow-up pass, the new scales
         const int idx = base;  // the one-pass tables use the scaled passes' order
         const OneArgs f = {tl->d_tiles,   tl->d_arrivals, tl->d_count,      tl->d_ready,     tl->d_tile_max,
-                           tl->d_folded,  tl->d_redo,     tl->wait_ticks,   tl->wait_polls};
+                           tl->d_folded,  tl->d_redo,     tl->wait_ticks,   tl->wait_polls,
+                           tl->n_tensors};
         const uint32_t shift = tl->shift - kOneSubLog;  // one-pass tiles per record: 2^shift
         const uint32_t tiles = uint32_t(tl->stats.grid_blocks) / kOneSub;
         hipLaunchKernelGGL(OneKernels::fns[idx], dim3(tl->one_grid), dim3(kOneBlock), 0, stream, tl->d_items, shift,
@@ -2595,7 +2682,7 @@ int plan_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count, 
 // Whether the device keeps at least twice the largest tensor's one-pass
 // workgroups resident (else tl->one_pass is cleared, or, when the caller
 // asked for one pass, ADAM_EINVAL); sets the wait in real-time clock ticks.
-int one_pass_fits(adam_tl *tl, int device, const Plan &plan, const adam_tl_desc *desc)
+int one_pass_fits(adam_tl *tl, int device, Plan &plan, const adam_tl_desc *desc)
 {
     int cus = 0, khz = 0, per_cu = INT32_MAX;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
@@ -2617,9 +2704,12 @@ int one_pass_fits(adam_tl *tl, int device, const Plan &plan, const adam_tl_desc 
     if (desc->dispatch_tiles != 0) grid = std::min<int64_t>(grid, std::max(1, desc->dispatch_tiles / int32_t(kOneSub)));
     // no workgroup may hold three tiles of one tensor: every tensor's tiles
     // must lie within 2 * grid - 1 consecutive positions
+    // (and each tensor's arrivals counted per spread counter)
     bool fits = grid > 0;
     const uint32_t shift = tl->shift - kOneSubLog;
-    for (size_t k = 0; fits && k < plan.arrivals.size(); ++k) {
+    const size_t n = plan.arrivals.size();
+    std::vector<uint32_t> spread((1 + kOneSpread) * n, 0u);
+    for (size_t k = 0; fits && k < n; ++k) {
         const uint32_t lo = plan.tile_ranges[2 * k] / kOneSub, hi = plan.tile_ranges[2 * k + 1] / kOneSub;
         uint32_t first = UINT32_MAX, end = 0;
         for (uint32_t u = lo; u < hi; ++u) {
@@ -2627,14 +2717,17 @@ int one_pass_fits(adam_tl *tl, int device, const Plan &plan, const adam_tl_desc 
             const uint32_t p = one_position(u, total);
             first = std::min(first, p);
             end = std::max(end, p + 1);
+            ++spread[(1 + p % kOneSpread) * n + k];
         }
         fits = end <= first || int64_t(end - first) < 2 * grid;
+        for (uint32_t s = 0; s < kOneSpread; ++s) spread[k] += spread[(1 + s) * n + k] != 0u ? 1u : 0u;
     }
     if (!fits) {
         if (desc->scaled_passes == 1) return ADAM_EINVAL;
         tl->one_pass = false;
         return ADAM_OK;
     }
+    plan.arrivals.swap(spread);
     tl->one_grid = uint32_t(grid);
     const int64_t us = desc->scaled_wait_us == 0 ? kOneWaitUs : std::max(0, desc->scaled_wait_us);
     tl->wait_ticks = uint64_t(us) * uint64_t(std::max(khz, 1)) / 1000u;
@@ -2746,8 +2839,9 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     const size_t one_off = align_up(folded_off + (scaled ? 6 * sizeof(uint32_t) * tl->n_tensors : 0), 8);
     const size_t one_tiles = size_t(tl->stats.grid_blocks / kOneSub);
     // the part that starts at zero: published scales, counts, follow-up list
-    const size_t one_zero = 3 * sizeof(uint64_t) * tl->n_tensors + sizeof(uint32_t) * (tl->n_tensors + 1 + one_tiles);
-    const size_t total = one_off + (tl->one_pass ? one_zero + sizeof(uint32_t) * tl->n_tensors : 0);
+    const size_t counters = (1 + kOneSpread) * size_t(tl->n_tensors);
+    const size_t one_zero = 3 * sizeof(uint64_t) * tl->n_tensors + sizeof(uint32_t) * (counters + 1 + one_tiles);
+    const size_t total = one_off + (tl->one_pass ? one_zero + sizeof(uint32_t) * counters : 0);
     void *mem = nullptr;
     if (hipMalloc(&mem, total) != hipSuccess) {
         (void)hipGetLastError();
@@ -2767,7 +2861,7 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     if (tl->one_pass) {
         tl->d_ready = reinterpret_cast<uint64_t *>(base + one_off);
         tl->d_count = reinterpret_cast<uint32_t *>(tl->d_ready + 3 * size_t(tl->n_tensors));
-        tl->d_redo = tl->d_count + tl->n_tensors;
+        tl->d_redo = tl->d_count + counters;
         tl->d_arrivals = tl->d_redo + 1 + one_tiles;
     }
     bool ok = hipMemcpyAsync(tl->d_items, plan.items.data(), table_bytes, hipMemcpyHostToDevice,
