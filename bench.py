@@ -330,10 +330,14 @@ def summarize_dram(w, req_dir: str, stall_dir: str) -> None:
             key = (_short(r["Kernel_Name"]), r["Dispatch_Id"])
             vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
             grids[key] = int(r["Grid_Size"]) // int(r["Workgroup_Size"])
-        big = max(g for (n, _), g in grids.items() if is_main(n))
+        # the kernel that streams the elements (the one-pass follow-up pass,
+        # which has nothing to store unless a wait ran out, is not it)
+        def streams(n):
+            return is_main(n) and not n.startswith("adam_scaled_one_redo")
+        big = max(g for (n, _), g in grids.items() if streams(n))
         per = {}
         for key, c in vals.items():
-            if grids[key] == big and is_main(key[0]):
+            if grids[key] == big and streams(key[0]):
                 per.setdefault(key[0], []).append(c)
         return per
 
