@@ -135,9 +135,8 @@ typedef struct {
                                 waits for the rest of its tensor before it
                                 leaves its stores to the follow-up pass:
                                 0 = 200 us, > 0 = that many us, -1 = no wait
-                                (every tile but each tensor's last is stored
-                                by the follow-up pass).  Results do not
-                                depend on it.                                  */
+                                (every tile is stored by the follow-up
+                                pass).  Results do not depend on it.          */
 } adam_tl_desc;
 
 /* Per-group hyperparameters (apex defaults: betas (0.9, 0.999), eps 1e-8,
@@ -398,9 +397,10 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
  * (adam_tl_desc.scaled_wait_us), and a per-tensor kernel writes the new
  * scales.  Same results bit for bit.  It needs every tensor within 2M
  * elements and 4-element accesses, and a device that keeps the kernel's
- * grid resident; on MI355X it measured slower than two passes (its
- * per-tile exchange between workgroups goes through device-coherent
- * memory), so two passes are the default.
+ * grid resident: on MI355X it is 8% faster than two passes when the device
+ * is its own, but with other kernels resident beside it (a collective on
+ * another stream) its waits run out and the follow-up kernel does much of
+ * the work, so two passes are the default.
  * Arguments and errors as adam_step; ADAM_EINVAL for a handle without
  * scaled state. */
 int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,

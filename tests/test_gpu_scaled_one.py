@@ -5,7 +5,7 @@ and stores its tile; tiles whose wait runs out are recomputed and stored by
 a follow-up pass.  Bit for bit against the oracle (values, scales and the
 param-sync copy) and against the two-pass step, through host, capturable,
 noop and graph-replayed steps; the follow-up pass is exercised by running
-with no wait at all (every tile but each tensor's last goes through it) and
+with no wait at all (every tile goes through it) and
 with a 1 us wait."""
 import zlib
 
