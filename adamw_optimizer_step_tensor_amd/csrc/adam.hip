@@ -1158,7 +1158,9 @@ struct OneArgs {
     uint32_t *tile_max;        // per one-pass tile: three magnitude maxima
     uint32_t *folded;          // per tensor: three magnitude maxima, three reciprocal scales (float bits)
     uint32_t *redo;            // [0]: tiles left to the follow-up pass, then their indices
+    uint32_t *started;         // workgroups of the kernel that have started (0 between steps)
     uint64_t wait_ticks;       // a workgroup's wait, in ticks of the device's real-time clock; 0: none
+    uint64_t grace_ticks;      // after this long, a wait ends if not every workgroup has started
     uint32_t wait_polls;       // and at most this many polls of the scales (each takes longer than 0.25 us)
     uint32_t tensors;          // non-empty tensors (the row length of arrivals and count)
 };
@@ -1506,6 +1508,10 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
     auto published = [](const uint64_t *q) { return (q[0] & q[1] & q[2] & kPublished) != 0u; };
 
     uint32_t pos = blockIdx.x;
+    // counted in, so that a wait can tell whether the tiles it waits for
+    // belong to workgroups that are not running yet (other kernels holding
+    // the compute units they need)
+    if (tid == 0) __hip_atomic_fetch_add(f.started, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     OneRaw<S::gt> raw[2];  // the current and the next tile's lane groups, alternating
     {
         const uint32_t t = tile_at(pos);
@@ -1540,6 +1546,11 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
                     __builtin_amdgcn_s_sleep(16);
                     look(q);
                     seen = published(q);
+                    // not every workgroup running: leave the tile to the
+                    // follow-up pass rather than wait for one that is not
+                    if (!seen && __builtin_amdgcn_s_memrealtime() - t0 >= f.grace_ticks &&
+                        shared_load(f.started) < gridDim.x)
+                        break;
                 }
             }
             if (seen) {
@@ -1804,7 +1815,10 @@ __global__ void adam_scaled_one_finish(float *const *__restrict__ scale_ptrs, On
 {
     if (block != nullptr && block->skip) return;
     const uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k == 0) shared_store(f.redo, 0u);
+    if (k == 0) {
+        shared_store(f.redo, 0u);
+        shared_store(f.started, 0u);
+    }
     if (k >= tensors) return;
     float *s = scale_ptrs[k];
 #pragma unroll
@@ -2071,6 +2085,7 @@ uint32_t one_position(uint32_t u, uint32_t total)
 constexpr int64_t kOneMaxTensorTiles = (int64_t(1) << 21) / kOneTile;  // tensors of at most 2M elements
 constexpr uint32_t kOneRedoBlocks = 1024;  // workgroups of the follow-up pass
 constexpr int kOneWaitUs = 200;            // default wait of a one-pass workgroup
+constexpr int kOneGraceUs = 20;            // its wait while not every workgroup has started
 
 // Splits a scaled-state list into pieces of consecutive tensors (see
 // kMaxPieces): about equal tiles each, cut only at tensor boundaries, every
@@ -2404,7 +2419,8 @@ struct adam_tl {
     bool one_pass;
     uint64_t *d_ready;
     uint32_t *d_count, *d_redo, *d_arrivals;
-    uint64_t wait_ticks;
+    uint32_t *d_started;
+    uint64_t wait_ticks, grace_ticks;
     uint32_t wait_polls;
     uint32_t one_grid;     // workgroups of the persistent one-pass kernel
     uint32_t n_tensors;    // non-empty tensors
@@ -2495,8 +2511,8 @@ int launch_scaled(const adam_tl *tl, int mode, const StepArgs &args, hipStream_t
         // the one-pass kernel, its follow-up pass, the new scales
         const int idx = base;  // the one-pass tables use the scaled passes' order
         const OneArgs f = {tl->d_tiles,   tl->d_arrivals, tl->d_count,      tl->d_ready,     tl->d_tile_max,
-                           tl->d_folded,  tl->d_redo,     tl->wait_ticks,   tl->wait_polls,
-                           tl->n_tensors};
+                           tl->d_folded,  tl->d_redo,     tl->d_started,    tl->wait_ticks,  tl->grace_ticks,
+                           tl->wait_polls, tl->n_tensors};
         const uint32_t shift = tl->shift - kOneSubLog;  // one-pass tiles per record: 2^shift
         const uint32_t tiles = uint32_t(tl->stats.grid_blocks) / kOneSub;
         hipLaunchKernelGGL(OneKernels::fns[idx], dim3(tl->one_grid), dim3(kOneBlock), 0, stream, tl->d_items, shift,
@@ -2735,6 +2751,7 @@ int one_pass_fits(adam_tl *tl, int device, Plan &plan, const adam_tl_desc *desc)
     const int64_t us = desc->scaled_wait_us == 0 ? kOneWaitUs : std::max(0, desc->scaled_wait_us);
     tl->wait_ticks = uint64_t(us) * uint64_t(std::max(khz, 1)) / 1000u;
     if (us > 0 && tl->wait_ticks == 0) tl->wait_ticks = 1;
+    tl->grace_ticks = std::min<uint64_t>(tl->wait_ticks, uint64_t(kOneGraceUs) * uint64_t(std::max(khz, 1)) / 1000u);
     // a poll (a device-coherent load and a sleep of 1024 cycles) takes well
     // over 0.25 us, so this many polls outlast the wait: the loop ends even
     // if the clock did not advance
@@ -2777,7 +2794,8 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     tl->one_pass = plan.stats.scaled_passes == 1;
     tl->d_ready = nullptr;
     tl->d_arrivals = tl->d_count = tl->d_redo = nullptr;
-    tl->wait_ticks = 0;
+    tl->d_started = nullptr;
+    tl->wait_ticks = tl->grace_ticks = 0;
     tl->wait_polls = 0;
     tl->one_grid = 0;
     tl->n_tensors = uint32_t(plan.stats.nonempty);
@@ -2829,7 +2847,8 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     // layout: [work table][scalar block][partial sums][scale pointers]
     //         [tile ranges][per-tile maxima][per-tensor maxima]
     //         [one pass: published reciprocal scales (three 64-bit words)
-    //          and counts per tensor; follow-up list; arrivals per tensor]
+    //          and counts per tensor; follow-up list; started count;
+    //          arrivals per tensor]
     const bool scaled = tl->kind == Kind::Scaled;
     const size_t table_bytes = plan.items.size() * sizeof(WorkItem);
     const size_t block_off = table_bytes;
@@ -2843,7 +2862,7 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
     const size_t one_tiles = size_t(tl->stats.grid_blocks / kOneSub);
     // the part that starts at zero: published scales, counts, follow-up list
     const size_t counters = (1 + kOneSpread) * size_t(tl->n_tensors);
-    const size_t one_zero = 3 * sizeof(uint64_t) * tl->n_tensors + sizeof(uint32_t) * (counters + 1 + one_tiles);
+    const size_t one_zero = 3 * sizeof(uint64_t) * tl->n_tensors + sizeof(uint32_t) * (counters + 2 + one_tiles);
     const size_t total = one_off + (tl->one_pass ? one_zero + sizeof(uint32_t) * counters : 0);
     void *mem = nullptr;
     if (hipMalloc(&mem, total) != hipSuccess) {
@@ -2865,7 +2884,8 @@ int build_tl(const adam_tensor *tensors, const adam_tensor *alts, int64_t count,
         tl->d_ready = reinterpret_cast<uint64_t *>(base + one_off);
         tl->d_count = reinterpret_cast<uint32_t *>(tl->d_ready + 3 * size_t(tl->n_tensors));
         tl->d_redo = tl->d_count + counters;
-        tl->d_arrivals = tl->d_redo + 1 + one_tiles;
+        tl->d_started = tl->d_redo + 1 + one_tiles;
+        tl->d_arrivals = tl->d_started + 1;
     }
     bool ok = hipMemcpyAsync(tl->d_items, plan.items.data(), table_bytes, hipMemcpyHostToDevice,
                              stream) == hipSuccess;

@@ -7,6 +7,7 @@ param-sync copy) and against the two-pass step, through host, capturable,
 noop and graph-replayed steps; the follow-up pass is exercised by running
 with no wait at all (every tile goes through it) and
 with a 1 us wait."""
+import time
 import zlib
 
 import numpy as np
@@ -110,6 +111,41 @@ def test_one_pass_small_persistent_grids(torch, orc, grid, sizes, wait_us):
                             dict(scaled_passes=1, dispatch_tiles=8 * grid, scaled_wait_us=wait_us))
     assert (info["scaled_passes"], info["dispatches"]) == (1, 1)
     assert_bitwise(got, ref, ctx=f"grid {grid}")
+
+
+def test_one_pass_beside_another_kernel(torch, orc):
+    """A one-pass step launched while matrix products on another stream hold
+    the compute units, so that its persistent workgroups start over time
+    rather than together: a wait for tiles of workgroups that have not
+    started ends after a short grace and leaves its tile to the follow-up
+    pass.  The results stay exact, and the step takes nowhere near its
+    waits' full bound per tile."""
+    sizes = [1 << 20] * 12 + [70001, 4097]
+    host = _host("f16_scaled", "bf16", "bf16", 98, sizes=sizes)
+    hl, hr = hp_pair(0.9, 0.95, 1e-8, 0.1, 1)
+    ref = copies(host)
+    dev = DeviceSet(host)
+    tl = A.adam_tl_build(dev.tensors, desc_for(host, scaled_passes=1))
+    assert tl.info()["scaled_passes"] == 1
+    a = torch.randn(4096, 4096, device="cuda")
+    side = torch.cuda.Stream()
+    step, st = A.HostStep(0), [0]
+    ot = oracle_tensors(ref)
+    times = []
+    for _ in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            prods = [a @ a for _ in range(4)]
+        t0 = time.perf_counter()
+        A.adam_step_scaled(tl, hl, 1.6e-3, step, 0.5)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+        del prods
+        orc.group_step(ot, hr, 1.6e-3, st, 0.5)
+    got = dev.readback()
+    tl.destroy()
+    assert_bitwise(got, ref, ctx="beside matrix products")
+    assert max(times) < 1.0, times
 
 
 def test_one_pass_needs_tensors_within_two_rounds(torch):
