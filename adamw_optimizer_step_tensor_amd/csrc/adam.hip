@@ -2079,9 +2079,11 @@ uint32_t one_position(uint32_t u, uint32_t total)
     return u - q + (q % kOneRun) * kXcds + q / kOneRun;
 }
 
-// A one-pass list's largest tensor, in one-pass tiles (2M elements): half of
-// what MI355X keeps resident of the one-pass kernel (1280 workgroups at 5
-// per compute unit); the handle checks the device's own figure.
+// A one-pass list's largest tensor, in one-pass tiles (2M elements): 512
+// tiles, two thirds of one round of MI355X's resident grid (768 workgroups,
+// 3 per compute unit), so that a workgroup's wait for a tensor is covered by
+// the next tile it computes; the handle also checks the device's own grid
+// (every tensor within 2 * grid - 1 positions).
 constexpr int64_t kOneMaxTensorTiles = (int64_t(1) << 21) / kOneTile;  // tensors of at most 2M elements
 constexpr uint32_t kOneRedoBlocks = 1024;  // workgroups of the follow-up pass
 constexpr int kOneWaitUs = 200;            // default wait of a one-pass workgroup

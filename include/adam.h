@@ -396,11 +396,12 @@ int adam_step_remainders_capturable(const adam_tl *tl, const adam_hparams *hp, c
  * twice); a follow-up kernel stores any tile whose bounded wait ran out
  * (adam_tl_desc.scaled_wait_us), and a per-tensor kernel writes the new
  * scales.  Same results bit for bit.  It needs every tensor within 2M
- * elements and 4-element accesses, and a device that keeps the kernel's
- * grid resident: on MI355X it is 8% faster than two passes when the device
- * is its own, but with other kernels resident beside it (a collective on
- * another stream) its waits run out and the follow-up kernel does much of
- * the work, so two passes are the default.
+ * elements and 4-element accesses.  On MI355X it takes 7-10% less time
+ * than two passes.  It relies on its grid being resident: each workgroup
+ * counts itself in when it starts, and while not all have (other kernels
+ * holding compute units), a wait ends after 20 us and leaves the tile to
+ * the follow-up kernel, so the step still finishes and stays exact.  Two
+ * passes depend on nothing being resident and are the default.
  * Arguments and errors as adam_step; ADAM_EINVAL for a handle without
  * scaled state. */
 int adam_step_scaled(const adam_tl *tl, const adam_hparams *hp, float lr, int32_t *step_io,
