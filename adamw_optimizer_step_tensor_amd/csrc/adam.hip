@@ -2276,8 +2276,9 @@ int make_plan(const adam_tensor *tensors, const adam_tensor *alts, int64_t count
     if (st.nonempty >= (int64_t(1) << 31) / 3) return ADAM_EINVAL;
 
     int64_t chunk = desc->chunk_elems != 0 ? desc->chunk_elems : auto_chunk(sizes, tile);
-    // one-pass scaled state (only when asked: measured slower than two
-    // passes on MI355X) takes records of whole one-pass tiles
+    // one-pass scaled state (only when asked: two passes, which depend on
+    // nothing being resident, are the default) takes records of whole
+    // one-pass tiles
     const bool want_one = scaled && desc->scaled_passes == 1;
     if (want_one && desc->chunk_elems == 0) chunk = std::max<int64_t>(chunk, kOneTile);
     uint32_t shift = 0;
