@@ -363,6 +363,30 @@ __device__ __forceinline__ uint32_t narrow16(float x)
         return f16_bits_rne(x);
 }
 
+// bf16 bits of a float through gfx950's float -> bf16 conversion
+// instruction: the same bits as bf16_bits_rne for every float, NaN payloads
+// included (compared over all 2^32 inputs on the GPU), in one instruction
+// where the integer form takes five.  The one-pass scaled kernel stores
+// with it (1% faster there); the two-pass store pass measured 3% slower
+// with it and keeps the integer form.  The empty register constraint keeps
+// the compiler from folding the producing operation into the conversion.
+__device__ __forceinline__ uint32_t bf16_bits_hw(float x)
+{
+    asm("" : "+v"(x));
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// narrow16 with the bf16 conversion instruction (same bits).
+template <int T>
+__device__ __forceinline__ uint32_t narrow16_hw(float x)
+{
+    static_assert(T == kBF16 || T == kF16, "16-bit type");
+    if constexpr (T == kBF16)
+        return bf16_bits_hw(x);
+    else
+        return f16_bits_rne(x);
+}
+
 // Remainder encoding.  The fp32 master word is the bf16 half shifted up plus
 // the sign-extended int16 remainder (mod 2^32): a negative remainder borrows
 // one from the bf16 half, which is how the stored bf16 was rounded up.
@@ -1213,10 +1237,10 @@ __device__ __forceinline__ void one_element(const WorkItem &w, int i, const Coef
 template <class S>
 __device__ __forceinline__ void one_store_element(const WorkItem &w, int i, const float *r, float P, float M, float V)
 {
-    store_one<uint16_t>(w.p, i, uint16_t(narrow16<S::st>(P * r[0])));
-    store_one<uint16_t>(w.m, i, uint16_t(narrow16<S::st>(M * r[1])));
-    store_one<uint16_t>(w.v, i, uint16_t(narrow16<S::st>(V * r[2])));
-    if constexpr (S::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(narrow16<S::ot>(P)));
+    store_one<uint16_t>(w.p, i, uint16_t(narrow16_hw<S::st>(P * r[0])));
+    store_one<uint16_t>(w.m, i, uint16_t(narrow16_hw<S::st>(M * r[1])));
+    store_one<uint16_t>(w.v, i, uint16_t(narrow16_hw<S::st>(V * r[2])));
+    if constexpr (S::ot != kNone) store_one<uint16_t>(w.p_out, i, uint16_t(narrow16_hw<S::ot>(P)));
 }
 
 // The lane's elements of a one-pass tile (start, n elements of record w).
@@ -1306,9 +1330,9 @@ __device__ __forceinline__ void one_store(const WorkItem &w, int start, int n, c
                 uint32_t hp[kLane], hm[kLane], hv[kLane];
 #pragma unroll
                 for (int e = 0; e < kLane; ++e) {
-                    hp[e] = narrow16<S::st>(x.P[j * kLane + e] * r[0]);
-                    hm[e] = narrow16<S::st>(x.M[j * kLane + e] * r[1]);
-                    hv[e] = narrow16<S::st>(x.V[j * kLane + e] * r[2]);
+                    hp[e] = narrow16_hw<S::st>(x.P[j * kLane + e] * r[0]);
+                    hm[e] = narrow16_hw<S::st>(x.M[j * kLane + e] * r[1]);
+                    hv[e] = narrow16_hw<S::st>(x.V[j * kLane + e] * r[2]);
                 }
                 const int gi = start / kLane + lg;
                 store_u16x4(w.p, gi, hp);
@@ -1317,7 +1341,7 @@ __device__ __forceinline__ void one_store(const WorkItem &w, int start, int n, c
                 if constexpr (S::ot != kNone) {
                     uint32_t o[kLane];
 #pragma unroll
-                    for (int e = 0; e < kLane; ++e) o[e] = narrow16<S::ot>(x.P[j * kLane + e]);
+                    for (int e = 0; e < kLane; ++e) o[e] = narrow16_hw<S::ot>(x.P[j * kLane + e]);
                     store_u16x4(w.p_out, gi, o);
                 }
             }
@@ -1584,9 +1608,9 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
 #pragma unroll
                 for (int e = 0; e < kLane; ++e) {
                     P[e] = keep[0][j * kLane + e][tid];
-                    hp[e] = narrow16<S::st>(P[e] * r[0]);
-                    hm[e] = narrow16<S::st>(keep[1][j * kLane + e][tid] * r[1]);
-                    hv[e] = narrow16<S::st>(keep[2][j * kLane + e][tid] * r[2]);
+                    hp[e] = narrow16_hw<S::st>(P[e] * r[0]);
+                    hm[e] = narrow16_hw<S::st>(keep[1][j * kLane + e][tid] * r[1]);
+                    hv[e] = narrow16_hw<S::st>(keep[2][j * kLane + e][tid] * r[2]);
                 }
                 const int gi = start / kLane + lg;
                 store_u16x4(w.p, gi, hp);
@@ -1595,7 +1619,7 @@ __global__ __launch_bounds__(kOneBlock) void adam_scaled_one(const WorkItem *__r
                 if constexpr (S::ot != kNone) {
                     uint32_t o[kLane];
 #pragma unroll
-                    for (int e = 0; e < kLane; ++e) o[e] = narrow16<S::ot>(P[e]);
+                    for (int e = 0; e < kLane; ++e) o[e] = narrow16_hw<S::ot>(P[e]);
                     store_u16x4(w.p_out, gi, o);
                 }
             }

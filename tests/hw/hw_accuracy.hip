@@ -4,8 +4,13 @@
 // both are within 2^-22 (relative) of the exact value for normal inputs,
 // that a subnormal input to the reciprocal gives +inf or an accurate value,
 // and that sqrt(0) = 0 and rcp(+inf) = 0.  The tests call hw_accuracy() and
-// check those assumptions on the device they run on.
+// check those assumptions on the device they run on.  bf16_conversion()
+// checks the other fact the kernels rely on: the float -> bf16 conversion
+// instruction, which the one-pass scaled kernel stores with, gives the bits
+// of round to nearest even for every float (NaN: sign and top payload kept,
+// made quiet).
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -66,7 +71,75 @@ __global__ void specials(float *o)
     }
 }
 
+constexpr uint32_t kBf16Blocks = 16384;
+constexpr uint32_t kPerBf16Block = uint32_t((uint64_t(1) << 32) / kBf16Blocks);
+
+// Block b covers the bit patterns [b * kPerBf16Block, (b + 1) * kPerBf16Block):
+// counts those whose conversion by the instruction differs from round to
+// nearest even (written out on the bits: add 0x7FFF plus the lowest kept
+// bit, keep the high half; a NaN keeps sign and top payload, quiet bit set),
+// and the smallest such pattern.
+__global__ __launch_bounds__(kThreads) void bf16_probe(uint32_t *count, uint32_t *first)
+{
+    uint32_t n = 0, lo = 0xFFFFFFFFu;
+    for (uint32_t i = threadIdx.x; i < kPerBf16Block; i += kThreads) {
+        const uint32_t u = blockIdx.x * kPerBf16Block + i;
+        float x = __uint_as_float(u);
+        asm("" : "+v"(x));
+        const uint32_t hw = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+        const uint32_t rne = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u >> 16) | 0x40u : (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+        if (hw != rne) {
+            ++n;
+            lo = min(lo, u);
+        }
+    }
+    __shared__ uint32_t sn[kThreads], sl[kThreads];
+    sn[threadIdx.x] = n;
+    sl[threadIdx.x] = lo;
+    __syncthreads();
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+        if (threadIdx.x < o) {
+            sn[threadIdx.x] += sn[threadIdx.x + o];
+            sl[threadIdx.x] = min(sl[threadIdx.x], sl[threadIdx.x + o]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        count[blockIdx.x] = sn[0];
+        first[blockIdx.x] = sl[0];
+    }
+}
+
 }  // namespace
+
+// *mismatches: floats whose bf16 conversion by the instruction differs from
+// round to nearest even, over all 2^32 bit patterns; *first: the smallest
+// such pattern (0xFFFFFFFF when there is none).  Returns 0, or -1 on a HIP
+// error.
+extern "C" int bf16_conversion(uint64_t *mismatches, uint32_t *first)
+{
+    uint32_t *d_count = nullptr, *d_first = nullptr;
+    int rc = -1;
+    if (hipMalloc(&d_count, sizeof(uint32_t) * kBf16Blocks) == hipSuccess &&
+        hipMalloc(&d_first, sizeof(uint32_t) * kBf16Blocks) == hipSuccess) {
+        hipLaunchKernelGGL(bf16_probe, dim3(kBf16Blocks), dim3(kThreads), 0, 0, d_count, d_first);
+        std::vector<uint32_t> count(kBf16Blocks), lo(kBf16Blocks);
+        if (hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess &&
+            hipMemcpy(count.data(), d_count, sizeof(uint32_t) * kBf16Blocks, hipMemcpyDeviceToHost) == hipSuccess &&
+            hipMemcpy(lo.data(), d_first, sizeof(uint32_t) * kBf16Blocks, hipMemcpyDeviceToHost) == hipSuccess) {
+            *mismatches = 0;
+            *first = 0xFFFFFFFFu;
+            for (uint32_t b = 0; b < kBf16Blocks; ++b) {
+                *mismatches += count[b];
+                *first = std::min(*first, lo[b]);
+            }
+            rc = 0;
+        }
+    }
+    (void)hipFree(d_count);
+    (void)hipFree(d_first);
+    return rc;
+}
 
 // per_exp_sqrt[e], per_exp_rcp[e] (e = biased exponent 0..254): largest
 // relative error over that binade (sqrt: inputs of that binade; rcp: inputs

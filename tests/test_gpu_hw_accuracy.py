@@ -4,7 +4,9 @@ the fp32 square root and reciprocal instructions are within 2^-23 (one
 ulp, half the 2^-22 the pass's error bound assumes) of the exact values for
 normal inputs (square root: every normal input; reciprocal: inputs below
 2^126, whose reciprocal is normal); a reciprocal of a subnormal input is
-+inf or accurate; sqrt(0) = 0 and rcp(+inf) = 0."""
++inf or accurate; sqrt(0) = 0 and rcp(+inf) = 0.  And the one the one-pass
+scaled kernel's stores rely on: the float -> bf16 conversion instruction
+rounds every float to nearest even, NaN payloads as the integer form."""
 import ctypes
 import os
 
@@ -56,3 +58,15 @@ def test_special_values(measured):
     assert sp[1] == 0.0
     assert np.isinf(sp[2]) and sp[2] > 0
     assert np.isinf(sp[3]) and sp[3] > 0
+
+
+def test_bf16_conversion_instruction_rounds_to_nearest_even():
+    from gpu_helpers import torch_mod
+
+    if not torch_mod().cuda.is_available():
+        pytest.skip("no GPU")
+    assert os.path.exists(LIB), "tests/hw/libhw_accuracy.so is not built (run __graft_entry__.build())"
+    lib = ctypes.CDLL(LIB)
+    mismatches, first = ctypes.c_uint64(0), ctypes.c_uint32(0)
+    assert lib.bf16_conversion(ctypes.byref(mismatches), ctypes.byref(first)) == 0
+    assert mismatches.value == 0, f"{mismatches.value} floats differ, first {first.value:#010x}"
